@@ -1,0 +1,230 @@
+"""Plain float64 MLA decode (test infrastructure only; see the package docstring).
+
+Readings of the pages used here (the pages fix none of these numbers; the
+workload descriptions do, and where both are silent the plainest reading is
+taken):
+  * one latent row of 576 values per cached token, shared by all heads; the key
+    is the whole row, the value is its first 512 entries (the absorbed form of
+    MLA that the pages switch on with matrix absorption for DeepSeek decode --
+    mhpq.cn article on PaddleNLP inference flags, section on speculative
+    decoding parameters);
+  * q_len > 1 query tokens per sequence (PaddleNLP issue #10157, MLA operator
+    overview: decode with more than one token per request; MTP section: the
+    verification batch keeps its size). Query i of s sees keys j <= L - s + i;
+  * pages of 64 tokens reached through a block table;
+  * LSE is the natural-log log-sum-exp of the scaled scores;
+  * a row with no visible key gives O = 0 and LSE = -inf.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+PAGE_TOKENS = 64
+D_QK = 576
+D_V = 512
+
+
+# --------------------------------------------------------------------------
+# Storage formats, decoded exactly to float64.
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64. A bf16 value is the top half of a float32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):      # NaN patterns stay NaN
+        return u.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_value(code: int) -> float:
+    """Value of one OCP FP8 E4M3FN code, from the format definition.
+
+    sign 1 bit, exponent 4 bits (bias 7), mantissa 3 bits. Exponent field 0
+    encodes subnormals m/8 * 2^-6. S.1111.111 is NaN; there is no infinity, so
+    S.1111.110 = 448 is the largest finite magnitude.
+    """
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return math.nan
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** -6
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+E4M3FN_TABLE = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
+    return E4M3FN_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+# --------------------------------------------------------------------------
+# Paged gather and the causal rule.
+# --------------------------------------------------------------------------
+
+def sequence_rows(cache: np.ndarray, block_table_row: np.ndarray, n: int,
+                  kv_dtype: str = "bf16", kv_scale: np.ndarray | None = None) -> np.ndarray:
+    """The first n latent rows of one sequence, float64 [n, 576].
+
+    Token j lives in page block_table_row[j // 64], slot j % 64. For the fp8
+    cache the row is the decoded code times that token's fp32 scale (the
+    product is exact in float64).
+    """
+    j = np.arange(n)
+    pages = np.asarray(block_table_row)[j // PAGE_TOKENS].astype(np.int64)
+    slots = j % PAGE_TOKENS
+    raw = cache[pages, slots]
+    if kv_dtype == "bf16":
+        return bf16_bits_to_f64(raw)
+    if kv_dtype == "fp8_e4m3":
+        return decode_e4m3fn(raw) * kv_scale[pages, slots].astype(np.float64)[:, None]
+    raise ValueError(kv_dtype)
+
+
+def visible_counts(seqlen: int, q_len: int, num_heads: int) -> np.ndarray:
+    """Keys visible to each of the q_len*num_heads rows (row = i*H + h).
+
+    Query i sees keys 0 .. L - s + i, i.e. L - s + i + 1 keys, clipped to
+    [0, L]; every head of one query token sees the same keys.
+    """
+    i = np.arange(q_len * num_heads) // num_heads
+    return np.clip(seqlen - q_len + i + 1, 0, seqlen).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Attention, plain definition.
+# --------------------------------------------------------------------------
+
+def attend(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+           visible: np.ndarray):
+    """O[r] = sum_j p_rj V_j, LSE[r] = log sum_j exp(z_rj) over j < visible[r].
+
+    z = scale * q_r . K_j; p_r = softmax of z_r over the visible keys. The full
+    score matrix [R, n] is materialised. Returns (O [R, Dv], lse [R]) float64.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    R, n = q_rows.shape[0], K.shape[0]
+    O = np.zeros((R, V.shape[1]), dtype=np.float64)
+    lse = np.full(R, -np.inf, dtype=np.float64)
+    if n == 0:
+        return O, lse
+    Z = float(scale) * (q_rows @ K.T)
+    mask = np.arange(n)[None, :] < np.asarray(visible)[:, None]
+    Z = np.where(mask, Z, -np.inf)
+    live = np.asarray(visible) > 0
+    if not live.any():
+        return O, lse
+    Zl = Z[live]
+    m = Zl.max(axis=1)
+    E = np.exp(Zl - m[:, None])
+    l = E.sum(axis=1)
+    P = E / l[:, None]
+    O[live] = P @ V
+    lse[live] = m + np.log(l)
+    return O, lse
+
+
+def attend_partials(q_rows, K, V, scale, visible, cuts):
+    """Attention restricted to key chunks [cuts[k], cuts[k+1]), one partial each.
+
+    Each partial is (O_k, LSE_k) of the keys in the chunk that are visible to
+    the row; a chunk with no visible key gives O_k = 0, LSE_k = -inf.
+    """
+    parts = []
+    visible = np.asarray(visible)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        vis = np.clip(visible - a, 0, b - a)
+        parts.append(attend(q_rows, K[a:b], V[a:b], scale, vis))
+    return parts
+
+
+def lse_merge(outs, lses):
+    """Merge partials of disjoint key sets.
+
+    LSE = M + log sum_k exp(LSE_k - M), M = max_k LSE_k;
+    O = sum_k exp(LSE_k - LSE) O_k. Partials with LSE_k = -inf weigh 0; if all
+    are -inf the result is O = 0, LSE = -inf.
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    M = lses.max(axis=0)
+    finite = np.isfinite(M)
+    Ms = np.where(finite, M, 0.0)
+    w = np.where(np.isfinite(lses), np.exp(lses - Ms[None]), 0.0)
+    tot = w.sum(axis=0)
+    lse = np.where(finite, Ms + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    coef = np.where(finite[None], w / np.where(finite, tot, 1.0)[None], 0.0)
+    O = np.einsum("kr,krd->rd", coef, outs)
+    return O, lse
+
+
+def mla_decode_sequence(q_bits_b, cache, block_table_row, seqlen, softmax_scale,
+                        kv_dtype="bf16", kv_scale=None):
+    """One sequence: q_bits_b uint16 [s, H, 576] -> (O [s, H, 512], lse [s, H])."""
+    s, H, _ = q_bits_b.shape
+    q_rows = bf16_bits_to_f64(q_bits_b).reshape(s * H, D_QK)
+    L = int(seqlen)
+    rows = sequence_rows(cache, block_table_row, L, kv_dtype, kv_scale)
+    O, lse = attend(q_rows, rows, rows[:, :D_V], softmax_scale, visible_counts(L, s, H))
+    return O.reshape(s, H, D_V), lse.reshape(s, H)
+
+
+def mla_decode(q_bits, cache, block_table, seqlens, softmax_scale, kv_dtype="bf16",
+               kv_scale=None, batch_indices=None):
+    """Whole batch (or the listed sequences): out [B, s, H, 512], lse [B, s, H] float64."""
+    B, s, H, _ = q_bits.shape
+    idx = range(B) if batch_indices is None else list(batch_indices)
+    out = np.zeros((len(idx), s, H, D_V), dtype=np.float64)
+    lse = np.zeros((len(idx), s, H), dtype=np.float64)
+    for k, b in enumerate(idx):
+        out[k], lse[k] = mla_decode_sequence(q_bits[b], cache, block_table[b], seqlens[b],
+                                              softmax_scale, kv_dtype, kv_scale)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# Split-KV schedule (integer work; the GPU scheduler must match it exactly).
+# --------------------------------------------------------------------------
+
+def split_schedule(seqlens, num_units, min_tiles_per_unit=8):
+    """Cut the flattened (sequence, 64-token tile) space into contiguous units.
+
+    T_b = ceil(L_b / 64) tiles per sequence, prefix[b] = sum of T before b,
+    T = prefix[B]. Every unit covers the same number of tiles,
+    payload = max(ceil(T / num_units), min_tiles_per_unit) (at least 1), so
+    unit u covers flattened tiles [u*payload, min((u+1)*payload, T)). A
+    sequence whose tiles fall in k units is split into k partials; the piece in
+    unit u is split number u - floor(prefix[b] / payload). A sequence with no
+    tiles has 0 partials.
+
+    Returns a dict of plain Python ints/lists:
+      payload, units_used (units with at least one tile), prefix [B+1],
+      num_splits [B], split_offset [B+1] (cumulative), total_partials.
+    """
+    L = [int(x) for x in seqlens]
+    T_b = [(x + PAGE_TOKENS - 1) // PAGE_TOKENS for x in L]
+    prefix = [0]
+    for t in T_b:
+        prefix.append(prefix[-1] + t)
+    T = prefix[-1]
+    units = max(int(num_units), 1)
+    payload = max(-(-T // units), int(min_tiles_per_unit), 1)
+    num_splits = []
+    for b, t in enumerate(T_b):
+        if t == 0:
+            num_splits.append(0)
+        else:
+            first = prefix[b] // payload
+            last = (prefix[b] + t - 1) // payload
+            num_splits.append(last - first + 1)
+    split_offset = [0]
+    for k in num_splits:
+        split_offset.append(split_offset[-1] + k)
+    return dict(payload=payload, units_used=-(-T // payload) if T else 0, prefix=prefix,
+                num_splits=num_splits, split_offset=split_offset,
+                total_partials=split_offset[-1])

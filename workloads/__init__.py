@@ -1,0 +1,217 @@
+"""Seeded synthetic inputs for MLA decode over a paged latent KV cache.
+
+This module only draws random numbers and lays out storage: it rounds draws to
+the storage formats (bf16 bit patterns; OCP FP8 E4M3FN codes with one fp32
+scale per token), builds the page pool and the block table, and poisons unused
+page slots. It holds none of the attention arithmetic. Both the CPU oracle and
+the GPU path consume exactly the bytes it returns.
+
+Shapes (all row-major, contiguous):
+  q_bits       uint16 [B, s, H, 576]   bf16 bit patterns (512 latent + 64 rope)
+  cache        uint16 [P, 64, 576]     bf16 bit patterns, or
+               uint8  [P, 64, 576]     E4M3FN codes
+  kv_scale     float32 [P, 64]         per-token dequant scale (fp8 only)
+  block_table  int32  [B, max_pages]   page ids, -1 past each sequence's pages
+  seqlens      int32  [B]
+
+Draw order for one workload (one numpy PCG64 stream): sequence lengths, the
+page permutation, q, then the latent cache page by page.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+PAGE_TOKENS = 64
+D_QK = 576      # latent (512) + rope (64)
+D_V = 512
+D_ROPE = 64
+E4M3_MAX = 448.0
+BF16_NAN = 0x7FC0
+E4M3_NAN = 0x7F
+DEFAULT_SCALE = 1.0 / math.sqrt(192.0)
+
+
+@dataclass
+class Workload:
+    name: str
+    q_bits: np.ndarray
+    cache: np.ndarray
+    kv_scale: Optional[np.ndarray]
+    block_table: np.ndarray
+    seqlens: np.ndarray
+    softmax_scale: float
+    kv_dtype: str                      # "bf16" or "fp8_e4m3"
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self):
+        return int(self.q_bits.shape[0])
+
+    @property
+    def q_len(self):
+        return int(self.q_bits.shape[1])
+
+    @property
+    def num_heads(self):
+        return int(self.q_bits.shape[2])
+
+    @property
+    def num_pages(self):
+        return int(self.cache.shape[0])
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (round to nearest, ties to even); finite inputs."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def _e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3FN codes, round to nearest even, |x| <= 448 assumed."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def pages_for(seqlens: np.ndarray) -> np.ndarray:
+    return (np.asarray(seqlens, dtype=np.int64) + PAGE_TOKENS - 1) // PAGE_TOKENS
+
+
+def make_workload(name: str, batch: int, num_heads: int, q_len: int, seqlens,
+                  kv_dtype: str = "bf16", seed: int = 0, table: str = "shuffled",
+                  softmax_scale: float = DEFAULT_SCALE, poison_tail: bool = True,
+                  rng: Optional[np.random.Generator] = None,
+                  page_chunk: int = 512) -> Workload:
+    """Build one workload. `seqlens` is an int array or a callable(rng) -> array.
+
+    table: "identity" (pages laid out in (sequence, tile) order) or "shuffled"
+    (a random permutation of the pool assigned in (sequence, tile) order).
+    """
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
+    if callable(seqlens):
+        seqlens = seqlens(rng)
+    seqlens = np.asarray(seqlens, dtype=np.int32).reshape(batch)
+    npg = pages_for(seqlens)
+    total_pages = int(npg.sum())
+    max_pages = max(int(npg.max()) if batch else 0, 1)
+    if table == "identity":
+        perm = np.arange(total_pages, dtype=np.int64)
+    elif table == "shuffled":
+        perm = rng.permutation(total_pages)
+    else:
+        raise ValueError(table)
+    block_table = np.full((batch, max_pages), -1, dtype=np.int32)
+    pos = 0
+    for b in range(batch):
+        n = int(npg[b])
+        block_table[b, :n] = perm[pos:pos + n]
+        pos += n
+
+    q32 = rng.standard_normal((batch, q_len, num_heads, D_QK), dtype=np.float32)
+    q_bits = f32_to_bf16_bits(q32)
+    del q32
+
+    P = max(total_pages, 1)
+    if kv_dtype == "bf16":
+        cache = np.zeros((P, PAGE_TOKENS, D_QK), dtype=np.uint16)
+        kv_scale = None
+    elif kv_dtype == "fp8_e4m3":
+        cache = np.zeros((P, PAGE_TOKENS, D_QK), dtype=np.uint8)
+        kv_scale = np.ones((P, PAGE_TOKENS), dtype=np.float32)
+    else:
+        raise ValueError(kv_dtype)
+    for p0 in range(0, total_pages, page_chunk):
+        p1 = min(total_pages, p0 + page_chunk)
+        x = rng.standard_normal((p1 - p0, PAGE_TOKENS, D_QK), dtype=np.float32)
+        if kv_dtype == "bf16":
+            cache[p0:p1] = f32_to_bf16_bits(x)
+        else:
+            # one scale per token: absmax over its 576 dims / 448; an all-zero
+            # token keeps scale 1 (any scale encodes it as zero codes)
+            amax = np.abs(x).max(axis=2)
+            sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+            y = np.clip(x / sc[:, :, None], -E4M3_MAX, E4M3_MAX)
+            cache[p0:p1] = _e4m3_encode(y)
+            kv_scale[p0:p1] = sc
+        del x
+
+    if poison_tail:
+        # slots past L_b on each sequence's last page hold NaN: a correct
+        # kernel never lets them reach the output
+        for b in range(batch):
+            L = int(seqlens[b])
+            if L % PAGE_TOKENS:
+                last = block_table[b, L // PAGE_TOKENS]
+                cache[last, L % PAGE_TOKENS:, :] = BF16_NAN if kv_dtype == "bf16" else E4M3_NAN
+                if kv_scale is not None:
+                    kv_scale[last, L % PAGE_TOKENS:] = np.nan
+
+    return Workload(name=name, q_bits=q_bits, cache=cache, kv_scale=kv_scale,
+                    block_table=block_table, seqlens=seqlens,
+                    softmax_scale=float(softmax_scale), kv_dtype=kv_dtype,
+                    meta={"seed": seed, "table": table, "total_pages": total_pages})
+
+
+# ---------------------------------------------------------------------------
+# The five workloads the measurements are quoted on, and scaled-down variants
+# with the same structure for parity tests the CPU oracle finishes in seconds.
+# ---------------------------------------------------------------------------
+
+def _uniform_lengths(lo, hi, n):
+    return lambda rng: rng.integers(lo, hi + 1, size=n, dtype=np.int64).astype(np.int32)
+
+
+def _ragged_lengths(n_short, lo, hi, long_len):
+    def draw(rng):
+        u = rng.uniform(math.log(lo), math.log(hi), size=n_short)
+        short = np.floor(np.exp(u)).astype(np.int64)
+        idx = int(rng.integers(0, n_short + 1))
+        out = np.insert(short, idx, long_len)
+        return out.astype(np.int32)
+    return draw
+
+
+CONFIGS = {
+    # name: (batch, heads, q_len, seqlens, kv dtype, table)
+    "tiny": dict(batch=1, num_heads=16, q_len=1, seqlens=[256], kv_dtype="bf16", table="identity"),
+    "share16": dict(batch=64, num_heads=16, q_len=1, seqlens=_uniform_lengths(1024, 4096, 64),
+                    kv_dtype="bf16", table="shuffled"),
+    "mtp": dict(batch=128, num_heads=128, q_len=2, seqlens=[4096] * 128, kv_dtype="bf16", table="shuffled"),
+    "ragged": dict(batch=32, num_heads=128, q_len=1, seqlens=_ragged_lengths(31, 512, 16384, 65536),
+                   kv_dtype="bf16", table="shuffled"),
+    "fp8": dict(batch=128, num_heads=128, q_len=2, seqlens=[8192] * 128, kv_dtype="fp8_e4m3",
+                table="shuffled"),
+}
+
+CONFIG_TEXT = {
+    "tiny": "batch 1, H=16, q_len=1, seqlen 256, bf16, identity block table",
+    "share16": "batch 64, H=16, q_len=1, seqlens U[1024,4096], bf16, permuted block table",
+    "mtp": "batch 128, H=128, q_len=2 causal, seqlen 4096, bf16, shuffled block table",
+    "ragged": "batch 32, H=128, q_len=1, 31 log-uniform seqlens in [512,16384] + one 65536, bf16",
+    "fp8": "batch 128, H=128, q_len=2 causal, seqlen 8192, fp8 e4m3 cache + per-token fp32 scale",
+}
+
+# Same structure, fewer sequences / shorter contexts.
+SMALL = {
+    "tiny": dict(CONFIGS["tiny"]),
+    "share16": dict(batch=6, num_heads=16, q_len=1, seqlens=_uniform_lengths(1024, 4096, 6),
+                    kv_dtype="bf16", table="shuffled"),
+    "mtp": dict(batch=3, num_heads=128, q_len=2, seqlens=[4096, 1000, 130], kv_dtype="bf16",
+                table="shuffled"),
+    "ragged": dict(batch=5, num_heads=128, q_len=1, seqlens=_ragged_lengths(4, 512, 4000, 16384),
+                   kv_dtype="bf16", table="shuffled"),
+    "fp8": dict(batch=3, num_heads=128, q_len=2, seqlens=[8192, 777, 65], kv_dtype="fp8_e4m3",
+                table="shuffled"),
+}
+
+
+def config(name: str, seed: int = 0, small: bool = False, **overrides) -> Workload:
+    spec = dict((SMALL if small else CONFIGS)[name])
+    spec.update(overrides)
+    return make_workload(name + ("-small" if small else ""), seed=seed, **spec)
