@@ -1,0 +1,172 @@
+/*
+ * mla_decode.h -- C ABI of libmla_decode.so: Multi-head Latent Attention (MLA)
+ * decode over a paged latent KV cache, hand-written HIP kernels for gfx950
+ * (MI355X).
+ *
+ * What is computed (PaddleNLP issue #10157, "Multi-head Latent Attention (MLA)
+ * operator", overview: one MLA pass is data load, QK GEMM, softmax update and
+ * PV GEMM, adapted to decode with more than one token per request; its MTP
+ * section: q_len > 1 verification at the original batch size):
+ *
+ *   for every sequence b, query token i < q_len, head h < num_heads:
+ *     n      = clamp(L_b - q_len + i + 1, 0, L_b)      (causal rule)
+ *     z_j    = softmax_scale * dot(q[b,i,h,0:576], K_j)     j < n
+ *     out[b,i,h,:] = sum_j softmax(z)_j * V_j            V_j = K_j[0:512]
+ *     lse[b,i,h]   = ln sum_j exp(z_j)                   (natural log)
+ *   K_j is the 576-value latent row of token j (512 latent + 64 rope), shared
+ *   by all heads; token j lives in page block_table[b][j / 64], slot j % 64.
+ *   A row with n == 0 gets out = 0, lse = -inf.
+ *   For the fp8 cache K_j = kv_scale[page][slot] * e4m3(code) (OCP E4M3FN).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument documented "device" is a device address on the
+ *     current HIP device; the caller allocates, owns and frees all memory.
+ *     The library allocates nothing and keeps no device state across calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it: no host synchronisation, no allocation.
+ *   - Tensors are dense row-major (C order) with the shapes given.
+ *   - Argument checking is host-side only (the library never reads device
+ *     memory on the host). Checks run before any HIP call, so errors in
+ *     arguments are reported even on a machine without a GPU.
+ *   - Return value: an mla_status_t (as int). On failure mla_last_error()
+ *     returns a thread-local message. Nothing is thrown or aborted across
+ *     the ABI.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+#define MLA_PAGE_TOKENS 64   /* tokens per cache page */
+#define MLA_D_QK 576         /* query / latent row width: 512 latent + 64 rope */
+#define MLA_D_V 512          /* value width: the first 512 entries of the row */
+#define MLA_MAX_ROWS 4096    /* q_len * num_heads limit per sequence */
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,  /* NULL pointer, bad size, misaligned base pointer */
+  MLA_ERR_UNSUPPORTED = 2,  /* dtype or device not supported (needs gfx950) */
+  MLA_ERR_WORKSPACE = 3,    /* metadata or workspace buffer too small */
+  MLA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} mla_status_t;
+
+typedef enum {
+  MLA_KV_BF16 = 0,          /* cache holds bf16 values */
+  MLA_KV_FP8_E4M3 = 1       /* cache holds OCP E4M3FN codes + fp32 per-token scale */
+} mla_kv_dtype_t;
+
+/* Library ABI version (MLA_ABI_VERSION of the build). */
+int mla_abi_version(void);
+
+/* Static string naming a status code. */
+const char* mla_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/*
+ * Split-KV planning (host only, no device access).
+ *
+ * The split schedule cuts the flattened (sequence, 64-token tile) space into
+ * `num_units` contiguous work units of equal tile count (FlashDecoding-style
+ * splitting of the cache, named among the attention features in PaddleNLP
+ * issue #10157's overview; the cache is cut into partitions that are merged
+ * afterwards in the Append Attention flags of the mhpq.cn article on PaddleNLP
+ * inference flags). With T_b = ceil(L_b/64) and T = sum T_b:
+ *   payload = max(ceil(T / num_units), min_tiles_per_unit, 1)
+ *   unit u covers flattened tiles [u*payload, min((u+1)*payload, T)).
+ * A sequence touched by k > 1 units is computed as k partials and merged.
+ *
+ * mla_default_num_units: a unit count that fills the current device for this
+ *   shape (0 if the device cannot be queried).
+ * mla_metadata_bytes: size of the metadata buffer for (batch, num_units).
+ * mla_workspace_bytes: size of the partials workspace for the shape:
+ *   (batch + num_units) * q_len * num_heads * (512 + 1) * 4 bytes, rounded up.
+ */
+int mla_default_num_units(int batch, int q_len, int num_heads);
+size_t mla_metadata_bytes(int batch, int num_units);
+size_t mla_workspace_bytes(int batch, int q_len, int num_heads, int num_units);
+
+/*
+ * mla_get_split_metadata: build the split schedule on the device.
+ *   cache_seqlens  device int32 [batch], L_b >= 0 (negative values count as 0)
+ *   batch          >= 1
+ *   num_units      >= 1, the number of work units (see above)
+ *   min_tiles_per_unit  >= 0; 0 selects the default (8)
+ *   metadata       device buffer of >= mla_metadata_bytes(batch, num_units)
+ *                  bytes, 4-byte aligned; fully written by this call
+ *   stream         hipStream_t
+ * One small kernel, stream-ordered. Reuse the metadata for every layer of a
+ * decode step that has the same cache_seqlens.
+ */
+int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int num_units,
+                           int min_tiles_per_unit, void* metadata, size_t metadata_bytes,
+                           void* stream);
+
+/*
+ * mla_decode_fwd: the decode attention (data load, QK GEMM, online softmax,
+ * PV GEMM) and, when split, the LSE merge of the partials.
+ *   q              device bf16 [batch, q_len, num_heads, 576], 16-byte aligned
+ *   kv_cache       device [num_pages, 64, 576] of bf16 (MLA_KV_BF16) or E4M3FN
+ *                  bytes (MLA_KV_FP8_E4M3), 16-byte aligned
+ *   kv_scale       device fp32 [num_pages, 64], one scale per token; required
+ *                  for MLA_KV_FP8_E4M3, ignored (may be NULL) for bf16
+ *   kv_dtype       mla_kv_dtype_t
+ *   num_pages      pages in the pool (>= 1)
+ *   block_table    device int32 [batch, max_pages_per_seq]; entries
+ *                  [0, ceil(L_b/64)) of row b must be valid page ids < num_pages;
+ *                  later entries are never read
+ *   max_pages_per_seq  row stride of block_table (>= 1)
+ *   cache_seqlens  device int32 [batch]; caller contract:
+ *                  ceil(L_b/64) <= max_pages_per_seq
+ *   batch, q_len, num_heads   >= 1; q_len * num_heads <= MLA_MAX_ROWS
+ *   softmax_scale  finite
+ *   out            device fp32 [batch, q_len, num_heads, 512], 16-byte aligned
+ *   lse            device fp32 [batch, q_len, num_heads], 4-byte aligned
+ *   metadata       NULL: one work unit per sequence, no partials, no merge
+ *                  (workspace unused). Otherwise the buffer written by
+ *                  mla_get_split_metadata for the same cache_seqlens, batch
+ *                  and num_units.
+ *   num_units      the value given to mla_get_split_metadata (ignored if
+ *                  metadata is NULL)
+ *   workspace      device buffer of >= mla_workspace_bytes(batch, q_len,
+ *                  num_heads, num_units) bytes, 16-byte aligned (split only)
+ *   stream         hipStream_t
+ * Slots of a sequence's last page past L_b may hold any bytes (NaN included):
+ * they never reach the outputs. Results are bitwise reproducible for a fixed
+ * schedule (no atomics on the output path).
+ */
+int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                   int num_pages, const int32_t* block_table, int max_pages_per_seq,
+                   const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
+                   float softmax_scale, float* out, float* lse,
+                   const void* metadata, int num_units, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * mla_combine: merge per-sequence partials by their log-sum-exp.
+ *   part_out        device fp32 [num_partials, rows_per_seq, 512], 16-byte aligned
+ *   part_lse        device fp32 [num_partials, rows_per_seq] (natural log)
+ *   seq_part_offsets device int32 [batch + 1], non-decreasing; sequence b owns
+ *                   partials [off[b], off[b+1])
+ *   batch, rows_per_seq  >= 1; rows_per_seq <= MLA_MAX_ROWS
+ *   out             device fp32 [batch, rows_per_seq, 512], 16-byte aligned
+ *   lse             device fp32 [batch, rows_per_seq]
+ * Per row: M = max_k lse_k; lse = M + ln sum_k exp(lse_k - M);
+ * out = sum_k exp(lse_k - lse) * part_out_k. Partials with lse_k = -inf weigh
+ * 0; a sequence with no partial (or only -inf ones) gets out = 0, lse = -inf.
+ */
+int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq_part_offsets,
+                int batch, int rows_per_seq, float* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,213 @@
+"""MLA decode over a paged latent KV cache on MI355X (gfx950).
+
+Thin Python binding of libmla_decode.so (C ABI in include/mla_decode.h):
+argument checking of tensor types/shapes and marshalling of device pointers
+and the current HIP stream. Every step of the computation runs in the HIP
+kernels of the library; there is no fallback: if the library is not built or
+cannot be loaded, every call raises.
+
+    plan = get_split_metadata(cache_seqlens, q_len, num_heads)     # once per step
+    out, lse = decode(q, kv_cache, block_table, cache_seqlens, scale, plan=plan)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = ["load_library", "library_path", "abi_version", "default_num_units", "metadata_bytes",
+           "workspace_bytes", "SplitPlan", "get_split_metadata", "decode", "combine",
+           "MLAError", "KV_BF16", "KV_FP8_E4M3", "PAGE_TOKENS", "D_QK", "D_V"]
+
+PAGE_TOKENS = 64
+D_QK = 576
+D_V = 512
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+_LIB_NAME = "libmla_decode.so"
+_lib = None
+
+
+class MLAError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+
+
+def load_library():
+    """Load libmla_decode.so (built in-tree by mla_decode_attention_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise MLAError(f"{path} is missing: build it with `python -m mla_decode_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    c_int, c_size, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    sigs = {
+        "mla_abi_version": (c_int, []),
+        "mla_status_string": (ctypes.c_char_p, [c_int]),
+        "mla_last_error": (ctypes.c_char_p, []),
+        "mla_default_num_units": (c_int, [c_int, c_int, c_int]),
+        "mla_metadata_bytes": (c_size, [c_int, c_int]),
+        "mla_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int]),
+        "mla_get_split_metadata": (c_int, [vp, c_int, c_int, c_int, vp, c_size, vp]),
+        "mla_decode_fwd": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
+                                   ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
+        "mla_combine": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        lib = load_library()
+        raise MLAError(f"{what}: {lib.mla_status_string(status).decode()}: "
+                       f"{lib.mla_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def abi_version() -> int:
+    return load_library().mla_abi_version()
+
+
+def default_num_units(batch: int, q_len: int, num_heads: int) -> int:
+    return load_library().mla_default_num_units(batch, q_len, num_heads)
+
+
+def metadata_bytes(batch: int, num_units: int) -> int:
+    return load_library().mla_metadata_bytes(batch, num_units)
+
+
+def workspace_bytes(batch: int, q_len: int, num_heads: int, num_units: int) -> int:
+    return load_library().mla_workspace_bytes(batch, q_len, num_heads, num_units)
+
+
+@dataclass
+class SplitPlan:
+    """Split schedule on the device plus the partials workspace it needs."""
+    metadata: torch.Tensor     # int32, device
+    num_units: int
+    batch: int
+    q_len: int
+    num_heads: int
+    workspace: torch.Tensor    # uint8, device
+
+
+def get_split_metadata(cache_seqlens: torch.Tensor, q_len: int, num_heads: int,
+                       num_units: Optional[int] = None, min_tiles_per_unit: int = 0,
+                       metadata: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> SplitPlan:
+    """Build the split-KV schedule for one decode step (reusable across layers)."""
+    lib = load_library()
+    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    batch = cache_seqlens.shape[0]
+    if num_units is None:
+        num_units = lib.mla_default_num_units(batch, q_len, num_heads)
+        if num_units < 1:
+            raise MLAError(f"mla_default_num_units failed: {lib.mla_last_error().decode()}")
+    nbytes = lib.mla_metadata_bytes(batch, num_units)
+    if metadata is None:
+        metadata = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=cache_seqlens.device)
+    wbytes = lib.mla_workspace_bytes(batch, q_len, num_heads, num_units)
+    if workspace is None:
+        workspace = torch.empty(wbytes, dtype=torch.uint8, device=cache_seqlens.device)
+    _check(lib.mla_get_split_metadata(_ptr(cache_seqlens), batch, num_units, min_tiles_per_unit,
+                                      _ptr(metadata), metadata.numel() * 4, _stream()),
+           "mla_get_split_metadata")
+    return SplitPlan(metadata, num_units, batch, q_len, num_heads, workspace)
+
+
+def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+           cache_seqlens: torch.Tensor, softmax_scale: float, kv_scale: Optional[torch.Tensor] = None,
+           plan: Optional[SplitPlan] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None):
+    """MLA decode attention. Returns (out fp32 [B,s,H,512], lse fp32 [B,s,H]).
+
+    q bf16 [B, s, H, 576]; kv_cache [P, 64, 576] bf16 (or uint8 / float8_e4m3fn
+    codes with kv_scale fp32 [P, 64]); block_table int32 [B, max_pages];
+    cache_seqlens int32 [B]. plan=None runs one work unit per sequence.
+    """
+    lib = load_library()
+    _need(q, "q", (torch.bfloat16,), 4)
+    B, s, H, d = q.shape
+    if d != D_QK:
+        raise ValueError(f"q last dim must be {D_QK}")
+    fp8_types = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+    _need(kv_cache, "kv_cache", (torch.bfloat16,) + fp8_types, 3)
+    if tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_QK):
+        raise ValueError(f"kv_cache must be [pages, {PAGE_TOKENS}, {D_QK}]")
+    kv_dtype = KV_BF16 if kv_cache.dtype == torch.bfloat16 else KV_FP8_E4M3
+    if kv_dtype == KV_FP8_E4M3:
+        if kv_scale is None:
+            raise ValueError("fp8 cache needs kv_scale")
+        _need(kv_scale, "kv_scale", (torch.float32,), 2)
+    _need(block_table, "block_table", (torch.int32,), 2)
+    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    if out is None:
+        out = torch.empty((B, s, H, D_V), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, s, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 4)
+    _need(lse, "lse", (torch.float32,), 3)
+    md = ws = None
+    units, wbytes = 0, 0
+    if plan is not None:
+        if (plan.batch, plan.q_len, plan.num_heads) != (B, s, H):
+            raise ValueError("plan was built for another shape")
+        md, ws, units, wbytes = plan.metadata, plan.workspace, plan.num_units, plan.workspace.numel()
+    _check(lib.mla_decode_fwd(_ptr(q), _ptr(kv_cache), _ptr(kv_scale), kv_dtype, kv_cache.shape[0],
+                              _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), B, s, H,
+                              float(softmax_scale), _ptr(out), _ptr(lse), _ptr(md), units, _ptr(ws),
+                              wbytes, _stream()), "mla_decode_fwd")
+    return out, lse
+
+
+def combine(part_out: torch.Tensor, part_lse: torch.Tensor, seq_part_offsets: torch.Tensor,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """LSE-merge partials: part_out [N, R, 512], part_lse [N, R], offsets int32 [B+1]."""
+    lib = load_library()
+    _need(part_out, "part_out", (torch.float32,), 3)
+    _need(part_lse, "part_lse", (torch.float32,), 2)
+    _need(seq_part_offsets, "seq_part_offsets", (torch.int32,), 1)
+    R = part_out.shape[1]
+    B = seq_part_offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty((B, R, D_V), dtype=torch.float32, device=part_out.device)
+    if lse is None:
+        lse = torch.empty((B, R), dtype=torch.float32, device=part_out.device)
+    _check(lib.mla_combine(_ptr(part_out), _ptr(part_lse), _ptr(seq_part_offsets), B, R, _ptr(out),
+                           _ptr(lse), _stream()), "mla_combine")
+    return out, lse

@@ -1,0 +1,227 @@
+// C ABI of libmla_decode.so (declared in include/mla_decode.h): host-side
+// argument checks, split planning and kernel launches. No device memory is
+// read or allocated here.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "mla_decode.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Device facts, queried once per device.
+struct DevInfo {
+  int checked = 0;
+  int supported = 0;
+  int cus = 0;
+  char arch[64] = "";
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+int device_info(DevInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MLA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    strncpy(d.arch, prop.gcnArchName, sizeof(d.arch) - 1);
+    d.supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.checked = 1;
+  }
+  *out = d;
+  if (!d.supported) return fail(MLA_ERR_UNSUPPORTED, "device arch %s is not gfx950", d.arch);
+  return MLA_OK;
+}
+
+size_t workspace_need(int batch, int q_len, int num_heads, int units) {
+  const size_t slots = (size_t)batch + (size_t)units;
+  const size_t rows = (size_t)q_len * (size_t)num_heads;
+  const size_t o_bytes = slots * rows * mla::kDv * sizeof(float);
+  const size_t l_bytes = slots * rows * sizeof(float);
+  return o_bytes + ((l_bytes + 255) & ~(size_t)255);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+int mla_default_num_units(int batch, int q_len, int num_heads) {
+  if (batch < 1 || q_len < 1 || num_heads < 1) return 0;
+  DevInfo d;
+  if (device_info(&d) != MLA_OK) return 0;
+  const int rows = q_len * num_heads;
+  const int var = mla::variant_for(rows);
+  const int rb = (rows + mla::variant_rows(var) - 1) / mla::variant_rows(var);
+  // one 147 KiB-LDS workgroup per CU; spread the row blocks of a unit over CUs
+  int units = d.cus / rb;
+  return units < 1 ? 1 : units;
+}
+
+size_t mla_metadata_bytes(int batch, int num_units) {
+  if (batch < 1 || num_units < 1) return 0;
+  return mla::metadata_words(batch, num_units) * sizeof(int32_t);
+}
+
+size_t mla_workspace_bytes(int batch, int q_len, int num_heads, int num_units) {
+  if (batch < 1 || q_len < 1 || num_heads < 1 || num_units < 1) return 0;
+  return workspace_need(batch, q_len, num_heads, num_units);
+}
+
+int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int num_units,
+                           int min_tiles_per_unit, void* metadata, size_t metadata_bytes,
+                           void* stream) {
+  if (!cache_seqlens || !metadata) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (num_units < 1) return fail(MLA_ERR_INVALID_ARG, "num_units must be >= 1 (got %d)", num_units);
+  if (min_tiles_per_unit < 0)
+    return fail(MLA_ERR_INVALID_ARG, "min_tiles_per_unit must be >= 0 (got %d)", min_tiles_per_unit);
+  if (!aligned(cache_seqlens, 4) || !aligned(metadata, 4))
+    return fail(MLA_ERR_INVALID_ARG, "cache_seqlens and metadata must be 4-byte aligned");
+  if (metadata_bytes < mla_metadata_bytes(batch, num_units))
+    return fail(MLA_ERR_WORKSPACE, "metadata buffer has %zu bytes, needs %zu", metadata_bytes,
+                mla_metadata_bytes(batch, num_units));
+  DevInfo d;
+  int st = device_info(&d);
+  if (st != MLA_OK) return st;
+  const int mt = min_tiles_per_unit == 0 ? mla::kDefaultMinTiles : min_tiles_per_unit;
+  hipError_t e = mla::launch_metadata(cache_seqlens, batch, num_units, mt, (int32_t*)metadata,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "metadata kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                   int num_pages, const int32_t* block_table, int max_pages_per_seq,
+                   const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
+                   float softmax_scale, float* out, float* lse, const void* metadata, int num_units,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_dtype %d is not supported", kv_dtype);
+  if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_scale)
+    return fail(MLA_ERR_INVALID_ARG, "fp8 cache needs kv_scale");
+  if (batch < 1 || q_len < 1 || num_heads < 1)
+    return fail(MLA_ERR_INVALID_ARG, "batch, q_len, num_heads must be >= 1 (got %d, %d, %d)", batch,
+                q_len, num_heads);
+  if ((long long)q_len * num_heads > MLA_MAX_ROWS)
+    return fail(MLA_ERR_INVALID_ARG, "q_len * num_heads = %lld exceeds %d", (long long)q_len * num_heads,
+                MLA_MAX_ROWS);
+  if (num_pages < 1 || max_pages_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARG, "num_pages and max_pages_per_seq must be >= 1");
+  if (!isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
+    return fail(MLA_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(block_table, 4) || !aligned(cache_seqlens, 4) ||
+      (kv_scale && !aligned(kv_scale, 4)))
+    return fail(MLA_ERR_INVALID_ARG, "lse, block_table, cache_seqlens, kv_scale must be 4-byte aligned");
+  if (metadata) {
+    if (num_units < 1) return fail(MLA_ERR_INVALID_ARG, "num_units must be >= 1 with metadata");
+    if (!aligned(metadata, 4)) return fail(MLA_ERR_INVALID_ARG, "metadata must be 4-byte aligned");
+    if (!workspace || !aligned(workspace, 16))
+      return fail(MLA_ERR_INVALID_ARG, "split decode needs a 16-byte aligned workspace");
+    const size_t need = workspace_need(batch, q_len, num_heads, num_units);
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  if (kv_dtype == MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "fp8 e4m3 cache is not built in this library version");
+  DevInfo d;
+  int st = device_info(&d);
+  if (st != MLA_OK) return st;
+
+  mla::DecodeParams p;
+  p.q = (const uint16_t*)q;
+  p.kv = (const uint8_t*)kv_cache;
+  p.kv_scale = kv_scale;
+  p.block_table = block_table;
+  p.seqlens = cache_seqlens;
+  p.out = out;
+  p.lse = lse;
+  p.md = (const int32_t*)metadata;
+  p.batch = batch;
+  p.q_len = q_len;
+  p.num_heads = num_heads;
+  p.rows = q_len * num_heads;
+  p.max_pages = max_pages_per_seq;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  const size_t slots = (size_t)batch + (size_t)num_units;
+  p.ws_out = metadata ? (float*)workspace : nullptr;
+  p.ws_lse = metadata ? (float*)((char*)workspace + slots * p.rows * mla::kDv * sizeof(float)) : nullptr;
+
+  const int var = mla::variant_for(p.rows);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = mla::launch_decode(p, var, metadata ? num_units : batch, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
+  if (metadata) {
+    const int32_t* offsets = (const int32_t*)metadata + mla::MD_HEADER + batch + 1;
+    e = mla::launch_combine(p.ws_out, p.ws_lse, offsets, 1, batch, p.rows, out, lse, 1, s);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq_part_offsets,
+                int batch, int rows_per_seq, float* out, float* lse, void* stream) {
+  if (!part_out || !part_lse || !seq_part_offsets || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (batch < 1 || rows_per_seq < 1 || rows_per_seq > MLA_MAX_ROWS)
+    return fail(MLA_ERR_INVALID_ARG, "batch >= 1 and 1 <= rows_per_seq <= %d required", MLA_MAX_ROWS);
+  if (!aligned(part_out, 16) || !aligned(out, 16))
+    return fail(MLA_ERR_INVALID_ARG, "part_out and out must be 16-byte aligned");
+  if (!aligned(part_lse, 4) || !aligned(lse, 4) || !aligned(seq_part_offsets, 4))
+    return fail(MLA_ERR_INVALID_ARG, "part_lse, lse, seq_part_offsets must be 4-byte aligned");
+  DevInfo d;
+  int st = device_info(&d);
+  if (st != MLA_OK) return st;
+  hipError_t e = mla::launch_combine(part_out, part_lse, seq_part_offsets, 0, batch, rows_per_seq, out,
+                                     lse, 0, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

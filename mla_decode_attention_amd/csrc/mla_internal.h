@@ -1,0 +1,60 @@
+// Internal interface between the C ABI (mla_api.hip) and the kernels
+// (mla_kernels.hip). Not installed; no HIP types beyond hipStream_t.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPage = 64;         // tokens per page = keys per tile
+constexpr int kDqk = 576;         // latent row: 512 latent + 64 rope
+constexpr int kDv = 512;          // value = first 512 entries of the row
+constexpr int kThreads = 256;     // 4 waves of 64 lanes per workgroup
+
+// Metadata layout (int32 words, device):
+//   [0] magic  [1] batch  [2] num_units  [3] payload  [4] total_partials
+//   [5] units_used  [6..7] reserved
+//   [8 .. 8+B]            prefix: first flattened tile of each sequence [B+1]
+//   [9+B .. 9+2B]         split_offset: first partial slot of each sequence [B+1]
+//   [10+2B .. 10+2B+U)    unit_first_seq: sequence holding each unit's first tile
+constexpr int kMdMagic = 0x4D4C4131;  // 'MLA1'
+enum { MD_MAGIC = 0, MD_BATCH = 1, MD_UNITS = 2, MD_PAYLOAD = 3, MD_TOTAL_PARTIALS = 4,
+       MD_UNITS_USED = 5, MD_HEADER = 8 };
+constexpr int kDefaultMinTiles = 8;
+
+inline size_t metadata_words(int batch, int units) {
+  return (size_t)MD_HEADER + 2 * ((size_t)batch + 1) + (size_t)units;
+}
+
+struct DecodeParams {
+  const uint16_t* q;          // bf16 bits [B, s, H, 576]
+  const uint8_t* kv;          // page pool bytes
+  const float* kv_scale;      // [P, 64] (fp8 only)
+  const int32_t* block_table; // [B, max_pages]
+  const int32_t* seqlens;     // [B]
+  float* out;                 // [B, s, H, 512]
+  float* lse;                 // [B, s, H]
+  const int32_t* md;          // metadata or nullptr (unsplit)
+  float* ws_out;              // partial O  [slots, R, 512]
+  float* ws_lse;              // partial LSE [slots, R]
+  int batch, q_len, num_heads, rows;
+  int max_pages;
+  float scale_log2;           // softmax_scale * log2(e)
+};
+
+// Kernel variants: rows of one workgroup and how its 4 waves share a tile.
+enum Variant {
+  VAR_NARROW16 = 0,   // 16 rows; each wave takes 16 of the tile's 64 keys
+  VAR_WIDE64 = 1,     // 64 rows; each wave takes 16 rows and all 64 keys
+};
+int variant_for(int rows);
+int variant_rows(int variant);
+
+hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s);
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles,
+                           int32_t* md, hipStream_t s);
+hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
+                          int offsets_stride_is_md, int batch, int rows, float* out, float* lse,
+                          int skip_single, hipStream_t s);
+
+}  // namespace mla

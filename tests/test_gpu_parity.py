@@ -1,0 +1,162 @@
+"""Parity of the HIP path (through the C ABI) with the CPU fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mla_decode_attention_amd as mla
+from workloads import config, make_workload, PAGE_TOKENS
+from _gpu_util import to_device, run_gpu, reference, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+# ----------------------------------------------------------------- small configs
+
+@pytest.mark.parametrize("name", ["tiny", "share16", "mtp", "ragged"])
+@pytest.mark.parametrize("split", [False, True])
+def test_small_config_parity(name, split):
+    w = config(name, small=True, seed=1)
+    out, lse, _ = run_gpu(w, split=split)
+    ref_out, ref_lse = reference(w)
+    assert_parity(w, out, lse, ref_out, ref_lse, f"{name} split={split}")
+
+
+@pytest.mark.parametrize("H,s", [(16, 1), (16, 2), (128, 1), (128, 2), (64, 3)])
+@pytest.mark.parametrize("split", [False, True])
+def test_edge_lengths(H, s, split):
+    lens = [1, 2, 63, 64, 65, 127, 129, 4097]
+    lens = [L for L in lens if L >= s] + [s]
+    w = make_workload("edges", len(lens), H, s, lens, seed=5)
+    out, lse, _ = run_gpu(w, split=split, num_units=13, min_tiles=1)
+    ref_out, ref_lse = reference(w)
+    assert_parity(w, out, lse, ref_out, ref_lse, f"H={H} s={s} split={split}")
+
+
+@pytest.mark.parametrize("H", [16, 32, 48, 64, 128])
+@pytest.mark.parametrize("s", [1, 2, 4, 6])
+def test_heads_and_query_tokens(H, s):
+    w = make_workload("hs", 3, H, s, [300, 64, 1000], seed=H * 10 + s)
+    out, lse, _ = run_gpu(w, split=True, num_units=7, min_tiles=1)
+    ref_out, ref_lse = reference(w)
+    assert_parity(w, out, lse, ref_out, ref_lse, f"H={H} s={s}")
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_empty_sequences_and_rows(split):
+    # L = 0 sequences and sequences shorter than q_len (rows with no visible key)
+    w = make_workload("empty", 5, 16, 3, [0, 1, 2, 70, 0], seed=9)
+    out, lse, _ = run_gpu(w, split=split, num_units=3, min_tiles=1)
+    ref_out, ref_lse = reference(w)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.all(out[4] == 0) and np.all(np.isneginf(lse[4]))
+    assert_parity(w, out, lse, ref_out, ref_lse, f"empty split={split}")
+
+
+# ----------------------------------------------------------------- invariants
+
+def _relayout_identity(w):
+    cache2 = np.zeros_like(w.cache)
+    bt2 = np.full_like(w.block_table, -1)
+    p = 0
+    for b in range(w.batch):
+        for t in range(-(-int(w.seqlens[b]) // PAGE_TOKENS)):
+            cache2[p] = w.cache[w.block_table[b, t]]
+            bt2[b, t] = p
+            p += 1
+    return cache2, bt2
+
+
+@pytest.mark.parametrize("H,s", [(16, 1), (128, 2)])
+def test_paging_invariance_bitwise(H, s):
+    w = make_workload("pg", 4, H, s, [700, 64, 1, 300], seed=11)
+    out1, lse1, _ = run_gpu(w, split=True, num_units=5, min_tiles=1)
+    w.cache, w.block_table = _relayout_identity(w)
+    out2, lse2, _ = run_gpu(w, split=True, num_units=5, min_tiles=1)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_run_to_run_bitwise():
+    w = config("ragged", small=True, seed=2)
+    d = to_device(w)
+    a = run_gpu(w, d, split=True)
+    b = run_gpu(w, d, split=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_split_and_unsplit_agree():
+    w = config("mtp", small=True, seed=3)
+    d = to_device(w)
+    o1, l1, _ = run_gpu(w, d, split=False)
+    o2, l2, _ = run_gpu(w, d, split=True, num_units=11, min_tiles=1)
+    ref_out, ref_lse = reference(w)
+    assert_parity(w, o1, l1, ref_out, ref_lse, "unsplit")
+    assert_parity(w, o2, l2, ref_out, ref_lse, "split")
+    assert np.max(np.abs(o1 - o2)) <= 1e-2 * np.max(np.abs(ref_out))
+
+
+# ----------------------------------------------------------------- scheduler + combine
+
+@pytest.mark.parametrize("lens,units,mt", [
+    ([256], 256, 0), ([4096] * 7, 16, 0), ([1, 63, 64, 65, 0, 700], 5, 1), ([0, 0], 4, 8),
+    ([65536, 512, 3000, 70], 64, 0), ([130] * 3, 1000, 1), (list(range(0, 5000, 37)), 250, 0),
+])
+def test_metadata_matches_oracle_schedule(lens, units, mt):
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    plan = mla.get_split_metadata(sl, 1, 16, num_units=units, min_tiles_per_unit=mt)
+    md = plan.metadata.cpu().numpy()
+    sch = oracle.split_schedule(lens, units, mt if mt else 8)
+    B = len(lens)
+    assert md[0] == 0x4D4C4131 and md[1] == B and md[2] == units
+    assert md[3] == sch["payload"] and md[4] == sch["total_partials"] and md[5] == sch["units_used"]
+    assert list(md[8:8 + B + 1]) == sch["prefix"]
+    assert list(md[9 + B:10 + 2 * B]) == sch["split_offset"]
+    # first sequence of each unit: the one holding flattened tile u * payload
+    first = md[10 + 2 * B:10 + 2 * B + units]
+    for u in range(units):
+        f = u * sch["payload"]
+        if f >= sch["prefix"][-1]:
+            assert first[u] == B
+        else:
+            b = max(i for i in range(B) if sch["prefix"][i] <= f)
+            assert first[u] == b and sch["prefix"][b + 1] > f
+
+
+@pytest.mark.parametrize("R", [16, 256])
+def test_combine_matches_oracle_merge(R):
+    rng = np.random.default_rng(R)
+    counts = [3, 1, 0, 5, 2]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offs[-1])
+    po = rng.standard_normal((N, R, 512)).astype(np.float32)
+    pl = (rng.standard_normal((N, R)) * 3).astype(np.float32)
+    pl[0, :5] = -np.inf                      # some partials saw no visible key
+    pl[3:8, 7] = -np.inf                     # a row with only -inf partials in sequence 3
+    out, lse = mla.combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                           torch.from_numpy(offs).cuda())
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(len(counts)):
+        k0, k1 = offs[b], offs[b + 1]
+        if k1 == k0:
+            assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b]))
+            continue
+        ro, rl = oracle.lse_merge(po[k0:k1].astype(np.float64), pl[k0:k1].astype(np.float64))
+        assert np.max(np.abs(out[b] - ro)) <= 1e-5 * max(1.0, np.max(np.abs(ro)))
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isneginf(lse[b]), ~fin)
+        assert np.max(np.abs(lse[b][fin] - rl[fin])) <= 1e-5
+
+
+# ----------------------------------------------------------------- full sizes, sampled
+
+@pytest.mark.parametrize("name", ["tiny", "share16", "mtp", "ragged"])
+def test_full_size_sampled(name):
+    """Whole-batch run in the launch configuration the benchmark times (default
+    split plan), checked against the oracle on a sample of sequences."""
+    w = config(name, seed=0)
+    out, lse, _ = run_gpu(w, split=True)
+    B = w.batch
+    sample = sorted({0, B - 1, int(np.argmax(w.seqlens)), B // 2})
+    ref_out, ref_lse = reference(w, batch_indices=sample)
+    assert_parity(w, out[sample], lse[sample], ref_out, ref_lse, f"{name} full, sample {sample}")

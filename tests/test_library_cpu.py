@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments from the host before touching any device (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_decode_attention_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: calls must fail first
+FAKE_ODD = ctypes.c_void_p(0x10008)    # 8-byte aligned, not 16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mla.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "mla_decode_fwd" in names and "mla_get_split_metadata" in names and "mla_combine" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    assert lib.mla_status_string(3) == b"MLA_ERR_WORKSPACE"
+    assert lib.mla_status_string(99) == b"MLA_ERR_UNKNOWN"
+
+
+def test_sizes(lib):
+    assert lib.mla_metadata_bytes(64, 256) == 4 * (8 + 2 * 65 + 256)
+    # (B + units) partial slots x rows x (512 + 1) fp32
+    assert lib.mla_workspace_bytes(64, 1, 16, 256) == 320 * 16 * 512 * 4 + ((320 * 16 * 4 + 255) // 256) * 256
+    assert lib.mla_metadata_bytes(0, 4) == 0
+    assert lib.mla_workspace_bytes(1, 0, 16, 4) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, scale=None, dtype=0, pages=4, bt=FAKE, maxp=4, sl=FAKE, B=1, s=1, H=16,
+             sm=0.072, out=FAKE, lse=FAKE, md=None, units=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.mla_decode_fwd(a["q"], a["kv"], a["scale"], a["dtype"], a["pages"], a["bt"], a["maxp"],
+                              a["sl"], a["B"], a["s"], a["H"], a["sm"], a["out"], a["lse"], a["md"],
+                              a["units"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID),
+    (dict(kv=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(B=0), INVALID),
+    (dict(s=0), INVALID),
+    (dict(H=0), INVALID),
+    (dict(s=6, H=1024), INVALID),            # rows over the limit
+    (dict(pages=0), INVALID),
+    (dict(maxp=0), INVALID),
+    (dict(sm=float("nan")), INVALID),
+    (dict(sm=float("inf")), INVALID),
+    (dict(q=FAKE_ODD), INVALID),
+    (dict(out=FAKE_ODD), INVALID),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(dtype=1), INVALID),                # fp8 without scales
+    (dict(md=FAKE, units=0, ws=FAKE, wsb=1 << 30), INVALID),
+    (dict(md=FAKE, units=8, ws=None), INVALID),
+    (dict(md=FAKE, units=8, ws=FAKE, wsb=1024), WORKSPACE),
+])
+def test_decode_argument_errors(lib, kw, expect):
+    st = _decode(lib, **kw)
+    assert st == expect, (st, lib.mla_last_error())
+    assert lib.mla_last_error() != b""
+
+
+def test_metadata_argument_errors(lib):
+    f = lib.mla_get_split_metadata
+    assert f(None, 4, 8, 0, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 0, 8, 0, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 0, 0, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 8, -1, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 8, 0, FAKE, 16, None) == WORKSPACE
+
+
+def test_combine_argument_errors(lib):
+    f = lib.mla_combine
+    assert f(None, FAKE, FAKE, 2, 16, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 0, 16, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 2, 5000, FAKE, FAKE, None) == INVALID
+    assert f(FAKE_ODD, FAKE, FAKE, 2, 16, FAKE, FAKE, None) == INVALID
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 16, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mla.decode(q, q, q, q, 0.1)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setattr(mla, "_lib", None)
+    monkeypatch.setattr(mla, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(mla.MLAError):
+        mla.load_library()
