@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Throughput of MLA decode over a paged latent KV cache on one MI355X.
+
+One step = one pass of the whole path over one batch: split schedule
+(mla_get_split_metadata), then mla_decode_fwd (attention kernel + LSE merge of
+split sequences). Inputs are seeded synthetic data already resident in HBM.
+To keep the 256 MB Infinity Cache from serving repeat reads, steps rotate over
+several copies of the page pool (each step reads a copy it did not read in the
+previous few steps).
+
+Prints ONE JSON line (default workload: batch 64, 16 heads, q_len 1, seqlens
+U[1024,4096], bf16 cache) with:
+  value      effective KV GB/s of the whole step (KV bytes / step time)
+  roofline   the attention kernel alone: algorithmic bytes (HBM-bound shapes)
+             or flops (MFMA-bound shapes) per launch / its mean launch time,
+             timed with HIP events on its own stream, vs the MI355X peak
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode TFLOP/s + effective KV GB/s, % of roofline, per batch/heads/q_len"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA (context for the fp8 cache)
+
+
+def algorithmic(w):
+    """Bytes and flops the method itself must move / compute for one step."""
+    import numpy as np
+    B, s, H = w.batch, w.q_len, w.num_heads
+    L = w.seqlens.astype(np.int64)
+    e, f = (2, 0) if w.kv_dtype == "bf16" else (1, 4)
+    kv = int(np.sum(L * (576 * e + f)))
+    pages = int(np.sum((L + 63) // 64))
+    q_bytes = B * s * H * 576 * 2
+    out_bytes = B * s * H * (512 + 1) * 4
+    meta = 4 * pages + 4 * B
+    vis = 0
+    for b in range(B):
+        for i in range(s):
+            vis += max(0, min(int(L[b]), int(L[b]) - s + i + 1))
+    flops = 2 * H * (576 + 512) * vis
+    return dict(kv_bytes=kv, bytes=kv + q_bytes + out_bytes + meta, flops=flops, exps=H * vis,
+                pages=pages, tokens=int(np.sum(L)))
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle as it stands, on whole sequences in order until `seconds` pass."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    e, f = (2, 0) if w.kv_dtype == "bf16" else (1, 4)
+    done, kv, flops = 0, 0, 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        oracle.mla_decode(w.q_bits, w.cache, w.block_table, w.seqlens, w.softmax_scale,
+                          w.kv_dtype, w.kv_scale, batch_indices=[b])
+        L = int(w.seqlens[b])
+        kv += L * (576 * e + f)
+        flops += 2 * w.num_heads * 1088 * sum(max(0, min(L, L - w.q_len + i + 1)) for i in range(w.q_len))
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences (whole sequences in batch order), "
+                      f"{dt:.1f} s wall, fp64 numpy", "tflops": flops / dt / 1e12,
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="share16", choices=["tiny", "share16", "mtp", "ragged", "fp8"])
+    ap.add_argument("--sets", type=int, default=0, help="pool copies to rotate (0 = auto)")
+    ap.add_argument("--num-units", type=int, default=0, help="split work units (0 = library default)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): this build "
+              "has no multi-GPU path; the per-GPU kernel is the whole computation.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mla_decode_attention_amd as mla
+    from workloads import config, CONFIG_TEXT
+
+    t_gen = time.perf_counter()
+    w = config(args.config, seed=0)
+    alg = algorithmic(w)
+    print(f"[bench] {args.config}: generated in {time.perf_counter() - t_gen:.1f} s; "
+          f"KV {alg['kv_bytes'] / 1e6:.1f} MB, {alg['flops'] / 1e9:.1f} GFLOP", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q = torch.from_numpy(w.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    if w.kv_dtype == "bf16":
+        kv0 = torch.from_numpy(w.cache.view(np.int16)).to(dev).view(torch.bfloat16)
+        scale0 = None
+    else:
+        kv0 = torch.from_numpy(w.cache).to(dev)
+        scale0 = torch.from_numpy(w.kv_scale).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seqlens).to(dev)
+    pool_bytes = kv0.numel() * kv0.element_size()
+    sets = args.sets or max(1, min(8, math.ceil(768e6 / max(pool_bytes, 1))))
+    kvs = [kv0] + [kv0.clone() for _ in range(sets - 1)]
+    scales = [scale0] + [None if scale0 is None else scale0.clone() for _ in range(sets - 1)]
+    out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
+    units = args.num_units or mla.default_num_units(w.batch, w.q_len, w.num_heads)
+    plan = mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units)
+
+    if args.calib_copy_mib:
+        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step(i):
+        mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units, metadata=plan.metadata,
+                               workspace=plan.workspace)
+        k = i % sets
+        mla.decode(q, kvs[k], bt, sl, w.softmax_scale, kv_scale=scales[k], plan=plan, out=out, lse=lse)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    mla.profile_enable(True)
+    mla.profile_read()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    mla.profile_enable(False)
+    step_ms = t0.elapsed_time(t1) / args.steps
+    main_ms_total, launches = mla.profile_read()
+    main_ms = main_ms_total / max(launches, 1)
+
+    step_s = step_ms * 1e-3
+    main_s = main_ms * 1e-3
+    kv_gbps = alg["kv_bytes"] / step_s / 1e9
+    tflops = alg["flops"] / step_s / 1e12
+    t_hbm = alg["bytes"] / (PEAK_HBM_GBPS * 1e9)
+    t_mfma = alg["flops"] / (PEAK_BF16_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        achieved = alg["bytes"] / main_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
+    else:
+        achieved = alg["flops"] / main_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": "decode_kernel", "kernel_ms": round(main_ms, 5), "launches": launches,
+                 "algorithmic_bytes": alg["bytes"], "algorithmic_flops": alg["flops"],
+                 "t_roof_us": round(max(t_hbm, t_mfma) * 1e6, 2)})
+
+    line = {
+        "metric": METRIC,
+        "value": round(kv_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {CONFIG_TEXT[args.config]}", "batch": w.batch,
+                   "heads": w.num_heads, "q_len": w.q_len, "kv_dtype": w.kv_dtype,
+                   "tokens": alg["tokens"], "pages": alg["pages"], "num_units": units,
+                   "pool_copies": sets, "seed": 0},
+        "tflops": round(tflops, 2),
+        "kv_gbps": round(kv_gbps, 1),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -165,6 +165,20 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
 int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq_part_offsets,
                 int batch, int rows_per_seq, float* out, float* lse, void* stream);
 
+/*
+ * Measurement hook (diagnostics, not part of the computation).
+ * mla_profile_enable(1): from now on every launch of the main decode kernel
+ *   (the attention pass of mla_decode_fwd, not the merge) is bracketed by a
+ *   pair of HIP events recorded on the caller's stream. Event pairs come from
+ *   a pool the library creates on first use (host-side HIP event objects; no
+ *   device memory). mla_profile_enable(0) stops recording.
+ * mla_profile_read: waits for the recorded events, returns the summed elapsed
+ *   time (ms) and the number of recorded launches, and clears the record.
+ * Not thread-safe with concurrent decode calls on other threads.
+ */
+int mla_profile_enable(int enable);
+int mla_profile_read(double* total_ms, int* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ from typing import Optional
 import torch
 
 __all__ = ["load_library", "library_path", "abi_version", "default_num_units", "metadata_bytes",
-           "workspace_bytes", "SplitPlan", "get_split_metadata", "decode", "combine",
+           "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "get_split_metadata", "decode", "combine",
            "MLAError", "KV_BF16", "KV_FP8_E4M3", "PAGE_TOKENS", "D_QK", "D_V"]
 
 PAGE_TOKENS = 64
@@ -60,6 +60,8 @@ def load_library():
         "mla_decode_fwd": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
                                    ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
         "mla_combine": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp]),
+        "mla_profile_enable": (c_int, [c_int]),
+        "mla_profile_read": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -193,6 +195,18 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                               float(softmax_scale), _ptr(out), _ptr(lse), _ptr(md), units, _ptr(ws),
                               wbytes, _stream()), "mla_decode_fwd")
     return out, lse
+
+
+def profile_enable(enable: bool = True):
+    """Record a HIP event pair around every main decode-kernel launch."""
+    _check(load_library().mla_profile_enable(1 if enable else 0), "mla_profile_enable")
+
+
+def profile_read():
+    """(total_ms, launches) of the recorded main-kernel launches; clears the record."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
+    _check(load_library().mla_profile_read(ctypes.byref(ms), ctypes.byref(n)), "mla_profile_read")
+    return ms.value, n.value
 
 
 def combine(part_out: torch.Tensor, part_lse: torch.Tensor, seq_part_offsets: torch.Tensor,

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "mla_decode.h"
 #include "mla_internal.h"
@@ -60,6 +61,26 @@ int device_info(DevInfo* out) {
   *out = d;
   if (!d.supported) return fail(MLA_ERR_UNSUPPORTED, "device arch %s is not gfx950", d.arch);
   return MLA_OK;
+}
+
+// Measurement hook state (see mla_profile_enable).
+struct Profile {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;                             // free events
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded;  // (start, stop)
+};
+Profile g_prof;
+
+hipEvent_t take_event() {
+  if (!g_prof.pool.empty()) {
+    hipEvent_t e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
 }
 
 size_t workspace_need(int batch, int q_len, int num_heads, int units) {
@@ -195,7 +216,21 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
 
   const int var = mla::variant_for(p.rows);
   hipStream_t s = (hipStream_t)stream;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.on) {
+      ev0 = take_event();
+      ev1 = take_event();
+      if (ev0 && ev1) hipEventRecord(ev0, s);
+    }
+  }
   hipError_t e = mla::launch_decode(p, var, metadata ? num_units : batch, s);
+  if (ev0 && ev1) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    hipEventRecord(ev1, s);
+    g_prof.recorded.emplace_back(ev0, ev1);
+  }
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   if (metadata) {
     const int32_t* offsets = (const int32_t*)metadata + mla::MD_HEADER + batch + 1;
@@ -222,6 +257,37 @@ int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq
                                      lse, 0, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+int mla_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = enable != 0;
+  return ok();
+}
+
+int mla_profile_read(double* total_ms, int* launches) {
+  if (!total_ms || !launches) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  double sum = 0.0;
+  int n = 0;
+  int st = MLA_OK;
+  for (auto& pr : g_prof.recorded) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) {
+      st = fail(MLA_ERR_HIP, "profile event: %s", hipGetErrorString(e));
+    } else {
+      sum += ms;
+      ++n;
+    }
+    g_prof.pool.push_back(pr.first);
+    g_prof.pool.push_back(pr.second);
+  }
+  g_prof.recorded.clear();
+  *total_ms = sum;
+  *launches = n;
+  return st == MLA_OK ? ok() : st;
 }
 
 }  // extern "C"

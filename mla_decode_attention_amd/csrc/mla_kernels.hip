@@ -9,19 +9,31 @@
 //  * Data load: one tile = one 64-token page (64 x 576 bf16 = 72 KiB) moved
 //    by direct global->LDS 16-byte loads (no register staging) into one of
 //    two LDS buffers, so the next page streams in while the current one is
-//    computed. Rows are XOR-swizzled in 16-byte chunks so both MFMA operand
-//    reads below are free of LDS bank conflicts.
-//  * QK GEMM: S^T[key, row] = K . Q^T with v_mfma_f32_16x16x32_bf16. Each
-//    wave keeps its 16 query rows (16 x 576 bf16) in registers for the whole
-//    KV loop; K comes from LDS. Every head of a sequence shares each tile.
-//  * Softmax: base-2 online softmax per row, reduced across the 4 lane groups
-//    that hold a row; causal/tail masking only on tiles that need it; the
-//    running max is raised lazily (only when it grows by more than 2^8), so
-//    the O accumulators are rarely rescaled.
+//    computed. The LDS layout (below) makes every MFMA operand fetch a
+//    per-lane constant address plus a compile-time offset, free of bank
+//    conflicts for both the QK and the transposed PV reads.
+//  * QK GEMM: S^T[key, row] = K . Q^T on bf16 MFMA with fp32 accumulation.
+//    Each wave keeps its query rows in registers for the whole KV loop; K
+//    comes from LDS. Every head of a sequence shares each tile.
+//  * Softmax: base-2 online softmax per row, reduced across the lanes that
+//    hold a row; causal/tail masking only on tiles that need it; the running
+//    max is raised lazily (only when it grows by more than 2^8), so the O
+//    accumulators are rarely rescaled.
 //  * PV GEMM: O^T[feature, row] += V^T . P^T. V is the first 512 columns of
 //    the same LDS tile, read transposed with ds_read_b64_tr_b16; P^T comes
 //    straight out of the QK accumulators in the layout the MFMA B operand
-//    wants, so P never goes through LDS.
+//    wants (the key order inside each MFMA k-step is permuted to match), so P
+//    never goes through LDS.
+//
+// Three variants by rows per sequence (R = q_len * heads):
+//   NARROW16 (R <= 16):  16 rows; the 4 waves split each tile's 64 keys, their
+//                        partial states are merged at the end (16x16 MFMA).
+//   WIDE64   (kept for reference): 64 rows; wave w owns rows 16w..16w+15
+//                        (16x16 MFMA).
+//   WIDE64X  (R > 16):   64 rows; QK split 2x2 (row half x key half) over the
+//                        waves, PV split by output columns (32x32 MFMA); P is
+//                        exchanged through LDS. About 2.2x fewer LDS bytes
+//                        per flop than WIDE64.
 //
 // Split-KV: work units of equal tile count over the flattened
 // (sequence, tile) space; sequences cut across units write partial (O, LSE)
@@ -38,14 +50,12 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kRowBytes = kDqk * 2;                  // 1152
 constexpr int kTileBytes = kPage * kRowBytes;        // 73728
-constexpr int kGroupBytes = 4096;                    // 32 features x 64 keys, bf16
 constexpr int kLoadsPerThread = kTileBytes / (kThreads * 16);  // 18
-constexpr int kQChunks = kDqk / 32;                  // 18 k-steps of 32
-constexpr int kFeatBlocks = kDv / 16;                // 32 output blocks of 16
 constexpr float kRescaleThreshold = 8.0f;            // log2 units
 constexpr float kLn2 = 0.6931471805599453f;
 // s_waitcnt immediate for vmcnt(0), expcnt/lgkmcnt untouched (gfx9 encoding)
@@ -53,12 +63,21 @@ constexpr int kVmcntZero = 0x0F70;
 
 static_assert(kLoadsPerThread * kThreads * 16 == kTileBytes, "tile must split evenly");
 
-// LDS tile layout (bf16). Feature f of key k is at byte
-//   (f / 32) * 4096 + (k / 16) * 1024 + ((f / 8) % 4) * 256 + (k % 16) * 16 + (f % 8) * 2
-// i.e. [32-feature group][16-key block][16-byte chunk of the group][key][8 values].
-// A QK operand fetch (16 keys x one 16-byte chunk per lane group) is then one
-// contiguous KiB in lane order, every address below is a per-lane constant plus
-// a compile-time offset, and one load instruction fills one contiguous KiB.
+
+// LDS tile layout (bf16). Chunk c (16 bytes = features 8c..8c+7) of key k
+// sits at byte
+//   lds_byte(k, c) = ((c / 8) * 512 + k * 8 + ((c ^ swz3(k)) % 8)) * 16
+// i.e. [128-byte line group of the row][key][chunk within the line, permuted
+// by a 3-bit function of the key]. One 1 KiB load instruction fills 8 keys x
+// one 128-byte line each (every 8 lanes read one whole cache line), and the
+// permutation keeps both MFMA operand fetches free of bank conflicts: 16
+// consecutive keys at one chunk (QK operand), and 4 consecutive keys x 2
+// adjacent chunks per 16 lanes (transposed V operand).
+__device__ __forceinline__ int swz3(int key) { return (((key >> 1) & 1) << 2) | ((key >> 2) & 3); }
+__device__ __forceinline__ int lds_byte(int key, int chunk) {
+  return ((chunk >> 3) * 512 + key * 8 + ((chunk ^ swz3(key)) & 7)) * 16;
+}
+constexpr int kLineGroupBytes = 8192;   // one 128-byte line of all 64 keys
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -82,19 +101,34 @@ __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint3
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Issue the 18 direct-to-LDS loads of one page (each lane: 16 bytes per load;
-// load i fills feature group i). Keys at or past `nvalid` re-read the last
-// valid key, so tail slots hold finite values (their probabilities are exactly
-// 0) and every wave issues exactly 18 loads.
-__device__ __forceinline__ void load_tile(const uint8_t* page, int nvalid, LDS_AS uint8_t* buf,
-                                          int tid) {
-  const int key = (tid >> 6) * 16 + (tid & 15);
-  const int src_key = key < nvalid ? key : nvalid - 1;
-  const uint32_t voff = src_key * kRowBytes + ((tid >> 4) & 3) * 16;
-  const uint32_t lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
+// The 18 direct-to-LDS loads of one page. Load i of thread t fills slot
+// i*256 + t: line group i/2, key 32(i%2) + t/8, in-line position t%8; the
+// lane fetches the chunk that belongs there, so the 8 lanes of an octet read
+// one whole 128-byte line of one key row. Keys at or past `nvalid` re-read the
+// last valid key, so tail slots hold finite values (their probabilities are
+// exactly 0). The loads are issued one at a time in between the MFMAs of the
+// previous tile.
+struct TileDma {
+  const uint8_t* page;
+  uint32_t voff[2], lds0;
+  __device__ __forceinline__ void plan(const uint8_t* pg, int nvalid, LDS_AS uint8_t* buf, int tid) {
+    page = pg;
 #pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) dma16(voff + 64 * i, page, lds0 + i * kGroupBytes);
-}
+    for (int par = 0; par < 2; ++par) {
+      const int key = 32 * par + (tid >> 3);
+      const int src_key = key < nvalid ? key : nvalid - 1;
+      voff[par] = src_key * kRowBytes + 16 * ((tid & 7) ^ swz3(key));
+    }
+    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
+  }
+  __device__ __forceinline__ void load(int i) const {
+    dma16(voff[i & 1] + 128 * (i >> 1), page, lds0 + i * 4096);
+  }
+  __device__ __forceinline__ void load_all() const {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i) load(i);
+  }
+};
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
@@ -104,6 +138,137 @@ __device__ __forceinline__ bf16x4 tr_read(const LDS_AS uint8_t* p) {
 }
 __device__ __forceinline__ bf16x8 ld128(const LDS_AS uint8_t* p) { return *(const LDS_AS bf16x8*)p; }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// ---------------------------------------------------------------------------
+// Work unit and tile stream shared by the variants.
+// ---------------------------------------------------------------------------
+struct TileInfo {
+  int b, t, L;
+  bool first, last;
+  bool final_out;   // epilogue writes the output (false: a partial slot)
+  int slot;         // partial slot when !final_out
+};
+
+struct KernelArgs {
+  DecodeParams p;
+  const int32_t* md;
+  const int32_t* prefix;
+  const int32_t* split_off;
+  const int32_t* seqlens;
+  const int32_t* block_table;
+  const uint16_t* qptr;
+  const uint8_t* kv;
+};
+
+// Flattened tile range [f_begin, f_end) of unit u and the prefetch cursor.
+// Everything the tile stream needs per tile is held in scalar registers or in
+// one VGPR of cached page ids (lane i = page of tile pc_t0 + i), so loading a
+// tile performs no metadata load; sequence changes (and every 64 tiles) reload
+// the cache.
+struct Unit {
+  int u, f_begin, f_end, b0, payload;
+  int bp, bp_first, bp_last, bp_L, bp_tiles;  // sequence of the prefetch cursor
+  bool bp_final;
+  int bp_slot;
+  int pc_t0, page_cache;
+
+  // false if the unit has no tiles
+  __device__ __forceinline__ bool init(const KernelArgs& a, int unit) {
+    u = unit;
+    payload = 1;
+    if (a.md) {
+      const int B = a.p.batch;
+      payload = a.md[MD_PAYLOAD];
+      const int T = a.prefix[B];
+      f_begin = u * payload;
+      if (f_begin >= T) return false;
+      f_end = min(f_begin + payload, T);
+      b0 = a.split_off[B + 1 + u];
+    } else {
+      b0 = u;
+      const int L = max(a.seqlens[b0], 0);
+      f_begin = 0;
+      f_end = (L + kPage - 1) / kPage;
+    }
+    f_begin = uniform(f_begin);
+    f_end = uniform(f_end);
+    b0 = uniform(b0);
+    payload = uniform(payload);
+    if (f_end <= f_begin) return false;
+    enter(a, b0, f_begin);
+    return true;
+  }
+  __device__ __forceinline__ void load_pages(const KernelArgs& a, int t0) {
+    pc_t0 = t0;
+    const int lane = threadIdx.x & 63;
+    const int t = t0 + lane;
+    page_cache = t < bp_tiles ? a.block_table[(size_t)bp * a.p.max_pages + t] : 0;
+    // drain here (rare path) so the per-tile readlane below needs no wait
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  }
+  // Make sequence bb (holding flattened tile f) the prefetch sequence.
+  __device__ __forceinline__ void enter(const KernelArgs& a, int bb, int f) {
+    bp = uniform(bb);
+    bp_L = uniform(max(a.seqlens[bp], 0));
+    bp_tiles = (bp_L + kPage - 1) / kPage;
+    bp_final = true;
+    bp_slot = 0;
+    if (a.md) {
+      bp_first = uniform(a.prefix[bp]);
+      bp_last = uniform(a.prefix[bp + 1]);
+      bp_final = uniform(a.split_off[bp + 1] - a.split_off[bp]) == 1;
+      bp_slot = uniform(a.split_off[bp] + (u - bp_first / payload));
+    } else {
+      bp_first = 0;
+      bp_last = f_end;
+    }
+    load_pages(a, f - bp_first);
+  }
+  // Scalar facts of flattened tile f and the plan of its loads into `dst`.
+  __device__ __forceinline__ TileInfo prepare(const KernelArgs& a, int f, LDS_AS uint8_t* dst, int tid,
+                                              TileDma& dma) {
+    if (f >= bp_last) {
+      int bb = bp + 1;
+      while (a.prefix[bb + 1] <= f) ++bb;   // skip sequences without tiles
+      enter(a, bb, f);
+    }
+    TileInfo ti;
+    ti.b = bp;
+    ti.t = f - bp_first;
+    ti.L = bp_L;
+    ti.first = (f == f_begin) || (ti.t == 0);
+    ti.last = (f + 1 == f_end) || (f + 1 == bp_last);
+    ti.final_out = bp_final;
+    ti.slot = bp_slot;
+    if (ti.t - pc_t0 >= 64) load_pages(a, ti.t);
+    const int page = uniform(__builtin_amdgcn_readlane(page_cache, ti.t - pc_t0));
+    const int nvalid = min(kPage, ti.L - ti.t * kPage);
+    dma.plan(a.kv + (size_t)page * kTileBytes, nvalid, dst, tid);
+    return ti;
+  }
+};
+
+// O = 0, LSE = -inf for rows [r0, r1) of an empty sequence (unsplit mode).
+__device__ __forceinline__ void write_empty(const DecodeParams& p, int b, int r0, int r1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = r0 + wave; r < min(r1, p.rows); r += 4) {
+    float* o = p.out + ((size_t)b * p.rows + r) * kDv;
+    for (int d = lane * 4; d < kDv; d += 256) *(f32x4*)(o + d) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (lane == 0) p.lse[(size_t)b * p.rows + r] = -INFINITY;
+  }
+}
+
+// Wait for this wave's loads of the current tile (issued during the previous
+// tile), then make every wave's loads visible.
+__device__ __forceinline__ void wait_tile() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// 16-row MFMA variants (NARROW16, WIDE64): v_mfma_f32_16x16x32_bf16 for QK
+// (and PV of WIDE64), v_mfma_f32_16x16x16_bf16 for PV of NARROW16.
+// ---------------------------------------------------------------------------
 template <int VAR>
 struct Cfg;
 template <>
@@ -122,14 +287,18 @@ constexpr int kPvDepth = 4;   // ... ahead of the PV MFMAs
 
 template <int VAR>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t* __restrict__ prefix,
-                   const int32_t* __restrict__ split_off, const int32_t* __restrict__ seqlens,
-                   const int32_t* __restrict__ block_table, const uint16_t* __restrict__ qptr,
-                   const uint8_t* __restrict__ kv) {
+void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
+    const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
+    const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
+    const uint8_t* __restrict__ kv_) {
+  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
+  (void)a;
   constexpr int KPW = Cfg<VAR>::kKeysPerWave;
   constexpr int NKB = KPW / 16;              // 16-key blocks per wave
   constexpr int ROWS_WG = Cfg<VAR>::kRowsWg;
   constexpr bool NARROW = (VAR == VAR_NARROW16);
+  constexpr int kQChunks = kDqk / 32;        // 18 k-steps of 32 features
+  constexpr int kFeatBlocks = kDv / 16;      // 32 output blocks of 16 features
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[kTileBytes];
@@ -137,6 +306,7 @@ void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t
   LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
   LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
 
+  const DecodeParams& p = a.p;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
@@ -145,72 +315,32 @@ void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t
   const int key_blk = NARROW ? wave : 0;     // first 16-key block of this wave
   const int u = blockIdx.x;
 
-  // ---- this unit's flattened tile range and first sequence
-  int f_begin, f_end, b;
-  int payload = 1;
-  if (md) {
-    const int B = p.batch;
-    payload = md[MD_PAYLOAD];
-    const int T = prefix[B];
-    f_begin = u * payload;
-    if (f_begin >= T) return;
-    f_end = min(f_begin + payload, T);
-    b = split_off[B + 1 + u];
-  } else {
-    b = u;
-    const int L = max(seqlens[b], 0);
-    f_begin = 0;
-    f_end = (L + kPage - 1) / kPage;
-    if (f_end == 0) {
-      // nothing cached: O = 0, LSE = -inf for this workgroup's rows
-      const int r0 = blockIdx.y * ROWS_WG;
-      for (int r = r0 + wave; r < min(r0 + ROWS_WG, R); r += 4) {
-        float* o = p.out + ((size_t)b * R + r) * kDv;
-        for (int d = lane * 4; d < kDv; d += 256) *(f32x4*)(o + d) = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (lane == 0) p.lse[(size_t)b * R + r] = -INFINITY;
-      }
-      return;
-    }
+  Unit unit;
+  if (!unit.init(a, u)) {
+    if (!a.md) write_empty(p, unit.b0, blockIdx.y * ROWS_WG, blockIdx.y * ROWS_WG + ROWS_WG);
+    return;
   }
-  f_begin = uniform(f_begin);
-  f_end = uniform(f_end);
-  b = uniform(b);
-  auto seq_first = [&](int bb) { return md ? prefix[bb] : 0; };
-  auto seq_last = [&](int bb) { return md ? prefix[bb + 1] : f_end; };
-
-  // Scalar facts of a tile, read when its load is issued (one iteration ahead)
-  // so nothing between the barrier and the MFMAs waits on a scalar load.
-  struct TileInfo {
-    int b, t, L;
-    bool first, last;
-  };
-  int bp = b;  // sequence cursor of the prefetch stream
-  auto issue = [&](int f, LDS_AS uint8_t* dst) {
-    while (f >= seq_last(bp)) ++bp;
-    bp = uniform(bp);
-    TileInfo ti;
-    ti.b = bp;
-    ti.t = uniform(f - seq_first(bp));
-    ti.L = uniform(seqlens[bp]);
-    ti.first = (f == f_begin) || (ti.t == 0);
-    ti.last = (f + 1 == f_end) || (f + 1 == seq_last(bp));
-    const int page = uniform(block_table[(size_t)bp * p.max_pages + ti.t]);
-    const int nvalid = min(kPage, ti.L - ti.t * kPage);
-    load_tile(kv + (size_t)page * kTileBytes, nvalid, dst, tid);
-    return ti;
-  };
 
   // ---- per-lane constant LDS offsets
-  // QK operand fetch: (16-key block kb, 16-byte chunk g of the feature group, key li)
-  const int qk_lane = key_blk * 1024 + lane * 16;
-  // V transposed fetch: keys 4g + li/4 of a 16-key block, features 16fb + 4(li%4)
-  const int v_lane = key_blk * 1024 + ((li & 3) >> 1) * 256 + (4 * g + (li >> 2)) * 16 + 8 * (li & 1);
+  // QK operand for k-step c: key 16(key_blk + kb) + li, chunk 4c + g
+  //   = (c/2) line groups + chunk 4(c%2) + g of the line; +2048 per 16 keys
+  int qk_lane[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) qk_lane[par] = lds_byte(16 * key_blk + li, 4 * par + g);
+  // V transposed fetch: keys 16 kblk + 4g + li/4, features 16fb + 4(li%4):
+  //   chunk 2fb + (li%4)/2 = (fb/4) line groups + chunk 2(fb%4) + (li%4)/2
+  int v_lane[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+    v_lane[q4] = lds_byte(16 * key_blk + 4 * g + (li >> 2), 2 * q4 + ((li & 3) >> 1)) + 8 * (li & 1);
 
   bf16x8 qreg[kQChunks];
   f32x4 o[kFeatBlocks];
   float m_run = -INFINITY, l_run = 0.f;
 
-  TileInfo next = issue(f_begin, buf0);
+  TileDma dma;
+  TileInfo next = unit.prepare(a, unit.f_begin, buf0, tid, dma);
+  dma.load_all();
 
   auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
     const TileInfo ti = next;
@@ -219,7 +349,7 @@ void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t
     if (ti.first) {
       // new sequence: its query rows into registers, fresh softmax state
       const int rr = row < R ? row : R - 1;
-      const bf16x8* qrow = (const bf16x8*)(qptr + ((size_t)bc * R + rr) * kDqk);
+      const bf16x8* qrow = (const bf16x8*)(a.qptr + ((size_t)bc * R + rr) * kDqk);
 #pragma unroll
       for (int c = 0; c < kQChunks; ++c) {
         bf16x8 v = qrow[4 * c + g];
@@ -234,47 +364,37 @@ void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t
       // place and the compiler needs no wait at their first use.
       __builtin_amdgcn_s_waitcnt(kVmcntZero);
     }
+    const bool final_out = ti.final_out;
+    const int slot = ti.slot;
 
-    // epilogue destination (scalar loads, done before the barrier)
-    bool final_out = true;
-    int slot = 0;
-    if (ti.last && md) {
-      const int ns = split_off[bc + 1] - split_off[bc];
-      final_out = (ns == 1);
-      slot = split_off[bc] + (u - prefix[bc] / payload);
-    }
-    final_out = uniform(final_out);
-    slot = uniform(slot);
-
-    if (f + 1 < f_end) {
-      next = issue(f + 1, nxt);
-      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    lds_barrier();
+    const bool more = f + 1 < unit.f_end;
+    wait_tile();
+    if (more) next = unit.prepare(a, f + 1, nxt, tid, dma);
 
     // ---- QK GEMM: S^T (keys x rows) for this wave's keys, K from LDS, Q^T in registers
     constexpr int NACC = NKB == 1 ? 2 : NKB;      // split a lone chain in two
     constexpr int NQK = kQChunks * NKB;
     f32x4 s[NACC];
 #pragma unroll
-    for (int a = 0; a < NACC; ++a) s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < NACC; ++x) s[x] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      const LDS_AS uint8_t* kp = cur + qk_lane;
+      auto kaddr = [&](int i) {
+        const int c = i / NKB, kb = i % NKB;
+        return cur + qk_lane[c & 1] + (c >> 1) * kLineGroupBytes + kb * 2048;
+      };
       bf16x8 ring[kQkDepth];
 #pragma unroll
-      for (int i = 0; i < kQkDepth; ++i) ring[i] = ld128(kp + (i / NKB) * kGroupBytes + (i % NKB) * 1024);
+      for (int i = 0; i < kQkDepth; ++i) ring[i] = ld128(kaddr(i));
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
         const int c = i / NKB, kb = i % NKB;
-        const bf16x8 a = ring[i % kQkDepth];
-        if (i + kQkDepth < NQK) {
-          const int j = i + kQkDepth;
-          ring[i % kQkDepth] = ld128(kp + (j / NKB) * kGroupBytes + (j % NKB) * 1024);
-        }
+        const bf16x8 av = ring[i % kQkDepth];
+        if (i + kQkDepth < NQK) ring[i % kQkDepth] = ld128(kaddr(i + kQkDepth));
         const int acc = NKB == 1 ? (c & 1) : kb;
-        s[acc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[c], s[acc], 0, 0, 0);
+        s[acc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[c], s[acc], 0, 0, 0);
+        // next tile's loads, spread over the QK MFMAs
+        constexpr int kEvery = NQK / kLoadsPerThread;
+        if (more && (i % kEvery) == kEvery - 1) dma.load(i / kEvery);
         sched_fence();
       }
     }
@@ -319,7 +439,9 @@ void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t
 
     // ---- PV GEMM: O^T (features x rows) += V^T . P^T, V^T read transposed from LDS
     {
-      const LDS_AS uint8_t* vp = cur + v_lane;
+      auto vaddr = [&](int fb, int kblk) {
+        return cur + v_lane[fb & 3] + (fb >> 2) * kLineGroupBytes + kblk * 2048;
+      };
       if constexpr (NARROW) {
         bf16x4 pb;
 #pragma unroll
@@ -327,14 +449,11 @@ void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t
         const i16x4 pbs = __builtin_bit_cast(i16x4, pb);
         bf16x4 ring[kPvDepth];
 #pragma unroll
-        for (int i = 0; i < kPvDepth; ++i) ring[i] = tr_read(vp + (i >> 1) * kGroupBytes + (i & 1) * 512);
+        for (int i = 0; i < kPvDepth; ++i) ring[i] = tr_read(vaddr(i, 0));
 #pragma unroll
         for (int fb = 0; fb < kFeatBlocks; ++fb) {
           const bf16x4 v = ring[fb % kPvDepth];
-          if (fb + kPvDepth < kFeatBlocks) {
-            const int j = fb + kPvDepth;
-            ring[fb % kPvDepth] = tr_read(vp + (j >> 1) * kGroupBytes + (j & 1) * 512);
-          }
+          if (fb + kPvDepth < kFeatBlocks) ring[fb % kPvDepth] = tr_read(vaddr(fb + kPvDepth, 0));
           o[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v), pbs, o[fb],
                                                             0, 0, 0);
           sched_fence();
@@ -350,25 +469,22 @@ void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t
           }
         }
         constexpr int NPV = 2 * kFeatBlocks;
-        auto vaddr = [&](int i, int second) {
-          const int c32 = i / kFeatBlocks, fb = i % kFeatBlocks;
-          return vp + (fb >> 1) * kGroupBytes + (fb & 1) * 512 + (2 * c32 + second) * 1024;
-        };
         bf16x4 r0[kPvDepth], r1[kPvDepth];
 #pragma unroll
         for (int i = 0; i < kPvDepth; ++i) {
-          r0[i] = tr_read(vaddr(i, 0));
-          r1[i] = tr_read(vaddr(i, 1));
+          r0[i] = tr_read(vaddr(i % kFeatBlocks, 2 * (i / kFeatBlocks)));
+          r1[i] = tr_read(vaddr(i % kFeatBlocks, 2 * (i / kFeatBlocks) + 1));
         }
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
           const int c32 = i / kFeatBlocks, fb = i % kFeatBlocks;
-          const bf16x8 a = __builtin_shufflevector(r0[i % kPvDepth], r1[i % kPvDepth], 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 av = __builtin_shufflevector(r0[i % kPvDepth], r1[i % kPvDepth], 0, 1, 2, 3, 4, 5, 6, 7);
           if (i + kPvDepth < NPV) {
-            r0[i % kPvDepth] = tr_read(vaddr(i + kPvDepth, 0));
-            r1[i % kPvDepth] = tr_read(vaddr(i + kPvDepth, 1));
+            const int j = i + kPvDepth;
+            r0[i % kPvDepth] = tr_read(vaddr(j % kFeatBlocks, 2 * (j / kFeatBlocks)));
+            r1[i % kPvDepth] = tr_read(vaddr(j % kFeatBlocks, 2 * (j / kFeatBlocks) + 1));
           }
-          o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[c32], o[fb], 0, 0, 0);
+          o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[c32], o[fb], 0, 0, 0);
           sched_fence();
         }
       }
@@ -450,12 +566,269 @@ void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t
     if constexpr (NARROW) lds_barrier();  // `cur` is the next prefetch target
   };
 
-  // Two copies of the step with the buffers fixed at compile time, so the
-  // compiler sees that LDS reads of one buffer never wait on the direct-to-LDS
-  // loads still landing in the other.
-  for (int f = f_begin; f < f_end; f += 2) {
+  // Two copies of the step with the buffers fixed at compile time.
+  for (int f = unit.f_begin; f < unit.f_end; f += 2) {
     step(f, buf0, buf1);
-    if (f + 1 < f_end) step(f + 1, buf1, buf0);
+    if (f + 1 < unit.f_end) step(f + 1, buf1, buf0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WIDE64X: 64 rows per workgroup on v_mfma_f32_32x32x16_bf16.
+//   QK is split 2 x 2 over the waves: wave w computes S^T[32 keys, 32 rows] for
+//   row half rh = w%2 and key half kh = w/2 of the tile (36 k-steps of 16
+//   features; Q of its 32 rows stays in registers).
+//   PV is split by output columns: wave w accumulates O^T[128 features, 64 rows]
+//   for features 128w..128w+127 (O: 128 registers per lane).
+//   C layout of a 32x32 block: lane l holds element [8j + 4h + i][l%32] for
+//   register r = 4j + i, h = l/32.
+//   In PV k-step ks = 2kh + s (keys 32kh + 16s + 0..15) the k-slot 8h + e is
+//   key 32kh + 16s + 4h + e (e < 4) or 32kh + 16s + 8 + 4h + (e - 4): exactly
+//   the S registers 8s..8s+7 of the QK wave's lane. So each QK lane stores its
+//   P values for a k-step as one 16-byte word, and the PV waves read it back
+//   as their MFMA B operand from the same lane position (P exchange through
+//   LDS with no transposition).
+//   The row max of a tile needs both key halves: the QK waves publish their
+//   half-tile maxima, and every wave derives the same running max for all 64
+//   rows (it needs the rescale factor of every row for its O columns).
+// ---------------------------------------------------------------------------
+constexpr int kQkDepthX = 4;
+constexpr int kPvDepthX = 4;
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
+    const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
+    const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
+    const uint8_t* __restrict__ kv_) {
+  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
+  (void)a;
+  constexpr int ROWS_WG = 64;
+  constexpr int kQSteps = kDqk / 16;         // 36 k-steps of 16 features
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) bf16x8 p_lds[4][2][64];   // [k-step][row half][lane]
+  __shared__ float smax[2][64];                                      // [key half][row]
+  __shared__ float ssum[2][64];
+  LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
+  LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
+
+  const DecodeParams& p = a.p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int rh = wave & 1, kh = wave >> 1;
+  const int R = p.rows;
+  const int row0 = blockIdx.y * ROWS_WG;
+  const int row_qk = row0 + 32 * rh + n;
+  const int u = blockIdx.x;
+
+  Unit unit;
+  if (!unit.init(a, u)) {
+    if (!a.md) write_empty(p, unit.b0, row0, row0 + ROWS_WG);
+    return;
+  }
+
+  // ---- per-lane constant LDS offsets
+  // QK operand for k-step c: key 32kh + n, chunk 2c + h
+  //   = (c/4) line groups + chunk 2(c%4) + h of the line
+  int k_lane[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) k_lane[q4] = lds_byte(32 * kh + n, 2 * q4 + h);
+  // V transposed fetch: 16-lane group q covers features 128w + 32fb + 16(q%2)
+  // + 0..15 and keys 16ks + 4h + j/4 (+8 for the second read): chunk
+  // 16w + 4fb + 2(q%2) + (j%4)/2 = (2w + fb/2) line groups + chunk
+  // 4(fb%2) + 2(q%2) + (j%4)/2 of the line; +2048 per k-step of 16 keys.
+  int v_lane[2][2];   // [second][fb % 2]
+  {
+    const int q = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int second = 0; second < 2; ++second)
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+        v_lane[second][par] = 2 * wave * kLineGroupBytes +
+                              lds_byte(4 * h + (j >> 2) + 8 * second, 4 * par + 2 * (q & 1) + ((j & 3) >> 1)) +
+                              8 * (j & 1);
+  }
+
+  bf16x8 qreg[kQSteps];
+  f32x16 o[4][2];                            // [feature block][row half]
+  float m_run[2] = {-INFINITY, -INFINITY};   // running max of rows row0 + n, row0 + 32 + n
+  float l_run = 0.f;                         // partial row sum of row_qk (this key half, lane half)
+
+  TileDma dma;
+  TileInfo next = unit.prepare(a, unit.f_begin, buf0, tid, dma);
+  dma.load_all();
+
+  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
+    const TileInfo ti = next;
+    const int bc = ti.b, t = ti.t, L = ti.L;
+
+    if (ti.first) {
+      const int rr = row_qk < R ? row_qk : R - 1;
+      const bf16x8* qrow = (const bf16x8*)(a.qptr + ((size_t)bc * R + rr) * kDqk);
+#pragma unroll
+      for (int c = 0; c < kQSteps; ++c) {
+        bf16x8 v = qrow[2 * c + h];
+        qreg[c] = row_qk < R ? v : bf16x8{};
+      }
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        o[fb][0] = f32x16{};
+        o[fb][1] = f32x16{};
+      }
+      m_run[0] = m_run[1] = -INFINITY;
+      l_run = 0.f;
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    }
+    const bool final_out = ti.final_out;
+    const int slot = ti.slot;
+
+    const bool more = f + 1 < unit.f_end;
+    wait_tile();
+    if (more) next = unit.prepare(a, f + 1, nxt, tid, dma);
+
+    // ---- QK GEMM: S^T[32 keys of half kh, 32 rows of half rh]
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    {
+      auto kaddr = [&](int c) { return cur + k_lane[c & 3] + (c >> 2) * kLineGroupBytes; };
+      bf16x8 ring[kQkDepthX];
+#pragma unroll
+      for (int i = 0; i < kQkDepthX; ++i) ring[i] = ld128(kaddr(i));
+#pragma unroll
+      for (int c = 0; c < kQSteps; ++c) {
+        const bf16x8 av = ring[c % kQkDepthX];
+        if (c + kQkDepthX < kQSteps) ring[c % kQkDepthX] = ld128(kaddr(c + kQkDepthX));
+        sacc[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], sacc[c & 1], 0, 0, 0);
+        // next tile's loads, one after every second QK MFMA
+        if (more && (c & 1)) dma.load(c >> 1);
+        sched_fence();
+      }
+    }
+    f32x16 sv = sacc[0] + sacc[1];
+
+    // ---- softmax: half-tile maxima -> shared running max -> P
+    const int key0 = t * kPage + 32 * kh + 4 * h;
+    const int vis = L - p.q_len + (row_qk < R ? row_qk : R - 1) / p.num_heads + 1;
+    const bool need_mask = (t * kPage + kPage) > (L - p.q_len + 1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = sv[r] * p.scale_log2;
+      if (need_mask && (key0 + 8 * (r >> 2) + (r & 3)) >= vis) v = -INFINITY;
+      sv[r] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (h == 0) smax[kh][32 * rh + n] = mx;
+    lds_barrier();
+
+    float alpha[2];
+    bool any_raise = false;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float tmax = fmaxf(smax[0][32 * rb + n], smax[1][32 * rb + n]);
+      const float m_new = fmaxf(m_run[rb], tmax);
+      const bool raise = m_new > m_run[rb] + kRescaleThreshold;
+      alpha[rb] = raise ? exp2_fast(m_run[rb] - m_new) : 1.0f;
+      if (raise) m_run[rb] = m_new;
+      any_raise |= raise;
+    }
+    if (__builtin_amdgcn_ballot_w64(any_raise)) {
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        o[fb][0] *= alpha[0];
+        o[fb][1] *= alpha[1];
+      }
+      l_run *= alpha[rh];
+    }
+    const float m_eff = (m_run[rh] == -INFINITY) ? 0.0f : m_run[rh];
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = exp2_fast(sv[8 * sidx + e] - m_eff);
+        l_run += pr;
+        pb[e] = (__bf16)pr;
+      }
+      p_lds[2 * kh + sidx][rh][lane] = pb;
+    }
+    lds_barrier();
+
+    // ---- PV GEMM: O^T[128 features of this wave, 64 rows] += V^T . P^T
+    {
+      auto vaddr = [&](int i, int second) {
+        const int ks = i >> 2, fb = i & 3;
+        return cur + v_lane[second][fb & 1] + (fb >> 1) * kLineGroupBytes + ks * 2048;
+      };
+      constexpr int NPV = 16;   // (k-step, feature block) pairs; each feeds 2 row halves
+      bf16x4 r0[kPvDepthX], r1[kPvDepthX];
+#pragma unroll
+      for (int i = 0; i < kPvDepthX; ++i) {
+        r0[i] = tr_read(vaddr(i, 0));
+        r1[i] = tr_read(vaddr(i, 1));
+      }
+      bf16x8 pbr[2];
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int ks = i >> 2, fb = i & 3;
+        if (fb == 0) {
+          pbr[0] = p_lds[ks][0][lane];
+          pbr[1] = p_lds[ks][1][lane];
+        }
+        const bf16x8 av = __builtin_shufflevector(r0[i % kPvDepthX], r1[i % kPvDepthX], 0, 1, 2, 3, 4, 5, 6, 7);
+        if (i + kPvDepthX < NPV) {
+          r0[i % kPvDepthX] = tr_read(vaddr(i + kPvDepthX, 0));
+          r1[i % kPvDepthX] = tr_read(vaddr(i + kPvDepthX, 1));
+        }
+        o[fb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbr[0], o[fb][0], 0, 0, 0);
+        o[fb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbr[1], o[fb][1], 0, 0, 0);
+        sched_fence();
+      }
+    }
+
+    lds_barrier();  // every wave is done with `cur`, p_lds and smax
+
+    if (!ti.last) return;
+
+    // ---- epilogue for sequence bc: full row sums, then O / l and LSE
+    const float lh = l_run + __shfl_xor(l_run, 32);
+    if (h == 0) ssum[kh][32 * rh + n] = lh;
+    lds_barrier();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = row0 + 32 * rb + n;
+      const float l_row = ssum[0][32 * rb + n] + ssum[1][32 * rb + n];
+      const bool live = l_row > 0.f;
+      const float inv = live ? 1.0f / l_row : 0.f;
+      if (row < R) {
+        float* dst_o;
+        float* dst_l;
+        if (final_out) {
+          dst_o = p.out + ((size_t)bc * R + row) * kDv;
+          dst_l = p.lse + (size_t)bc * R + row;
+        } else {
+          dst_o = p.ws_out + ((size_t)slot * R + row) * kDv;
+          dst_l = p.ws_lse + (size_t)slot * R + row;
+        }
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            f32x4 v = {o[fb][rb][4 * jj], o[fb][rb][4 * jj + 1], o[fb][rb][4 * jj + 2], o[fb][rb][4 * jj + 3]};
+            *(f32x4*)(dst_o + 128 * wave + 32 * fb + 8 * jj + 4 * h) = v * inv;
+          }
+        }
+        if (wave == 0 && h == 0)
+          *dst_l = live ? (m_run[rb] + log2_fast(l_row)) * kLn2 : -INFINITY;
+      }
+    }
+  };
+
+  for (int f = unit.f_begin; f < unit.f_end; f += 2) {
+    step(f, buf0, buf1);
+    if (f + 1 < unit.f_end) step(f + 1, buf1, buf0);
   }
 }
 
@@ -463,10 +836,38 @@ void decode_kernel(DecodeParams p, const int32_t* __restrict__ md, const int32_t
 // Split schedule (one workgroup). Integer only; matches the definition in the
 // header: equal tile counts per unit over the flattened (sequence, tile) space.
 // ---------------------------------------------------------------------------
+
+// Exclusive prefix sum over the 1024 threads of the block; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int t = lane < 16 ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int y = __shfl_up(t, d);
+      if (lane >= d) t += y;
+    }
+    if (lane < 16) wave_tot[16 + lane] = t;   // inclusive per-wave offsets
+  }
+  __syncthreads();
+  const int base = wave ? wave_tot[16 + wave - 1] : 0;
+  if (total) *total = wave_tot[31];
+  const int r = base + x - v;
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, int B, int units,
                                                         int min_tiles, int32_t* md) {
-  __shared__ int part[1024];
-  __shared__ int s_total, s_payload;
+  __shared__ int wave_tot[32];
   const int tid = threadIdx.x;
   const int per = (B + 1023) / 1024;
   const int lo = min(tid * per, B), hi = min(lo + per, B);
@@ -478,29 +879,14 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
 
   int acc = 0;
   for (int bb = lo; bb < hi; ++bb) acc += tiles(bb);
-  part[tid] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < 1024; ++i) {
-      const int v = part[i];
-      part[i] = run;
-      run += v;
-    }
-    s_total = run;
-    const int T = run;
-    const int by_units = (T + units - 1) / units;
-    s_payload = max(max(by_units, min_tiles), 1);
-  }
-  __syncthreads();
-  const int T = s_total, payload = s_payload;
-  int run = part[tid];
+  int T = 0;
+  int run = block_exclusive_scan(acc, wave_tot, &T);
+  const int payload = max(max((T + units - 1) / units, min_tiles), 1);
   for (int bb = lo; bb < hi; ++bb) {
     prefix[bb] = run;
     run += tiles(bb);
   }
   if (tid == 0) prefix[B] = T;
-  __syncthreads();
 
   acc = 0;
   for (int bb = lo; bb < hi; ++bb) {
@@ -508,27 +894,16 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
     const int pb = prefix[bb];
     acc += tb ? ((pb + tb - 1) / payload - pb / payload + 1) : 0;
   }
-  part[tid] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    int r = 0;
-    for (int i = 0; i < 1024; ++i) {
-      const int v = part[i];
-      part[i] = r;
-      r += v;
-    }
-    s_total = r;
-  }
-  __syncthreads();
-  run = part[tid];
+  int total_partials = 0;
+  run = block_exclusive_scan(acc, wave_tot, &total_partials);
   for (int bb = lo; bb < hi; ++bb) {
     split_off[bb] = run;
     const int tb = tiles(bb);
     const int pb = prefix[bb];
     run += tb ? ((pb + tb - 1) / payload - pb / payload + 1) : 0;
   }
-  if (tid == 0) split_off[B] = s_total;
-  __syncthreads();
+  if (tid == 0) split_off[B] = total_partials;
+  __syncthreads();   // prefix[] complete before the searches below
 
   for (int uu = tid; uu < units; uu += 1024) {
     const long long f = (long long)uu * payload;
@@ -548,7 +923,7 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
     md[MD_BATCH] = B;
     md[MD_UNITS] = units;
     md[MD_PAYLOAD] = payload;
-    md[MD_TOTAL_PARTIALS] = s_total;
+    md[MD_TOTAL_PARTIALS] = total_partials;
     md[MD_UNITS_USED] = T ? (T + payload - 1) / payload : 0;
     md[6] = 0;
     md[7] = 0;
@@ -556,63 +931,107 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
 }
 
 // ---------------------------------------------------------------------------
-// LSE merge of partials. 256 threads = 2 rows x 128 threads x 4 features.
+// LSE merge of partials: one workgroup per (sequence, pair of rows), 128
+// threads x 4 features per row. One pass gives the max and the rescaled sum of
+// the partial LSEs; a second pass accumulates the weighted partial outputs,
+// four partials in flight per step.
 // ---------------------------------------------------------------------------
-constexpr int kCombineRowsPerBlock = 16;
-
-__global__ __launch_bounds__(256) void combine_kernel(const float* part_out, const float* part_lse,
-                                                      const int32_t* offsets, int B, int R,
-                                                      float* out, float* lse, int skip_single) {
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_out,
+                                                      const float* __restrict__ part_lse,
+                                                      const int32_t* __restrict__ offsets, int B, int R,
+                                                      float* __restrict__ out, float* __restrict__ lse,
+                                                      int skip_single) {
   const int b = blockIdx.x;
   const int k0 = offsets[b];
   const int n = offsets[b + 1] - k0;
   if (skip_single && n == 1) return;
-  const int half = threadIdx.x >> 7;
+  const int r = blockIdx.y * 2 + (threadIdx.x >> 7);
+  if (r >= R) return;
   const int d = (threadIdx.x & 127) * 4;
-  const int r_end = min((int)(blockIdx.y + 1) * kCombineRowsPerBlock, R);
-  for (int r = blockIdx.y * kCombineRowsPerBlock + half; r < r_end; r += 2) {
-    float M = -INFINITY;
-    for (int k = 0; k < n; ++k) M = fmaxf(M, part_lse[(size_t)(k0 + k) * R + r]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float lse_v = -INFINITY;
-    if (M != -INFINITY) {
-      float tot = 0.f;
-      for (int k = 0; k < n; ++k) {
-        const float lk = part_lse[(size_t)(k0 + k) * R + r];
-        tot += (lk == -INFINITY) ? 0.f : expf(lk - M);
-      }
-      lse_v = M + logf(tot);
-      const float inv = 1.0f / tot;
-      for (int k = 0; k < n; ++k) {
-        const float lk = part_lse[(size_t)(k0 + k) * R + r];
-        if (lk == -INFINITY) continue;
-        const float w = expf(lk - M) * inv;
-        const f32x4 v = *(const f32x4*)(part_out + ((size_t)(k0 + k) * R + r) * kDv + d);
-        acc += w * v;
+  const float* pl = part_lse + (size_t)k0 * R + r;
+  const float* po = part_out + ((size_t)k0 * R + r) * kDv + d;
+  const size_t lstride = R, ostride = (size_t)R * kDv;
+
+  float M = -INFINITY, S = 0.f;
+  int k = 0;
+  for (; k + 4 <= n; k += 4) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = pl[(k + j) * lstride];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (v[j] == -INFINITY) continue;
+      if (v[j] > M) {
+        S = S * expf(M - v[j]) + 1.f;
+        M = v[j];
+      } else {
+        S += expf(v[j] - M);
       }
     }
-    *(f32x4*)(out + ((size_t)b * R + r) * kDv + d) = acc;
-    if (d == 0) lse[(size_t)b * R + r] = lse_v;
   }
+  for (; k < n; ++k) {
+    const float v = pl[k * lstride];
+    if (v == -INFINITY) continue;
+    if (v > M) {
+      S = S * expf(M - v) + 1.f;
+      M = v;
+    } else {
+      S += expf(v - M);
+    }
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lse_v = -INFINITY;
+  if (M != -INFINITY) {
+    lse_v = M + logf(S);
+    k = 0;
+    for (; k + 4 <= n; k += 4) {
+      float wk[4];
+      f32x4 ov[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = pl[(k + j) * lstride];
+        wk[j] = v == -INFINITY ? 0.f : expf(v - lse_v);
+        ov[j] = *(const f32x4*)(po + (k + j) * ostride);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc += wk[j] * ov[j];
+    }
+    for (; k < n; ++k) {
+      const float v = pl[k * lstride];
+      if (v == -INFINITY) continue;
+      acc += expf(v - lse_v) * *(const f32x4*)(po + k * ostride);
+    }
+  }
+  *(f32x4*)(out + ((size_t)b * R + r) * kDv + d) = acc;
+  if (d == 0) lse[(size_t)b * R + r] = lse_v;
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-int variant_for(int rows) { return rows <= 16 ? VAR_NARROW16 : VAR_WIDE64; }
+int variant_for(int rows) { return rows <= 16 ? VAR_NARROW16 : VAR_WIDE64X; }
 int variant_rows(int variant) { return variant == VAR_NARROW16 ? 16 : 64; }
 
 hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s) {
   const int rb = (p.rows + variant_rows(variant) - 1) / variant_rows(variant);
   dim3 grid(grid_units, rb);
-  const int32_t* prefix = p.md ? p.md + MD_HEADER : nullptr;
-  const int32_t* split_off = p.md ? prefix + p.batch + 1 : nullptr;
+  KernelArgs a;
+  a.p = p;
+  a.md = p.md;
+  a.prefix = p.md ? p.md + MD_HEADER : nullptr;
+  a.split_off = p.md ? a.prefix + p.batch + 1 : nullptr;
+  a.seqlens = p.seqlens;
+  a.block_table = p.block_table;
+  a.qptr = p.q;
+  a.kv = p.kv;
+#define MLA_KARGS a.p, a.md, a.prefix, a.split_off, a.seqlens, a.block_table, a.qptr, a.kv
   if (variant == VAR_NARROW16)
-    hipLaunchKernelGGL(decode_kernel<VAR_NARROW16>, grid, dim3(kThreads), 0, s, p, p.md, prefix, split_off,
-                       p.seqlens, p.block_table, p.q, p.kv);
+    hipLaunchKernelGGL(decode_kernel16<VAR_NARROW16>, grid, dim3(kThreads), 0, s, MLA_KARGS);
+  else if (variant == VAR_WIDE64)
+    hipLaunchKernelGGL(decode_kernel16<VAR_WIDE64>, grid, dim3(kThreads), 0, s, MLA_KARGS);
   else
-    hipLaunchKernelGGL(decode_kernel<VAR_WIDE64>, grid, dim3(kThreads), 0, s, p, p.md, prefix, split_off,
-                       p.seqlens, p.block_table, p.q, p.kv);
+    hipLaunchKernelGGL(decode_kernel_x, grid, dim3(kThreads), 0, s, MLA_KARGS);
+#undef MLA_KARGS
   return hipGetLastError();
 }
 
@@ -625,7 +1044,7 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
                           int /*unused*/, int batch, int rows, float* out, float* lse, int skip_single,
                           hipStream_t s) {
-  dim3 grid(batch, (rows + kCombineRowsPerBlock - 1) / kCombineRowsPerBlock);
+  dim3 grid(batch, (rows + 1) / 2);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, part_out, part_lse, offsets, batch, rows,
                      out, lse, skip_single);
   return hipGetLastError();
