@@ -189,8 +189,6 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
     if (workspace_bytes < need)
       return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   }
-  if (kv_dtype == MLA_KV_FP8_E4M3)
-    return fail(MLA_ERR_UNSUPPORTED, "fp8 e4m3 cache is not built in this library version");
   DevInfo d;
   int st = device_info(&d);
   if (st != MLA_OK) return st;
@@ -198,7 +196,7 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
   mla::DecodeParams p;
   p.q = (const uint16_t*)q;
   p.kv = (const uint8_t*)kv_cache;
-  p.kv_scale = kv_scale;
+  p.kv_scale = kv_dtype == MLA_KV_FP8_E4M3 ? kv_scale : nullptr;   // selects the fp8 kernels
   p.block_table = block_table;
   p.seqlens = cache_seqlens;
   p.out = out;
@@ -222,13 +220,13 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
     if (g_prof.on) {
       ev0 = take_event();
       ev1 = take_event();
-      if (ev0 && ev1) hipEventRecord(ev0, s);
+      if (ev0 && ev1) (void)hipEventRecord(ev0, s);
     }
   }
   hipError_t e = mla::launch_decode(p, var, metadata ? num_units : batch, s);
   if (ev0 && ev1) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    hipEventRecord(ev1, s);
+    (void)hipEventRecord(ev1, s);
     g_prof.recorded.emplace_back(ev0, ev1);
   }
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));

@@ -108,11 +108,30 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // last valid key, so tail slots hold finite values (their probabilities are
 // exactly 0). The loads are issued one at a time in between the MFMAs of the
 // previous tile.
-struct TileDma {
+// 4-byte direct-to-LDS load per lane (used for the fp8 per-token scales).
+__device__ __forceinline__ void dma4(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "memory");
+}
+
+template <bool FP8>
+struct TileDma;
+
+// bf16 page: 18 loads per thread straight into the tile layout.
+template <>
+struct TileDma<false> {
+  static constexpr int kLoads = kLoadsPerThread;
   const uint8_t* page;
   uint32_t voff[2], lds0;
-  __device__ __forceinline__ void plan(const uint8_t* pg, int nvalid, LDS_AS uint8_t* buf, int tid) {
-    page = pg;
+  __device__ __forceinline__ void plan(const uint8_t* kv, const float* /*kv_scale*/, int page_id,
+                                       int nvalid, LDS_AS uint8_t* buf, LDS_AS float* /*sbuf*/,
+                                       int tid) {
+    page = kv + (size_t)page_id * kTileBytes;
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int key = 32 * par + (tid >> 3);
@@ -124,11 +143,93 @@ struct TileDma {
   __device__ __forceinline__ void load(int i) const {
     dma16(voff[i & 1] + 128 * (i >> 1), page, lds0 + i * 4096);
   }
-  __device__ __forceinline__ void load_all() const {
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) load(i);
+};
+
+// fp8 page: a plain copy of the 36 KiB page into a staging buffer (9 loads per
+// thread, each load one contiguous KiB of the page), plus the page's 64
+// per-token scales (one 4-byte load per lane of wave 0). Keys at or past
+// `nvalid` re-read the last valid key and its scale.
+constexpr int kFp8RowBytes = kDqk;                        // 576
+constexpr int kFp8TileBytes = kPage * kFp8RowBytes;       // 36864
+constexpr int kFp8Loads = kFp8TileBytes / (kThreads * 16);  // 9
+static_assert(kFp8Loads * kThreads * 16 == kFp8TileBytes, "fp8 tile must split evenly");
+
+template <>
+struct TileDma<true> {
+  static constexpr int kLoads = kFp8Loads;
+  const uint8_t* page;
+  const uint8_t* scale;
+  uint32_t lds0, sc_lds, sc_off;
+  int nvalid, tid;
+  __device__ __forceinline__ void plan(const uint8_t* kv, const float* kv_scale, int page_id, int nv,
+                                       LDS_AS uint8_t* buf, LDS_AS float* sbuf, int t) {
+    page = kv + (size_t)page_id * kFp8TileBytes;
+    scale = (const uint8_t*)(kv_scale + (size_t)page_id * kPage);
+    nvalid = nv;
+    tid = t;
+    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
+    sc_lds = (uint32_t)uniform((int)(uintptr_t)sbuf);
+    const int lane = tid & 63;
+    sc_off = 4 * (lane < nvalid ? lane : nvalid - 1);
+  }
+  __device__ __forceinline__ void load(int i) const {
+    const int sidx = i * kThreads + tid;            // 16-byte slot of the page
+    uint32_t voff = sidx * 16;
+    if (nvalid < kPage) {
+      const int key = sidx / 36;
+      if (key >= nvalid) voff = (nvalid - 1) * kFp8RowBytes + (sidx - key * 36) * 16;
+    }
+    dma16(voff, page, lds0 + i * 4096);
+    if (i == 0 && tid < 64) dma4(sc_off, scale, sc_lds);
   }
 };
+
+// Spread the loads of the next tile evenly over the M QK MFMA slots of the
+// current one (issued back to back they stall the wave on the full
+// vector-memory queue): load k goes right after slot ((k + 1) * M) / N - 1.
+// Slots are compile-time constants in the unrolled loops, so this folds away.
+template <int M, class Dma>
+__device__ __forceinline__ void dma_slot(const Dma& dma, bool more, int slot) {
+  constexpr int N = Dma::kLoads;
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+    if (((k + 1) * M) / N - 1 == slot && more) dma.load(k);
+}
+
+template <class Dma>
+__device__ __forceinline__ void dma_all(const Dma& dma) {
+#pragma unroll
+  for (int k = 0; k < Dma::kLoads; ++k) dma.load(k);
+}
+
+// fp8 staging page -> bf16 tile (exact: every E4M3FN value is a bf16 value).
+// Each thread widens 9 slots of 16 codes into 2 chunks of 8 bf16 each.
+__device__ __forceinline__ void widen_fp8_tile(const LDS_AS uint8_t* stage, LDS_AS uint8_t* tile, int tid) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+#pragma unroll
+  for (int j = 0; j < kFp8Loads; ++j) {
+    const int sidx = j * kThreads + tid;
+    const int key = sidx / 36, c16 = sidx - key * 36;
+    const u32x4 w = *(const LDS_AS u32x4*)(stage + sidx * 16);
+    u32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false);
+      const bf16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true);
+      const unsigned u0 = __builtin_bit_cast(unsigned, x0), u1 = __builtin_bit_cast(unsigned, x1);
+      if (e < 2) {
+        lo[2 * e] = u0;
+        lo[2 * e + 1] = u1;
+      } else {
+        hi[2 * (e - 2)] = u0;
+        hi[2 * (e - 2) + 1] = u1;
+      }
+    }
+    *(LDS_AS u32x4*)(tile + lds_byte(key, 2 * c16)) = lo;
+    *(LDS_AS u32x4*)(tile + lds_byte(key, 2 * c16 + 1)) = hi;
+  }
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
@@ -225,8 +326,9 @@ struct Unit {
     load_pages(a, f - bp_first);
   }
   // Scalar facts of flattened tile f and the plan of its loads into `dst`.
-  __device__ __forceinline__ TileInfo prepare(const KernelArgs& a, int f, LDS_AS uint8_t* dst, int tid,
-                                              TileDma& dma) {
+  template <class Dma>
+  __device__ __forceinline__ TileInfo prepare(const KernelArgs& a, int f, LDS_AS uint8_t* dst,
+                                              LDS_AS float* sdst, int tid, Dma& dma) {
     if (f >= bp_last) {
       int bb = bp + 1;
       while (a.prefix[bb + 1] <= f) ++bb;   // skip sequences without tiles
@@ -243,7 +345,7 @@ struct Unit {
     if (ti.t - pc_t0 >= 64) load_pages(a, ti.t);
     const int page = uniform(__builtin_amdgcn_readlane(page_cache, ti.t - pc_t0));
     const int nvalid = min(kPage, ti.L - ti.t * kPage);
-    dma.plan(a.kv + (size_t)page * kTileBytes, nvalid, dst, tid);
+    dma.plan(a.kv, a.p.kv_scale, page, nvalid, dst, sdst, tid);
     return ti;
   }
 };
@@ -285,7 +387,7 @@ struct Cfg<VAR_WIDE64> {
 constexpr int kQkDepth = 6;   // LDS operand fetches in flight ahead of the QK MFMAs
 constexpr int kPvDepth = 4;   // ... ahead of the PV MFMAs
 
-template <int VAR>
+template <int VAR, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
     const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
@@ -303,8 +405,14 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[kTileBytes];
   __shared__ float mrg[2][4][16];
+  __shared__ __attribute__((aligned(16))) float sbuf[2][kPage];   // fp8 per-token scales
   LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
   LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
+  // fp8: buf0 holds the widened bf16 tile, buf1 the two fp8 staging pages
+  LDS_AS uint8_t* const stage0 = buf1;
+  LDS_AS uint8_t* const stage1 = buf1 + kFp8TileBytes;
+  LDS_AS float* const sb0 = (LDS_AS float*)(&sbuf[0][0]);
+  LDS_AS float* const sb1 = (LDS_AS float*)(&sbuf[1][0]);
 
   const DecodeParams& p = a.p;
   const int tid = threadIdx.x;
@@ -338,11 +446,15 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
   f32x4 o[kFeatBlocks];
   float m_run = -INFINITY, l_run = 0.f;
 
-  TileDma dma;
-  TileInfo next = unit.prepare(a, unit.f_begin, buf0, tid, dma);
-  dma.load_all();
+  TileDma<FP8> dma;
+  TileInfo next = unit.prepare(a, unit.f_begin, FP8 ? stage0 : buf0, sb0, tid, dma);
+  dma_all(dma);
 
-  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
+  // cur: bf16 tile computed in this step; nxt: where the next tile's loads go;
+  // stage / sbc / sbn: fp8 staging page of this tile and the scale buffers.
+  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt,
+                  const LDS_AS uint8_t* const stage, const LDS_AS float* const sbc,
+                  LDS_AS float* const sbn) {
     const TileInfo ti = next;
     const int bc = ti.b, t = ti.t, L = ti.L;
 
@@ -369,11 +481,16 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
     const bool more = f + 1 < unit.f_end;
     wait_tile();
-    if (more) next = unit.prepare(a, f + 1, nxt, tid, dma);
+    if constexpr (FP8) {
+      widen_fp8_tile(stage, cur, tid);
+      lds_barrier();
+    }
+    if (more) next = unit.prepare(a, f + 1, nxt, sbn, tid, dma);
 
     // ---- QK GEMM: S^T (keys x rows) for this wave's keys, K from LDS, Q^T in registers
     constexpr int NACC = NKB == 1 ? 2 : NKB;      // split a lone chain in two
     constexpr int NQK = kQChunks * NKB;
+    constexpr int NPV = NARROW ? kFeatBlocks : 2 * kFeatBlocks;   // PV MFMAs
     f32x4 s[NACC];
 #pragma unroll
     for (int x = 0; x < NACC; ++x) s[x] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -392,9 +509,7 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
         if (i + kQkDepth < NQK) ring[i % kQkDepth] = ld128(kaddr(i + kQkDepth));
         const int acc = NKB == 1 ? (c & 1) : kb;
         s[acc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[c], s[acc], 0, 0, 0);
-        // next tile's loads, spread over the QK MFMAs
-        constexpr int kEvery = NQK / kLoadsPerThread;
-        if (more && (i % kEvery) == kEvery - 1) dma.load(i / kEvery);
+        dma_slot<NQK>(dma, more, i);
         sched_fence();
       }
     }
@@ -404,12 +519,17 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
     const int key0 = t * kPage + key_blk * 16;
     const int vis = L - p.q_len + (row < R ? row : R - 1) / p.num_heads + 1;
     const bool need_mask = (t * kPage + kPage) > (L - p.q_len + 1);
+    // fp8: per-token scales of this lane's keys (folded into scores and P)
+    f32x4 ksc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      ksc[kb] = FP8 ? *(const LDS_AS f32x4*)(sbc + 16 * (key_blk + kb) + 4 * g) : f32x4{1.f, 1.f, 1.f, 1.f};
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = s[kb][r] * p.scale_log2;
+        float v = s[kb][r] * (FP8 ? ksc[kb][r] * p.scale_log2 : p.scale_log2);
         if (need_mask && (key0 + kb * 16 + 4 * g + r) >= vis) v = -INFINITY;
         s[kb][r] = v;
         mx = fmaxf(mx, v);
@@ -432,7 +552,7 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pr = exp2_fast(s[kb][r] - m_eff);
-        s[kb][r] = pr;
+        s[kb][r] = FP8 ? pr * ksc[kb][r] : pr;   // PV weight of the unscaled fp8 row
         l_run += pr;
       }
     }
@@ -468,7 +588,6 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
             pb[c32][4 + r] = (__bf16)s[2 * c32 + 1][r];
           }
         }
-        constexpr int NPV = 2 * kFeatBlocks;
         bf16x4 r0[kPvDepth], r1[kPvDepth];
 #pragma unroll
         for (int i = 0; i < kPvDepth; ++i) {
@@ -568,8 +687,13 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
   // Two copies of the step with the buffers fixed at compile time.
   for (int f = unit.f_begin; f < unit.f_end; f += 2) {
-    step(f, buf0, buf1);
-    if (f + 1 < unit.f_end) step(f + 1, buf1, buf0);
+    if constexpr (FP8) {
+      step(f, buf0, stage1, stage0, sb0, sb1);
+      if (f + 1 < unit.f_end) step(f + 1, buf0, stage0, stage1, sb1, sb0);
+    } else {
+      step(f, buf0, buf1, nullptr, nullptr, nullptr);
+      if (f + 1 < unit.f_end) step(f + 1, buf1, buf0, nullptr, nullptr, nullptr);
+    }
   }
 }
 
@@ -595,6 +719,7 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
 constexpr int kQkDepthX = 4;
 constexpr int kPvDepthX = 4;
 
+template <bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
     const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
@@ -610,8 +735,13 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   __shared__ __attribute__((aligned(16))) bf16x8 p_lds[4][2][64];   // [k-step][row half][lane]
   __shared__ float smax[2][64];                                      // [key half][row]
   __shared__ float ssum[2][64];
+  __shared__ __attribute__((aligned(16))) float sbuf[2][kPage];   // fp8 per-token scales
   LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
   LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
+  LDS_AS uint8_t* const stage0 = buf1;
+  LDS_AS uint8_t* const stage1 = buf1 + kFp8TileBytes;
+  LDS_AS float* const sb0 = (LDS_AS float*)(&sbuf[0][0]);
+  LDS_AS float* const sb1 = (LDS_AS float*)(&sbuf[1][0]);
 
   const DecodeParams& p = a.p;
   const int tid = threadIdx.x;
@@ -656,11 +786,15 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   float m_run[2] = {-INFINITY, -INFINITY};   // running max of rows row0 + n, row0 + 32 + n
   float l_run = 0.f;                         // partial row sum of row_qk (this key half, lane half)
 
-  TileDma dma;
-  TileInfo next = unit.prepare(a, unit.f_begin, buf0, tid, dma);
-  dma.load_all();
+  TileDma<FP8> dma;
+  TileInfo next = unit.prepare(a, unit.f_begin, FP8 ? stage0 : buf0, sb0, tid, dma);
+  dma_all(dma);
 
-  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
+  // cur: bf16 tile computed in this step; nxt: where the next tile's loads go;
+  // stage / sbc / sbn: fp8 staging page of this tile and the scale buffers.
+  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt,
+                  const LDS_AS uint8_t* const stage, const LDS_AS float* const sbc,
+                  LDS_AS float* const sbn) {
     const TileInfo ti = next;
     const int bc = ti.b, t = ti.t, L = ti.L;
 
@@ -686,7 +820,11 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
     const bool more = f + 1 < unit.f_end;
     wait_tile();
-    if (more) next = unit.prepare(a, f + 1, nxt, tid, dma);
+    if constexpr (FP8) {
+      widen_fp8_tile(stage, cur, tid);
+      lds_barrier();
+    }
+    if (more) next = unit.prepare(a, f + 1, nxt, sbn, tid, dma);
 
     // ---- QK GEMM: S^T[32 keys of half kh, 32 rows of half rh]
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -700,8 +838,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
         const bf16x8 av = ring[c % kQkDepthX];
         if (c + kQkDepthX < kQSteps) ring[c % kQkDepthX] = ld128(kaddr(c + kQkDepthX));
         sacc[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], sacc[c & 1], 0, 0, 0);
-        // next tile's loads, one after every second QK MFMA
-        if (more && (c & 1)) dma.load(c >> 1);
+        dma_slot<kQSteps>(dma, more, c);
         sched_fence();
       }
     }
@@ -711,10 +848,14 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     const int key0 = t * kPage + 32 * kh + 4 * h;
     const int vis = L - p.q_len + (row_qk < R ? row_qk : R - 1) / p.num_heads + 1;
     const bool need_mask = (t * kPage + kPage) > (L - p.q_len + 1);
+    f32x4 ksc[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      ksc[jj] = FP8 ? *(const LDS_AS f32x4*)(sbc + 32 * kh + 8 * jj + 4 * h) : f32x4{1.f, 1.f, 1.f, 1.f};
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float v = sv[r] * p.scale_log2;
+      float v = sv[r] * (FP8 ? ksc[r >> 2][r & 3] * p.scale_log2 : p.scale_log2);
       if (need_mask && (key0 + 8 * (r >> 2) + (r & 3)) >= vis) v = -INFINITY;
       sv[r] = v;
       mx = fmaxf(mx, v);
@@ -748,9 +889,10 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       bf16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pr = exp2_fast(sv[8 * sidx + e] - m_eff);
+        const int r = 8 * sidx + e;
+        const float pr = exp2_fast(sv[r] - m_eff);
         l_run += pr;
-        pb[e] = (__bf16)pr;
+        pb[e] = (__bf16)(FP8 ? pr * ksc[r >> 2][r & 3] : pr);
       }
       p_lds[2 * kh + sidx][rh][lane] = pb;
     }
@@ -827,8 +969,13 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   };
 
   for (int f = unit.f_begin; f < unit.f_end; f += 2) {
-    step(f, buf0, buf1);
-    if (f + 1 < unit.f_end) step(f + 1, buf1, buf0);
+    if constexpr (FP8) {
+      step(f, buf0, stage1, stage0, sb0, sb1);
+      if (f + 1 < unit.f_end) step(f + 1, buf0, stage0, stage1, sb1, sb0);
+    } else {
+      step(f, buf0, buf1, nullptr, nullptr, nullptr);
+      if (f + 1 < unit.f_end) step(f + 1, buf1, buf0, nullptr, nullptr, nullptr);
+    }
   }
 }
 
@@ -1025,12 +1172,17 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
   a.qptr = p.q;
   a.kv = p.kv;
 #define MLA_KARGS a.p, a.md, a.prefix, a.split_off, a.seqlens, a.block_table, a.qptr, a.kv
-  if (variant == VAR_NARROW16)
-    hipLaunchKernelGGL(decode_kernel16<VAR_NARROW16>, grid, dim3(kThreads), 0, s, MLA_KARGS);
-  else if (variant == VAR_WIDE64)
-    hipLaunchKernelGGL(decode_kernel16<VAR_WIDE64>, grid, dim3(kThreads), 0, s, MLA_KARGS);
-  else
-    hipLaunchKernelGGL(decode_kernel_x, grid, dim3(kThreads), 0, s, MLA_KARGS);
+  const bool fp8 = p.kv_scale != nullptr;
+  if (variant == VAR_NARROW16) {
+    if (fp8) hipLaunchKernelGGL((decode_kernel16<VAR_NARROW16, true>), grid, dim3(kThreads), 0, s, MLA_KARGS);
+    else hipLaunchKernelGGL((decode_kernel16<VAR_NARROW16, false>), grid, dim3(kThreads), 0, s, MLA_KARGS);
+  } else if (variant == VAR_WIDE64) {
+    if (fp8) hipLaunchKernelGGL((decode_kernel16<VAR_WIDE64, true>), grid, dim3(kThreads), 0, s, MLA_KARGS);
+    else hipLaunchKernelGGL((decode_kernel16<VAR_WIDE64, false>), grid, dim3(kThreads), 0, s, MLA_KARGS);
+  } else {
+    if (fp8) hipLaunchKernelGGL((decode_kernel_x<true>), grid, dim3(kThreads), 0, s, MLA_KARGS);
+    else hipLaunchKernelGGL((decode_kernel_x<false>), grid, dim3(kThreads), 0, s, MLA_KARGS);
+  }
 #undef MLA_KARGS
   return hipGetLastError();
 }

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 # ----------------------------------------------------------------- small configs
 
-@pytest.mark.parametrize("name", ["tiny", "share16", "mtp", "ragged"])
+@pytest.mark.parametrize("name", ["tiny", "share16", "mtp", "ragged", "fp8"])
 @pytest.mark.parametrize("split", [False, True])
 def test_small_config_parity(name, split):
     w = config(name, small=True, seed=1)
@@ -40,6 +40,19 @@ def test_heads_and_query_tokens(H, s):
     out, lse, _ = run_gpu(w, split=True, num_units=7, min_tiles=1)
     ref_out, ref_lse = reference(w)
     assert_parity(w, out, lse, ref_out, ref_lse, f"H={H} s={s}")
+
+
+@pytest.mark.parametrize("H,s", [(16, 1), (16, 3), (64, 2), (128, 2)])
+@pytest.mark.parametrize("split", [False, True])
+def test_fp8_cache_shapes(H, s, split):
+    """fp8 e4m3 cache with per-token scales across the three kernel variants,
+    ragged tails (NaN-poisoned codes and scales past each sequence)."""
+    lens = [1, 63, 64, 65, 300, 1000]
+    lens = [L for L in lens if L >= s] + [s]
+    w = make_workload("fp8-shapes", len(lens), H, s, lens, kv_dtype="fp8_e4m3", seed=17 + H + s)
+    out, lse, _ = run_gpu(w, split=split, num_units=9, min_tiles=1)
+    ref_out, ref_lse = reference(w)
+    assert_parity(w, out, lse, ref_out, ref_lse, f"fp8 H={H} s={s} split={split}")
 
 
 @pytest.mark.parametrize("split", [False, True])
@@ -150,7 +163,7 @@ def test_combine_matches_oracle_merge(R):
 
 # ----------------------------------------------------------------- full sizes, sampled
 
-@pytest.mark.parametrize("name", ["tiny", "share16", "mtp", "ragged"])
+@pytest.mark.parametrize("name", ["tiny", "share16", "mtp", "ragged", "fp8"])
 def test_full_size_sampled(name):
     """Whole-batch run in the launch configuration the benchmark times (default
     split plan), checked against the oracle on a sample of sequences."""
