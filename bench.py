@@ -55,6 +55,23 @@ def algorithmic(w):
                 pages=pages, tokens=int(np.sum(L)))
 
 
+def measured_traffic(config_name: str):
+    """HBM bytes per attention-kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+            t = json.load(f)
+        with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", "mla_kernels.hip"), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if t.get("kernel_source_sha256") != sha or config_name not in t.get("configs", {}):
+        return None
+    return int(t["configs"][config_name]["bytes"])
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle as it stands, on whole sequences in order until `seconds` pass."""
     import numpy as np
@@ -180,6 +197,7 @@ def main():
         achieved = alg["flops"] / main_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["traffic"] = measured_traffic(args.config)
     roof.update({"kernel": "decode_kernel", "kernel_ms": round(main_ms, 5), "launches": launches,
                  "algorithmic_bytes": alg["bytes"], "algorithmic_flops": alg["flops"],
                  "t_roof_us": round(max(t_hbm, t_mfma) * 1e6, 2)})
