@@ -220,13 +220,16 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
     if (g_prof.on) {
       ev0 = take_event();
       ev1 = take_event();
-      if (ev0 && ev1) (void)hipEventRecord(ev0, s);
+      if (!ev0 || !ev1) {
+        if (ev0) g_prof.pool.push_back(ev0);
+        if (ev1) g_prof.pool.push_back(ev1);
+        ev0 = ev1 = nullptr;
+      }
     }
   }
-  hipError_t e = mla::launch_decode(p, var, metadata ? num_units : batch, s);
+  hipError_t e = mla::launch_decode(p, var, metadata ? num_units : batch, s, ev0, ev1);
   if (ev0 && ev1) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    (void)hipEventRecord(ev1, s);
     g_prof.recorded.emplace_back(ev0, ev1);
   }
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));

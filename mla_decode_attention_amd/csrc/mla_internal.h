@@ -51,7 +51,9 @@ enum Variant {
 int variant_for(int rows);
 int variant_rows(int variant);
 
-hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s);
+// ev_start / ev_stop: optional events recorded by the kernel dispatch itself.
+hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s,
+                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles,
                            int32_t* md, hipStream_t s);
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,

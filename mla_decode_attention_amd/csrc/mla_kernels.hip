@@ -39,6 +39,7 @@
 // (sequence, tile) space; sequences cut across units write partial (O, LSE)
 // that the combine kernel merges by log-sum-exp.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <math.h>
 
@@ -51,6 +52,7 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kRowBytes = kDqk * 2;                  // 1152
@@ -69,11 +71,16 @@ static_assert(kLoadsPerThread * kThreads * 16 == kTileBytes, "tile must split ev
 //   lds_byte(k, c) = ((c / 8) * 512 + k * 8 + ((c ^ swz3(k)) % 8)) * 16
 // i.e. [128-byte line group of the row][key][chunk within the line, permuted
 // by a 3-bit function of the key]. One 1 KiB load instruction fills 8 keys x
-// one 128-byte line each (every 8 lanes read one whole cache line), and the
-// permutation keeps both MFMA operand fetches free of bank conflicts: 16
-// consecutive keys at one chunk (QK operand), and 4 consecutive keys x 2
-// adjacent chunks per 16 lanes (transposed V operand).
-__device__ __forceinline__ int swz3(int key) { return (((key >> 1) & 1) << 2) | ((key >> 2) & 3); }
+// one 128-byte line each (every 8 lanes read one whole cache line). With key
+// bits k0..k3, swz3 = (k1, k0^k2, k0^k3) (high to low bit), which keeps every
+// operand fetch of the kernels free of LDS bank conflicts (64 banks of 4
+// bytes; also with 32): 16 consecutive keys at one chunk (QK operand, 16
+// lanes per 16-byte-read cycle) and 8 consecutive keys x 2 adjacent chunks
+// or 4 keys x 4 chunks (transposed V operand, 32 lanes per 8-byte-read
+// cycle) all land on distinct banks.
+__device__ __forceinline__ int swz3(int key) {
+  return (((key >> 1) & 1) << 2) | (((key ^ (key >> 2)) & 1) << 1) | ((key ^ (key >> 3)) & 1);
+}
 __device__ __forceinline__ int lds_byte(int key, int chunk) {
   return ((chunk >> 3) * 512 + key * 8 + ((chunk ^ swz3(key)) & 7)) * 16;
 }
@@ -205,7 +212,6 @@ __device__ __forceinline__ void dma_all(const Dma& dma) {
 // fp8 staging page -> bf16 tile (exact: every E4M3FN value is a bf16 value).
 // Each thread widens 9 slots of 16 codes into 2 chunks of 8 bf16 each.
 __device__ __forceinline__ void widen_fp8_tile(const LDS_AS uint8_t* stage, LDS_AS uint8_t* tile, int tid) {
-  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 #pragma unroll
   for (int j = 0; j < kFp8Loads; ++j) {
@@ -697,6 +703,286 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
   }
 }
 
+// Register-staged page stream (producer waves of NARROW16PC, 256 threads).
+// Two register stages of one page each (18 x 16-byte loads per lane) keep two
+// pages in flight per workgroup while the consumers compute a third from LDS:
+// with two LDS buffers, direct-to-LDS loads could only ever have one page in
+// flight. Right after barrier B0 of tile f the producers write the stage
+// holding tile f+1 into the free LDS buffer and refill that stage with tile
+// f+3. Each refill is exactly 18 loads (a single cache line, never used, when
+// the unit has no such tile), so the wait before every LDS write is the static
+// "all but the 18 newest loads" the compiler derives. Barrier count per tile
+// matches the consumers' (B0, B1, B2).
+struct TileRegs {
+  static constexpr int kLoads = kLoadsPerThread;
+  const uint8_t* page;
+  uint32_t voff[2];
+  __device__ __forceinline__ void plan(const uint8_t* kv, const float* /*kv_scale*/, int page_id,
+                                       int nvalid, LDS_AS uint8_t* /*buf*/, LDS_AS float* /*sbuf*/,
+                                       int ptid) {
+    page = kv + (size_t)page_id * kTileBytes;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int key = 32 * par + (ptid >> 3);
+      const int src_key = key < nvalid ? key : nvalid - 1;
+      voff[par] = src_key * kRowBytes + 16 * ((ptid & 7) ^ swz3(key));
+    }
+  }
+  __device__ __forceinline__ void idle(const uint8_t* kv) {
+    page = kv;
+    voff[0] = voff[1] = 0;
+  }
+  __device__ __forceinline__ void load(u32x4 (&st)[kLoads]) const {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) st[i] = *(const u32x4*)(page + voff[i & 1] + 128 * (i >> 1));
+  }
+};
+
+__device__ __forceinline__ void store_page(const u32x4 (&st)[kLoadsPerThread], LDS_AS uint8_t* buf,
+                                           int ptid) {
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) *(LDS_AS u32x4*)(buf + i * 4096 + ptid * 16) = st[i];
+}
+
+__device__ __forceinline__ void produce_pages(const KernelArgs& a, Unit& unit, LDS_AS uint8_t* buf0,
+                                              LDS_AS uint8_t* buf1, int ptid) {
+  const int f0 = unit.f_begin, fe = unit.f_end;
+  TileRegs r;
+  auto plan = [&](int f) {
+    if (f < fe) (void)unit.prepare(a, f, buf0, nullptr, ptid, r);
+    else r.idle(a.kv);
+  };
+  u32x4 st0[kLoadsPerThread], st1[kLoadsPerThread];
+  plan(f0);
+  r.load(st0);
+  plan(f0 + 1);
+  r.load(st1);
+  store_page(st0, buf0, ptid);
+  plan(f0 + 2);
+  r.load(st0);
+  for (int f = f0; f < fe; f += 2) {
+    lds_barrier();   // B0 of tile f (in buf0)
+    if (f + 1 < fe) store_page(st1, buf1, ptid);
+    plan(f + 3);
+    r.load(st1);
+    lds_barrier();   // B1
+    lds_barrier();   // B2
+    if (f + 1 >= fe) break;
+    lds_barrier();   // B0 of tile f + 1 (in buf1)
+    if (f + 2 < fe) store_page(st0, buf0, ptid);
+    plan(f + 4);
+    r.load(st0);
+    lds_barrier();   // B1
+    lds_barrier();   // B2
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NARROW16PC (bf16 cache, up to 16 rows): 8 waves per workgroup, 2 per SIMD.
+//   Waves 4-7 are producers: they only stream the next page into LDS (their
+//   vector-memory issue stalls never hold up an MFMA wave).
+//   Waves 0-3 are consumers: wave c computes S^T for keys 16c..16c+15 of the
+//   tile (16x16x32 MFMA, Q^T of the 16 rows in registers), the 4 half-tile row
+//   maxima are exchanged in LDS, and each consumer writes its P values into LDS
+//   in the PV B-operand layout; then wave c accumulates O^T for output
+//   features 128c..128c+127 of all 16 rows (O: 32 registers), so no merge of
+//   per-wave outputs is needed at the end.
+//   PV k-step ks (keys 32ks..32ks+31): k-slot 8g + e is key 32ks + 4g + e
+//   (e < 4, from consumer 2ks) or 32ks + 16 + 4g + (e - 4) (from 2ks + 1).
+//   Three workgroup barriers per tile: B0 (tile in LDS, other buffer free),
+//   B1 (row maxima published), B2 (P and, on a sequence's last tile, the row
+//   sums published). The producers keep two pages in flight in registers
+//   (produce_pages).
+// ---------------------------------------------------------------------------
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
+    const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
+    const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
+    const uint8_t* __restrict__ kv_) {
+  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
+  constexpr int kQChunks = kDqk / 32;        // 18 k-steps of 32 features
+  constexpr int kFb = 8;                     // 16-feature output blocks per consumer
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) bf16x8 p_lds[2][64];   // [k-step][lane]
+  __shared__ float smax[4][16];
+  __shared__ float ssum[4][16];
+  LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
+  LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
+
+  const DecodeParams& p = a.p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const bool producer = wave >= 4;
+  const int cw = wave & 3;
+  const int g = lane >> 4, li = lane & 15;
+  const int R = p.rows;
+  const int row = li;
+  const int u = blockIdx.x;
+
+  Unit unit;
+  if (!unit.init(a, u)) {
+    if (!a.md && !producer) write_empty(p, unit.b0, 0, 16);
+    return;
+  }
+
+  // consumer LDS offsets (see decode_kernel16): QK operand of key 16cw + li,
+  // chunk 4c + g; transposed V operand of keys 4g + li/4 (+ 16 per key block)
+  int qk_lane[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) qk_lane[par] = lds_byte(16 * cw + li, 4 * par + g);
+  int v_lane[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+    v_lane[q4] = lds_byte(4 * g + (li >> 2), 2 * q4 + ((li & 3) >> 1)) + 8 * (li & 1);
+
+  bf16x8 qreg[kQChunks];
+  f32x4 o[kFb];
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (producer) {
+    produce_pages(a, unit, buf0, buf1, tid - 256);
+    return;
+  }
+
+  TileDma<false> plan_only;   // consumers use the tile facts, not the load plan
+  TileInfo next = unit.prepare(a, unit.f_begin, buf0, nullptr, tid & 255, plan_only);
+  for (int f = unit.f_begin; f < unit.f_end; ++f) {
+    const bool odd = ((f - unit.f_begin) & 1) != 0;
+    LDS_AS uint8_t* const cur = odd ? buf1 : buf0;
+    const TileInfo ti = next;
+    const bool more = f + 1 < unit.f_end;
+
+    lds_barrier();   // B0: tile f is in `cur`, everyone is done with the other buffer
+    if (more) next = unit.prepare(a, f + 1, buf0, nullptr, tid & 255, plan_only);
+
+    const int bc = ti.b, t = ti.t, L = ti.L;
+    if (ti.first) {
+      const int rr = row < R ? row : R - 1;
+      const bf16x8* qrow = (const bf16x8*)(a.qptr + ((size_t)bc * R + rr) * kDqk);
+#pragma unroll
+      for (int c = 0; c < kQChunks; ++c) {
+        bf16x8 v = qrow[4 * c + g];
+        qreg[c] = row < R ? v : bf16x8{};
+      }
+#pragma unroll
+      for (int fb = 0; fb < kFb; ++fb) o[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run = -INFINITY;
+      l_run = 0.f;
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    }
+
+    // QK: S^T[keys 16cw.., 16 rows]
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
+    {
+      auto kaddr = [&](int c) { return cur + qk_lane[c & 1] + (c >> 1) * kLineGroupBytes; };
+      bf16x8 ring[kQkDepth];
+#pragma unroll
+      for (int i = 0; i < kQkDepth; ++i) ring[i] = ld128(kaddr(i));
+#pragma unroll
+      for (int c = 0; c < kQChunks; ++c) {
+        const bf16x8 av = ring[c % kQkDepth];
+        if (c + kQkDepth < kQChunks) ring[c % kQkDepth] = ld128(kaddr(c + kQkDepth));
+        if (c & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[c], sb, 0, 0, 0);
+        else sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[c], sa, 0, 0, 0);
+        sched_fence();
+      }
+    }
+    f32x4 sv = sa + sb;
+
+    const int key0 = t * kPage + 16 * cw + 4 * g;
+    const int vis = L - p.q_len + (row < R ? row : R - 1) / p.num_heads + 1;
+    const bool need_mask = (t * kPage + kPage) > (L - p.q_len + 1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = sv[r] * p.scale_log2;
+      if (need_mask && (key0 + r) >= vis) v = -INFINITY;
+      sv[r] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) smax[cw][li] = mx;
+    lds_barrier();   // B1
+
+    const float tmax = fmaxf(fmaxf(smax[0][li], smax[1][li]), fmaxf(smax[2][li], smax[3][li]));
+    const float m_new = fmaxf(m_run, tmax);
+    const bool raise = m_new > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? exp2_fast(m_run - m_new) : 1.0f;
+      if (raise) m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int fb = 0; fb < kFb; ++fb) o[fb] *= alpha;
+    }
+    const float m_eff = (m_run == -INFINITY) ? 0.0f : m_run;
+    bf16x4 pq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pr = exp2_fast(sv[r] - m_eff);
+      l_run += pr;
+      pq[r] = (__bf16)pr;
+    }
+    *(LDS_AS bf16x4*)((LDS_AS uint8_t*)&p_lds[cw >> 1][lane] + 8 * (cw & 1)) = pq;
+    if (ti.last) {
+      float ls = l_run + __shfl_xor(l_run, 16);
+      ls += __shfl_xor(ls, 32);
+      if (g == 0) ssum[cw][li] = ls;
+    }
+    lds_barrier();   // B2
+
+    // PV: O^T[features 128cw.., 16 rows] += V^T . P^T
+    {
+      auto vaddr = [&](int i, int second) {
+        const int ks = i / kFb, fb = 8 * cw + (i % kFb);
+        return cur + v_lane[fb & 3] + (fb >> 2) * kLineGroupBytes + (2 * ks + second) * 2048;
+      };
+      constexpr int NPV = 2 * kFb;
+      bf16x4 r0[kPvDepth], r1[kPvDepth];
+#pragma unroll
+      for (int i = 0; i < kPvDepth; ++i) {
+        r0[i] = tr_read(vaddr(i, 0));
+        r1[i] = tr_read(vaddr(i, 1));
+      }
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int ks = i / kFb, fb = i % kFb;
+        if (fb == 0) pb = p_lds[ks][lane];
+        const bf16x8 av = __builtin_shufflevector(r0[i % kPvDepth], r1[i % kPvDepth], 0, 1, 2, 3, 4, 5, 6, 7);
+        if (i + kPvDepth < NPV) {
+          r0[i % kPvDepth] = tr_read(vaddr(i + kPvDepth, 0));
+          r1[i % kPvDepth] = tr_read(vaddr(i + kPvDepth, 1));
+        }
+        o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[fb], 0, 0, 0);
+        sched_fence();
+      }
+    }
+
+    if (ti.last) {
+      const float l_row = ssum[0][li] + ssum[1][li] + ssum[2][li] + ssum[3][li];
+      const bool live = l_row > 0.f;
+      const float inv = live ? 1.0f / l_row : 0.f;
+      if (row < R) {
+        float* dst_o;
+        float* dst_l;
+        if (ti.final_out) {
+          dst_o = p.out + ((size_t)bc * R + row) * kDv;
+          dst_l = p.lse + (size_t)bc * R + row;
+        } else {
+          dst_o = p.ws_out + ((size_t)ti.slot * R + row) * kDv;
+          dst_l = p.ws_lse + (size_t)ti.slot * R + row;
+        }
+#pragma unroll
+        for (int fb = 0; fb < kFb; ++fb) *(f32x4*)(dst_o + 128 * cw + 16 * fb + 4 * g) = o[fb] * inv;
+        if (cw == 0 && g == 0) *dst_l = live ? (m_run + log2_fast(l_row)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // WIDE64X: 64 rows per workgroup on v_mfma_f32_32x32x16_bf16.
 //   QK is split 2 x 2 over the waves: wave w computes S^T[32 keys, 32 rows] for
@@ -1159,7 +1445,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 int variant_for(int rows) { return rows <= 16 ? VAR_NARROW16 : VAR_WIDE64X; }
 int variant_rows(int variant) { return variant == VAR_NARROW16 ? 16 : 64; }
 
-hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s) {
+hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s,
+                         hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int rb = (p.rows + variant_rows(variant) - 1) / variant_rows(variant);
   dim3 grid(grid_units, rb);
   KernelArgs a;
@@ -1171,19 +1458,20 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
   a.block_table = p.block_table;
   a.qptr = p.q;
   a.kv = p.kv;
-#define MLA_KARGS a.p, a.md, a.prefix, a.split_off, a.seqlens, a.block_table, a.qptr, a.kv
+  // The events (may be null) are recorded by the dispatch itself, so their
+  // interval is the kernel's execution alone.
+#define MLA_LAUNCH(kernel, threads) \
+  hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, ev_start, ev_stop, 0, a.p, a.md, a.prefix, \
+                        a.split_off, a.seqlens, a.block_table, a.qptr, a.kv)
   const bool fp8 = p.kv_scale != nullptr;
   if (variant == VAR_NARROW16) {
-    if (fp8) hipLaunchKernelGGL((decode_kernel16<VAR_NARROW16, true>), grid, dim3(kThreads), 0, s, MLA_KARGS);
-    else hipLaunchKernelGGL((decode_kernel16<VAR_NARROW16, false>), grid, dim3(kThreads), 0, s, MLA_KARGS);
-  } else if (variant == VAR_WIDE64) {
-    if (fp8) hipLaunchKernelGGL((decode_kernel16<VAR_WIDE64, true>), grid, dim3(kThreads), 0, s, MLA_KARGS);
-    else hipLaunchKernelGGL((decode_kernel16<VAR_WIDE64, false>), grid, dim3(kThreads), 0, s, MLA_KARGS);
+    if (fp8) MLA_LAUNCH((decode_kernel16<VAR_NARROW16, true>), kThreads);
+    else MLA_LAUNCH(decode_kernel_pc, 2 * kThreads);
   } else {
-    if (fp8) hipLaunchKernelGGL((decode_kernel_x<true>), grid, dim3(kThreads), 0, s, MLA_KARGS);
-    else hipLaunchKernelGGL((decode_kernel_x<false>), grid, dim3(kThreads), 0, s, MLA_KARGS);
+    if (fp8) MLA_LAUNCH((decode_kernel_x<true>), kThreads);
+    else MLA_LAUNCH((decode_kernel_x<false>), kThreads);
   }
-#undef MLA_KARGS
+#undef MLA_LAUNCH
   return hipGetLastError();
 }
 
