@@ -28,6 +28,9 @@ def build(verbose: bool = True) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # no packed-fp32 VALU forms (v_pk_fma_f32 & co.) in device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA accumulators in VGPRs: the softmax rescale and the epilogue
+           # then touch O without AGPR<->VGPR copies
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wno-unused-result",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
     cmd += [os.path.join(HERE, s) for s in SOURCES]

@@ -237,6 +237,31 @@ __device__ __forceinline__ void widen_fp8_tile(const LDS_AS uint8_t* stage, LDS_
   }
 }
 
+// Pairwise reductions across lanes l and l ^ 32 (l ^ 16) on the VALU
+// (v_permlane32_swap / v_permlane16_swap), with no LDS round trip. Both lanes
+// of a pair combine the same two values in the same order, so they agree
+// bit for bit.
+__device__ __forceinline__ float max_xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -541,8 +566,7 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
         mx = fmaxf(mx, v);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m_run, mx);
     const bool raise = m_new > m_run + kRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -620,8 +644,7 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
     if (!ti.last) return;
 
     // ---- epilogue for sequence bc
-    float l_row = l_run + __shfl_xor(l_run, 16);
-    l_row += __shfl_xor(l_row, 32);
+    float l_row = sum_xor32(sum_xor16(l_run));
     float m_row = m_run;
 
     if constexpr (NARROW) {
@@ -902,8 +925,7 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
       sv[r] = v;
       mx = fmaxf(mx, v);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     if (g == 0) smax[cw][li] = mx;
     lds_barrier();   // B1
 
@@ -927,8 +949,7 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
     }
     *(LDS_AS bf16x4*)((LDS_AS uint8_t*)&p_lds[cw >> 1][lane] + 8 * (cw & 1)) = pq;
     if (ti.last) {
-      float ls = l_run + __shfl_xor(l_run, 16);
-      ls += __shfl_xor(ls, 32);
+      const float ls = sum_xor32(sum_xor16(l_run));
       if (g == 0) ssum[cw][li] = ls;
     }
     lds_barrier();   // B2
@@ -985,25 +1006,39 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
 
 // ---------------------------------------------------------------------------
 // WIDE64X: 64 rows per workgroup on v_mfma_f32_32x32x16_bf16.
-//   QK is split 2 x 2 over the waves: wave w computes S^T[32 keys, 32 rows] for
-//   row half rh = w%2 and key half kh = w/2 of the tile (36 k-steps of 16
-//   features; Q of its 32 rows stays in registers).
+//   QK is split over the waves by row half rh = w%2 and feature half fh = w/2:
+//   wave w computes the partial S^T[64 keys, 32 rows] over features
+//   288fh..288fh+287 (18 k-steps of 16 features for each of the two key
+//   blocks of 32). Holding Q of its 32 rows for half the features only (72
+//   registers) leaves the register file room for the 128 O accumulators and
+//   for deep LDS fetch rings. The two feature halves are added through LDS:
+//   wave (rh, fh) owns key block kh = fh for the softmax and receives the
+//   other feature half's partial scores for it.
 //   PV is split by output columns: wave w accumulates O^T[128 features, 64 rows]
 //   for features 128w..128w+127 (O: 128 registers per lane).
 //   C layout of a 32x32 block: lane l holds element [8j + 4h + i][l%32] for
 //   register r = 4j + i, h = l/32.
 //   In PV k-step ks = 2kh + s (keys 32kh + 16s + 0..15) the k-slot 8h + e is
 //   key 32kh + 16s + 4h + e (e < 4) or 32kh + 16s + 8 + 4h + (e - 4): exactly
-//   the S registers 8s..8s+7 of the QK wave's lane. So each QK lane stores its
+//   the S registers 8s..8s+7 of the owning wave's lane. So each lane stores its
 //   P values for a k-step as one 16-byte word, and the PV waves read it back
 //   as their MFMA B operand from the same lane position (P exchange through
 //   LDS with no transposition).
-//   The row max of a tile needs both key halves: the QK waves publish their
-//   half-tile maxima, and every wave derives the same running max for all 64
-//   rows (it needs the rescale factor of every row for its O columns).
+//   The row max of a tile needs both key blocks: the owning waves publish
+//   their half-tile maxima, and every wave derives the same running max for
+//   all 64 rows (it needs the rescale factor of every row for its O columns).
+//   LDS: two bf16 tiles (bf16 cache) or one bf16 tile plus the next page's
+//   codes and scales (fp8 cache); a 16 KiB exchange area that holds the
+//   partial scores, then the P operand, then (epilogue) the row sums; the row
+//   maxima live in the rope columns of the current tile, dead once QK is done.
 // ---------------------------------------------------------------------------
-constexpr int kQkDepthX = 4;
+constexpr int kQkDepthX = 8;
 constexpr int kPvDepthX = 4;
+// The next page's loads are spread over the 36 QK MFMA slots. (Spreading
+// them over the PV slots too issues the last ones so late that the next
+// tile's wait grows by more than the issue stalls it saves.)
+constexpr int kDmaSlotsX = 36;
+constexpr int kXchgBytes = 16384;
 
 template <bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -1012,28 +1047,26 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
     const uint8_t* __restrict__ kv_) {
   const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
-  (void)a;
   constexpr int ROWS_WG = 64;
-  constexpr int kQSteps = kDqk / 16;         // 36 k-steps of 16 features
+  constexpr int kQHalf = kDqk / 32;          // 18 k-steps of 16 features per feature half
+  constexpr int NQ = 2 * kQHalf;             // QK MFMAs per wave and tile: (k-step, key block)
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) bf16x8 p_lds[4][2][64];   // [k-step][row half][lane]
-  __shared__ float smax[2][64];                                      // [key half][row]
-  __shared__ float ssum[2][64];
-  __shared__ __attribute__((aligned(16))) float sbuf[2][kPage];   // fp8 per-token scales
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[FP8 ? kFp8TileBytes + 2 * kPage * 4 : kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t xchg[kXchgBytes];
   LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
   LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
-  LDS_AS uint8_t* const stage0 = buf1;
-  LDS_AS uint8_t* const stage1 = buf1 + kFp8TileBytes;
-  LDS_AS float* const sb0 = (LDS_AS float*)(&sbuf[0][0]);
-  LDS_AS float* const sb1 = (LDS_AS float*)(&sbuf[1][0]);
+  LDS_AS uint8_t* const xb = (LDS_AS uint8_t*)(xchg);
+  // fp8: page codes staged in smem1, per-token scales (double buffered) after them
+  LDS_AS float* const sb0 = (LDS_AS float*)(buf1 + kFp8TileBytes);
+  LDS_AS float* const sb1 = sb0 + kPage;
 
   const DecodeParams& p = a.p;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
-  const int rh = wave & 1, kh = wave >> 1;
+  const int rh = wave & 1, fh = wave >> 1;
+  const int kh = fh;                         // key block this wave owns after the exchange
   const int R = p.rows;
   const int row0 = blockIdx.y * ROWS_WG;
   const int row_qk = row0 + 32 * rh + n;
@@ -1046,11 +1079,13 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   }
 
   // ---- per-lane constant LDS offsets
-  // QK operand for k-step c: key 32kh + n, chunk 2c + h
-  //   = (c/4) line groups + chunk 2(c%4) + h of the line
-  int k_lane[4];
+  // QK operand of key block kb, k-step c = 4m + q: key 32kb + n, chunk
+  // 36fh + 2c + h = lds_byte(key, 36fh + 2q + h) + m line groups
+  int k_lane[2][4];
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) k_lane[q4] = lds_byte(32 * kh + n, 2 * q4 + h);
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) k_lane[kb][q4] = lds_byte(32 * kb + n, 36 * fh + 2 * q4 + h);
   // V transposed fetch: 16-lane group q covers features 128w + 32fb + 16(q%2)
   // + 0..15 and keys 16ks + 4h + j/4 (+8 for the second read): chunk
   // 16w + 4fb + 2(q%2) + (j%4)/2 = (2w + fb/2) line groups + chunk
@@ -1066,21 +1101,30 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
                               lds_byte(4 * h + (j >> 2) + 8 * second, 4 * par + 2 * (q & 1) + ((j & 3) >> 1)) +
                               8 * (j & 1);
   }
+  // exchange area: partial scores [rh][key block][4 x 16 B][lane]
+  LDS_AS uint8_t* const x_give = xb + ((rh * 2 + (1 - kh)) * 4 * 64 + lane) * 16;
+  const LDS_AS uint8_t* const x_take = xb + ((rh * 2 + kh) * 4 * 64 + lane) * 16;
 
-  bf16x8 qreg[kQSteps];
+  bf16x8 qreg[kQHalf];
   f32x16 o[4][2];                            // [feature block][row half]
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) {
+    o[fb][0] = f32x16{};
+    o[fb][1] = f32x16{};
+  }
   float m_run[2] = {-INFINITY, -INFINITY};   // running max of rows row0 + n, row0 + 32 + n
-  float l_run = 0.f;                         // partial row sum of row_qk (this key half, lane half)
+  float l_run = 0.f;                         // partial row sum of row_qk (this key block, lane half)
+  bool restart = true;                       // next rescale zeroes O and l (a sequence starts)
 
   TileDma<FP8> dma;
-  TileInfo next = unit.prepare(a, unit.f_begin, FP8 ? stage0 : buf0, sb0, tid, dma);
+  TileInfo next = unit.prepare(a, unit.f_begin, FP8 ? buf1 : buf0, sb0, tid, dma);
   dma_all(dma);
 
-  // cur: bf16 tile computed in this step; nxt: where the next tile's loads go;
-  // stage / sbc / sbn: fp8 staging page of this tile and the scale buffers.
+  // cur: bf16 tile computed in this step; nxt: where the next tile's loads go
+  // (fp8: the staging area again, free once the current page is widened);
+  // sbc / sbn: fp8 scales of this tile and of the next one.
   auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt,
-                  const LDS_AS uint8_t* const stage, const LDS_AS float* const sbc,
-                  LDS_AS float* const sbn) {
+                  const LDS_AS float* const sbc, LDS_AS float* const sbn) {
     const TileInfo ti = next;
     const int bc = ti.b, t = ti.t, L = ti.L;
 
@@ -1088,17 +1132,14 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       const int rr = row_qk < R ? row_qk : R - 1;
       const bf16x8* qrow = (const bf16x8*)(a.qptr + ((size_t)bc * R + rr) * kDqk);
 #pragma unroll
-      for (int c = 0; c < kQSteps; ++c) {
-        bf16x8 v = qrow[2 * c + h];
+      for (int c = 0; c < kQHalf; ++c) {
+        bf16x8 v = qrow[36 * fh + 2 * c + h];
         qreg[c] = row_qk < R ? v : bf16x8{};
       }
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb) {
-        o[fb][0] = f32x16{};
-        o[fb][1] = f32x16{};
-      }
+      // O and l restart through the rescale below (alpha = 0), so the
+      // accumulators are never reset outside the one rescale path
       m_run[0] = m_run[1] = -INFINITY;
-      l_run = 0.f;
+      restart = true;
       __builtin_amdgcn_s_waitcnt(kVmcntZero);
     }
     const bool final_out = ti.final_out;
@@ -1107,30 +1148,51 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     const bool more = f + 1 < unit.f_end;
     wait_tile();
     if constexpr (FP8) {
-      widen_fp8_tile(stage, cur, tid);
+      widen_fp8_tile(buf1, cur, tid);
       lds_barrier();
     }
     if (more) next = unit.prepare(a, f + 1, nxt, sbn, tid, dma);
 
-    // ---- QK GEMM: S^T[32 keys of half kh, 32 rows of half rh]
+    // ---- QK GEMM: partial S^T[64 keys, 32 rows of half rh] over feature half fh
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
     {
-      auto kaddr = [&](int c) { return cur + k_lane[c & 3] + (c >> 2) * kLineGroupBytes; };
+      auto kaddr = [&](int i) {
+        const int c = i >> 1, kb = i & 1;
+        return cur + k_lane[kb][c & 3] + (c >> 2) * kLineGroupBytes;
+      };
       bf16x8 ring[kQkDepthX];
 #pragma unroll
       for (int i = 0; i < kQkDepthX; ++i) ring[i] = ld128(kaddr(i));
 #pragma unroll
-      for (int c = 0; c < kQSteps; ++c) {
-        const bf16x8 av = ring[c % kQkDepthX];
-        if (c + kQkDepthX < kQSteps) ring[c % kQkDepthX] = ld128(kaddr(c + kQkDepthX));
-        sacc[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], sacc[c & 1], 0, 0, 0);
-        dma_slot<kQSteps>(dma, more, c);
+      for (int i = 0; i < NQ; ++i) {
+        const bf16x8 av = ring[i % kQkDepthX];
+        if (i + kQkDepthX < NQ) ring[i % kQkDepthX] = ld128(kaddr(i + kQkDepthX));
+        sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[i >> 1], sacc[i & 1], 0, 0, 0);
+        dma_slot<kDmaSlotsX>(dma, more, i);
         sched_fence();
       }
     }
-    f32x16 sv = sacc[0] + sacc[1];
+
+    // ---- add the two feature halves: give the other key block's partial,
+    //      take the partner's partial for key block kh
+    {
+      const f32x16 give = kh ? sacc[0] : sacc[1];
+#pragma unroll
+      for (int part = 0; part < 4; ++part)
+        *(LDS_AS f32x4*)(x_give + part * 1024) =
+            f32x4{give[4 * part], give[4 * part + 1], give[4 * part + 2], give[4 * part + 3]};
+    }
+    lds_barrier();
+    f32x16 sv = kh ? sacc[1] : sacc[0];
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      const f32x4 v = *(const LDS_AS f32x4*)(x_take + part * 1024);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[4 * part + e] += v[e];
+    }
 
     // ---- softmax: half-tile maxima -> shared running max -> P
+    LDS_AS float* const smax = (LDS_AS float*)(cur + 8 * kLineGroupBytes);   // [key block][row]
     const int key0 = t * kPage + 32 * kh + 4 * h;
     const int vis = L - p.q_len + (row_qk < R ? row_qk : R - 1) / p.num_heads + 1;
     const bool need_mask = (t * kPage + kPage) > (L - p.q_len + 1);
@@ -1146,21 +1208,22 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       sv[r] = v;
       mx = fmaxf(mx, v);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (h == 0) smax[kh][32 * rh + n] = mx;
+    mx = max_xor32(mx);
+    if (h == 0) smax[kh * 64 + 32 * rh + n] = mx;
     lds_barrier();
 
     float alpha[2];
-    bool any_raise = false;
+    bool any_raise = restart;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const float tmax = fmaxf(smax[0][32 * rb + n], smax[1][32 * rb + n]);
+      const float tmax = fmaxf(smax[32 * rb + n], smax[64 + 32 * rb + n]);
       const float m_new = fmaxf(m_run[rb], tmax);
       const bool raise = m_new > m_run[rb] + kRescaleThreshold;
-      alpha[rb] = raise ? exp2_fast(m_run[rb] - m_new) : 1.0f;
+      alpha[rb] = restart ? 0.0f : raise ? exp2_fast(m_run[rb] - m_new) : 1.0f;
       if (raise) m_run[rb] = m_new;
       any_raise |= raise;
     }
+    restart = false;
     if (__builtin_amdgcn_ballot_w64(any_raise)) {
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
@@ -1170,6 +1233,8 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       l_run *= alpha[rh];
     }
     const float m_eff = (m_run[rh] == -INFINITY) ? 0.0f : m_run[rh];
+    // P operand [k-step][row half][lane] in the exchange area (the partial
+    // scores there were consumed before the barrier above)
 #pragma unroll
     for (int sidx = 0; sidx < 2; ++sidx) {
       bf16x8 pb;
@@ -1180,7 +1245,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
         l_run += pr;
         pb[e] = (__bf16)(FP8 ? pr * ksc[r >> 2][r & 3] : pr);
       }
-      p_lds[2 * kh + sidx][rh][lane] = pb;
+      *(LDS_AS bf16x8*)(xb + (((2 * kh + sidx) * 2 + rh) * 64 + lane) * 16) = pb;
     }
     lds_barrier();
 
@@ -1202,8 +1267,8 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       for (int i = 0; i < NPV; ++i) {
         const int ks = i >> 2, fb = i & 3;
         if (fb == 0) {
-          pbr[0] = p_lds[ks][0][lane];
-          pbr[1] = p_lds[ks][1][lane];
+          pbr[0] = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 0) * 64 + lane) * 16);
+          pbr[1] = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 1) * 64 + lane) * 16);
         }
         const bf16x8 av = __builtin_shufflevector(r0[i % kPvDepthX], r1[i % kPvDepthX], 0, 1, 2, 3, 4, 5, 6, 7);
         if (i + kPvDepthX < NPV) {
@@ -1212,22 +1277,24 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
         }
         o[fb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbr[0], o[fb][0], 0, 0, 0);
         o[fb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbr[1], o[fb][1], 0, 0, 0);
+        if (kDmaSlotsX > NQ) dma_slot<kDmaSlotsX>(dma, more, NQ + i);
         sched_fence();
       }
     }
 
-    lds_barrier();  // every wave is done with `cur`, p_lds and smax
+    lds_barrier();  // every wave is done with `cur` and the exchange area
 
     if (!ti.last) return;
 
     // ---- epilogue for sequence bc: full row sums, then O / l and LSE
-    const float lh = l_run + __shfl_xor(l_run, 32);
-    if (h == 0) ssum[kh][32 * rh + n] = lh;
+    LDS_AS float* const ssum = (LDS_AS float*)xb;   // [key block][row]
+    const float lh = sum_xor32(l_run);
+    if (h == 0) ssum[kh * 64 + 32 * rh + n] = lh;
     lds_barrier();
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int row = row0 + 32 * rb + n;
-      const float l_row = ssum[0][32 * rb + n] + ssum[1][32 * rb + n];
+      const float l_row = ssum[32 * rb + n] + ssum[64 + 32 * rb + n];
       const bool live = l_row > 0.f;
       const float inv = live ? 1.0f / l_row : 0.f;
       if (row < R) {
@@ -1256,11 +1323,11 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
   for (int f = unit.f_begin; f < unit.f_end; f += 2) {
     if constexpr (FP8) {
-      step(f, buf0, stage1, stage0, sb0, sb1);
-      if (f + 1 < unit.f_end) step(f + 1, buf0, stage0, stage1, sb1, sb0);
+      step(f, buf0, buf1, sb0, sb1);
+      if (f + 1 < unit.f_end) step(f + 1, buf0, buf1, sb1, sb0);
     } else {
-      step(f, buf0, buf1, nullptr, nullptr, nullptr);
-      if (f + 1 < unit.f_end) step(f + 1, buf1, buf0, nullptr, nullptr, nullptr);
+      step(f, buf0, buf1, nullptr, nullptr);
+      if (f + 1 < unit.f_end) step(f + 1, buf1, buf0, nullptr, nullptr);
     }
   }
 }
