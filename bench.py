@@ -55,16 +55,27 @@ def algorithmic(w):
                 pages=pages, tokens=int(np.sum(L)))
 
 
+def kernel_source_digest() -> str:
+    """SHA-256 of the kernel source with comments and blank space removed, so
+    that editing a comment does not count as changing the kernel."""
+    import hashlib
+    import re
+    with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", "mla_kernels.hip")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = "\n".join(" ".join(line.split()) for line in src.splitlines() if line.strip())
+    return hashlib.sha256(src.encode()).hexdigest()
+
+
 def measured_traffic(config_name: str):
     """HBM bytes per attention-kernel launch from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel
     source has changed since the counters were taken."""
-    import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
             t = json.load(f)
-        with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", "mla_kernels.hip"), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_digest()
     except OSError:
         return None
     if t.get("kernel_source_sha256") != sha or config_name not in t.get("configs", {}):

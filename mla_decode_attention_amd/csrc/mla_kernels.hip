@@ -6,34 +6,36 @@
 // warp-group pipelines described there are prior art only; this is the
 // CDNA4 mapping:
 //
-//  * Data load: one tile = one 64-token page (64 x 576 bf16 = 72 KiB) moved
-//    by direct global->LDS 16-byte loads (no register staging) into one of
-//    two LDS buffers, so the next page streams in while the current one is
-//    computed. The LDS layout (below) makes every MFMA operand fetch a
-//    per-lane constant address plus a compile-time offset, free of bank
-//    conflicts for both the QK and the transposed PV reads.
+//  * Data load: one tile = one 64-token page (64 x 576 bf16 = 72 KiB) in one
+//    of two LDS buffers, so the next page streams in while the current one is
+//    computed. The 16-row kernel streams pages through the registers of
+//    dedicated producer waves; the 64-row kernels use direct global->LDS
+//    16-byte loads issued between MFMAs. The LDS layout (below) makes every
+//    MFMA operand fetch a per-lane constant address plus a compile-time
+//    offset, free of bank conflicts.
 //  * QK GEMM: S^T[key, row] = K . Q^T on bf16 MFMA with fp32 accumulation.
-//    Each wave keeps its query rows in registers for the whole KV loop; K
-//    comes from LDS. Every head of a sequence shares each tile.
+//    Each wave keeps its query rows (or a feature half of them) in registers
+//    for the whole KV loop; K comes from LDS. Every head of a sequence shares
+//    each tile.
 //  * Softmax: base-2 online softmax per row, reduced across the lanes that
 //    hold a row; causal/tail masking only on tiles that need it; the running
 //    max is raised lazily (only when it grows by more than 2^8), so the O
 //    accumulators are rarely rescaled.
 //  * PV GEMM: O^T[feature, row] += V^T . P^T. V is the first 512 columns of
-//    the same LDS tile, read transposed with ds_read_b64_tr_b16; P^T comes
-//    straight out of the QK accumulators in the layout the MFMA B operand
-//    wants (the key order inside each MFMA k-step is permuted to match), so P
-//    never goes through LDS.
+//    the same LDS tile, read transposed with ds_read_b64_tr_b16; P^T leaves
+//    the QK accumulators in the layout the MFMA B operand wants (the key
+//    order inside each MFMA k-step is permuted to match), and is exchanged
+//    through LDS between the waves that own keys and the waves that own
+//    output features.
 //
-// Three variants by rows per sequence (R = q_len * heads):
-//   NARROW16 (R <= 16):  16 rows; the 4 waves split each tile's 64 keys, their
-//                        partial states are merged at the end (16x16 MFMA).
-//   WIDE64   (kept for reference): 64 rows; wave w owns rows 16w..16w+15
-//                        (16x16 MFMA).
-//   WIDE64X  (R > 16):   64 rows; QK split 2x2 (row half x key half) over the
-//                        waves, PV split by output columns (32x32 MFMA); P is
-//                        exchanged through LDS. About 2.2x fewer LDS bytes
-//                        per flop than WIDE64.
+// Variants by rows per sequence (R = q_len * heads):
+//   NARROW16PC (R <= 16, bf16): 8 waves, 4 producers + 4 consumers; the
+//                        consumers split the keys for QK and the output
+//                        features for PV (16x16 MFMA).
+//   NARROW16   (R <= 16, fp8):  4 waves split each tile's 64 keys, partial
+//                        states merged at the end (16x16 MFMA).
+//   WIDE64X    (R > 16): 64 rows; QK split 2x2 (row half x feature half) over
+//                        the waves, PV split by output columns (32x32 MFMA).
 //
 // Split-KV: work units of equal tile count over the flattened
 // (sequence, tile) space; sequences cut across units write partial (O, LSE)
