@@ -13,6 +13,10 @@ overview) splits one MLA pass into data load, QK GEMM, online-softmax update
 and PV GEMM; the online softmax reaches the same result as the plain softmax up
 to rounding order, so the oracle is the plain softmax written out.
 
+It also holds the cache append (each sequence's newest latent rows stored in
+their pages, quantised per token to E4M3FN for the 8-bit cache), the step
+just before attention in a decode step.
+
 Every function is pinned by tests that do not reuse it (closed forms,
 invariants, a pure-Python brute force, library cross-checks); see tests/.
 """
@@ -21,4 +25,5 @@ from .mla_oracle import (  # noqa: F401
     bf16_bits_to_f64, e4m3fn_value, E4M3FN_TABLE, decode_e4m3fn,
     sequence_rows, visible_counts, attend, attend_partials, lse_merge,
     mla_decode, mla_decode_sequence, split_schedule,
+    E4M3FN_MAX, encode_e4m3fn, quantize_token_e4m3, append_kv,
 )

@@ -228,3 +228,79 @@ def split_schedule(seqlens, num_units, min_tiles_per_unit=8):
     return dict(payload=payload, units_used=-(-T // payload) if T else 0, prefix=prefix,
                 num_splits=num_splits, split_offset=split_offset,
                 total_partials=split_offset[-1])
+
+
+# --------------------------------------------------------------------------
+# Appending new tokens' latent rows to the cache (the step before attention
+# in a decode step; cache quantisation C8 of PaddleNLP issue #10157's
+# overview, read as OCP E4M3FN codes with one fp32 scale per token).
+# --------------------------------------------------------------------------
+
+E4M3FN_MAX = 448.0
+
+
+def encode_e4m3fn(x) -> np.ndarray:
+    """Nearest OCP E4M3FN code to each value, ties to the code with the even
+    mantissa (round to nearest even), read off the format's value table.
+
+    Only |x| <= 448 is accepted (callers clamp first). The sign of x is kept,
+    so values that round to zero give 0x00 or 0x80.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.abs(x) <= E4M3FN_MAX):
+        raise ValueError("encode_e4m3fn takes |x| <= 448")
+    pos = E4M3FN_TABLE[:0x7F]                       # codes 0x00..0x7E, ascending 0..448
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - pos[lo]
+    d_hi = pos[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << np.uint8(7))
+
+
+def quantize_token_e4m3(x_f32) -> tuple[np.ndarray, np.float32]:
+    """One token's row -> (E4M3FN codes, fp32 scale).
+
+    scale = max|x| / 448 in fp32 (1 for an all-zero row); code = nearest-even
+    E4M3FN of clamp(x / scale, -448, 448), the division done in fp32. Every
+    fp32 operation here is a single correctly rounded IEEE operation.
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x)))
+    scale = np.float32(amax / np.float32(E4M3FN_MAX)) if amax > 0 else np.float32(1.0)
+    y = np.clip((x / scale).astype(np.float32), -E4M3FN_MAX, E4M3FN_MAX)
+    return encode_e4m3fn(y), scale
+
+
+def append_kv(latent_bits, block_table, seqlens, cache, kv_scale=None, kv_dtype="bf16"):
+    """Store each sequence's newest latent rows in their pages; returns new
+    (cache, kv_scale) arrays (inputs are not modified).
+
+    latent_bits: bf16 bits [B, s, 576]; seqlens include the new tokens, so
+    token i of sequence b is position j = L_b - s + i, stored at page
+    block_table[b][j // 64], slot j % 64. Positions j < 0 are skipped.
+    bf16 cache: the bits are copied. fp8 cache: quantize_token_e4m3 of the
+    row's exact fp32 values.
+    """
+    latent_bits = np.asarray(latent_bits, dtype=np.uint16)
+    B, s, _ = latent_bits.shape
+    cache = np.array(cache, copy=True)
+    kv_scale = None if kv_scale is None else np.array(kv_scale, copy=True)
+    for b in range(B):
+        L = int(seqlens[b])
+        for i in range(s):
+            j = L - s + i
+            if j < 0:
+                continue
+            page = int(block_table[b][j // PAGE_TOKENS])
+            slot = j % PAGE_TOKENS
+            if kv_dtype == "bf16":
+                cache[page, slot] = latent_bits[b, i]
+            else:
+                x = bf16_bits_to_f64(latent_bits[b, i]).astype(np.float32)   # exact
+                codes, sc = quantize_token_e4m3(x)
+                cache[page, slot] = codes
+                kv_scale[page, slot] = sc
+    return cache, kv_scale

@@ -400,3 +400,76 @@ def test_workload_generators_are_seeded_and_shaped():
     pg = f.block_table[0, 0]
     vals = oracle.decode_e4m3fn(f.cache[pg, :min(64, L)])
     assert np.all(np.max(np.abs(vals), axis=1) == 448.0)
+
+
+# ----------------------------------------------------------------- cache append (E4M3FN encode)
+
+def _finite_codes():
+    return [c for c in range(256) if (c & 0x7F) != 0x7F]
+
+
+def test_e4m3_encode_round_trips_every_code():
+    # every finite code's value encodes back to that code (the format definition)
+    codes = np.array(_finite_codes(), dtype=np.uint8)
+    vals = np.array([oracle.e4m3fn_value(int(c)) for c in codes])
+    assert np.array_equal(oracle.encode_e4m3fn(vals), codes)
+
+
+def test_e4m3_encode_ties_go_to_even_and_neighbours_to_nearest():
+    pos = [oracle.e4m3fn_value(c) for c in range(0x7F)]   # 0 .. 448
+    for c in range(0x7E):
+        lo, hi = pos[c], pos[c + 1]
+        mid = (lo + hi) / 2            # exact in float64
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.encode_e4m3fn([mid])[0] == even
+        assert oracle.encode_e4m3fn([-mid])[0] == even | 0x80
+        step = (hi - lo) * 1e-6
+        assert oracle.encode_e4m3fn([mid - step])[0] == c
+        assert oracle.encode_e4m3fn([mid + step])[0] == c + 1
+
+
+def test_e4m3_encode_matches_torch_on_random_values():
+    # library cross-check: torch's float32 -> float8_e4m3fn (round to nearest even)
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 1, 20000),
+                        rng.normal(0, 2.0 ** -8, 20000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.encode_e4m3fn(x.astype(np.float64)), ref)
+
+
+def test_quantize_token_closed_forms():
+    rng = np.random.default_rng(8)
+    x = rng.normal(0, 3, 576).astype(np.float32)
+    codes, sc = oracle.quantize_token_e4m3(x)
+    assert sc == np.float32(np.abs(x).max() / np.float32(448))
+    k = int(np.argmax(np.abs(x)))
+    assert codes[k] == (0x7E if x[k] > 0 else 0xFE)           # the largest entry maps to +-448
+    back = oracle.decode_e4m3fn(codes) * np.float64(sc)
+    # relative error of E4M3 (3 mantissa bits) is at most 2^-4 for normal codes;
+    # absolute error below the smallest normal is at most half a subnormal step
+    err = np.abs(back - x.astype(np.float64))
+    assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * float(sc)) + 1e-12)
+    z_codes, z_sc = oracle.quantize_token_e4m3(np.zeros(576, np.float32))
+    assert z_sc == 1.0 and np.all(z_codes == 0)
+
+
+def test_append_kv_places_rows_and_skips_negative_positions():
+    rng = np.random.default_rng(9)
+    B, s = 3, 2
+    seqlens = np.array([130, 1, 64], dtype=np.int32)     # 1 < s: position -1 is skipped
+    bt = np.array([[5, 2, 7], [0, -1, -1], [3, -1, -1]], dtype=np.int32)
+    lat = f32_to_bf16_bits(rng.normal(size=(B, s, 576)).astype(np.float32))
+    cache = np.zeros((8, 64, 576), np.uint16)
+    new, _ = oracle.append_kv(lat, bt, seqlens, cache)
+    expect = np.zeros_like(cache)
+    expect[7, 0] = lat[0, 0]; expect[7, 1] = lat[0, 1]       # positions 128, 129 -> page bt[0][2]
+    expect[0, 0] = lat[1, 1]                                  # position 0 (token 1); token 0 skipped
+    expect[3, 62] = lat[2, 0]; expect[3, 63] = lat[2, 1]     # positions 62, 63
+    assert np.array_equal(new, expect)
+    c8 = np.zeros((8, 64, 576), np.uint8)
+    s8 = np.ones((8, 64), np.float32)
+    n8, ns = oracle.append_kv(lat, bt, seqlens, c8, s8, "fp8_e4m3")
+    x = oracle.bf16_bits_to_f64(lat[0, 1]).astype(np.float32)
+    codes, sc = oracle.quantize_token_e4m3(x)
+    assert np.array_equal(n8[7, 1], codes) and ns[7, 1] == sc
+    assert np.count_nonzero(ns != 1) == 5
