@@ -166,6 +166,36 @@ int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq
                 int batch, int rows_per_seq, float* out, float* lse, void* stream);
 
 /*
+ * mla_append_kv: store each sequence's newest latent rows in their cache
+ * pages -- the step just before attention in a decode step. The 8-bit cache
+ * is the C8 precision among the cache precisions listed in PaddleNLP issue
+ * #10157's overview, stored here as OCP E4M3FN codes with one fp32 scale per
+ * token.
+ *   latent         device bf16 bits [batch, new_tokens, 576], 16-byte aligned
+ *   batch, new_tokens   >= 1
+ *   block_table    device int32 [batch, max_pages_per_seq]
+ *   cache_seqlens  device int32 [batch]: lengths that already INCLUDE the new
+ *                  tokens (the same array the following mla_decode_fwd uses).
+ *                  Token i of sequence b is position j = L_b - new_tokens + i,
+ *                  stored at page block_table[b][j / 64], slot j % 64.
+ *                  Positions j < 0, j / 64 >= max_pages_per_seq, or page ids
+ *                  outside [0, num_pages) are skipped (nothing is written).
+ *   kv_cache       device [num_pages, 64, 576] bf16 or E4M3FN codes; written
+ *                  only at the appended (page, slot) rows; 16-byte aligned
+ *   kv_scale       device fp32 [num_pages, 64] (fp8 only; NULL for bf16);
+ *                  written only at the appended rows
+ *   kv_dtype       mla_kv_dtype_t
+ * bf16: the row's bits are copied. fp8: scale = max_d |x_d| / 448 (1 for an
+ * all-zero row) and code_d = nearest-even E4M3FN of clamp(x_d / scale, -448,
+ * 448), every step one correctly rounded fp32 operation. Rows with
+ * non-finite values are not supported. Two calls that append to the same
+ * (page, slot) race; different sequences must not share appended positions.
+ */
+int mla_append_kv(const void* latent, int batch, int new_tokens, const int32_t* block_table,
+                  int max_pages_per_seq, const int32_t* cache_seqlens, void* kv_cache, float* kv_scale,
+                  int kv_dtype, int num_pages, void* stream);
+
+/*
  * Measurement hook (diagnostics, not part of the computation).
  * mla_profile_enable(1): from now on every launch of the main decode kernel
  *   (the attention pass of mla_decode_fwd, not the merge) is bracketed by a

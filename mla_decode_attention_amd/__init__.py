@@ -6,6 +6,7 @@ and the current HIP stream. Every step of the computation runs in the HIP
 kernels of the library; there is no fallback: if the library is not built or
 cannot be loaded, every call raises.
 
+    append_kv(latent, block_table, cache_seqlens, kv_cache)          # new tokens' rows
     plan = get_split_metadata(cache_seqlens, q_len, num_heads)     # once per step
     out, lse = decode(q, kv_cache, block_table, cache_seqlens, scale, plan=plan)
 """
@@ -19,7 +20,7 @@ from typing import Optional
 import torch
 
 __all__ = ["load_library", "library_path", "abi_version", "default_num_units", "metadata_bytes",
-           "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "get_split_metadata", "decode", "combine",
+           "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "get_split_metadata", "decode", "combine", "append_kv",
            "MLAError", "KV_BF16", "KV_FP8_E4M3", "PAGE_TOKENS", "D_QK", "D_V"]
 
 PAGE_TOKENS = 64
@@ -60,6 +61,7 @@ def load_library():
         "mla_decode_fwd": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
                                    ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
         "mla_combine": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp]),
+        "mla_append_kv": (c_int, [vp, c_int, c_int, vp, c_int, vp, vp, vp, c_int, c_int, vp]),
         "mla_profile_enable": (c_int, [c_int]),
         "mla_profile_read": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]),
     }
@@ -225,3 +227,36 @@ def combine(part_out: torch.Tensor, part_lse: torch.Tensor, seq_part_offsets: to
     _check(lib.mla_combine(_ptr(part_out), _ptr(part_lse), _ptr(seq_part_offsets), B, R, _ptr(out),
                            _ptr(lse), _stream()), "mla_combine")
     return out, lse
+
+
+def append_kv(latent: torch.Tensor, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+              kv_cache: torch.Tensor, kv_scale: Optional[torch.Tensor] = None):
+    """Store each sequence's newest latent rows in their pages (in place).
+
+    latent bf16 [B, new_tokens, 576]; cache_seqlens int32 [B] already count the
+    new tokens (token i goes to position L_b - new_tokens + i); kv_cache
+    [P, 64, 576] bf16, or uint8 / float8_e4m3fn codes with kv_scale fp32
+    [P, 64] (per-token E4M3FN quantisation).
+    """
+    lib = load_library()
+    _need(latent, "latent", (torch.bfloat16,), 3)
+    B, s, d = latent.shape
+    if d != D_QK:
+        raise ValueError(f"latent last dim must be {D_QK}")
+    fp8_types = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+    _need(kv_cache, "kv_cache", (torch.bfloat16,) + fp8_types, 3)
+    if tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_QK):
+        raise ValueError(f"kv_cache must be [pages, {PAGE_TOKENS}, {D_QK}]")
+    kv_dtype = KV_BF16 if kv_cache.dtype == torch.bfloat16 else KV_FP8_E4M3
+    if kv_dtype == KV_FP8_E4M3:
+        if kv_scale is None:
+            raise ValueError("fp8 cache needs kv_scale")
+        _need(kv_scale, "kv_scale", (torch.float32,), 2)
+    _need(block_table, "block_table", (torch.int32,), 2)
+    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    _check(lib.mla_append_kv(_ptr(latent), B, s, _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
+                             _ptr(kv_cache), _ptr(kv_scale), kv_dtype, kv_cache.shape[0], _stream()),
+           "mla_append_kv")
+    return kv_cache, kv_scale

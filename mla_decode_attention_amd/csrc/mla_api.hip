@@ -260,6 +260,33 @@ int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq
   return ok();
 }
 
+int mla_append_kv(const void* latent, int batch, int new_tokens, const int32_t* block_table,
+                  int max_pages_per_seq, const int32_t* cache_seqlens, void* kv_cache, float* kv_scale,
+                  int kv_dtype, int num_pages, void* stream) {
+  if (!latent || !block_table || !cache_seqlens || !kv_cache)
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (batch < 1 || new_tokens < 1 || max_pages_per_seq < 1 || num_pages < 1)
+    return fail(MLA_ERR_INVALID_ARG, "batch, new_tokens, max_pages_per_seq, num_pages must be >= 1");
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_dtype %d not supported", kv_dtype);
+  if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_scale)
+    return fail(MLA_ERR_INVALID_ARG, "fp8 cache needs kv_scale");
+  if (kv_dtype == MLA_KV_BF16 && kv_scale)
+    return fail(MLA_ERR_INVALID_ARG, "kv_scale must be NULL for a bf16 cache");
+  if (!aligned(latent, 16) || !aligned(kv_cache, 16))
+    return fail(MLA_ERR_INVALID_ARG, "latent and kv_cache must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(cache_seqlens, 4) || (kv_scale && !aligned(kv_scale, 4)))
+    return fail(MLA_ERR_INVALID_ARG, "block_table, cache_seqlens, kv_scale must be 4-byte aligned");
+  DevInfo d;
+  int st = device_info(&d);
+  if (st != MLA_OK) return st;
+  hipError_t e = mla::launch_append((const uint16_t*)latent, batch, new_tokens, block_table, max_pages_per_seq,
+                                    cache_seqlens, (uint8_t*)kv_cache, kv_scale,
+                                    kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 0, num_pages, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "append kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int mla_profile_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.on = enable != 0;

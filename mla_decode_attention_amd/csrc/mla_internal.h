@@ -56,6 +56,9 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles,
                            int32_t* md, hipStream_t s);
+hipError_t launch_append(const uint16_t* latent, int batch, int new_tokens, const int32_t* block_table,
+                         int max_pages, const int32_t* seqlens, uint8_t* kv, float* kv_scale, int fp8,
+                         int num_pages, hipStream_t s);
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
                           int offsets_stride_is_md, int batch, int rows, float* out, float* lse,
                           int skip_single, hipStream_t s);

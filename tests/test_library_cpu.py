@@ -102,6 +102,23 @@ def test_combine_argument_errors(lib):
     assert f(FAKE_ODD, FAKE, FAKE, 2, 16, FAKE, FAKE, None) == INVALID
 
 
+def test_append_argument_errors(lib):
+    f = lib.mla_append_kv
+    ok_args = dict(lat=FAKE, B=2, s=1, bt=FAKE, maxp=4, sl=FAKE, kv=FAKE, sc=None, dt=0, P=8)
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return f(a["lat"], a["B"], a["s"], a["bt"], a["maxp"], a["sl"], a["kv"], a["sc"], a["dt"], a["P"], None)
+    assert call(lat=None) == INVALID
+    assert call(B=0) == INVALID
+    assert call(s=0) == INVALID
+    assert call(P=0) == INVALID
+    assert call(dt=7) == UNSUPPORTED
+    assert call(dt=1, sc=None) == INVALID           # fp8 needs scales
+    assert call(dt=0, sc=FAKE) == INVALID           # bf16 takes none
+    assert call(lat=FAKE_ODD) == INVALID
+    assert call(kv=FAKE_ODD) == INVALID
+
+
 def test_binding_rejects_host_tensors():
     import torch
     q = torch.zeros(1, 1, 16, 576, dtype=torch.bfloat16)
