@@ -174,6 +174,27 @@ def mla_decode_sequence(q_bits_b, cache, block_table_row, seqlen, softmax_scale,
     return O.reshape(s, H, D_V), lse.reshape(s, H)
 
 
+def mla_decode_varlen(q_bits, cu_q, cache, block_table, seqlens, softmax_scale, kv_dtype="bf16",
+                      kv_scale=None, batch_indices=None):
+    """Per-sequence q_len (the MTP verification of PaddleNLP issue #10157: each
+    request checks 1 + its own number of draft tokens). q_bits uint16 [T, H, 576];
+    the s_b = cu_q[b+1] - cu_q[b] query tokens of sequence b are rows
+    cu_q[b]..cu_q[b+1], and query i of them sees keys j <= L_b - s_b + i.
+    Returns out [T, H, 512], lse [T, H] float64 (rows of sequences not listed in
+    batch_indices stay 0 / -inf)."""
+    T, H, _ = q_bits.shape
+    out = np.zeros((T, H, D_V), dtype=np.float64)
+    lse = np.full((T, H), -np.inf, dtype=np.float64)
+    idx = range(len(seqlens)) if batch_indices is None else list(batch_indices)
+    for b in idx:
+        r0, r1 = int(cu_q[b]), int(cu_q[b + 1])
+        if r1 == r0:
+            continue
+        out[r0:r1], lse[r0:r1] = mla_decode_sequence(q_bits[r0:r1], cache, block_table[b], seqlens[b],
+                                                      softmax_scale, kv_dtype, kv_scale)
+    return out, lse
+
+
 def mla_decode(q_bits, cache, block_table, seqlens, softmax_scale, kv_dtype="bf16",
                kv_scale=None, batch_indices=None):
     """Whole batch (or the listed sequences): out [B, s, H, 512], lse [B, s, H] float64."""

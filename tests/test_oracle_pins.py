@@ -473,3 +473,37 @@ def test_append_kv_places_rows_and_skips_negative_positions():
     codes, sc = oracle.quantize_token_e4m3(x)
     assert np.array_equal(n8[7, 1], codes) and ns[7, 1] == sc
     assert np.count_nonzero(ns != 1) == 5
+
+
+# ----------------------------------------------------------------- per-sequence q_len
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_varlen_brute_force_agreement(kv):
+    # each sequence's rows against the pure-Python definition with its own q_len
+    w = make_workload("vl", 4, 2, 1, [5, 9, 4, 2], kv_dtype=kv, seed=31, q_lens=[1, 3, 0, 3])
+    out, lse = oracle.mla_decode_varlen(w.q_bits, w.cu_q, w.cache, w.block_table, w.seqlens,
+                                        w.softmax_scale, w.kv_dtype, w.kv_scale)
+    assert out.shape == (7, 2, D_V) and lse.shape == (7, 2)
+    for b in range(4):
+        r0, r1 = int(w.cu_q[b]), int(w.cu_q[b + 1])
+        if r1 == r0:
+            continue
+        one = make_workload("vl1", 1, 2, r1 - r0, [int(w.seqlens[b])], kv_dtype=kv, seed=0)
+        one.q_bits = w.q_bits[r0:r1][None]
+        one.cache, one.kv_scale, one.block_table = w.cache, w.kv_scale, w.block_table[b:b + 1]
+        bo, bl = brute_force(one)
+        fin = np.isfinite(bl[0])
+        assert np.array_equal(fin, np.isfinite(lse[r0:r1]))
+        assert np.max(np.abs(out[r0:r1] - bo[0])) <= 1e-12 * max(1.0, np.max(np.abs(bo)))
+        assert np.max(np.abs(lse[r0:r1][fin] - bl[0][fin])) <= 1e-12 * max(1.0, np.max(np.abs(bl[0][fin])))
+    # sequence 3 (q_len 3 > L 2): its first query sees no key
+    assert np.all(np.isneginf(lse[4])) and np.all(out[4] == 0)
+
+
+def test_varlen_uniform_q_len_equals_batched_call():
+    w = make_workload("vu", 3, 4, 2, [70, 3, 200], seed=32)
+    flat = w.q_bits.reshape(-1, 4, 576)
+    cu = np.arange(0, 7, 2, dtype=np.int32)
+    o1, l1 = oracle.mla_decode_varlen(flat, cu, w.cache, w.block_table, w.seqlens, w.softmax_scale)
+    o2, l2 = run_oracle(w)
+    assert np.array_equal(o1, o2.reshape(-1, 4, D_V)) and np.array_equal(l1, l2.reshape(-1, 4))

@@ -7,7 +7,10 @@ page slots. It holds none of the attention arithmetic. Both the CPU oracle and
 the GPU path consume exactly the bytes it returns.
 
 Shapes (all row-major, contiguous):
-  q_bits       uint16 [B, s, H, 576]   bf16 bit patterns (512 latent + 64 rope)
+  q_bits       uint16 [B, s, H, 576]   bf16 bit patterns (512 latent + 64 rope), or
+               uint16 [T, H, 576]      with a per-sequence q_len: the query
+                                       tokens of sequence b are rows
+                                       cu_q[b] .. cu_q[b+1] (cu_q int32 [B+1])
   cache        uint16 [P, 64, 576]     bf16 bit patterns, or
                uint8  [P, 64, 576]     E4M3FN codes
   kv_scale     float32 [P, 64]         per-token dequant scale (fp8 only)
@@ -15,7 +18,8 @@ Shapes (all row-major, contiguous):
   seqlens      int32  [B]
 
 Draw order for one workload (one numpy PCG64 stream): sequence lengths, the
-page permutation, q, then the latent cache page by page.
+page permutation, the per-sequence query counts (if drawn), q, then the
+latent cache page by page.
 """
 from __future__ import annotations
 
@@ -46,18 +50,32 @@ class Workload:
     softmax_scale: float
     kv_dtype: str                      # "bf16" or "fp8_e4m3"
     meta: dict = field(default_factory=dict)
+    cu_q: Optional[np.ndarray] = None  # int32 [B+1] when q_len varies per sequence
+
+    @property
+    def varlen(self):
+        return self.cu_q is not None
 
     @property
     def batch(self):
-        return int(self.q_bits.shape[0])
+        return int(self.seqlens.shape[0])
+
+    @property
+    def q_lens(self):
+        if self.varlen:
+            return np.diff(self.cu_q).astype(np.int32)
+        return np.full(self.batch, self.q_bits.shape[1], dtype=np.int32)
 
     @property
     def q_len(self):
+        """Query tokens per sequence (the largest one for a per-sequence q_len)."""
+        if self.varlen:
+            return int(self.q_lens.max()) if self.batch else 0
         return int(self.q_bits.shape[1])
 
     @property
     def num_heads(self):
-        return int(self.q_bits.shape[2])
+        return int(self.q_bits.shape[-2])
 
     @property
     def num_pages(self):
@@ -86,8 +104,12 @@ def make_workload(name: str, batch: int, num_heads: int, q_len: int, seqlens,
                   kv_dtype: str = "bf16", seed: int = 0, table: str = "shuffled",
                   softmax_scale: float = DEFAULT_SCALE, poison_tail: bool = True,
                   rng: Optional[np.random.Generator] = None,
-                  page_chunk: int = 512) -> Workload:
+                  page_chunk: int = 512, q_lens=None) -> Workload:
     """Build one workload. `seqlens` is an int array or a callable(rng) -> array.
+
+    q_lens (optional): per-sequence query counts (an int array or a
+    callable(rng) -> array); q is then drawn as [sum(q_lens), H, 576] with
+    offsets cu_q, and `q_len` is ignored.
 
     table: "identity" (pages laid out in (sequence, tile) order) or "shuffled"
     (a random permutation of the pool assigned in (sequence, tile) order).
@@ -113,7 +135,15 @@ def make_workload(name: str, batch: int, num_heads: int, q_len: int, seqlens,
         block_table[b, :n] = perm[pos:pos + n]
         pos += n
 
-    q32 = rng.standard_normal((batch, q_len, num_heads, D_QK), dtype=np.float32)
+    cu_q = None
+    if q_lens is not None:
+        if callable(q_lens):
+            q_lens = q_lens(rng)
+        q_lens = np.asarray(q_lens, dtype=np.int32).reshape(batch)
+        cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+        q32 = rng.standard_normal((int(cu_q[-1]), num_heads, D_QK), dtype=np.float32)
+    else:
+        q32 = rng.standard_normal((batch, q_len, num_heads, D_QK), dtype=np.float32)
     q_bits = f32_to_bf16_bits(q32)
     del q32
 
@@ -155,7 +185,7 @@ def make_workload(name: str, batch: int, num_heads: int, q_len: int, seqlens,
     return Workload(name=name, q_bits=q_bits, cache=cache, kv_scale=kv_scale,
                     block_table=block_table, seqlens=seqlens,
                     softmax_scale=float(softmax_scale), kv_dtype=kv_dtype,
-                    meta={"seed": seed, "table": table, "total_pages": total_pages})
+                    meta={"seed": seed, "table": table, "total_pages": total_pages}, cu_q=cu_q)
 
 
 # ---------------------------------------------------------------------------
@@ -187,6 +217,9 @@ CONFIGS = {
                    kv_dtype="bf16", table="shuffled"),
     "fp8": dict(batch=128, num_heads=128, q_len=2, seqlens=[8192] * 128, kv_dtype="fp8_e4m3",
                 table="shuffled"),
+    # per-sequence q_len: each sequence verifies 1 + its own number of draft tokens
+    "varlen": dict(batch=128, num_heads=128, q_len=6, q_lens=_uniform_lengths(1, 6, 128),
+                   seqlens=[4096] * 128, kv_dtype="bf16", table="shuffled"),
 }
 
 CONFIG_TEXT = {
@@ -195,6 +228,7 @@ CONFIG_TEXT = {
     "mtp": "batch 128, H=128, q_len=2 causal, seqlen 4096, bf16, shuffled block table",
     "ragged": "batch 32, H=128, q_len=1, 31 log-uniform seqlens in [512,16384] + one 65536, bf16",
     "fp8": "batch 128, H=128, q_len=2 causal, seqlen 8192, fp8 e4m3 cache + per-token fp32 scale",
+    "varlen": "batch 128, H=128, per-sequence q_len U{1..6} causal, seqlen 4096, bf16, shuffled block table",
 }
 
 # Same structure, fewer sequences / shorter contexts.
@@ -208,6 +242,8 @@ SMALL = {
                    kv_dtype="bf16", table="shuffled"),
     "fp8": dict(batch=3, num_heads=128, q_len=2, seqlens=[8192, 777, 65], kv_dtype="fp8_e4m3",
                 table="shuffled"),
+    "varlen": dict(batch=5, num_heads=128, q_len=6, q_lens=[1, 6, 3, 2, 5], seqlens=[4096, 700, 65, 6, 1300],
+                   kv_dtype="bf16", table="shuffled"),
 }
 
 
