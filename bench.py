@@ -38,16 +38,18 @@ PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA (context for the fp8 cac
 def algorithmic(w):
     """Bytes and flops the method itself must move / compute for one step."""
     import numpy as np
-    B, s, H = w.batch, w.q_len, w.num_heads
+    B, H = w.batch, w.num_heads
+    q_lens = [int(x) for x in w.q_lens]
     L = w.seqlens.astype(np.int64)
     e, f = (2, 0) if w.kv_dtype == "bf16" else (1, 4)
     kv = int(np.sum(L * (576 * e + f)))
     pages = int(np.sum((L + 63) // 64))
-    q_bytes = B * s * H * 576 * 2
-    out_bytes = B * s * H * (512 + 1) * 4
-    meta = 4 * pages + 4 * B
+    q_bytes = sum(q_lens) * H * 576 * 2
+    out_bytes = sum(q_lens) * H * (512 + 1) * 4
+    meta = 4 * pages + 4 * B + (4 * (B + 1) if w.varlen else 0)
     vis = 0
     for b in range(B):
+        s = q_lens[b]
         for i in range(s):
             vis += max(0, min(int(L[b]), int(L[b]) - s + i + 1))
     flops = 2 * H * (576 + 512) * vis
@@ -96,11 +98,16 @@ def cpu_baseline(w, seconds: float):
     done, kv, flops = 0, 0, 0
     t0 = time.perf_counter()
     for b in range(w.batch):
-        oracle.mla_decode(w.q_bits, w.cache, w.block_table, w.seqlens, w.softmax_scale,
-                          w.kv_dtype, w.kv_scale, batch_indices=[b])
+        if w.varlen:
+            oracle.mla_decode_varlen(w.q_bits, w.cu_q, w.cache, w.block_table, w.seqlens, w.softmax_scale,
+                                     w.kv_dtype, w.kv_scale, batch_indices=[b])
+        else:
+            oracle.mla_decode(w.q_bits, w.cache, w.block_table, w.seqlens, w.softmax_scale,
+                              w.kv_dtype, w.kv_scale, batch_indices=[b])
         L = int(w.seqlens[b])
+        s = int(w.q_lens[b])
         kv += L * (576 * e + f)
-        flops += 2 * w.num_heads * 1088 * sum(max(0, min(L, L - w.q_len + i + 1)) for i in range(w.q_len))
+        flops += 2 * w.num_heads * 1088 * sum(max(0, min(L, L - s + i + 1)) for i in range(s))
         done += 1
         if time.perf_counter() - t0 >= seconds:
             break
@@ -116,7 +123,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="share16", choices=["tiny", "share16", "mtp", "ragged", "fp8"])
+    ap.add_argument("--config", default="share16", choices=["tiny", "share16", "mtp", "ragged", "fp8", "varlen"])
     ap.add_argument("--sets", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--num-units", type=int, default=0, help="split work units (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -157,8 +164,14 @@ def main():
     sets = args.sets or max(1, min(8, math.ceil(768e6 / max(pool_bytes, 1))))
     kvs = [kv0] + [kv0.clone() for _ in range(sets - 1)]
     scales = [scale0] + [None if scale0 is None else scale0.clone() for _ in range(sets - 1)]
-    out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.float32, device=dev)
-    lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
+    if w.varlen:
+        cu_q = torch.from_numpy(w.cu_q).to(dev)
+        T = int(w.cu_q[-1])
+        out = torch.empty((T, w.num_heads, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((T, w.num_heads), dtype=torch.float32, device=dev)
+    else:
+        out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
     units = args.num_units or mla.default_num_units(w.batch, w.q_len, w.num_heads)
     plan = mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units)
 
@@ -173,7 +186,11 @@ def main():
         mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units, metadata=plan.metadata,
                                workspace=plan.workspace)
         k = i % sets
-        mla.decode(q, kvs[k], bt, sl, w.softmax_scale, kv_scale=scales[k], plan=plan, out=out, lse=lse)
+        if w.varlen:
+            mla.decode_varlen(q, cu_q, w.q_len, kvs[k], bt, sl, w.softmax_scale, kv_scale=scales[k], plan=plan,
+                              out=out, lse=lse)
+        else:
+            mla.decode(q, kvs[k], bt, sl, w.softmax_scale, kv_scale=scales[k], plan=plan, out=out, lse=lse)
 
     for i in range(args.warmup):
         step(i)
@@ -227,7 +244,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {CONFIG_TEXT[args.config]}", "batch": w.batch,
-                   "heads": w.num_heads, "q_len": w.q_len, "kv_dtype": w.kv_dtype,
+                   "heads": w.num_heads, "q_len": w.q_len if not w.varlen else "per-sequence, max %d" % w.q_len,
+                   "query_tokens": int(sum(w.q_lens)), "kv_dtype": w.kv_dtype,
                    "tokens": alg["tokens"], "pages": alg["pages"], "num_units": units,
                    "pool_copies": sets, "seed": 0},
         "tflops": round(tflops, 2),

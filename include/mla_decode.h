@@ -150,6 +150,35 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
                    void* stream);
 
 /*
+ * mla_decode_fwd_varlen: mla_decode_fwd with a query count per sequence, so
+ * one forward verifies sequences that accepted different numbers of draft
+ * tokens in the previous round (PaddleNLP issue #10157, MTP section: the
+ * verification pass keeps the batch and handles each request's 1 + drafts
+ * tokens; q_len up to 6 there).
+ *   q              device bf16 bits [total_q, num_heads, 576], 16-byte aligned;
+ *                  the s_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] query tokens
+ *                  of sequence b are rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]
+ *   cu_seqlens_q   device int32 [batch + 1], cu[0] = 0, non-decreasing,
+ *                  cu[batch] <= total_q, every s_b <= max_q_len (caller
+ *                  contract: the library does not read it on the host)
+ *   total_q        rows of q (>= 1); max_q_len >= 1, max_q_len * num_heads <= MLA_MAX_ROWS
+ *   out, lse       device fp32 [total_q, num_heads, 512] / [total_q, num_heads];
+ *                  rows of sequences with s_b = 0 and rows past cu[batch] are
+ *                  not written
+ * Causal rule per sequence: query i < s_b sees keys j <= L_b - s_b + i.
+ * metadata / workspace: from mla_get_split_metadata and
+ * mla_workspace_bytes(batch, max_q_len, num_heads, num_units), as for
+ * mla_decode_fwd. All other arguments, errors and guarantees are those of
+ * mla_decode_fwd.
+ */
+int mla_decode_fwd_varlen(const void* q, const int32_t* cu_seqlens_q, int total_q, int max_q_len,
+                          const void* kv_cache, const float* kv_scale, int kv_dtype, int num_pages,
+                          const int32_t* block_table, int max_pages_per_seq, const int32_t* cache_seqlens,
+                          int batch, int num_heads, float softmax_scale, float* out, float* lse,
+                          const void* metadata, int num_units, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * mla_combine: merge per-sequence partials by their log-sum-exp.
  *   part_out        device fp32 [num_partials, rows_per_seq, 512], 16-byte aligned
  *   part_lse        device fp32 [num_partials, rows_per_seq] (natural log)

@@ -20,7 +20,7 @@ from typing import Optional
 import torch
 
 __all__ = ["load_library", "library_path", "abi_version", "default_num_units", "metadata_bytes",
-           "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "get_split_metadata", "decode", "combine", "append_kv",
+           "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "get_split_metadata", "decode", "decode_varlen", "combine", "append_kv",
            "MLAError", "KV_BF16", "KV_FP8_E4M3", "PAGE_TOKENS", "D_QK", "D_V"]
 
 PAGE_TOKENS = 64
@@ -62,6 +62,8 @@ def load_library():
                                    ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
         "mla_combine": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp]),
         "mla_append_kv": (c_int, [vp, c_int, c_int, vp, c_int, vp, vp, vp, c_int, c_int, vp]),
+        "mla_decode_fwd_varlen": (c_int, [vp, vp, c_int, c_int, vp, vp, c_int, c_int, vp, c_int, vp, c_int,
+                                          c_int, ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
         "mla_profile_enable": (c_int, [c_int]),
         "mla_profile_read": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]),
     }
@@ -196,6 +198,56 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                               _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), B, s, H,
                               float(softmax_scale), _ptr(out), _ptr(lse), _ptr(md), units, _ptr(ws),
                               wbytes, _stream()), "mla_decode_fwd")
+    return out, lse
+
+
+def decode_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, max_q_len: int, kv_cache: torch.Tensor,
+                  block_table: torch.Tensor, cache_seqlens: torch.Tensor, softmax_scale: float,
+                  kv_scale: Optional[torch.Tensor] = None, plan: Optional[SplitPlan] = None,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """MLA decode with a query count per sequence. Returns (out fp32 [T,H,512], lse fp32 [T,H]).
+
+    q bf16 [T, H, 576]; cu_seqlens_q int32 [B+1] (sequence b owns q rows
+    cu[b]..cu[b+1], at most max_q_len of them); other arguments as decode().
+    A plan comes from get_split_metadata(cache_seqlens, max_q_len, H).
+    """
+    lib = load_library()
+    _need(q, "q", (torch.bfloat16,), 3)
+    T, H, d = q.shape
+    if d != D_QK:
+        raise ValueError(f"q last dim must be {D_QK}")
+    _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,), 1)
+    B = cu_seqlens_q.shape[0] - 1
+    fp8_types = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+    _need(kv_cache, "kv_cache", (torch.bfloat16,) + fp8_types, 3)
+    if tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_QK):
+        raise ValueError(f"kv_cache must be [pages, {PAGE_TOKENS}, {D_QK}]")
+    kv_dtype = KV_BF16 if kv_cache.dtype == torch.bfloat16 else KV_FP8_E4M3
+    if kv_dtype == KV_FP8_E4M3:
+        if kv_scale is None:
+            raise ValueError("fp8 cache needs kv_scale")
+        _need(kv_scale, "kv_scale", (torch.float32,), 2)
+    _need(block_table, "block_table", (torch.int32,), 2)
+    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    if out is None:
+        out = torch.empty((T, H, D_V), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    _need(lse, "lse", (torch.float32,), 2)
+    md = ws = None
+    units, wbytes = 0, 0
+    if plan is not None:
+        if (plan.batch, plan.q_len, plan.num_heads) != (B, max_q_len, H):
+            raise ValueError("plan was built for another shape")
+        md, ws, units, wbytes = plan.metadata, plan.workspace, plan.num_units, plan.workspace.numel()
+    _check(lib.mla_decode_fwd_varlen(_ptr(q), _ptr(cu_seqlens_q), T, int(max_q_len), _ptr(kv_cache),
+                                     _ptr(kv_scale), kv_dtype, kv_cache.shape[0], _ptr(block_table),
+                                     block_table.shape[1], _ptr(cache_seqlens), B, H, float(softmax_scale),
+                                     _ptr(out), _ptr(lse), _ptr(md), units, _ptr(ws), wbytes, _stream()),
+           "mla_decode_fwd_varlen")
     return out, lse
 
 

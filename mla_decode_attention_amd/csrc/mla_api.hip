@@ -155,11 +155,18 @@ int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int num_unit
   return ok();
 }
 
-int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
-                   int num_pages, const int32_t* block_table, int max_pages_per_seq,
-                   const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
-                   float softmax_scale, float* out, float* lse, const void* metadata, int num_units,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of mla_decode_fwd (cu_q == nullptr: q_len query tokens per
+// sequence) and mla_decode_fwd_varlen (cu_q: per-sequence offsets, q_len is
+// the largest count, q holds total_q tokens).
+int decode_impl(const void* q, const int32_t* cu_q, int total_q, const void* kv_cache, const float* kv_scale,
+                int kv_dtype, int num_pages, const int32_t* block_table, int max_pages_per_seq,
+                const int32_t* cache_seqlens, int batch, int q_len, int num_heads, float softmax_scale,
+                float* out, float* lse, const void* metadata, int num_units, void* workspace,
+                size_t workspace_bytes, void* stream) {
   if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !lse)
     return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
@@ -172,14 +179,17 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
   if ((long long)q_len * num_heads > MLA_MAX_ROWS)
     return fail(MLA_ERR_INVALID_ARG, "q_len * num_heads = %lld exceeds %d", (long long)q_len * num_heads,
                 MLA_MAX_ROWS);
+  if (cu_q && total_q < 1) return fail(MLA_ERR_INVALID_ARG, "total_q must be >= 1");
+  if ((long long)(cu_q ? total_q : (long long)batch * q_len) * num_heads > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARG, "query rows exceed the 32-bit row index");
   if (num_pages < 1 || max_pages_per_seq < 1)
     return fail(MLA_ERR_INVALID_ARG, "num_pages and max_pages_per_seq must be >= 1");
   if (!isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
     return fail(MLA_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
   if (!aligned(lse, 4) || !aligned(block_table, 4) || !aligned(cache_seqlens, 4) ||
-      (kv_scale && !aligned(kv_scale, 4)))
-    return fail(MLA_ERR_INVALID_ARG, "lse, block_table, cache_seqlens, kv_scale must be 4-byte aligned");
+      (kv_scale && !aligned(kv_scale, 4)) || (cu_q && !aligned(cu_q, 4)))
+    return fail(MLA_ERR_INVALID_ARG, "lse, block_table, cache_seqlens, kv_scale, cu_seqlens_q must be 4-byte aligned");
   if (metadata) {
     if (num_units < 1) return fail(MLA_ERR_INVALID_ARG, "num_units must be >= 1 with metadata");
     if (!aligned(metadata, 4)) return fail(MLA_ERR_INVALID_ARG, "metadata must be 4-byte aligned");
@@ -199,6 +209,7 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
   p.kv_scale = kv_dtype == MLA_KV_FP8_E4M3 ? kv_scale : nullptr;   // selects the fp8 kernels
   p.block_table = block_table;
   p.seqlens = cache_seqlens;
+  p.cu_q = cu_q;
   p.out = out;
   p.lse = lse;
   p.md = (const int32_t*)metadata;
@@ -206,6 +217,7 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
   p.q_len = q_len;
   p.num_heads = num_heads;
   p.rows = q_len * num_heads;
+  p.q_rows = cu_q ? total_q * num_heads : batch * p.rows;
   p.max_pages = max_pages_per_seq;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   const size_t slots = (size_t)batch + (size_t)num_units;
@@ -235,10 +247,36 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   if (metadata) {
     const int32_t* offsets = (const int32_t*)metadata + mla::MD_HEADER + batch + 1;
-    e = mla::launch_combine(p.ws_out, p.ws_lse, offsets, 1, batch, p.rows, out, lse, 1, s);
+    e = mla::launch_combine(p.ws_out, p.ws_lse, offsets, cu_q, num_heads, batch, p.rows, out, lse, 1, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                   int num_pages, const int32_t* block_table, int max_pages_per_seq,
+                   const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
+                   float softmax_scale, float* out, float* lse, const void* metadata, int num_units,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, nullptr, 0, kv_cache, kv_scale, kv_dtype, num_pages, block_table, max_pages_per_seq,
+                     cache_seqlens, batch, q_len, num_heads, softmax_scale, out, lse, metadata, num_units,
+                     workspace, workspace_bytes, stream);
+}
+
+int mla_decode_fwd_varlen(const void* q, const int32_t* cu_seqlens_q, int total_q, int max_q_len,
+                          const void* kv_cache, const float* kv_scale, int kv_dtype, int num_pages,
+                          const int32_t* block_table, int max_pages_per_seq, const int32_t* cache_seqlens,
+                          int batch, int num_heads, float softmax_scale, float* out, float* lse,
+                          const void* metadata, int num_units, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!cu_seqlens_q) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  return decode_impl(q, cu_seqlens_q, total_q, kv_cache, kv_scale, kv_dtype, num_pages, block_table,
+                     max_pages_per_seq, cache_seqlens, batch, max_q_len, num_heads, softmax_scale, out, lse,
+                     metadata, num_units, workspace, workspace_bytes, stream);
 }
 
 int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq_part_offsets,
@@ -254,8 +292,8 @@ int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq
   DevInfo d;
   int st = device_info(&d);
   if (st != MLA_OK) return st;
-  hipError_t e = mla::launch_combine(part_out, part_lse, seq_part_offsets, 0, batch, rows_per_seq, out,
-                                     lse, 0, (hipStream_t)stream);
+  hipError_t e = mla::launch_combine(part_out, part_lse, seq_part_offsets, nullptr, 1, batch, rows_per_seq,
+                                     out, lse, 0, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -27,17 +27,20 @@ inline size_t metadata_words(int batch, int units) {
 }
 
 struct DecodeParams {
-  const uint16_t* q;          // bf16 bits [B, s, H, 576]
+  const uint16_t* q;          // bf16 bits [B, s, H, 576], or [T, H, 576] with cu_q
   const uint8_t* kv;          // page pool bytes
   const float* kv_scale;      // [P, 64] (fp8 only)
   const int32_t* block_table; // [B, max_pages]
   const int32_t* seqlens;     // [B]
-  float* out;                 // [B, s, H, 512]
-  float* lse;                 // [B, s, H]
+  const int32_t* cu_q;        // [B+1] query-token offsets (per-sequence q_len) or nullptr
+  float* out;                 // [B, s, H, 512] or [T, H, 512]
+  float* lse;                 // [B, s, H] or [T, H]
   const int32_t* md;          // metadata or nullptr (unsplit)
-  float* ws_out;              // partial O  [slots, R, 512]
-  float* ws_lse;              // partial LSE [slots, R]
-  int batch, q_len, num_heads, rows;
+  float* ws_out;              // partial O  [slots, rows, 512]
+  float* ws_lse;              // partial LSE [slots, rows]
+  int batch, q_len, num_heads;
+  int rows;                   // rows per sequence (q_len * H; the largest one with cu_q)
+  int q_rows;                 // rows held by q (B * rows, or T * H with cu_q)
   int max_pages;
   float scale_log2;           // softmax_scale * log2(e)
 };
@@ -59,8 +62,10 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min
 hipError_t launch_append(const uint16_t* latent, int batch, int new_tokens, const int32_t* block_table,
                          int max_pages, const int32_t* seqlens, uint8_t* kv, float* kv_scale, int fp8,
                          int num_pages, hipStream_t s);
+// cu_q (nullable): per-sequence query offsets; sequence b then owns rows
+// [0, (cu_q[b+1] - cu_q[b]) * num_heads) and writes out rows from cu_q[b] * num_heads.
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
-                          int offsets_stride_is_md, int batch, int rows, float* out, float* lse,
-                          int skip_single, hipStream_t s);
+                          const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
+                          float* lse, int skip_single, hipStream_t s);
 
 }  // namespace mla

@@ -281,6 +281,9 @@ struct TileInfo {
   bool first, last;
   bool final_out;   // epilogue writes the output (false: a partial slot)
   int slot;         // partial slot when !final_out
+  int qlen;         // query tokens of sequence b
+  int rows;         // its rows (qlen * heads)
+  int qrow0;        // row of q / out holding its row 0
 };
 
 struct KernelArgs {
@@ -294,6 +297,16 @@ struct KernelArgs {
   const uint8_t* kv;
 };
 
+// Query tokens of sequence b and the q / out row holding its row 0: uniform
+// q_len (rows = q_len * heads per sequence, sequences back to back) or the
+// per-sequence offsets cu_q (q_len_b = cu_q[b+1] - cu_q[b]).
+__device__ __forceinline__ int seq_qlen(const DecodeParams& p, int b) {
+  return p.cu_q ? uniform(p.cu_q[b + 1] - p.cu_q[b]) : p.q_len;
+}
+__device__ __forceinline__ int seq_qrow0(const DecodeParams& p, int b) {
+  return p.cu_q ? uniform(p.cu_q[b]) * p.num_heads : b * p.rows;
+}
+
 // Flattened tile range [f_begin, f_end) of unit u and the prefetch cursor.
 // Everything the tile stream needs per tile is held in scalar registers or in
 // one VGPR of cached page ids (lane i = page of tile pc_t0 + i), so loading a
@@ -304,6 +317,7 @@ struct Unit {
   int bp, bp_first, bp_last, bp_L, bp_tiles;  // sequence of the prefetch cursor
   bool bp_final;
   int bp_slot;
+  int bp_qlen, bp_qrow0;                       // query tokens and first q/out row
   int pc_t0, page_cache;
 
   // false if the unit has no tiles
@@ -345,6 +359,8 @@ struct Unit {
     bp = uniform(bb);
     bp_L = uniform(max(a.seqlens[bp], 0));
     bp_tiles = (bp_L + kPage - 1) / kPage;
+    bp_qlen = seq_qlen(a.p, bp);
+    bp_qrow0 = seq_qrow0(a.p, bp);
     bp_final = true;
     bp_slot = 0;
     if (a.md) {
@@ -375,6 +391,9 @@ struct Unit {
     ti.last = (f + 1 == f_end) || (f + 1 == bp_last);
     ti.final_out = bp_final;
     ti.slot = bp_slot;
+    ti.qlen = bp_qlen;
+    ti.rows = bp_qlen * a.p.num_heads;
+    ti.qrow0 = bp_qrow0;
     if (ti.t - pc_t0 >= 64) load_pages(a, ti.t);
     const int page = uniform(__builtin_amdgcn_readlane(page_cache, ti.t - pc_t0));
     const int nvalid = min(kPage, ti.L - ti.t * kPage);
@@ -386,10 +405,11 @@ struct Unit {
 // O = 0, LSE = -inf for rows [r0, r1) of an empty sequence (unsplit mode).
 __device__ __forceinline__ void write_empty(const DecodeParams& p, int b, int r0, int r1) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = r0 + wave; r < min(r1, p.rows); r += 4) {
-    float* o = p.out + ((size_t)b * p.rows + r) * kDv;
+  const int rows = seq_qlen(p, b) * p.num_heads, base = seq_qrow0(p, b);
+  for (int r = r0 + wave; r < min(r1, rows); r += 4) {
+    float* o = p.out + ((size_t)base + r) * kDv;
     for (int d = lane * 4; d < kDv; d += 256) *(f32x4*)(o + d) = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (lane == 0) p.lse[(size_t)b * p.rows + r] = -INFINITY;
+    if (lane == 0) p.lse[(size_t)base + r] = -INFINITY;
   }
 }
 
@@ -493,12 +513,12 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
     if (ti.first) {
       // new sequence: its query rows into registers, fresh softmax state
-      const int rr = row < R ? row : R - 1;
-      const bf16x8* qrow = (const bf16x8*)(a.qptr + ((size_t)bc * R + rr) * kDqk);
+      const int rr = row < ti.rows ? row : max(ti.rows - 1, 0);
+      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
 #pragma unroll
       for (int c = 0; c < kQChunks; ++c) {
         bf16x8 v = qrow[4 * c + g];
-        qreg[c] = row < R ? v : bf16x8{};
+        qreg[c] = row < ti.rows ? v : bf16x8{};
       }
 #pragma unroll
       for (int fb = 0; fb < kFeatBlocks; ++fb) o[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -550,8 +570,8 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
     // ---- online softmax (base 2)
     const int key0 = t * kPage + key_blk * 16;
-    const int vis = L - p.q_len + (row < R ? row : R - 1) / p.num_heads + 1;
-    const bool need_mask = (t * kPage + kPage) > (L - p.q_len + 1);
+    const int vis = L - ti.qlen + (row < ti.rows ? row : max(ti.rows - 1, 0)) / p.num_heads + 1;
+    const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
     // fp8: per-token scales of this lane's keys (folded into scores and P)
     f32x4 ksc[NKB];
 #pragma unroll
@@ -698,12 +718,12 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
       const bool live = l_row > 0.f;
       const float inv = live ? 1.0f / l_row : 0.f;
       const float lse_v = live ? (m_row + log2_fast(l_row)) * kLn2 : -INFINITY;
-      if (row < R) {
+      if (row < ti.rows) {
         float* dst_o;
         float* dst_l;
         if (final_out) {
-          dst_o = p.out + ((size_t)bc * R + row) * kDv;
-          dst_l = p.lse + (size_t)bc * R + row;
+          dst_o = p.out + ((size_t)ti.qrow0 + row) * kDv;
+          dst_l = p.lse + (size_t)ti.qrow0 + row;
         } else {
           dst_o = p.ws_out + ((size_t)slot * R + row) * kDv;
           dst_l = p.ws_lse + (size_t)slot * R + row;
@@ -884,12 +904,12 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
 
     const int bc = ti.b, t = ti.t, L = ti.L;
     if (ti.first) {
-      const int rr = row < R ? row : R - 1;
-      const bf16x8* qrow = (const bf16x8*)(a.qptr + ((size_t)bc * R + rr) * kDqk);
+      const int rr = row < ti.rows ? row : max(ti.rows - 1, 0);
+      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
 #pragma unroll
       for (int c = 0; c < kQChunks; ++c) {
         bf16x8 v = qrow[4 * c + g];
-        qreg[c] = row < R ? v : bf16x8{};
+        qreg[c] = row < ti.rows ? v : bf16x8{};
       }
 #pragma unroll
       for (int fb = 0; fb < kFb; ++fb) o[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -917,8 +937,8 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
     f32x4 sv = sa + sb;
 
     const int key0 = t * kPage + 16 * cw + 4 * g;
-    const int vis = L - p.q_len + (row < R ? row : R - 1) / p.num_heads + 1;
-    const bool need_mask = (t * kPage + kPage) > (L - p.q_len + 1);
+    const int vis = L - ti.qlen + (row < ti.rows ? row : max(ti.rows - 1, 0)) / p.num_heads + 1;
+    const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -988,12 +1008,12 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
       const float l_row = ssum[0][li] + ssum[1][li] + ssum[2][li] + ssum[3][li];
       const bool live = l_row > 0.f;
       const float inv = live ? 1.0f / l_row : 0.f;
-      if (row < R) {
+      if (row < ti.rows) {
         float* dst_o;
         float* dst_l;
         if (ti.final_out) {
-          dst_o = p.out + ((size_t)bc * R + row) * kDv;
-          dst_l = p.lse + (size_t)bc * R + row;
+          dst_o = p.out + ((size_t)ti.qrow0 + row) * kDv;
+          dst_l = p.lse + (size_t)ti.qrow0 + row;
         } else {
           dst_o = p.ws_out + ((size_t)ti.slot * R + row) * kDv;
           dst_l = p.ws_lse + (size_t)ti.slot * R + row;
@@ -1120,7 +1140,9 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
   TileDma<FP8> dma;
   TileInfo next = unit.prepare(a, unit.f_begin, FP8 ? buf1 : buf0, sb0, tid, dma);
-  dma_all(dma);
+  // a row block past a sequence's rows (per-sequence q_len) skips its tiles:
+  // no loads, no compute
+  if (row0 < next.rows) dma_all(dma);
 
   // cur: bf16 tile computed in this step; nxt: where the next tile's loads go
   // (fp8: the staging area again, free once the current page is widened);
@@ -1129,14 +1151,15 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
                   const LDS_AS float* const sbc, LDS_AS float* const sbn) {
     const TileInfo ti = next;
     const int bc = ti.b, t = ti.t, L = ti.L;
+    const bool skip = row0 >= ti.rows;
 
-    if (ti.first) {
-      const int rr = row_qk < R ? row_qk : R - 1;
-      const bf16x8* qrow = (const bf16x8*)(a.qptr + ((size_t)bc * R + rr) * kDqk);
+    if (ti.first && !skip) {
+      const int rr = row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0);
+      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
 #pragma unroll
       for (int c = 0; c < kQHalf; ++c) {
         bf16x8 v = qrow[36 * fh + 2 * c + h];
-        qreg[c] = row_qk < R ? v : bf16x8{};
+        qreg[c] = row_qk < ti.rows ? v : bf16x8{};
       }
       // O and l restart through the rescale below (alpha = 0), so the
       // accumulators are never reset outside the one rescale path
@@ -1149,11 +1172,16 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
     const bool more = f + 1 < unit.f_end;
     wait_tile();
+    if (more) next = unit.prepare(a, f + 1, nxt, sbn, tid, dma);
+    const bool load_next = more && row0 < next.rows;
+    if (skip) {
+      if (load_next) dma_all(dma);
+      return;
+    }
     if constexpr (FP8) {
       widen_fp8_tile(buf1, cur, tid);
       lds_barrier();
     }
-    if (more) next = unit.prepare(a, f + 1, nxt, sbn, tid, dma);
 
     // ---- QK GEMM: partial S^T[64 keys, 32 rows of half rh] over feature half fh
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -1170,7 +1198,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
         const bf16x8 av = ring[i % kQkDepthX];
         if (i + kQkDepthX < NQ) ring[i % kQkDepthX] = ld128(kaddr(i + kQkDepthX));
         sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[i >> 1], sacc[i & 1], 0, 0, 0);
-        dma_slot<kDmaSlotsX>(dma, more, i);
+        dma_slot<kDmaSlotsX>(dma, load_next, i);
         sched_fence();
       }
     }
@@ -1196,8 +1224,8 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     // ---- softmax: half-tile maxima -> shared running max -> P
     LDS_AS float* const smax = (LDS_AS float*)(cur + 8 * kLineGroupBytes);   // [key block][row]
     const int key0 = t * kPage + 32 * kh + 4 * h;
-    const int vis = L - p.q_len + (row_qk < R ? row_qk : R - 1) / p.num_heads + 1;
-    const bool need_mask = (t * kPage + kPage) > (L - p.q_len + 1);
+    const int vis = L - ti.qlen + (row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0)) / p.num_heads + 1;
+    const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
     f32x4 ksc[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
@@ -1299,12 +1327,12 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       const float l_row = ssum[32 * rb + n] + ssum[64 + 32 * rb + n];
       const bool live = l_row > 0.f;
       const float inv = live ? 1.0f / l_row : 0.f;
-      if (row < R) {
+      if (row < ti.rows) {
         float* dst_o;
         float* dst_l;
         if (final_out) {
-          dst_o = p.out + ((size_t)bc * R + row) * kDv;
-          dst_l = p.lse + (size_t)bc * R + row;
+          dst_o = p.out + ((size_t)ti.qrow0 + row) * kDv;
+          dst_l = p.lse + (size_t)ti.qrow0 + row;
         } else {
           dst_o = p.ws_out + ((size_t)slot * R + row) * kDv;
           dst_l = p.ws_lse + (size_t)slot * R + row;
@@ -1440,15 +1468,19 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_out,
                                                       const float* __restrict__ part_lse,
-                                                      const int32_t* __restrict__ offsets, int B, int R,
-                                                      float* __restrict__ out, float* __restrict__ lse,
-                                                      int skip_single) {
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ cu_q, int num_heads,
+                                                      int B, int R, float* __restrict__ out,
+                                                      float* __restrict__ lse, int skip_single) {
   const int b = blockIdx.x;
   const int k0 = offsets[b];
   const int n = offsets[b + 1] - k0;
   if (skip_single && n == 1) return;
   const int r = blockIdx.y * 2 + (threadIdx.x >> 7);
-  if (r >= R) return;
+  // partial slots hold R rows; sequence b owns the first rows_b of them
+  const int rows_b = cu_q ? (cu_q[b + 1] - cu_q[b]) * num_heads : R;
+  const size_t out_row0 = cu_q ? (size_t)cu_q[b] * num_heads : (size_t)b * R;
+  if (r >= rows_b) return;
   const int d = (threadIdx.x & 127) * 4;
   const float* pl = part_lse + (size_t)k0 * R + r;
   const float* po = part_out + ((size_t)k0 * R + r) * kDv + d;
@@ -1504,8 +1536,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       acc += expf(v - lse_v) * *(const f32x4*)(po + k * ostride);
     }
   }
-  *(f32x4*)(out + ((size_t)b * R + r) * kDv + d) = acc;
-  if (d == 0) lse[(size_t)b * R + r] = lse_v;
+  *(f32x4*)(out + (out_row0 + r) * kDv + d) = acc;
+  if (d == 0) lse[out_row0 + r] = lse_v;
 }
 
 // ---------------------------------------------------------------------------
@@ -1551,11 +1583,11 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min
 }
 
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
-                          int /*unused*/, int batch, int rows, float* out, float* lse, int skip_single,
-                          hipStream_t s) {
+                          const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
+                          float* lse, int skip_single, hipStream_t s) {
   dim3 grid(batch, (rows + 1) / 2);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, part_out, part_lse, offsets, batch, rows,
-                     out, lse, skip_single);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, part_out, part_lse, offsets, cu_q, num_heads,
+                     batch, rows, out, lse, skip_single);
   return hipGetLastError();
 }
 

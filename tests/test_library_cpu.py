@@ -119,6 +119,17 @@ def test_append_argument_errors(lib):
     assert call(kv=FAKE_ODD) == INVALID
 
 
+def test_varlen_argument_errors(lib):
+    f = lib.mla_decode_fwd_varlen
+    def call(cu=FAKE, T=4, mq=2, H=16):
+        return f(FAKE, cu, T, mq, FAKE, None, 0, 4, FAKE, 4, FAKE, 2, H, ctypes.c_float(0.072), FAKE, FAKE,
+                 None, 0, None, 0, None)
+    assert call(cu=None) == INVALID
+    assert call(T=0) == INVALID
+    assert call(mq=0) == INVALID
+    assert call(mq=300, H=16) == INVALID      # rows over the limit
+
+
 def test_binding_rejects_host_tensors():
     import torch
     q = torch.zeros(1, 1, 16, 576, dtype=torch.bfloat16)
