@@ -128,6 +128,10 @@ def main():
     ap.add_argument("--num-units", type=int, default=0, help="split work units (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--append-tokens", type=int, default=0,
+                    help="also run the cache append (mla_append_kv) of this many new tokens per sequence "
+                         "in every step, before the decode (their rows are the last positions of each "
+                         "sequence)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -182,7 +186,16 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    latent = None
+    if args.append_tokens:
+        g = torch.Generator(device="cpu").manual_seed(1)
+        lat32 = torch.randn((w.batch, args.append_tokens, 576), generator=g)
+        latent = lat32.to(torch.bfloat16).to(dev)
+
     def step(i):
+        if latent is not None:
+            k = i % sets
+            mla.append_kv(latent, bt, sl, kvs[k], scales[k])
         mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units, metadata=plan.metadata,
                                workspace=plan.workspace)
         k = i % sets
@@ -247,7 +260,7 @@ def main():
                    "heads": w.num_heads, "q_len": w.q_len if not w.varlen else "per-sequence, max %d" % w.q_len,
                    "query_tokens": int(sum(w.q_lens)), "kv_dtype": w.kv_dtype,
                    "tokens": alg["tokens"], "pages": alg["pages"], "num_units": units,
-                   "pool_copies": sets, "seed": 0},
+                   "pool_copies": sets, "seed": 0, "append_tokens": args.append_tokens},
         "tflops": round(tflops, 2),
         "kv_gbps": round(kv_gbps, 1),
         "roofline": roof,

@@ -286,6 +286,35 @@ struct TileInfo {
   int qrow0;        // row of q / out holding its row 0
 };
 
+// TileInfo through LDS (8 ints): the producers of the narrow kernel publish
+// the facts of the tiles they stream, so the compute waves never wait on the
+// metadata loads of a sequence change.
+__device__ __forceinline__ void put_info(LDS_AS int* d, const TileInfo& ti) {
+  d[0] = ti.b;
+  d[1] = ti.t;
+  d[2] = ti.L;
+  d[3] = (ti.first ? 1 : 0) | (ti.last ? 2 : 0) | (ti.final_out ? 4 : 0);
+  d[4] = ti.slot;
+  d[5] = ti.qlen;
+  d[6] = ti.rows;
+  d[7] = ti.qrow0;
+}
+__device__ __forceinline__ TileInfo get_info(const LDS_AS int* d) {
+  TileInfo ti;
+  ti.b = __builtin_amdgcn_readfirstlane(d[0]);
+  ti.t = __builtin_amdgcn_readfirstlane(d[1]);
+  ti.L = __builtin_amdgcn_readfirstlane(d[2]);
+  const int fl = __builtin_amdgcn_readfirstlane(d[3]);
+  ti.first = (fl & 1) != 0;
+  ti.last = (fl & 2) != 0;
+  ti.final_out = (fl & 4) != 0;
+  ti.slot = __builtin_amdgcn_readfirstlane(d[4]);
+  ti.qlen = __builtin_amdgcn_readfirstlane(d[5]);
+  ti.rows = __builtin_amdgcn_readfirstlane(d[6]);
+  ti.qrow0 = __builtin_amdgcn_readfirstlane(d[7]);
+  return ti;
+}
+
 struct KernelArgs {
   DecodeParams p;
   const int32_t* md;
@@ -790,12 +819,18 @@ __device__ __forceinline__ void store_page(const u32x4 (&st)[kLoadsPerThread], L
 }
 
 __device__ __forceinline__ void produce_pages(const KernelArgs& a, Unit& unit, LDS_AS uint8_t* buf0,
-                                              LDS_AS uint8_t* buf1, int ptid) {
+                                              LDS_AS uint8_t* buf1, LDS_AS int* info_ring, int ptid) {
   const int f0 = unit.f_begin, fe = unit.f_end;
   TileRegs r;
+  // plan the loads of tile f and publish its facts in info_ring[f % 4] (read
+  // by the consumers after a barrier that follows this write)
   auto plan = [&](int f) {
-    if (f < fe) (void)unit.prepare(a, f, buf0, nullptr, ptid, r);
-    else r.idle(a.kv);
+    if (f < fe) {
+      const TileInfo ti = unit.prepare(a, f, buf0, nullptr, ptid, r);
+      if (ptid == 0) put_info(info_ring + 8 * (f & 3), ti);
+    } else {
+      r.idle(a.kv);
+    }
   };
   u32x4 st0[kLoadsPerThread], st1[kLoadsPerThread];
   plan(f0);
@@ -853,8 +888,10 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
   __shared__ __attribute__((aligned(16))) bf16x8 p_lds[2][64];   // [k-step][lane]
   __shared__ float smax[4][16];
   __shared__ float ssum[4][16];
+  __shared__ int info_lds[4][8];                                  // tile facts, ring of 4
   LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
   LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
+  LDS_AS int* const info_ring = (LDS_AS int*)(&info_lds[0][0]);
 
   const DecodeParams& p = a.p;
   const int tid = threadIdx.x;
@@ -887,35 +924,39 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
   float m_run = -INFINITY, l_run = 0.f;
 
   if (producer) {
-    produce_pages(a, unit, buf0, buf1, tid - 256);
+    produce_pages(a, unit, buf0, buf1, info_ring, tid - 256);
     return;
   }
 
-  TileDma<false> plan_only;   // consumers use the tile facts, not the load plan
-  TileInfo next = unit.prepare(a, unit.f_begin, buf0, nullptr, tid & 255, plan_only);
+  // Query rows of a sequence into registers, issued ahead of their first tile
+  // (no wait here). Rows past the sequence's own read its last row: finite
+  // values whose results are never stored, so no select waits on the loads.
+  auto fetch_q = [&](const TileInfo& nt) {
+    const int rr = row < nt.rows ? row : max(nt.rows - 1, 0);
+    const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(nt.qrow0 + rr, p.q_rows - 1) * kDqk);
+#pragma unroll
+    for (int c = 0; c < kQChunks; ++c) qreg[c] = qrow[4 * c + g];
+  };
+  {
+    TileDma<false> plan_only;   // the first tile's facts, to fetch its query rows early
+    fetch_q(unit.prepare(a, unit.f_begin, buf0, nullptr, tid & 255, plan_only));
+  }
+
   for (int f = unit.f_begin; f < unit.f_end; ++f) {
     const bool odd = ((f - unit.f_begin) & 1) != 0;
     LDS_AS uint8_t* const cur = odd ? buf1 : buf0;
-    const TileInfo ti = next;
     const bool more = f + 1 < unit.f_end;
 
     lds_barrier();   // B0: tile f is in `cur`, everyone is done with the other buffer
-    if (more) next = unit.prepare(a, f + 1, buf0, nullptr, tid & 255, plan_only);
+    const TileInfo ti = get_info(info_ring + 8 * (f & 3));
 
     const int bc = ti.b, t = ti.t, L = ti.L;
     if (ti.first) {
-      const int rr = row < ti.rows ? row : max(ti.rows - 1, 0);
-      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
-#pragma unroll
-      for (int c = 0; c < kQChunks; ++c) {
-        bf16x8 v = qrow[4 * c + g];
-        qreg[c] = row < ti.rows ? v : bf16x8{};
-      }
 #pragma unroll
       for (int fb = 0; fb < kFb; ++fb) o[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
       m_run = -INFINITY;
       l_run = 0.f;
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);   // its query rows (fetched a tile ahead)
     }
 
     // QK: S^T[keys 16cw.., 16 rows]
@@ -935,6 +976,11 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
       }
     }
     f32x4 sv = sa + sb;
+    if (more) {
+      // the next tile starts a sequence: its query rows now (qreg is free)
+      const TileInfo nt = get_info(info_ring + 8 * ((f + 1) & 3));
+      if (nt.first) fetch_q(nt);
+    }
 
     const int key0 = t * kPage + 16 * cw + 4 * g;
     const int vis = L - ti.qlen + (row < ti.rows ? row : max(ti.rows - 1, 0)) / p.num_heads + 1;
