@@ -109,6 +109,12 @@ __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint3
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// x, hidden from the optimiser: values derived from it are recomputed where
+// they are used instead of being hoisted out of the tile loop into registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // The 18 direct-to-LDS loads of one page. Load i of thread t fills slot
 // i*256 + t: line group i/2, key 32(i%2) + t/8, in-line position t%8; the
@@ -432,10 +438,11 @@ struct Unit {
 };
 
 // O = 0, LSE = -inf for rows [r0, r1) of an empty sequence (unsplit mode).
-__device__ __forceinline__ void write_empty(const DecodeParams& p, int b, int r0, int r1) {
+// Called by waves 0..nwaves-1 of the block.
+__device__ __forceinline__ void write_empty(const DecodeParams& p, int b, int r0, int r1, int nwaves) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rows = seq_qlen(p, b) * p.num_heads, base = seq_qrow0(p, b);
-  for (int r = r0 + wave; r < min(r1, rows); r += 4) {
+  for (int r = r0 + wave; r < min(r1, rows); r += nwaves) {
     float* o = p.out + ((size_t)base + r) * kDv;
     for (int d = lane * 4; d < kDv; d += 256) *(f32x4*)(o + d) = f32x4{0.f, 0.f, 0.f, 0.f};
     if (lane == 0) p.lse[(size_t)base + r] = -INFINITY;
@@ -507,7 +514,7 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
   Unit unit;
   if (!unit.init(a, u)) {
-    if (!a.md) write_empty(p, unit.b0, blockIdx.y * ROWS_WG, blockIdx.y * ROWS_WG + ROWS_WG);
+    if (!a.md) write_empty(p, unit.b0, blockIdx.y * ROWS_WG, blockIdx.y * ROWS_WG + ROWS_WG, 4);
     return;
   }
 
@@ -905,7 +912,7 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
 
   Unit unit;
   if (!unit.init(a, u)) {
-    if (!a.md && !producer) write_empty(p, unit.b0, 0, 16);
+    if (!a.md && !producer) write_empty(p, unit.b0, 0, 16, 4);
     return;
   }
 
@@ -1073,51 +1080,141 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
 }
 
 // ---------------------------------------------------------------------------
-// WIDE64X: 64 rows per workgroup on v_mfma_f32_32x32x16_bf16.
-//   QK is split over the waves by row half rh = w%2 and feature half fh = w/2:
-//   wave w computes the partial S^T[64 keys, 32 rows] over features
-//   288fh..288fh+287 (18 k-steps of 16 features for each of the two key
-//   blocks of 32). Holding Q of its 32 rows for half the features only (72
-//   registers) leaves the register file room for the 128 O accumulators and
-//   for deep LDS fetch rings. The two feature halves are added through LDS:
-//   wave (rh, fh) owns key block kh = fh for the softmax and receives the
-//   other feature half's partial scores for it.
-//   PV is split by output columns: wave w accumulates O^T[128 features, 64 rows]
-//   for features 128w..128w+127 (O: 128 registers per lane).
+// WIDE64X: 64 rows per workgroup on v_mfma_f32_32x32x16_bf16, 8 waves (two
+// per SIMD, so one wave's LDS fetches and softmax run under the other's MFMAs).
+//   Wave w has row half rh = w%2, feature half fh = (w/2)%2 and key half
+//   kh = w/4. QK: wave w computes the partial S^T[32 keys of half kh, 32 rows
+//   of half rh] over features 288fh..288fh+287 (18 k-steps of 16 features),
+//   holding Q of its 32 rows for those features (72 registers). Every K byte of
+//   the tile is read from LDS by two waves (the two row halves).
+//   The two feature halves are added through LDS: wave w keeps the 16 keys
+//   16kq..16kq+15 of the tile, kq = 2kh + fh, and takes the partner's partial
+//   scores for them (partner w ^ 2).
+//   PV is split by output columns: wave w accumulates O^T[64 features, 64 rows]
+//   for features 64w..64w+63 (O: 64 registers per lane).
 //   C layout of a 32x32 block: lane l holds element [8j + 4h + i][l%32] for
 //   register r = 4j + i, h = l/32.
-//   In PV k-step ks = 2kh + s (keys 32kh + 16s + 0..15) the k-slot 8h + e is
-//   key 32kh + 16s + 4h + e (e < 4) or 32kh + 16s + 8 + 4h + (e - 4): exactly
-//   the S registers 8s..8s+7 of the owning wave's lane. So each lane stores its
-//   P values for a k-step as one 16-byte word, and the PV waves read it back
-//   as their MFMA B operand from the same lane position (P exchange through
-//   LDS with no transposition).
-//   The row max of a tile needs both key blocks: the owning waves publish
-//   their half-tile maxima, and every wave derives the same running max for
-//   all 64 rows (it needs the rescale factor of every row for its O columns).
+//   In PV k-step ks (keys 16ks..16ks+15) the k-slot 8h + e is key
+//   16ks + 4h + e (e < 4) or 16ks + 8 + 4h + (e - 4): exactly the kept S
+//   registers of the owning wave's lane. So each lane stores its P values for
+//   a k-step as one 16-byte word, and the PV waves read it back as their MFMA
+//   B operand from the same lane position (P exchange through LDS with no
+//   transposition).
+//   The row max of a tile needs all four key quarters: the owning waves publish
+//   their quarter maxima, and every wave derives the same running max for all
+//   64 rows (it needs the rescale factor of every row for its O columns).
 //   LDS: two bf16 tiles (bf16 cache) or one bf16 tile plus the next page's
 //   codes and scales (fp8 cache); a 16 KiB exchange area that holds the
 //   partial scores, then the P operand, then (epilogue) the row sums; the row
 //   maxima live in the rope columns of the current tile, dead once QK is done.
 // ---------------------------------------------------------------------------
-constexpr int kQkDepthX = 8;
+constexpr int kThreadsX = 512;
+constexpr int kQkDepthX = 4;
 constexpr int kPvDepthX = 4;
-// The next page's loads are spread over the 36 QK MFMA slots. (Spreading
-// them over the PV slots too issues the last ones so late that the next
-// tile's wait grows by more than the issue stalls it saves.)
-constexpr int kDmaSlotsX = 36;
 constexpr int kXchgBytes = 16384;
+constexpr int kLoadsX = kTileBytes / (kThreadsX * 16);                         // 9
+constexpr int kFp8SlotsX = kFp8TileBytes / 16;                                 // 2304
+constexpr int kFp8LoadsX = (kFp8SlotsX + kThreadsX - 1) / kThreadsX;           // 5
+static_assert(kLoadsX * kThreadsX * 16 == kTileBytes, "tile must split evenly");
 
 template <bool FP8>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+struct TileDmaX;
+
+// bf16 page, 512 threads: load i of thread t fills LDS slot 512i + t, i.e.
+// line group i, key t/8, in-line position t%8; the lane fetches the chunk
+// that belongs there, so the 8 lanes of an octet read one whole 128-byte line
+// of one key row. Keys at or past `nvalid` re-read the last valid key.
+template <>
+struct TileDmaX<false> {
+  static constexpr int kLoads = kLoadsX;
+  const uint8_t* page;
+  uint32_t voff, lds0;
+  __device__ __forceinline__ void plan(const uint8_t* kv, const float* /*kv_scale*/, int page_id,
+                                       int nvalid, LDS_AS uint8_t* buf, LDS_AS float* /*sbuf*/,
+                                       int tid) {
+    page = kv + (size_t)page_id * kTileBytes;
+    const int key = tid >> 3;
+    const int src_key = key < nvalid ? key : nvalid - 1;
+    voff = src_key * kRowBytes + 16 * ((tid & 7) ^ swz3(key));
+    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
+  }
+  // the per-load offset goes into the scalar base, so the lane offset is one register
+  __device__ __forceinline__ void load(int i) const { dma16(voff, page + 128 * i, lds0 + i * 8192); }
+};
+
+// fp8 page, 512 threads: a plain copy of the 36 KiB page into the staging
+// buffer (slot 512i + t; the last load is made by waves 0-3 only), plus the
+// 64 per-token scales (one 4-byte load per lane of wave 0).
+template <>
+struct TileDmaX<true> {
+  static constexpr int kLoads = kFp8LoadsX;
+  const uint8_t* page;
+  const uint8_t* scale;
+  uint32_t lds0, sc_lds, sc_off;
+  int nvalid, tid;
+  __device__ __forceinline__ void plan(const uint8_t* kv, const float* kv_scale, int page_id, int nv,
+                                       LDS_AS uint8_t* buf, LDS_AS float* sbuf, int t) {
+    page = kv + (size_t)page_id * kFp8TileBytes;
+    scale = (const uint8_t*)(kv_scale + (size_t)page_id * kPage);
+    nvalid = nv;
+    tid = t;
+    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
+    sc_lds = (uint32_t)uniform((int)(uintptr_t)sbuf);
+    const int lane = tid & 63;
+    sc_off = 4 * (lane < nvalid ? lane : nvalid - 1);
+  }
+  __device__ __forceinline__ void load(int i) const {
+    if (i * kThreadsX + (tid & ~63) >= kFp8SlotsX) return;   // wave-uniform
+    // lane offset recomputed per load (not hoisted into five registers)
+    const int sidx = i * kThreadsX + opaque(tid);
+    uint32_t voff = sidx * 16;
+    if (nvalid < kPage) {
+      // tail page: slots of keys at or past nvalid re-read the last valid key
+      const int key = sidx / 36;
+      if (key >= nvalid) voff = (nvalid - 1) * kFp8RowBytes + (sidx - key * 36) * 16;
+    }
+    dma16(voff, page, lds0 + i * kThreadsX * 16);
+    if (i == 0 && tid < 64) dma4(sc_off, scale, sc_lds);
+  }
+};
+
+// fp8 staging page -> bf16 tile with 512 threads (see widen_fp8_tile).
+__device__ __forceinline__ void widen_fp8_tile_x(const LDS_AS uint8_t* stage, LDS_AS uint8_t* tile, int tid) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+#pragma unroll
+  for (int j = 0; j < kFp8LoadsX; ++j) {
+    const int sidx = j * kThreadsX + opaque(tid);
+    if (sidx >= kFp8SlotsX) break;
+    const int key = sidx / 36, c16 = sidx - key * 36;
+    const u32x4 w = *(const LDS_AS u32x4*)(stage + sidx * 16);
+    u32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false);
+      const bf16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true);
+      const unsigned u0 = __builtin_bit_cast(unsigned, x0), u1 = __builtin_bit_cast(unsigned, x1);
+      if (e < 2) {
+        lo[2 * e] = u0;
+        lo[2 * e + 1] = u1;
+      } else {
+        hi[2 * (e - 2)] = u0;
+        hi[2 * (e - 2) + 1] = u1;
+      }
+    }
+    *(LDS_AS u32x4*)(tile + lds_byte(key, 2 * c16)) = lo;
+    *(LDS_AS u32x4*)(tile + lds_byte(key, 2 * c16 + 1)) = hi;
+  }
+}
+
+template <bool FP8>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
     const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
     const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
     const uint8_t* __restrict__ kv_) {
   const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
   constexpr int ROWS_WG = 64;
-  constexpr int kQHalf = kDqk / 32;          // 18 k-steps of 16 features per feature half
-  constexpr int NQ = 2 * kQHalf;             // QK MFMAs per wave and tile: (k-step, key block)
+  constexpr int NQ = kDqk / 32;              // 18 QK MFMAs per wave and tile (k-steps of one feature half)
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[FP8 ? kFp8TileBytes + 2 * kPage * 4 : kTileBytes];
@@ -1131,10 +1228,10 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
   const DecodeParams& p = a.p;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = uniform(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int rh = wave & 1, fh = wave >> 1;
-  const int kh = fh;                         // key block this wave owns after the exchange
+  const int rh = wave & 1, fh = (wave >> 1) & 1, kh = wave >> 2;
+  const int kq = 2 * kh + fh;                // key quarter this wave owns after the exchange
   const int R = p.rows;
   const int row0 = blockIdx.y * ROWS_WG;
   const int row_qk = row0 + 32 * rh + n;
@@ -1142,49 +1239,48 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
   Unit unit;
   if (!unit.init(a, u)) {
-    if (!a.md) write_empty(p, unit.b0, row0, row0 + ROWS_WG);
+    if (!a.md) write_empty(p, unit.b0, row0, row0 + ROWS_WG, kThreadsX / 64);
     return;
   }
 
   // ---- per-lane constant LDS offsets
-  // QK operand of key block kb, k-step c = 4m + q: key 32kb + n, chunk
-  // 36fh + 2c + h = lds_byte(key, 36fh + 2q + h) + m line groups
-  int k_lane[2][4];
+  // QK operand, k-step c = 4m + q: key 32kh + n, chunk 36fh + 2c + h
+  // = lds_byte(key, 36fh + 2q + h) + m line groups
+  int k_lane[4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) k_lane[kb][q4] = lds_byte(32 * kb + n, 36 * fh + 2 * q4 + h);
-  // V transposed fetch: 16-lane group q covers features 128w + 32fb + 16(q%2)
+  for (int q4 = 0; q4 < 4; ++q4) k_lane[q4] = lds_byte(32 * kh + n, 36 * fh + 2 * q4 + h);
+  // V transposed fetch: 16-lane group q covers features 64w + 32fb + 16(q%2)
   // + 0..15 and keys 16ks + 4h + j/4 (+8 for the second read): chunk
-  // 16w + 4fb + 2(q%2) + (j%4)/2 = (2w + fb/2) line groups + chunk
-  // 4(fb%2) + 2(q%2) + (j%4)/2 of the line; +2048 per k-step of 16 keys.
-  int v_lane[2][2];   // [second][fb % 2]
+  // 8w + 4fb + 2(q%2) + (j%4)/2 = line group w, chunk 4fb + 2(q%2) + (j%4)/2
+  // of the line; +2048 per k-step of 16 keys.
+  int v_lane[2][2];   // [second][fb]
   {
     const int q = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int second = 0; second < 2; ++second)
 #pragma unroll
-      for (int par = 0; par < 2; ++par)
-        v_lane[second][par] = 2 * wave * kLineGroupBytes +
-                              lds_byte(4 * h + (j >> 2) + 8 * second, 4 * par + 2 * (q & 1) + ((j & 3) >> 1)) +
-                              8 * (j & 1);
+      for (int fb = 0; fb < 2; ++fb)
+        v_lane[second][fb] = wave * kLineGroupBytes +
+                             lds_byte(4 * h + (j >> 2) + 8 * second, 4 * fb + 2 * (q & 1) + ((j & 3) >> 1)) +
+                             8 * (j & 1);
   }
-  // exchange area: partial scores [rh][key block][4 x 16 B][lane]
-  LDS_AS uint8_t* const x_give = xb + ((rh * 2 + (1 - kh)) * 4 * 64 + lane) * 16;
-  const LDS_AS uint8_t* const x_take = xb + ((rh * 2 + kh) * 4 * 64 + lane) * 16;
+  // exchange area: partial scores [wave][2 x 16 B][lane]; a wave reads its
+  // partner's (w ^ 2) block
+  LDS_AS uint8_t* const x_give = xb + (wave * 2 * 64 + lane) * 16;
+  const LDS_AS uint8_t* const x_take = xb + ((wave ^ 2) * 2 * 64 + lane) * 16;
 
-  bf16x8 qreg[kQHalf];
-  f32x16 o[4][2];                            // [feature block][row half]
+  bf16x8 qreg[NQ];
+  f32x16 o[2][2];                            // [feature block][row half]
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb) {
+  for (int fb = 0; fb < 2; ++fb) {
     o[fb][0] = f32x16{};
     o[fb][1] = f32x16{};
   }
   float m_run[2] = {-INFINITY, -INFINITY};   // running max of rows row0 + n, row0 + 32 + n
-  float l_run = 0.f;                         // partial row sum of row_qk (this key block, lane half)
+  float l_run = 0.f;                         // partial row sum of row_qk (this key quarter, lane half)
   bool restart = true;                       // next rescale zeroes O and l (a sequence starts)
 
-  TileDma<FP8> dma;
+  TileDmaX<FP8> dma;
   TileInfo next = unit.prepare(a, unit.f_begin, FP8 ? buf1 : buf0, sb0, tid, dma);
   // a row block past a sequence's rows (per-sequence q_len) skips its tiles:
   // no loads, no compute
@@ -1196,14 +1292,14 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt,
                   const LDS_AS float* const sbc, LDS_AS float* const sbn) {
     const TileInfo ti = next;
-    const int bc = ti.b, t = ti.t, L = ti.L;
+    const int t = ti.t, L = ti.L;
     const bool skip = row0 >= ti.rows;
 
     if (ti.first && !skip) {
       const int rr = row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0);
       const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
 #pragma unroll
-      for (int c = 0; c < kQHalf; ++c) {
+      for (int c = 0; c < NQ; ++c) {
         bf16x8 v = qrow[36 * fh + 2 * c + h];
         qreg[c] = row_qk < ti.rows ? v : bf16x8{};
       }
@@ -1225,17 +1321,14 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       return;
     }
     if constexpr (FP8) {
-      widen_fp8_tile(buf1, cur, tid);
+      widen_fp8_tile_x(buf1, cur, tid);
       lds_barrier();
     }
 
-    // ---- QK GEMM: partial S^T[64 keys, 32 rows of half rh] over feature half fh
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    // ---- QK GEMM: partial S^T[32 keys of half kh, 32 rows of half rh] over feature half fh
+    f32x16 sacc = f32x16{};
     {
-      auto kaddr = [&](int i) {
-        const int c = i >> 1, kb = i & 1;
-        return cur + k_lane[kb][c & 3] + (c >> 2) * kLineGroupBytes;
-      };
+      auto kaddr = [&](int c) { return cur + k_lane[c & 3] + (c >> 2) * kLineGroupBytes; };
       bf16x8 ring[kQkDepthX];
 #pragma unroll
       for (int i = 0; i < kQkDepthX; ++i) ring[i] = ld128(kaddr(i));
@@ -1243,56 +1336,63 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       for (int i = 0; i < NQ; ++i) {
         const bf16x8 av = ring[i % kQkDepthX];
         if (i + kQkDepthX < NQ) ring[i % kQkDepthX] = ld128(kaddr(i + kQkDepthX));
-        sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[i >> 1], sacc[i & 1], 0, 0, 0);
-        dma_slot<kDmaSlotsX>(dma, load_next, i);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[i], sacc, 0, 0, 0);
+        dma_slot<NQ>(dma, load_next, i);
         sched_fence();
       }
     }
 
-    // ---- add the two feature halves: give the other key block's partial,
-    //      take the partner's partial for key block kh
-    {
-      const f32x16 give = kh ? sacc[0] : sacc[1];
+    // ---- add the two feature halves: keep registers 8fh..8fh+7 (keys
+    //      16kq + 0..15), give registers 8(1-fh).. to the partner. fh is
+    //      wave-uniform: a scalar branch with constant register indices
+    //      (a select on fh would become a per-element indexed extract).
+    float sv[8];
+    if (fh) {
 #pragma unroll
-      for (int part = 0; part < 4; ++part)
-        *(LDS_AS f32x4*)(x_give + part * 1024) =
-            f32x4{give[4 * part], give[4 * part + 1], give[4 * part + 2], give[4 * part + 3]};
+      for (int e = 0; e < 8; ++e) sv[e] = sacc[8 + e];
+      *(LDS_AS f32x4*)(x_give) = f32x4{sacc[0], sacc[1], sacc[2], sacc[3]};
+      *(LDS_AS f32x4*)(x_give + 1024) = f32x4{sacc[4], sacc[5], sacc[6], sacc[7]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = sacc[e];
+      *(LDS_AS f32x4*)(x_give) = f32x4{sacc[8], sacc[9], sacc[10], sacc[11]};
+      *(LDS_AS f32x4*)(x_give + 1024) = f32x4{sacc[12], sacc[13], sacc[14], sacc[15]};
     }
     lds_barrier();
-    f32x16 sv = kh ? sacc[1] : sacc[0];
 #pragma unroll
-    for (int part = 0; part < 4; ++part) {
+    for (int part = 0; part < 2; ++part) {
       const f32x4 v = *(const LDS_AS f32x4*)(x_take + part * 1024);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sv[4 * part + e] += v[e];
     }
 
-    // ---- softmax: half-tile maxima -> shared running max -> P
-    LDS_AS float* const smax = (LDS_AS float*)(cur + 8 * kLineGroupBytes);   // [key block][row]
-    const int key0 = t * kPage + 32 * kh + 4 * h;
+    // ---- softmax: quarter-tile maxima -> shared running max -> P
+    LDS_AS float* const smax = (LDS_AS float*)(cur + 8 * kLineGroupBytes);   // [key quarter][row]
+    const int key0 = t * kPage + 16 * kq + 4 * h;
     const int vis = L - ti.qlen + (row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0)) / p.num_heads + 1;
     const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
-    f32x4 ksc[4];
+    f32x4 ksc[2];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      ksc[jj] = FP8 ? *(const LDS_AS f32x4*)(sbc + 32 * kh + 8 * jj + 4 * h) : f32x4{1.f, 1.f, 1.f, 1.f};
+    for (int jj = 0; jj < 2; ++jj)
+      ksc[jj] = FP8 ? *(const LDS_AS f32x4*)(sbc + 16 * kq + 8 * jj + 4 * h) : f32x4{1.f, 1.f, 1.f, 1.f};
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 8; ++r) {
       float v = sv[r] * (FP8 ? ksc[r >> 2][r & 3] * p.scale_log2 : p.scale_log2);
       if (need_mask && (key0 + 8 * (r >> 2) + (r & 3)) >= vis) v = -INFINITY;
       sv[r] = v;
       mx = fmaxf(mx, v);
     }
     mx = max_xor32(mx);
-    if (h == 0) smax[kh * 64 + 32 * rh + n] = mx;
+    if (h == 0) smax[kq * 64 + 32 * rh + n] = mx;
     lds_barrier();
 
     float alpha[2];
     bool any_raise = restart;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const float tmax = fmaxf(smax[32 * rb + n], smax[64 + 32 * rb + n]);
+      const float tmax = fmaxf(fmaxf(smax[32 * rb + n], smax[64 + 32 * rb + n]),
+                               fmaxf(smax[128 + 32 * rb + n], smax[192 + 32 * rb + n]));
       const float m_new = fmaxf(m_run[rb], tmax);
       const bool raise = m_new > m_run[rb] + kRescaleThreshold;
       alpha[rb] = restart ? 0.0f : raise ? exp2_fast(m_run[rb] - m_new) : 1.0f;
@@ -1302,7 +1402,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     restart = false;
     if (__builtin_amdgcn_ballot_w64(any_raise)) {
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb) {
+      for (int fb = 0; fb < 2; ++fb) {
         o[fb][0] *= alpha[0];
         o[fb][1] *= alpha[1];
       }
@@ -1311,27 +1411,25 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     const float m_eff = (m_run[rh] == -INFINITY) ? 0.0f : m_run[rh];
     // P operand [k-step][row half][lane] in the exchange area (the partial
     // scores there were consumed before the barrier above)
-#pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx) {
+    {
       bf16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int r = 8 * sidx + e;
-        const float pr = exp2_fast(sv[r] - m_eff);
+        const float pr = exp2_fast(sv[e] - m_eff);
         l_run += pr;
-        pb[e] = (__bf16)(FP8 ? pr * ksc[r >> 2][r & 3] : pr);
+        pb[e] = (__bf16)(FP8 ? pr * ksc[e >> 2][e & 3] : pr);
       }
-      *(LDS_AS bf16x8*)(xb + (((2 * kh + sidx) * 2 + rh) * 64 + lane) * 16) = pb;
+      *(LDS_AS bf16x8*)(xb + ((kq * 2 + rh) * 64 + lane) * 16) = pb;
     }
     lds_barrier();
 
-    // ---- PV GEMM: O^T[128 features of this wave, 64 rows] += V^T . P^T
+    // ---- PV GEMM: O^T[64 features of this wave, 64 rows] += V^T . P^T
     {
       auto vaddr = [&](int i, int second) {
-        const int ks = i >> 2, fb = i & 3;
-        return cur + v_lane[second][fb & 1] + (fb >> 1) * kLineGroupBytes + ks * 2048;
+        const int ks = i >> 1, fb = i & 1;
+        return cur + v_lane[second][fb] + ks * 2048;
       };
-      constexpr int NPV = 16;   // (k-step, feature block) pairs; each feeds 2 row halves
+      constexpr int NPV = 8;   // (k-step, feature block) pairs; each feeds 2 row halves
       bf16x4 r0[kPvDepthX], r1[kPvDepthX];
 #pragma unroll
       for (int i = 0; i < kPvDepthX; ++i) {
@@ -1341,7 +1439,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       bf16x8 pbr[2];
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
-        const int ks = i >> 2, fb = i & 3;
+        const int ks = i >> 1, fb = i & 1;
         if (fb == 0) {
           pbr[0] = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 0) * 64 + lane) * 16);
           pbr[1] = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 1) * 64 + lane) * 16);
@@ -1353,24 +1451,25 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
         }
         o[fb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbr[0], o[fb][0], 0, 0, 0);
         o[fb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbr[1], o[fb][1], 0, 0, 0);
-        if (kDmaSlotsX > NQ) dma_slot<kDmaSlotsX>(dma, more, NQ + i);
         sched_fence();
       }
     }
 
-    lds_barrier();  // every wave is done with `cur` and the exchange area
-
+    // The next step's first barrier orders this PV's LDS reads before any
+    // write into `cur` or the exchange area; only the epilogue needs one here.
     if (!ti.last) return;
+    lds_barrier();   // every wave is done reading P from the exchange area
 
-    // ---- epilogue for sequence bc: full row sums, then O / l and LSE
-    LDS_AS float* const ssum = (LDS_AS float*)xb;   // [key block][row]
+    // ---- epilogue for this sequence: full row sums, then O / l and LSE
+    LDS_AS float* const ssum = (LDS_AS float*)xb;   // [key quarter][row]
     const float lh = sum_xor32(l_run);
-    if (h == 0) ssum[kh * 64 + 32 * rh + n] = lh;
+    if (h == 0) ssum[kq * 64 + 32 * rh + n] = lh;
     lds_barrier();
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int row = row0 + 32 * rb + n;
-      const float l_row = ssum[32 * rb + n] + ssum[64 + 32 * rb + n];
+      const float l_row = (ssum[32 * rb + n] + ssum[64 + 32 * rb + n]) +
+                          (ssum[128 + 32 * rb + n] + ssum[192 + 32 * rb + n]);
       const bool live = l_row > 0.f;
       const float inv = live ? 1.0f / l_row : 0.f;
       if (row < ti.rows) {
@@ -1384,11 +1483,11 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
           dst_l = p.ws_lse + (size_t)slot * R + row;
         }
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb) {
+        for (int fb = 0; fb < 2; ++fb) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             f32x4 v = {o[fb][rb][4 * jj], o[fb][rb][4 * jj + 1], o[fb][rb][4 * jj + 2], o[fb][rb][4 * jj + 3]};
-            *(f32x4*)(dst_o + 128 * wave + 32 * fb + 8 * jj + 4 * h) = v * inv;
+            *(f32x4*)(dst_o + 64 * wave + 32 * fb + 8 * jj + 4 * h) = v * inv;
           }
         }
         if (wave == 0 && h == 0)
@@ -1615,8 +1714,8 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
     if (fp8) MLA_LAUNCH((decode_kernel16<VAR_NARROW16, true>), kThreads);
     else MLA_LAUNCH(decode_kernel_pc, 2 * kThreads);
   } else {
-    if (fp8) MLA_LAUNCH((decode_kernel_x<true>), kThreads);
-    else MLA_LAUNCH((decode_kernel_x<false>), kThreads);
+    if (fp8) MLA_LAUNCH((decode_kernel_x<true>), kThreadsX);
+    else MLA_LAUNCH((decode_kernel_x<false>), kThreadsX);
   }
 #undef MLA_LAUNCH
   return hipGetLastError();
