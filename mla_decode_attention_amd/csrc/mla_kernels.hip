@@ -44,6 +44,7 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 #include <math.h>
+#include <utility>
 
 #include "mla_internal.h"
 
@@ -215,6 +216,18 @@ template <class Dma>
 __device__ __forceinline__ void dma_all(const Dma& dma) {
 #pragma unroll
   for (int k = 0; k < Dma::kLoads; ++k) dma.load(k);
+}
+
+// Same spreading for loaders whose load index is a template argument (so it
+// can become an immediate offset); the caller decides `more` once, outside
+// its MFMA loop.
+template <int M, class Dma, int... K>
+__device__ __forceinline__ void dma_slot_ct(const Dma& dma, int slot, std::integer_sequence<int, K...>) {
+  ((((K + 1) * M) / Dma::kLoads - 1 == slot ? dma.template load_ct<K>() : void()), ...);
+}
+template <int M, class Dma>
+__device__ __forceinline__ void dma_slot_ct(const Dma& dma, int slot) {
+  dma_slot_ct<M>(dma, slot, std::make_integer_sequence<int, Dma::kLoads>{});
 }
 
 // fp8 staging page -> bf16 tile (exact: every E4M3FN value is a bf16 value).
@@ -1140,6 +1153,8 @@ struct TileDmaX<false> {
   }
   // the per-load offset goes into the scalar base, so the lane offset is one register
   __device__ __forceinline__ void load(int i) const { dma16(voff, page + 128 * i, lds0 + i * 8192); }
+  template <int I>
+  __device__ __forceinline__ void load_ct() const { load(I); }
 };
 
 // fp8 page, 512 threads: a plain copy of the 36 KiB page into the staging
@@ -1176,6 +1191,8 @@ struct TileDmaX<true> {
     dma16(voff, page, lds0 + i * kThreadsX * 16);
     if (i == 0 && tid < 64) dma4(sc_off, scale, sc_lds);
   }
+  template <int I>
+  __device__ __forceinline__ void load_ct() const { load(I); }
 };
 
 // fp8 staging page -> bf16 tile with 512 threads (see widen_fp8_tile).
@@ -1279,6 +1296,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   float m_run[2] = {-INFINITY, -INFINITY};   // running max of rows row0 + n, row0 + 32 + n
   float l_run = 0.f;                         // partial row sum of row_qk (this key quarter, lane half)
   bool restart = true;                       // next rescale zeroes O and l (a sequence starts)
+  int row_tok = 0;                           // query token of row_qk in the current sequence
 
   TileDmaX<FP8> dma;
   TileInfo next = unit.prepare(a, unit.f_begin, FP8 ? buf1 : buf0, sb0, tid, dma);
@@ -1307,6 +1325,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       // accumulators are never reset outside the one rescale path
       m_run[0] = m_run[1] = -INFINITY;
       restart = true;
+      row_tok = rr / p.num_heads;
       __builtin_amdgcn_s_waitcnt(kVmcntZero);
     }
     const bool final_out = ti.final_out;
@@ -1327,7 +1346,9 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
     // ---- QK GEMM: partial S^T[32 keys of half kh, 32 rows of half rh] over feature half fh
     f32x16 sacc = f32x16{};
-    {
+    // one copy of the loop with the next tile's loads and one without, so
+    // the load slots need no per-slot branch
+    auto qk = [&](auto with_loads) {
       auto kaddr = [&](int c) { return cur + k_lane[c & 3] + (c >> 2) * kLineGroupBytes; };
       bf16x8 ring[kQkDepthX];
 #pragma unroll
@@ -1337,10 +1358,12 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
         const bf16x8 av = ring[i % kQkDepthX];
         if (i + kQkDepthX < NQ) ring[i % kQkDepthX] = ld128(kaddr(i + kQkDepthX));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[i], sacc, 0, 0, 0);
-        dma_slot<NQ>(dma, load_next, i);
+        if constexpr (decltype(with_loads)::value) dma_slot_ct<NQ>(dma, i);
         sched_fence();
       }
-    }
+    };
+    if (load_next) qk(std::true_type{});
+    else qk(std::false_type{});
 
     // ---- add the two feature halves: keep registers 8fh..8fh+7 (keys
     //      16kq + 0..15), give registers 8(1-fh).. to the partner. fh is
@@ -1366,25 +1389,52 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       for (int e = 0; e < 4; ++e) sv[4 * part + e] += v[e];
     }
 
-    // ---- softmax: quarter-tile maxima -> shared running max -> P
+    // ---- softmax. P is computed against the running max before the tile
+    //      maxima of the other waves are known: with the lazy rescale the
+    //      running max moves only when some row's tile max exceeds it by more
+    //      than the threshold (so P <= 2^threshold otherwise). The quarter
+    //      maxima are published with P; after the barrier every wave checks
+    //      all 64 rows (the same decision in every wave) and, on the rare tiles
+    //      that raise a row's max (always on a sequence's first tile), rescales
+    //      O and l and rewrites P behind one more barrier.
     LDS_AS float* const smax = (LDS_AS float*)(cur + 8 * kLineGroupBytes);   // [key quarter][row]
     const int key0 = t * kPage + 16 * kq + 4 * h;
-    const int vis = L - ti.qlen + (row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0)) / p.num_heads + 1;
+    // keys at or past vis are masked (causal rule / cache tail); only the
+    // tiles that reach past L - qlen + 1 can hold such keys
     const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
     f32x4 ksc[2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
       ksc[jj] = FP8 ? *(const LDS_AS f32x4*)(sbc + 16 * kq + 8 * jj + 4 * h) : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sv[r] *= FP8 ? ksc[r >> 2][r & 3] * p.scale_log2 : p.scale_log2;
+    if (__builtin_expect(need_mask, 0)) {
+      const int vis = L - ti.qlen + row_tok + 1;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if ((key0 + 8 * (r >> 2) + (r & 3)) >= vis) sv[r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float v = sv[r] * (FP8 ? ksc[r >> 2][r & 3] * p.scale_log2 : p.scale_log2);
-      if (need_mask && (key0 + 8 * (r >> 2) + (r & 3)) >= vis) v = -INFINITY;
-      sv[r] = v;
-      mx = fmaxf(mx, v);
-    }
+    for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sv[r]);
     mx = max_xor32(mx);
     if (h == 0) smax[kq * 64 + 32 * rh + n] = mx;
+    // P operand [k-step][row half][lane] in the exchange area (the partial
+    // scores there were consumed before the barrier above)
+    LDS_AS bf16x8* const p_out = (LDS_AS bf16x8*)(xb + ((kq * 2 + rh) * 64 + lane) * 16);
+    float l_tile = 0.f;
+    auto make_p = [&](float m_ref) {
+      bf16x8 pb;
+      l_tile = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = exp2_fast(sv[e] - m_ref);
+        l_tile += pr;
+        pb[e] = (__bf16)(FP8 ? pr * ksc[e >> 2][e & 3] : pr);
+      }
+      *p_out = pb;
+    };
+    if (!restart) make_p(m_run[rh]);   // finite once a sequence has started
     lds_barrier();
 
     float alpha[2];
@@ -1407,21 +1457,10 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
         o[fb][1] *= alpha[1];
       }
       l_run *= alpha[rh];
+      make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
+      lds_barrier();
     }
-    const float m_eff = (m_run[rh] == -INFINITY) ? 0.0f : m_run[rh];
-    // P operand [k-step][row half][lane] in the exchange area (the partial
-    // scores there were consumed before the barrier above)
-    {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pr = exp2_fast(sv[e] - m_eff);
-        l_run += pr;
-        pb[e] = (__bf16)(FP8 ? pr * ksc[e >> 2][e & 3] : pr);
-      }
-      *(LDS_AS bf16x8*)(xb + ((kq * 2 + rh) * 64 + lane) * 16) = pb;
-    }
-    lds_barrier();
+    l_run += l_tile;
 
     // ---- PV GEMM: O^T[64 features of this wave, 64 rows] += V^T . P^T
     {
