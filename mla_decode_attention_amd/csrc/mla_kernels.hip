@@ -1331,9 +1331,11 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     const bool final_out = ti.final_out;
     const int slot = ti.slot;
 
+    // the next tile's facts and load plan (addresses only) are set up while
+    // this tile's loads may still be landing
     const bool more = f + 1 < unit.f_end;
-    wait_tile();
     if (more) next = unit.prepare(a, f + 1, nxt, sbn, tid, dma);
+    wait_tile();
     const bool load_next = more && row0 < next.rows;
     if (skip) {
       if (load_next) dma_all(dma);
@@ -1419,6 +1421,12 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sv[r]);
     mx = max_xor32(mx);
     if (h == 0) smax[kq * 64 + 32 * rh + n] = mx;
+    // A wave that sees a row max past the threshold stamps the tile index
+    // into the flag word (left over values of other tiles never match f; a
+    // stray match would only take the exact slow path below).
+    LDS_AS int* const raise_flag = (LDS_AS int*)(smax + 256);
+    if (!restart && __builtin_amdgcn_ballot_w64(mx > m_run[rh] + kRescaleThreshold) && lane == 0)
+      *raise_flag = f;
     // P operand [k-step][row half][lane] in the exchange area (the partial
     // scores there were consumed before the barrier above)
     LDS_AS bf16x8* const p_out = (LDS_AS bf16x8*)(xb + ((kq * 2 + rh) * 64 + lane) * 16);
@@ -1434,23 +1442,23 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       }
       *p_out = pb;
     };
-    if (!restart) make_p(m_run[rh]);   // finite once a sequence has started
+    // (a row whose keys were all masked so far keeps m = -inf: reference 0, P = 0)
+    if (!restart) make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
     lds_barrier();
 
-    float alpha[2];
-    bool any_raise = restart;
+    if (restart || uniform(*raise_flag) == f) {
+      // some row's max moved (or a sequence starts): every wave derives the
+      // new running max of all 64 rows from the quarter maxima
+      float alpha[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float tmax = fmaxf(fmaxf(smax[32 * rb + n], smax[64 + 32 * rb + n]),
-                               fmaxf(smax[128 + 32 * rb + n], smax[192 + 32 * rb + n]));
-      const float m_new = fmaxf(m_run[rb], tmax);
-      const bool raise = m_new > m_run[rb] + kRescaleThreshold;
-      alpha[rb] = restart ? 0.0f : raise ? exp2_fast(m_run[rb] - m_new) : 1.0f;
-      if (raise) m_run[rb] = m_new;
-      any_raise |= raise;
-    }
-    restart = false;
-    if (__builtin_amdgcn_ballot_w64(any_raise)) {
+      for (int rb = 0; rb < 2; ++rb) {
+        const float tmax = fmaxf(fmaxf(smax[32 * rb + n], smax[64 + 32 * rb + n]),
+                                 fmaxf(smax[128 + 32 * rb + n], smax[192 + 32 * rb + n]));
+        const float m_new = fmaxf(m_run[rb], tmax);
+        const bool raise = m_new > m_run[rb] + kRescaleThreshold;
+        alpha[rb] = restart ? 0.0f : raise ? exp2_fast(m_run[rb] - m_new) : 1.0f;
+        if (raise) m_run[rb] = m_new;
+      }
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) {
         o[fb][0] *= alpha[0];
@@ -1460,6 +1468,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
       lds_barrier();
     }
+    restart = false;
     l_run += l_tile;
 
     // ---- PV GEMM: O^T[64 features of this wave, 64 rows] += V^T . P^T
