@@ -173,3 +173,45 @@ def test_full_size_sampled(name):
     sample = sorted({0, B - 1, int(np.argmax(w.seqlens)), B // 2})
     ref_out, ref_lse = reference(w, batch_indices=sample)
     assert_parity(w, out[sample], lse[sample], ref_out, ref_lse, f"{name} full, sample {sample}")
+
+
+# ------------------------------------------------------- lazy-rescale coverage
+
+def _ramp_cache(w, amp, seed):
+    """Rewrite every live key j of sequence b as noise + amp * (j / L_b) * v,
+    with one shared random direction v: rows whose query leans on v see their
+    scores climb through the sequence, so the running max moves many times
+    (well past the lazy-rescale threshold) and on tiles in the middle of a
+    split unit; the other rows see falling scores."""
+    from workloads import f32_to_bf16_bits, _e4m3_encode, E4M3_MAX
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal(w.cache.shape[-1]).astype(np.float32)
+    for b, L in enumerate(w.seqlens):
+        L = int(L)
+        if L == 0:
+            continue
+        j = np.arange(L)
+        x = (0.3 * rng.standard_normal((L, v.size)) + amp * (j / L)[:, None] * v[None, :]).astype(np.float32)
+        pages = w.block_table[b, j // PAGE_TOKENS]
+        if w.kv_dtype == "bf16":
+            w.cache[pages, j % PAGE_TOKENS] = f32_to_bf16_bits(x)
+        else:
+            amax = np.abs(x).max(axis=1)
+            sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+            w.cache[pages, j % PAGE_TOKENS] = _e4m3_encode(np.clip(x / sc[:, None], -E4M3_MAX, E4M3_MAX))
+            w.kv_scale[pages, j % PAGE_TOKENS] = sc
+    return w
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("H,s", [(16, 1), (16, 2), (128, 2)])
+@pytest.mark.parametrize("split", [False, True])
+def test_rising_scores_rescale(kv_dtype, H, s, split):
+    lens = [1000, 700, 130, 64]
+    w = _ramp_cache(make_workload("ramp", len(lens), H, s, lens, kv_dtype=kv_dtype, seed=31 + H + s), 6.0, 5)
+    out, lse, _ = run_gpu(w, split=split, num_units=7, min_tiles=1)
+    ref_out, ref_lse = reference(w)
+    # the ramp really moves the running max: the largest score of many rows
+    # sits far above their first tile's
+    assert float(np.max(ref_lse)) > 20.0
+    assert_parity(w, out, lse, ref_out, ref_lse, f"ramp {kv_dtype} H={H} s={s} split={split}")
