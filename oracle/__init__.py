@@ -25,5 +25,5 @@ from .mla_oracle import (  # noqa: F401
     bf16_bits_to_f64, e4m3fn_value, E4M3FN_TABLE, decode_e4m3fn,
     sequence_rows, visible_counts, attend, attend_partials, lse_merge,
     mla_decode, mla_decode_sequence, mla_decode_varlen, split_schedule,
-    E4M3FN_MAX, encode_e4m3fn, quantize_token_e4m3, append_kv,
+    E4M3FN_MAX, encode_e4m3fn, quantize_token_e4m3, append_kv, quantize_query_rows_e4m3,
 )

@@ -164,10 +164,16 @@ def lse_merge(outs, lses):
 
 
 def mla_decode_sequence(q_bits_b, cache, block_table_row, seqlen, softmax_scale,
-                        kv_dtype="bf16", kv_scale=None):
-    """One sequence: q_bits_b uint16 [s, H, 576] -> (O [s, H, 512], lse [s, H])."""
+                        kv_dtype="bf16", kv_scale=None, q_values=None):
+    """One sequence: q_bits_b uint16 [s, H, 576] -> (O [s, H, 512], lse [s, H]).
+
+    q_values (optional, float64 [s, H, 576]) replaces the decoded q_bits, e.g.
+    the E4M3 image of the queries from quantize_query_rows_e4m3."""
     s, H, _ = q_bits_b.shape
-    q_rows = bf16_bits_to_f64(q_bits_b).reshape(s * H, D_QK)
+    if q_values is None:
+        q_rows = bf16_bits_to_f64(q_bits_b).reshape(s * H, D_QK)
+    else:
+        q_rows = np.asarray(q_values, dtype=np.float64).reshape(s * H, D_QK)
     L = int(seqlen)
     rows = sequence_rows(cache, block_table_row, L, kv_dtype, kv_scale)
     O, lse = attend(q_rows, rows, rows[:, :D_V], softmax_scale, visible_counts(L, s, H))
@@ -196,15 +202,18 @@ def mla_decode_varlen(q_bits, cu_q, cache, block_table, seqlens, softmax_scale, 
 
 
 def mla_decode(q_bits, cache, block_table, seqlens, softmax_scale, kv_dtype="bf16",
-               kv_scale=None, batch_indices=None):
-    """Whole batch (or the listed sequences): out [B, s, H, 512], lse [B, s, H] float64."""
+               kv_scale=None, batch_indices=None, q_values=None):
+    """Whole batch (or the listed sequences): out [B, s, H, 512], lse [B, s, H] float64.
+
+    q_values (optional, float64 [B, s, H, 576]) replaces the decoded q_bits."""
     B, s, H, _ = q_bits.shape
     idx = range(B) if batch_indices is None else list(batch_indices)
     out = np.zeros((len(idx), s, H, D_V), dtype=np.float64)
     lse = np.zeros((len(idx), s, H), dtype=np.float64)
     for k, b in enumerate(idx):
         out[k], lse[k] = mla_decode_sequence(q_bits[b], cache, block_table[b], seqlens[b],
-                                              softmax_scale, kv_dtype, kv_scale)
+                                              softmax_scale, kv_dtype, kv_scale,
+                                              None if q_values is None else q_values[b])
     return out, lse
 
 
@@ -325,3 +334,19 @@ def append_kv(latent_bits, block_table, seqlens, cache, kv_scale=None, kv_dtype=
                 cache[page, slot] = codes
                 kv_scale[page, slot] = sc
     return cache, kv_scale
+
+
+def quantize_query_rows_e4m3(q_bits) -> np.ndarray:
+    """E4M3 image of the query rows for a decode that runs the contractions on
+    FP8 operands (PaddleNLP issue #10157, quantization section: SageAttention2
+    quantises the attention operands dynamically and dequantises the products
+    once). Each row of 576 values is quantised like a cache token:
+    quantize_token_e4m3 (scale = max|row| / 448 in fp32, nearest-even codes);
+    returns scale * value(code) as float64, shape of q_bits (bf16 bits)."""
+    q = bf16_bits_to_f64(q_bits).astype(np.float32)
+    flat = q.reshape(-1, q.shape[-1])
+    out = np.empty(flat.shape, dtype=np.float64)
+    for r in range(flat.shape[0]):
+        codes, sc = quantize_token_e4m3(flat[r])
+        out[r] = decode_e4m3fn(codes) * np.float64(sc)
+    return out.reshape(q.shape)

@@ -507,3 +507,48 @@ def test_varlen_uniform_q_len_equals_batched_call():
     o1, l1 = oracle.mla_decode_varlen(flat, cu, w.cache, w.block_table, w.seqlens, w.softmax_scale)
     o2, l2 = run_oracle(w)
     assert np.array_equal(o1, o2.reshape(-1, 4, D_V)) and np.array_equal(l1, l2.reshape(-1, 4))
+
+
+# ------------------------------------------- E4M3 image of the query rows
+
+def test_query_quantisation_worked_example():
+    """Row max 1.0 -> scale 1/448 (fp32); 0.3 * 448 = 134.4 lies between the
+    E4M3 codes 128 and 144 (spacing 16 in [128, 256)), so it maps to 128/448;
+    -1.0 maps to -448 * scale exactly; 0 stays 0."""
+    row = np.zeros(576, dtype=np.float32)
+    row[0], row[1], row[2] = 1.0, 0.3, -1.0
+    got = oracle.quantize_query_rows_e4m3(_bits(row)[None])[0]
+    sc = np.float64(np.float32(np.float32(1.0) / np.float32(448.0)))
+    assert got[0] == 448 * sc and got[2] == -448 * sc
+    assert got[1] == 128 * sc
+    assert np.all(got[3:] == 0)
+
+
+def test_query_quantisation_bound_and_powers_of_two():
+    rng = np.random.default_rng(5)
+    q = _bits(rng.standard_normal((3, 4, 576)).astype(np.float32))
+    x = oracle.bf16_bits_to_f64(q)
+    got = oracle.quantize_query_rows_e4m3(q)
+    assert got.shape == x.shape
+    amax = np.abs(x).max(axis=-1, keepdims=True)
+    # normal-range values keep a relative error <= 2^-4 (3 mantissa bits, nearest);
+    # values below the smallest normal (2^-6 after scaling) an absolute one <= 2^-10 * scale
+    scale = amax / 448
+    err = np.abs(got - x)
+    assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale) * (1 + 1e-6))
+    # the row maximum is reproduced (up to the fp32 scale)
+    assert np.allclose(np.abs(got).max(axis=-1), amax[..., 0], rtol=1e-6)
+    # a row of powers of two with max 2^k: scale 2^k / 448 is not a power of
+    # two, but 2^j / scale for j <= k is representable when the quotient is;
+    # zero rows stay zero
+    z = np.zeros((1, 576), dtype=np.float32)
+    assert np.all(oracle.quantize_query_rows_e4m3(_bits(z)) == 0)
+
+
+def test_decode_with_query_values_matches_bits():
+    """q_values equal to the decoded q_bits reproduce the default result."""
+    w = make_workload("qv", 2, 16, 2, [70, 130], seed=4)
+    o1, l1 = oracle.mla_decode(w.q_bits, w.cache, w.block_table, w.seqlens, w.softmax_scale)
+    o2, l2 = oracle.mla_decode(w.q_bits, w.cache, w.block_table, w.seqlens, w.softmax_scale,
+                               q_values=oracle.bf16_bits_to_f64(w.q_bits))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
