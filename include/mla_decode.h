@@ -150,6 +150,32 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
                    void* stream);
 
 /*
+ * mla_decode_fwd_fp8mma: mla_decode_fwd for an fp8 cache with both
+ * contractions on fp8 matrix cores. PaddleNLP issue #10157 (quantization
+ * section, SageAttention2) quantises P to FP8 and multiplies it with FP8 V,
+ * dequantising the product once; this entry point does that and also
+ * quantises the query rows:
+ *   q8 = E4M3(q / sq) per row with sq = max|q_row| / 448 (round to nearest
+ *   even); scores from the E4M3 codes of q8 and the cache, times sq, the
+ *   key's per-token scale and softmax_scale; P'_j = P_j * s_j (s_j the
+ *   per-token scale) quantised to E4M3 per (row, 32-key block) with a
+ *   power-of-two scale, undone exactly by the MFMA's block scale.
+ * The result is an approximation of mla_decode_fwd's: on the normally
+ * distributed test data the O error is a few percent of max|O| (the E4M3
+ * rounding of q and P, relative 2^-4 per element) and the LSE error about
+ * 0.03; the tests state the bound. Row sums and the LSE use unquantised P.
+ *   kv_dtype       must be MLA_KV_FP8_E4M3 (else MLA_ERR_UNSUPPORTED)
+ * Every other argument, the split plan, the workspace and the errors are
+ * those of mla_decode_fwd; any q_len * num_heads <= MLA_MAX_ROWS works (rows
+ * go in blocks of 64).
+ */
+int mla_decode_fwd_fp8mma(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                          int num_pages, const int32_t* block_table, int max_pages_per_seq,
+                          const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
+                          float softmax_scale, float* out, float* lse, const void* metadata, int num_units,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mla_decode_fwd_varlen: mla_decode_fwd with a query count per sequence, so
  * one forward verifies sequences that accepted different numbers of draft
  * tokens in the previous round (PaddleNLP issue #10157, MTP section: the

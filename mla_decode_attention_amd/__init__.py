@@ -60,6 +60,8 @@ def load_library():
         "mla_get_split_metadata": (c_int, [vp, c_int, c_int, c_int, vp, c_size, vp]),
         "mla_decode_fwd": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
                                    ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
+        "mla_decode_fwd_fp8mma": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
+                                          ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
         "mla_combine": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp]),
         "mla_append_kv": (c_int, [vp, c_int, c_int, vp, c_int, vp, vp, vp, c_int, c_int, vp]),
         "mla_decode_fwd_varlen": (c_int, [vp, vp, c_int, c_int, vp, vp, c_int, c_int, vp, c_int, vp, c_int,
@@ -157,12 +159,14 @@ def get_split_metadata(cache_seqlens: torch.Tensor, q_len: int, num_heads: int,
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
            cache_seqlens: torch.Tensor, softmax_scale: float, kv_scale: Optional[torch.Tensor] = None,
            plan: Optional[SplitPlan] = None, out: Optional[torch.Tensor] = None,
-           lse: Optional[torch.Tensor] = None):
+           lse: Optional[torch.Tensor] = None, fp8_mma: bool = False):
     """MLA decode attention. Returns (out fp32 [B,s,H,512], lse fp32 [B,s,H]).
 
     q bf16 [B, s, H, 576]; kv_cache [P, 64, 576] bf16 (or uint8 / float8_e4m3fn
     codes with kv_scale fp32 [P, 64]); block_table int32 [B, max_pages];
     cache_seqlens int32 [B]. plan=None runs one work unit per sequence.
+    fp8_mma=True (fp8 cache only) runs mla_decode_fwd_fp8mma: queries and P
+    quantised to E4M3, an approximation of the default path.
     """
     lib = load_library()
     _need(q, "q", (torch.bfloat16,), 4)
@@ -194,10 +198,11 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
         if (plan.batch, plan.q_len, plan.num_heads) != (B, s, H):
             raise ValueError("plan was built for another shape")
         md, ws, units, wbytes = plan.metadata, plan.workspace, plan.num_units, plan.workspace.numel()
-    _check(lib.mla_decode_fwd(_ptr(q), _ptr(kv_cache), _ptr(kv_scale), kv_dtype, kv_cache.shape[0],
+    name = "mla_decode_fwd_fp8mma" if fp8_mma else "mla_decode_fwd"
+    _check(getattr(lib, name)(_ptr(q), _ptr(kv_cache), _ptr(kv_scale), kv_dtype, kv_cache.shape[0],
                               _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), B, s, H,
                               float(softmax_scale), _ptr(out), _ptr(lse), _ptr(md), units, _ptr(ws),
-                              wbytes, _stream()), "mla_decode_fwd")
+                              wbytes, _stream()), name)
     return out, lse
 
 

@@ -166,9 +166,11 @@ int decode_impl(const void* q, const int32_t* cu_q, int total_q, const void* kv_
                 int kv_dtype, int num_pages, const int32_t* block_table, int max_pages_per_seq,
                 const int32_t* cache_seqlens, int batch, int q_len, int num_heads, float softmax_scale,
                 float* out, float* lse, const void* metadata, int num_units, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool fp8_mma = false) {
   if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !lse)
     return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (fp8_mma && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "the fp8-MFMA path needs an fp8 cache (kv_dtype %d)", kv_dtype);
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
     return fail(MLA_ERR_UNSUPPORTED, "kv_dtype %d is not supported", kv_dtype);
   if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_scale)
@@ -224,7 +226,7 @@ int decode_impl(const void* q, const int32_t* cu_q, int total_q, const void* kv_
   p.ws_out = metadata ? (float*)workspace : nullptr;
   p.ws_lse = metadata ? (float*)((char*)workspace + slots * p.rows * mla::kDv * sizeof(float)) : nullptr;
 
-  const int var = mla::variant_for(p.rows);
+  const int var = fp8_mma ? mla::VAR_Q8 : mla::variant_for(p.rows);
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   {
@@ -265,6 +267,16 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
   return decode_impl(q, nullptr, 0, kv_cache, kv_scale, kv_dtype, num_pages, block_table, max_pages_per_seq,
                      cache_seqlens, batch, q_len, num_heads, softmax_scale, out, lse, metadata, num_units,
                      workspace, workspace_bytes, stream);
+}
+
+int mla_decode_fwd_fp8mma(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                          int num_pages, const int32_t* block_table, int max_pages_per_seq,
+                          const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
+                          float softmax_scale, float* out, float* lse, const void* metadata, int num_units,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, nullptr, 0, kv_cache, kv_scale, kv_dtype, num_pages, block_table, max_pages_per_seq,
+                     cache_seqlens, batch, q_len, num_heads, softmax_scale, out, lse, metadata, num_units,
+                     workspace, workspace_bytes, stream, true);
 }
 
 int mla_decode_fwd_varlen(const void* q, const int32_t* cu_seqlens_q, int total_q, int max_q_len,

@@ -130,6 +130,18 @@ def test_varlen_argument_errors(lib):
     assert call(mq=300, H=16) == INVALID      # rows over the limit
 
 
+def test_fp8mma_argument_errors(lib):
+    f = lib.mla_decode_fwd_fp8mma
+    def call(dtype=1, scale=FAKE, q=FAKE, s=1):
+        return f(q, FAKE, scale, dtype, 4, FAKE, 4, FAKE, 1, s, 16, ctypes.c_float(0.072), FAKE, FAKE,
+                 None, 0, None, 0, None)
+    assert call(dtype=0, scale=None) == UNSUPPORTED   # bf16 cache: no fp8 contraction path
+    assert call(dtype=1, scale=None) == INVALID       # fp8 needs scales
+    assert call(q=None) == INVALID
+    assert call(s=0) == INVALID
+    assert lib.mla_last_error() != b""
+
+
 def test_binding_rejects_host_tensors():
     import torch
     q = torch.zeros(1, 1, 16, 576, dtype=torch.bfloat16)
