@@ -123,7 +123,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="share16", choices=["tiny", "share16", "mtp", "ragged", "fp8", "varlen"])
+    ap.add_argument("--config", default="share16",
+                    choices=["tiny", "share16", "mtp", "ragged", "fp8", "varlen", "fp8mma"],
+                    help="workload; fp8mma = the fp8 workload on mla_decode_fwd_fp8mma (queries and P in "
+                         "E4M3, fp8 matrix cores; an approximation of the default path)")
     ap.add_argument("--sets", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--num-units", type=int, default=0, help="split work units (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -147,8 +150,10 @@ def main():
     import mla_decode_attention_amd as mla
     from workloads import config, CONFIG_TEXT
 
+    fp8_mma = args.config == "fp8mma"
+    wname = "fp8" if fp8_mma else args.config
     t_gen = time.perf_counter()
-    w = config(args.config, seed=0)
+    w = config(wname, seed=0)
     alg = algorithmic(w)
     print(f"[bench] {args.config}: generated in {time.perf_counter() - t_gen:.1f} s; "
           f"KV {alg['kv_bytes'] / 1e6:.1f} MB, {alg['flops'] / 1e9:.1f} GFLOP", file=sys.stderr, flush=True)
@@ -203,7 +208,8 @@ def main():
             mla.decode_varlen(q, cu_q, w.q_len, kvs[k], bt, sl, w.softmax_scale, kv_scale=scales[k], plan=plan,
                               out=out, lse=lse)
         else:
-            mla.decode(q, kvs[k], bt, sl, w.softmax_scale, kv_scale=scales[k], plan=plan, out=out, lse=lse)
+            mla.decode(q, kvs[k], bt, sl, w.softmax_scale, kv_scale=scales[k], plan=plan, out=out, lse=lse,
+                       fp8_mma=fp8_mma)
 
     for i in range(args.warmup):
         step(i)
@@ -229,15 +235,16 @@ def main():
     kv_gbps = alg["kv_bytes"] / step_s / 1e9
     tflops = alg["flops"] / step_s / 1e12
     t_hbm = alg["bytes"] / (PEAK_HBM_GBPS * 1e9)
-    t_mfma = alg["flops"] / (PEAK_BF16_TFLOPS * 1e12)
+    peak_mfma = PEAK_FP8_TFLOPS if fp8_mma else PEAK_BF16_TFLOPS   # the contraction dtype's peak
+    t_mfma = alg["flops"] / (peak_mfma * 1e12)
     if t_hbm >= t_mfma:
         achieved = alg["bytes"] / main_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
     else:
         achieved = alg["flops"] / main_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_mfma,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4), "traffic": None}
     roof["traffic"] = measured_traffic(args.config)
     roof.update({"kernel": "decode_kernel", "kernel_ms": round(main_ms, 5), "launches": launches,
                  "algorithmic_bytes": alg["bytes"], "algorithmic_flops": alg["flops"],
@@ -254,9 +261,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if fp8_mma else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: {CONFIG_TEXT[args.config]}", "batch": w.batch,
+        "config": {"workload": f"{args.config}: {CONFIG_TEXT[wname]}" + (
+                       "; queries and P in E4M3 on fp8 MFMA (mla_decode_fwd_fp8mma)" if fp8_mma else ""),
+                   "batch": w.batch,
                    "heads": w.num_heads, "q_len": w.q_len if not w.varlen else "per-sequence, max %d" % w.q_len,
                    "query_tokens": int(sum(w.q_lens)), "kv_dtype": w.kv_dtype,
                    "tokens": alg["tokens"], "pages": alg["pages"], "num_units": units,
