@@ -350,3 +350,44 @@ def quantize_query_rows_e4m3(q_bits) -> np.ndarray:
         codes, sc = quantize_token_e4m3(flat[r])
         out[r] = decode_e4m3fn(codes) * np.float64(sc)
     return out.reshape(q.shape)
+
+
+# --------------------------------------------------------------------------
+# Prefill / extend, the un-absorbed form (the second workload): per head the
+# key is [k_nope_h (128), k_rope (64, shared by the heads)], head dim 192 (the
+# DeepSeek head dim of PaddleNLP issue #10157, quantization section,
+# SageAttention), and the value is v_h (128).
+# --------------------------------------------------------------------------
+D_NOPE = 128
+D_ROPE = 64
+D_QK_PREFILL = D_NOPE + D_ROPE
+D_V_PREFILL = 128
+
+
+def mla_prefill(q_bits, k_nope_bits, k_rope_bits, v_bits, cu_q, cu_k, softmax_scale, batch_indices=None):
+    """Causal attention of new tokens over their sequence's keys.
+
+    q [Tq, H, 192], k_nope [Tk, H, 128], k_rope [Tk, 64], v [Tk, H, 128], all
+    bf16 bits. Sequence b owns queries cu_q[b]..cu_q[b+1] (N_b of them) and
+    keys cu_k[b]..cu_k[b+1] (L_b >= N_b); its N_b queries are the last N_b of
+    its L_b tokens, so query i sees keys j <= L_b - N_b + i (prefill: N_b = L_b;
+    extend: a cached prefix of L_b - N_b tokens). Returns out [Tq, H, 128] and
+    lse [Tq, H] float64 (natural log); rows of unlisted sequences stay 0 / -inf.
+    """
+    Tq, H, _ = q_bits.shape
+    out = np.zeros((Tq, H, D_V_PREFILL), dtype=np.float64)
+    lse = np.full((Tq, H), -np.inf, dtype=np.float64)
+    idx = range(len(cu_q) - 1) if batch_indices is None else list(batch_indices)
+    for b in idx:
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        N, L = q1 - q0, k1 - k0
+        if N == 0:
+            continue
+        vis = visible_counts(L, N, 1)
+        rope = bf16_bits_to_f64(k_rope_bits[k0:k1])
+        for h in range(H):
+            K = np.concatenate([bf16_bits_to_f64(k_nope_bits[k0:k1, h]), rope], axis=1)
+            V = bf16_bits_to_f64(v_bits[k0:k1, h])
+            out[q0:q1, h], lse[q0:q1, h] = attend(bf16_bits_to_f64(q_bits[q0:q1, h]), K, V, softmax_scale, vis)
+    return out, lse

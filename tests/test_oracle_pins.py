@@ -552,3 +552,92 @@ def test_decode_with_query_values_matches_bits():
     o2, l2 = oracle.mla_decode(w.q_bits, w.cache, w.block_table, w.seqlens, w.softmax_scale,
                                q_values=oracle.bf16_bits_to_f64(w.q_bits))
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------ prefill / extend (un-absorbed)
+
+def test_prefill_brute_force():
+    """Pure-Python loops: per sequence, head and query, the scores over the
+    visible keys (query i of N sees keys j <= L - N + i), then softmax and the
+    weighted sum; the key is k_nope of that head followed by the shared rope."""
+    from workloads import make_prefill_workload
+    w = make_prefill_workload("bf", [3, 2, 1], [5, 2, 4], 2, seed=11)
+    out, lse = oracle.mla_prefill(w.q_bits, w.k_nope_bits, w.k_rope_bits, w.v_bits, w.cu_q, w.cu_k,
+                                  w.softmax_scale)
+    q = oracle.bf16_bits_to_f64(w.q_bits)
+    kn = oracle.bf16_bits_to_f64(w.k_nope_bits)
+    kr = oracle.bf16_bits_to_f64(w.k_rope_bits)
+    v = oracle.bf16_bits_to_f64(w.v_bits)
+    for b in range(3):
+        q0, q1, k0, k1 = int(w.cu_q[b]), int(w.cu_q[b + 1]), int(w.cu_k[b]), int(w.cu_k[b + 1])
+        N, L = q1 - q0, k1 - k0
+        for h in range(2):
+            for i in range(N):
+                z = []
+                for j in range(L - N + i + 1):
+                    acc = 0.0
+                    for d in range(128):
+                        acc += q[q0 + i, h, d] * kn[k0 + j, h, d]
+                    for d in range(64):
+                        acc += q[q0 + i, h, 128 + d] * kr[k0 + j, d]
+                    z.append(acc * w.softmax_scale)
+                m = max(z)
+                e = [math.exp(x - m) for x in z]
+                tot = sum(e)
+                assert abs(lse[q0 + i, h] - (m + math.log(tot))) < 1e-12
+                for d in range(0, 128, 17):
+                    ref = sum(e[j] * v[k0 + j, h, d] for j in range(len(z))) / tot
+                    assert abs(out[q0 + i, h, d] - ref) < 1e-12
+
+
+def test_prefill_absorption_identity():
+    """The un-absorbed form against the absorbed decode oracle on the same
+    attention: with latent rows c_j (entries in {-1,0,1}), a 0/1 map W_uk that
+    sends each latent dim to one of the 128 nope dims (and W_uv likewise),
+    k_nope = W_uk^T c, v = W_uv^T c and q_latent = W_uk q_nope, every value is
+    an exact bf16 integer, the scores agree, and O_prefill = W_uv^T O_decode."""
+    rng = np.random.default_rng(3)
+    L, s, H = 70, 2, 3
+    c = rng.integers(-1, 2, size=(L, 512)).astype(np.float32)
+    r = rng.integers(-1, 2, size=(L, 64)).astype(np.float32)
+    Wuk = np.zeros((H, 512, 128), np.float32)
+    Wuv = np.zeros((H, 512, 128), np.float32)
+    for h in range(H):
+        Wuk[h, np.arange(512), rng.integers(0, 128, 512)] = 1
+        Wuv[h, np.arange(512), rng.integers(0, 128, 512)] = 1
+    qn = rng.integers(-1, 2, size=(s, H, 128)).astype(np.float32)
+    qr = rng.integers(-1, 2, size=(s, H, 64)).astype(np.float32)
+    kn = np.einsum("ld,hdk->lhk", c, Wuk)
+    v = np.einsum("ld,hdk->lhk", c, Wuv)
+    qlat = np.einsum("hdk,shk->shd", Wuk, qn)
+    assert np.abs(kn).max() <= 256 and np.abs(qlat).max() <= 256   # exact in bf16
+    scale = 0.05
+    # un-absorbed: s new tokens at the end of L
+    po, pl = oracle.mla_prefill(_bits(np.concatenate([qn, qr], -1)), _bits(kn), _bits(r), _bits(v),
+                                np.array([0, s], np.int32), np.array([0, L], np.int32), scale)
+    # absorbed: one sequence in pages of 64, q = [W_uk q_nope, q_rope]
+    pages = (L + 63) // 64
+    cache = np.zeros((pages, 64, 576), np.uint16)
+    rows = _bits(np.concatenate([c, r], -1))
+    for j in range(L):
+        cache[j // 64, j % 64] = rows[j]
+    bt = np.arange(pages, dtype=np.int32)[None]
+    do, dl = oracle.mla_decode(_bits(np.concatenate([qlat, qr], -1))[None], cache, bt,
+                               np.array([L], np.int32), scale)
+    assert np.allclose(pl, dl[0], rtol=0, atol=1e-12)
+    assert np.allclose(po, np.einsum("shd,hdk->shk", do[0], Wuv), rtol=0, atol=1e-10)
+
+
+def test_prefill_extend_equals_prefill_rows():
+    """An extend of the last N tokens returns the last N rows of the full
+    prefill of the same L tokens (same keys, same visibility), up to the
+    summation order of the BLAS product."""
+    from workloads import make_prefill_workload
+    w = make_prefill_workload("full", [90], [90], 4, seed=2)
+    full_o, full_l = oracle.mla_prefill(w.q_bits, w.k_nope_bits, w.k_rope_bits, w.v_bits, w.cu_q, w.cu_k,
+                                        w.softmax_scale)
+    N = 25
+    ext_o, ext_l = oracle.mla_prefill(w.q_bits[-N:], w.k_nope_bits, w.k_rope_bits, w.v_bits,
+                                      np.array([0, N], np.int32), w.cu_k, w.softmax_scale)
+    assert np.allclose(ext_o, full_o[-N:], rtol=0, atol=1e-12)
+    assert np.allclose(ext_l, full_l[-N:], rtol=0, atol=1e-12)

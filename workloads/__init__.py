@@ -251,3 +251,88 @@ def config(name: str, seed: int = 0, small: bool = False, **overrides) -> Worklo
     spec = dict((SMALL if small else CONFIGS)[name])
     spec.update(overrides)
     return make_workload(name + ("-small" if small else ""), seed=seed, **spec)
+
+
+# ---------------------------------------------------------------------------
+# Second workload: prefill / extend in the un-absorbed form. Packed,
+# contiguous tensors (no pages): q [Tq, H, 192], k_nope [Tk, H, 128],
+# k_rope [Tk, 64] (shared by the heads), v [Tk, H, 128], bf16 bits; sequence b
+# owns queries cu_q[b]..cu_q[b+1] and keys cu_k[b]..cu_k[b+1]. Draw order: q,
+# k_nope, k_rope, v (one PCG64 stream).
+# ---------------------------------------------------------------------------
+D_NOPE = 128
+D_ROPE = 64
+D_QK_PREFILL = D_NOPE + D_ROPE
+D_V_PREFILL = 128
+
+
+@dataclass
+class PrefillWorkload:
+    name: str
+    q_bits: np.ndarray
+    k_nope_bits: np.ndarray
+    k_rope_bits: np.ndarray
+    v_bits: np.ndarray
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+    softmax_scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self):
+        return int(self.cu_q.shape[0] - 1)
+
+    @property
+    def num_heads(self):
+        return int(self.q_bits.shape[1])
+
+    @property
+    def q_lens(self):
+        return np.diff(self.cu_q).astype(np.int64)
+
+    @property
+    def k_lens(self):
+        return np.diff(self.cu_k).astype(np.int64)
+
+
+def make_prefill_workload(name: str, q_lens, k_lens, num_heads: int, seed: int = 0,
+                          softmax_scale: float = DEFAULT_SCALE) -> PrefillWorkload:
+    """q_lens[b] new tokens at the end of k_lens[b] tokens (q_lens <= k_lens)."""
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    k_lens = np.asarray(k_lens, dtype=np.int64)
+    if np.any(q_lens > k_lens) or np.any(q_lens < 0):
+        raise ValueError("need 0 <= q_len <= k_len per sequence")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
+    Tq, Tk, H = int(cu_q[-1]), int(cu_k[-1]), num_heads
+    q = f32_to_bf16_bits(rng.standard_normal((max(Tq, 1), H, D_QK_PREFILL), dtype=np.float32))[:Tq]
+    kn = f32_to_bf16_bits(rng.standard_normal((max(Tk, 1), H, D_NOPE), dtype=np.float32))[:Tk]
+    kr = f32_to_bf16_bits(rng.standard_normal((max(Tk, 1), D_ROPE), dtype=np.float32))[:Tk]
+    v = f32_to_bf16_bits(rng.standard_normal((max(Tk, 1), H, D_V_PREFILL), dtype=np.float32))[:Tk]
+    return PrefillWorkload(name=name, q_bits=np.ascontiguousarray(q), k_nope_bits=np.ascontiguousarray(kn),
+                           k_rope_bits=np.ascontiguousarray(kr), v_bits=np.ascontiguousarray(v),
+                           cu_q=cu_q, cu_k=cu_k, softmax_scale=float(softmax_scale),
+                           meta={"seed": seed})
+
+
+# DeepSeek-V3 attention on one GPU's share of a TP8 deployment (128 / 8 = 16
+# heads): a long prefill, and extends of 1024 new tokens after an 8K prefix.
+PREFILL_CONFIGS = {
+    "prefill": dict(q_lens=[8192, 8192], k_lens=[8192, 8192], num_heads=16),
+    "extend": dict(q_lens=[1024] * 4, k_lens=[9216] * 4, num_heads=16),
+}
+PREFILL_TEXT = {
+    "prefill": "un-absorbed MLA prefill, 2 sequences x 8192 tokens, H=16, head dim 192 (128 nope + 64 rope), v 128, causal",
+    "extend": "un-absorbed MLA extend, 4 sequences x 1024 new tokens after 8192 cached, H=16, head dim 192, v 128",
+}
+PREFILL_SMALL = {
+    "prefill": dict(q_lens=[300, 129, 64, 1], k_lens=[300, 129, 64, 1], num_heads=16),
+    "extend": dict(q_lens=[100, 64, 3], k_lens=[400, 64, 700], num_heads=16),
+}
+
+
+def prefill_config(name: str, seed: int = 0, small: bool = False) -> PrefillWorkload:
+    spec = (PREFILL_SMALL if small else PREFILL_CONFIGS)[name]
+    return make_prefill_workload(name + ("-small" if small else ""), spec["q_lens"], spec["k_lens"],
+                                 spec["num_heads"], seed=seed)
