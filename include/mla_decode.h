@@ -205,6 +205,36 @@ int mla_decode_fwd_varlen(const void* q, const int32_t* cu_seqlens_q, int total_
                           void* stream);
 
 /*
+ * mla_prefill_fwd: the second workload, prefill / extend attention in the
+ * un-absorbed MLA form. Per head the key is [k_nope_h, k_rope] (head dim 192
+ * = 128 + 64, the DeepSeek head dim PaddleNLP issue #10157 gives for its long
+ * prefill attention, quantization section, SageAttention; the rope part is
+ * shared by all heads) and the value is v_h (128). Sequence b's N_b new
+ * tokens are the last N_b of its L_b tokens (prefill: N_b = L_b; extend: a
+ * cached prefix of L_b - N_b tokens); query i sees keys j <= L_b - N_b + i.
+ *   q              device bf16 bits [total_q, num_heads, 192], 16-byte aligned
+ *   k_nope         device bf16 bits [total_k, num_heads, 128], 16-byte aligned
+ *   k_rope         device bf16 bits [total_k, 64], 16-byte aligned
+ *   v              device bf16 bits [total_k, num_heads, 128], 16-byte aligned
+ *   cu_seqlens_q   device int32 [batch + 1]: sequence b owns q rows
+ *                  cu_q[b] .. cu_q[b+1] (N_b <= max_q_len)
+ *   cu_seqlens_k   device int32 [batch + 1]: sequence b owns key rows
+ *                  cu_k[b] .. cu_k[b+1] (L_b >= N_b; caller contract, not
+ *                  read on the host)
+ *   batch, max_q_len, num_heads   >= 1; num_heads <= 65535
+ *   softmax_scale  finite (1/sqrt(192) for DeepSeek)
+ *   out            device fp32 [total_q, num_heads, 128], 16-byte aligned
+ *   lse            device fp32 [total_q, num_heads] (natural log)
+ *   stream         hipStream_t or NULL
+ * Rows of sequences with N_b = 0 are not written. The library allocates
+ * nothing. Errors: MLA_ERR_INVALID_ARG for NULL or misaligned pointers and
+ * out-of-range sizes, MLA_ERR_HIP for a failed launch.
+ */
+int mla_prefill_fwd(const void* q, const void* k_nope, const void* k_rope, const void* v,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int max_q_len,
+                    int num_heads, float softmax_scale, float* out, float* lse, void* stream);
+
+/*
  * mla_combine: merge per-sequence partials by their log-sum-exp.
  *   part_out        device fp32 [num_partials, rows_per_seq, 512], 16-byte aligned
  *   part_lse        device fp32 [num_partials, rows_per_seq] (natural log)

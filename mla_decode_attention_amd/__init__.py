@@ -63,6 +63,7 @@ def load_library():
         "mla_decode_fwd_fp8mma": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
                                           ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
         "mla_combine": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp]),
+        "mla_prefill_fwd": (c_int, [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, ctypes.c_float, vp, vp, vp]),
         "mla_append_kv": (c_int, [vp, c_int, c_int, vp, c_int, vp, vp, vp, c_int, c_int, vp]),
         "mla_decode_fwd_varlen": (c_int, [vp, vp, c_int, c_int, vp, vp, c_int, c_int, vp, c_int, vp, c_int,
                                           c_int, ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
@@ -203,6 +204,43 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                               _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), B, s, H,
                               float(softmax_scale), _ptr(out), _ptr(lse), _ptr(md), units, _ptr(ws),
                               wbytes, _stream()), name)
+    return out, lse
+
+
+def prefill(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
+            cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_q_len: int, softmax_scale: float,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Prefill / extend attention, un-absorbed MLA. Returns (out fp32 [Tq,H,128], lse fp32 [Tq,H]).
+
+    q bf16 [Tq, H, 192]; k_nope bf16 [Tk, H, 128]; k_rope bf16 [Tk, 64]; v bf16
+    [Tk, H, 128]; cu_seqlens_q / cu_seqlens_k int32 [B+1]. Sequence b's
+    queries are the last N_b of its L_b tokens (causal).
+    """
+    lib = load_library()
+    _need(q, "q", (torch.bfloat16,), 3)
+    Tq, H, d = q.shape
+    if d != 192:
+        raise ValueError("q last dim must be 192")
+    _need(k_nope, "k_nope", (torch.bfloat16,), 3)
+    _need(k_rope, "k_rope", (torch.bfloat16,), 2)
+    _need(v, "v", (torch.bfloat16,), 3)
+    Tk = k_nope.shape[0]
+    if tuple(k_nope.shape) != (Tk, H, 128) or tuple(k_rope.shape) != (Tk, 64) or tuple(v.shape) != (Tk, H, 128):
+        raise ValueError("k_nope [Tk,H,128], k_rope [Tk,64], v [Tk,H,128] expected")
+    _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,), 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", (torch.int32,), 1)
+    B = cu_seqlens_q.shape[0] - 1
+    if B < 1 or cu_seqlens_k.shape[0] != B + 1:
+        raise ValueError("cu_seqlens_q / cu_seqlens_k must both have batch + 1 entries")
+    if out is None:
+        out = torch.empty((Tq, H, 128), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    _need(lse, "lse", (torch.float32,), 2)
+    _check(lib.mla_prefill_fwd(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(cu_seqlens_q),
+                               _ptr(cu_seqlens_k), B, int(max_q_len), H, float(softmax_scale), _ptr(out),
+                               _ptr(lse), _stream()), "mla_prefill_fwd")
     return out, lse
 
 

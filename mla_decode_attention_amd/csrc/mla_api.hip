@@ -291,6 +291,32 @@ int mla_decode_fwd_varlen(const void* q, const int32_t* cu_seqlens_q, int total_
                      metadata, num_units, workspace, workspace_bytes, stream);
 }
 
+int mla_prefill_fwd(const void* q, const void* k_nope, const void* k_rope, const void* v,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int max_q_len,
+                    int num_heads, float softmax_scale, float* out, float* lse, void* stream) {
+  if (!q || !k_nope || !k_rope || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (batch < 1 || max_q_len < 1 || num_heads < 1)
+    return fail(MLA_ERR_INVALID_ARG, "batch, max_q_len, num_heads must be >= 1 (got %d, %d, %d)", batch,
+                max_q_len, num_heads);
+  if (num_heads > 65535) return fail(MLA_ERR_INVALID_ARG, "num_heads must be <= 65535");
+  const long long nblk = ((long long)max_q_len + mla::prefill_rows_per_block() - 1) / mla::prefill_rows_per_block();
+  if (nblk * batch > INT32_MAX) return fail(MLA_ERR_INVALID_ARG, "batch * query blocks exceeds the grid");
+  if (!isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (!aligned(q, 16) || !aligned(k_nope, 16) || !aligned(k_rope, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(MLA_ERR_INVALID_ARG, "q, k_nope, k_rope, v and out must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return fail(MLA_ERR_INVALID_ARG, "lse and the offsets must be 4-byte aligned");
+  DevInfo d;
+  int st = device_info(&d);
+  if (st != MLA_OK) return st;
+  hipError_t e = mla::launch_prefill((const uint16_t*)q, (const uint16_t*)k_nope, (const uint16_t*)k_rope,
+                                     (const uint16_t*)v, cu_seqlens_q, cu_seqlens_k, batch, max_q_len, num_heads,
+                                     softmax_scale, out, lse, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq_part_offsets,
                 int batch, int rows_per_seq, float* out, float* lse, void* stream) {
   if (!part_out || !part_lse || !seq_part_offsets || !out || !lse)

@@ -69,4 +69,10 @@ hipError_t launch_combine(const float* part_out, const float* part_lse, const in
                           const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
                           float* lse, int skip_single, hipStream_t s);
 
+// Prefill / extend (un-absorbed MLA, head dim 192 = 128 + 64 shared rope, v 128).
+int prefill_rows_per_block();
+hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,
+                          const int32_t* cu_q, const int32_t* cu_k, int batch, int max_q_len, int num_heads,
+                          float softmax_scale, float* out, float* lse, hipStream_t s);
+
 }  // namespace mla

@@ -1,0 +1,315 @@
+// Prefill / extend attention in the un-absorbed MLA form, gfx950.
+//
+// The second workload: new tokens attend causally over their sequence. Per
+// head the key is [k_nope_h (128), k_rope (64, shared by all heads)] -- head
+// dim 192, the DeepSeek head dim PaddleNLP issue #10157 names for its long
+// prefill attention (quantization section, SageAttention) -- and the value is
+// v_h (128). Query i of the N new tokens of a sequence of L sees keys
+// j <= L - N + i.
+//
+// One workgroup = 128 query rows of one (sequence, head): 4 waves of 32 rows,
+// two workgroups per CU. Keys stream in tiles of 64 through LDS (double
+// buffered, direct global->LDS 16-byte loads): K from k_nope and k_rope, V
+// from v, in the swizzled chunk layout of the decode kernels (conflict-free
+// MFMA operand fetches). Per tile and wave:
+//   QK: S^T[64 keys, 32 rows] on v_mfma_f32_32x32x16_bf16, K from LDS, Q^T
+//       (12 k-steps of 16 dims, 48 registers) from registers;
+//   softmax: each lane owns one row (column of S^T) and 32 of its scores, so
+//       the row max and sum need one cross-lane step (lane ^ 32) and no LDS;
+//       base-2 online softmax with the lazy rescale (threshold 2^8);
+//   PV: O^T[128, 32 rows] += V^T . P^T. The S^T accumulator registers of a
+//       16-key half block are already the B operand of that PV k-step (the
+//       key order inside the k-step is permuted to match, and V^T is read
+//       with the same permutation through ds_read_b64_tr_b16), so P never
+//       leaves the registers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace prefill {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kDNope = 128, kDRope = 64, kDK = kDNope + kDRope, kDVh = 128;
+constexpr int kTile = 64;                    // keys per tile
+constexpr int kRowsWg = 128;                 // query rows per workgroup
+constexpr int kThreads = 256;
+constexpr int kLineGroup = 8192;             // one 128-byte line of 64 keys
+constexpr int kKBytes = kTile * kDK * 2;     // 24576
+constexpr int kVBytes = kTile * kDVh * 2;    // 16384
+constexpr int kStage = kKBytes + kVBytes;    // 40960
+constexpr float kRescaleThreshold = 8.0f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// chunk c (8 bf16) of key k: [line group c/8][key][c%8 permuted by the key]
+__device__ __forceinline__ int swz3(int key) {
+  return (((key >> 1) & 1) << 2) | (((key ^ (key >> 2)) & 1) << 1) | ((key ^ (key >> 3)) & 1);
+}
+__device__ __forceinline__ int lds_byte(int key, int chunk) {
+  return ((chunk >> 3) * 512 + key * 8 + ((chunk ^ swz3(key)) & 7)) * 16;
+}
+
+__device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "memory");
+}
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_loads() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  barrier_lds();
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ bf16x8 ld128(const LDS_AS uint8_t* p) { return *(const LDS_AS bf16x8*)p; }
+__device__ __forceinline__ bf16x4 tr_read(const LDS_AS uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
+}
+
+struct Args {
+  const uint16_t* q;        // [Tq, H, 192]
+  const uint8_t* k_nope;    // [Tk, H, 128] bf16
+  const uint8_t* k_rope;    // [Tk, 64] bf16
+  const uint8_t* v;         // [Tk, H, 128] bf16
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  float* out;               // [Tq, H, 128]
+  float* lse;               // [Tq, H]
+  int H, nblk;
+  float scale_log2;
+};
+
+// The loads of one key tile into one stage. Load i of thread t fills slot
+// 256i + t of a 64-key region: line group i/2, key 32(i%2) + t/8, in-line
+// position t%8; K loads 0-3 come from k_nope (chunks 0..15), 4-5 from k_rope
+// (chunks 16..23), V loads 0-3 from v. Keys at or past `nvalid` re-read the
+// last valid key.
+struct TilePlan {
+  const uint8_t* kn;        // k_nope row of key 0 of the tile, head h
+  const uint8_t* kr;        // k_rope row of key 0
+  const uint8_t* vv;        // v row of key 0, head h
+  uint32_t off_h[2], off_r[2];   // per key parity: row offsets (head-strided / rope)
+  uint32_t pos16[2];             // 16 * (in-line chunk of this lane's slot), per key parity
+};
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(Args a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
+  LDS_AS uint8_t* const stage0 = (LDS_AS uint8_t*)smem;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int head = blockIdx.y;
+  // longest query blocks first (causal work grows with the block index)
+  const int b = uniform((int)blockIdx.x / a.nblk);
+  const int qb = uniform(a.nblk - 1 - (int)blockIdx.x % a.nblk);
+  const int q0 = uniform(a.cu_q[b]), N = uniform(a.cu_q[b + 1] - q0);
+  const int k0 = uniform(a.cu_k[b]), L = uniform(a.cu_k[b + 1] - k0);
+  const int i0 = qb * kRowsWg;               // first query index of the block
+  if (i0 >= N) return;
+  const int H = a.H;
+  const int off = L - N;                     // query i sees keys j <= off + i
+  const int last_key = off + min(N, i0 + kRowsWg) - 1;
+  const int ntiles = last_key >= 0 ? last_key / kTile + 1 : 0;
+  const int qi = i0 + 32 * wave + n;         // this lane's query (PV/softmax row)
+  const bool row_live = qi < N;
+
+  // ---- query rows: B operand of S^T = K Q^T, k-step c holds dims 16c + 8h..+7
+  bf16x8 qreg[12];
+  {
+    const bf16x8* qrow = (const bf16x8*)(a.q + ((size_t)(q0 + min(qi, N - 1)) * H + head) * kDK);
+#pragma unroll
+    for (int c = 0; c < 12; ++c) {
+      const bf16x8 v = qrow[2 * c + h];
+      qreg[c] = row_live ? v : bf16x8{};
+    }
+  }
+
+  // ---- load plan (per lane, fixed across tiles)
+  const size_t rowK = (size_t)H * kDNope * 2;   // bytes between keys in k_nope / v
+  uint32_t lds_k0 = (uint32_t)uniform((int)(uintptr_t)(stage0 + (tid & ~63) * 16));
+  auto issue = [&](int t, int stage) {
+    const int kt0 = t * kTile;
+    const int nvalid = min(kTile, L - kt0);
+    const uint8_t* kn = a.k_nope + ((size_t)(k0 + kt0) * H + head) * (kDNope * 2);
+    const uint8_t* kr = a.k_rope + (size_t)(k0 + kt0) * (kDRope * 2);
+    const uint8_t* vv = a.v + ((size_t)(k0 + kt0) * H + head) * (kDVh * 2);
+    const uint32_t lds = lds_k0 + stage * kStage;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int key = 32 * (i & 1) + (tid >> 3);
+      const int src = key < nvalid ? key : nvalid - 1;
+      const int c = 8 * (i >> 1) + ((tid & 7) ^ swz3(key));
+      if (i < 4) dma16((uint32_t)(src * rowK + c * 16), kn, lds + i * 4096);
+      else dma16((uint32_t)(src * (kDRope * 2) + (c - 16) * 16), kr, lds + i * 4096);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 32 * (i & 1) + (tid >> 3);
+      const int src = key < nvalid ? key : nvalid - 1;
+      const int c = 8 * (i >> 1) + ((tid & 7) ^ swz3(key));
+      dma16((uint32_t)(src * rowK + c * 16), vv, lds + kKBytes + i * 4096);
+    }
+  };
+
+  // per-lane LDS offsets: K operand (key 32kb + n, chunk 2c + h), V^T reads
+  int k_lane[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) k_lane[kb][q4] = lds_byte(32 * kb + n, 2 * q4 + h);
+  int v_lane[2][2];   // [second][fb % 2]
+  {
+    const int qq = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int second = 0; second < 2; ++second)
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+        v_lane[second][par] = kKBytes + lds_byte(4 * h + (j >> 2) + 8 * second, 4 * par + 2 * (qq & 1) + ((j & 3) >> 1)) +
+                              8 * (j & 1);
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) o[fb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  bool first = true;
+
+  if (ntiles > 0) issue(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    LDS_AS uint8_t* const cur = stage0 + (t & 1) * kStage;
+    wait_loads();
+    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+
+    // ---- QK: S^T[64 keys, 32 rows]
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    {
+      auto kaddr = [&](int i) {
+        const int c = i >> 1, kb = i & 1;
+        return cur + k_lane[kb][c & 3] + (c >> 2) * kLineGroup;
+      };
+      constexpr int NQ = 24, D = 6;
+      bf16x8 ring[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) ring[i] = ld128(kaddr(i));
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const bf16x8 av = ring[i % D];
+        if (i + D < NQ) ring[i % D] = ld128(kaddr(i + D));
+        sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[i >> 1], sacc[i & 1], 0, 0, 0);
+      }
+    }
+
+    // ---- softmax: row qi, keys 64t + 32kb + 8(r/4) + 4h + r%4
+    const int kt0 = t * kTile;
+    const bool need_mask = kt0 + kTile - 1 > off + i0;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = sacc[kb][r] * a.scale_log2;
+        if (need_mask && kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) > off + qi) v = -INFINITY;
+        sacc[kb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = xor32_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const bool raise = first || m_new > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = first ? 0.0f : raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      if (raise) m_run = m_new;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) o[fb] *= alpha;
+      l_run *= alpha;
+    }
+    first = false;
+    const float m_eff = m_run == -INFINITY ? 0.0f : m_run;
+    bf16x8 pb[4];                             // PV k-step ks = 2kb + s: S registers 8s..8s+7 of block kb
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = __builtin_amdgcn_exp2f(sacc[ks >> 1][8 * (ks & 1) + e] - m_eff);
+        l_run += pr;
+        pb[ks][e] = (__bf16)pr;
+      }
+
+    // ---- PV: O^T[128 dims, 32 rows] += V^T . P^T
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        const LDS_AS uint8_t* base = cur + (fb >> 1) * kLineGroup + ks * 2048;
+        const bf16x4 r0 = tr_read(base + v_lane[0][fb & 1]);
+        const bf16x4 r1 = tr_read(base + v_lane[1][fb & 1]);
+        const bf16x8 av = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[fb], 0, 0, 0);
+      }
+  }
+
+  // ---- epilogue: O / l, LSE = (m + log2 l) ln 2
+  const float l_row = xor32_sum(l_run);
+  if (!row_live) return;
+  const bool live = l_row > 0.f;
+  const float inv = live ? 1.0f / l_row : 0.f;
+  const size_t row = (size_t)(q0 + qi) * H + head;
+  float* dst = a.out + row * kDVh;
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x4 v = {o[fb][4 * jj], o[fb][4 * jj + 1], o[fb][4 * jj + 2], o[fb][4 * jj + 3]};
+      *(f32x4*)(dst + 32 * fb + 8 * jj + 4 * h) = v * inv;
+    }
+  if (h == 0) a.lse[row] = live ? (m_run + __builtin_amdgcn_logf(l_row)) * kLn2 : -INFINITY;
+}
+
+}  // namespace prefill
+
+int prefill_rows_per_block() { return prefill::kRowsWg; }
+
+hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,
+                          const int32_t* cu_q, const int32_t* cu_k, int batch, int max_q_len, int num_heads,
+                          float softmax_scale, float* out, float* lse, hipStream_t s) {
+  prefill::Args a;
+  a.q = q;
+  a.k_nope = (const uint8_t*)k_nope;
+  a.k_rope = (const uint8_t*)k_rope;
+  a.v = (const uint8_t*)v;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.out = out;
+  a.lse = lse;
+  a.H = num_heads;
+  a.nblk = (max_q_len + prefill::kRowsWg - 1) / prefill::kRowsWg;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  dim3 grid(batch * a.nblk, num_heads);
+  hipLaunchKernelGGL(prefill::prefill_kernel, grid, dim3(prefill::kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -142,6 +142,21 @@ def test_fp8mma_argument_errors(lib):
     assert lib.mla_last_error() != b""
 
 
+def test_prefill_argument_errors(lib):
+    f = lib.mla_prefill_fwd
+    def call(q=FAKE, cu=FAKE, B=2, mq=128, H=16, sm=0.072, out=FAKE):
+        return f(q, FAKE, FAKE, FAKE, cu, FAKE, B, mq, H, ctypes.c_float(sm), out, FAKE, None)
+    assert call(q=None) == INVALID
+    assert call(cu=None) == INVALID
+    assert call(B=0) == INVALID
+    assert call(mq=0) == INVALID
+    assert call(H=0) == INVALID
+    assert call(H=70000) == INVALID
+    assert call(sm=float("nan")) == INVALID
+    assert call(q=FAKE_ODD) == INVALID
+    assert call(out=FAKE_ODD) == INVALID
+
+
 def test_binding_rejects_host_tensors():
     import torch
     q = torch.zeros(1, 1, 16, 576, dtype=torch.bfloat16)
