@@ -58,12 +58,14 @@ def algorithmic(w):
 
 
 def kernel_source_digest() -> str:
-    """SHA-256 of the kernel source with comments and blank space removed, so
-    that editing a comment does not count as changing the kernel."""
+    """SHA-256 of the attention kernel sources with comments and blank space
+    removed, so that editing a comment does not count as changing a kernel."""
     import hashlib
     import re
-    with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", "mla_kernels.hip")) as f:
-        src = f.read()
+    src = ""
+    for name in ("mla_kernels.hip", "mla_prefill.hip"):
+        with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", name)) as f:
+            src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     src = "\n".join(" ".join(line.split()) for line in src.splitlines() if line.strip())
@@ -118,15 +120,133 @@ def cpu_baseline(w, seconds: float):
             "seconds": round(dt, 2)}
 
 
+def prefill_algorithmic(w):
+    """Flops (QK 192 + PV 128 multiply-adds per visible (row, key) pair per
+    head) and bytes (q, k_nope, k_rope, v once; out and lse) of one call."""
+    import numpy as np
+    vis = 0
+    for N, L in zip(w.q_lens, w.k_lens):
+        N, L = int(N), int(L)
+        vis += N * (L - N) + N * (N + 1) // 2
+    H = w.num_heads
+    flops = 2 * H * (192 + 128) * vis
+    Tq, Tk = int(w.cu_q[-1]), int(w.cu_k[-1])
+    nbytes = Tq * H * 192 * 2 + Tk * (H * 128 * 2 + 64 * 2 + H * 128 * 2) + Tq * H * (128 + 1) * 4
+    return dict(flops=flops, bytes=nbytes, visible_pairs=vis)
+
+
+def prefill_cpu_baseline(w, seconds: float):
+    """The prefill oracle on a bounded sample: the first rows of sequence 0,
+    as an extend (a query at position p sees keys 0..p), doubling the row
+    count until `seconds` pass."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    N0, L0 = int(w.q_lens[0]), int(w.k_lens[0])
+    n, flops, dt = 16, 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        n = min(n, N0)
+        p_end = L0 - N0 + n            # keys 0 .. p_end - 1 cover the first n queries
+        t1 = time.perf_counter()
+        oracle.mla_prefill(w.q_bits[:n], w.k_nope_bits[:p_end], w.k_rope_bits[:p_end], w.v_bits[:p_end],
+                           np.array([0, n], np.int32), np.array([0, p_end], np.int32), w.softmax_scale)
+        dt_i = time.perf_counter() - t1
+        flops = 2 * w.num_heads * 320 * (n * (p_end - n) + n * (n + 1) // 2)
+        dt = dt_i
+        if n == N0 or time.perf_counter() - t0 >= seconds or dt_i * 4 > seconds:
+            break
+        n *= 2
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {N0} queries of sequence 0 (an extend over its first {p_end} keys), "
+                      f"{dt:.1f} s wall for that call, fp64 numpy", "seconds": round(dt, 2)}
+
+
+def bench_prefill(args):
+    import numpy as np
+    import torch
+    import mla_decode_attention_amd as mla
+    from workloads import prefill_config, PREFILL_TEXT
+
+    w = prefill_config(args.config, seed=0)
+    alg = prefill_algorithmic(w)
+    print(f"[bench] {args.config}: {alg['flops'] / 1e12:.2f} TFLOP per call", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dv = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    q, kn, kr, v = dv(w.q_bits), dv(w.k_nope_bits), dv(w.k_rope_bits), dv(w.v_bits)
+    cq = torch.from_numpy(w.cu_q).to(dev)
+    ck = torch.from_numpy(w.cu_k).to(dev)
+    Tq, H = q.shape[0], w.num_heads
+    out = torch.empty((Tq, H, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+    max_q = int(w.q_lens.max())
+
+    def step():
+        mla.prefill(q, kn, kr, v, cq, ck, max_q, w.softmax_scale, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mla.profile_enable(True)
+    mla.profile_read()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    mla.profile_enable(False)
+    step_ms = t0.elapsed_time(t1) / args.steps
+    k_total, launches = mla.profile_read()
+    k_ms = k_total / max(launches, 1)
+    tflops = alg["flops"] / (step_ms * 1e-3) / 1e12
+    achieved = alg["flops"] / (k_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.config),
+            "kernel": "prefill_kernel", "kernel_ms": round(k_ms, 5), "launches": launches,
+            "algorithmic_bytes": alg["bytes"], "algorithmic_flops": alg["flops"],
+            "t_roof_us": round(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e6, 2)}
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {PREFILL_TEXT[args.config]}", "batch": w.batch, "heads": H,
+                   "query_tokens": Tq, "key_tokens": int(w.cu_k[-1]), "visible_pairs": alg["visible_pairs"],
+                   "seed": 0},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="share16",
-                    choices=["tiny", "share16", "mtp", "ragged", "fp8", "varlen", "fp8mma"],
+                    choices=["tiny", "share16", "mtp", "ragged", "fp8", "varlen", "fp8mma", "prefill", "extend"],
                     help="workload; fp8mma = the fp8 workload on mla_decode_fwd_fp8mma (queries and P in "
-                         "E4M3, fp8 matrix cores; an approximation of the default path)")
+                         "E4M3, fp8 matrix cores; an approximation of the default path); prefill / extend = "
+                         "the second workload (mla_prefill_fwd, un-absorbed MLA, value in TFLOP/s)")
     ap.add_argument("--sets", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--num-units", type=int, default=0, help="split work units (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -144,6 +264,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): this build "
               "has no multi-GPU path; the per-GPU kernel is the whole computation.", file=sys.stderr)
         sys.exit(2)
+
+    if args.config in ("prefill", "extend"):
+        return bench_prefill(args)
 
     import numpy as np
     import torch

@@ -282,9 +282,10 @@ int mla_append_kv(const void* latent, int batch, int new_tokens, const int32_t* 
 
 /*
  * Measurement hook (diagnostics, not part of the computation).
- * mla_profile_enable(1): from now on every launch of the main decode kernel
- *   (the attention pass of mla_decode_fwd, not the merge) is bracketed by a
- *   pair of HIP events recorded on the caller's stream. Event pairs come from
+ * mla_profile_enable(1): from now on every launch of the main attention
+ *   kernel (the attention pass of mla_decode_fwd and its variants, not the
+ *   merge; the kernel of mla_prefill_fwd) is bracketed by a pair of HIP events
+ *   recorded by the dispatch on the caller's stream. Event pairs come from
  *   a pool the library creates on first use (host-side HIP event objects; no
  *   device memory). mla_profile_enable(0) stops recording.
  * mla_profile_read: waits for the recorded events, returns the summed elapsed

@@ -310,9 +310,26 @@ int mla_prefill_fwd(const void* q, const void* k_nope, const void* k_rope, const
   DevInfo d;
   int st = device_info(&d);
   if (st != MLA_OK) return st;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.on) {
+      ev0 = take_event();
+      ev1 = take_event();
+      if (!ev0 || !ev1) {
+        if (ev0) g_prof.pool.push_back(ev0);
+        if (ev1) g_prof.pool.push_back(ev1);
+        ev0 = ev1 = nullptr;
+      }
+    }
+  }
   hipError_t e = mla::launch_prefill((const uint16_t*)q, (const uint16_t*)k_nope, (const uint16_t*)k_rope,
                                      (const uint16_t*)v, cu_seqlens_q, cu_seqlens_k, batch, max_q_len, num_heads,
-                                     softmax_scale, out, lse, (hipStream_t)stream);
+                                     softmax_scale, out, lse, (hipStream_t)stream, ev0, ev1);
+  if (ev0 && ev1) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.recorded.emplace_back(ev0, ev1);
+  }
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -73,6 +73,7 @@ hipError_t launch_combine(const float* part_out, const float* part_lse, const in
 int prefill_rows_per_block();
 hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,
                           const int32_t* cu_q, const int32_t* cu_k, int batch, int max_q_len, int num_heads,
-                          float softmax_scale, float* out, float* lse, hipStream_t s);
+                          float softmax_scale, float* out, float* lse, hipStream_t s,
+                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 }  // namespace mla

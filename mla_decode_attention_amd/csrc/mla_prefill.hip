@@ -23,6 +23,7 @@
 //       with the same permutation through ds_read_b64_tr_b16), so P never
 //       leaves the registers.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <math.h>
 
@@ -294,7 +295,8 @@ int prefill_rows_per_block() { return prefill::kRowsWg; }
 
 hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,
                           const int32_t* cu_q, const int32_t* cu_k, int batch, int max_q_len, int num_heads,
-                          float softmax_scale, float* out, float* lse, hipStream_t s) {
+                          float softmax_scale, float* out, float* lse, hipStream_t s, hipEvent_t ev_start,
+                          hipEvent_t ev_stop) {
   prefill::Args a;
   a.q = q;
   a.k_nope = (const uint8_t*)k_nope;
@@ -308,7 +310,8 @@ hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint1
   a.nblk = (max_q_len + prefill::kRowsWg - 1) / prefill::kRowsWg;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   dim3 grid(batch * a.nblk, num_heads);
-  hipLaunchKernelGGL(prefill::prefill_kernel, grid, dim3(prefill::kThreads), 0, s, a);
+  // the events (may be null) are recorded by the dispatch itself
+  hipExtLaunchKernelGGL(prefill::prefill_kernel, grid, dim3(prefill::kThreads), 0, s, ev_start, ev_stop, 0, a);
   return hipGetLastError();
 }
 
