@@ -224,20 +224,23 @@ void prefill_kernel(Args a) {
       }
     }
 
-    // ---- softmax: row qi, keys 64t + 32kb + 8(r/4) + 4h + r%4
+    // ---- softmax: row qi, keys 64t + 32kb + 8(r/4) + 4h + r%4. The max is
+    //      taken on the raw scores (the scale is positive), and the scale is
+    //      folded into the exponent: P = 2^(s * c - m).
     const int kt0 = t * kTile;
-    const bool need_mask = kt0 + kTile - 1 > off + i0;
+    if (kt0 + kTile - 1 > off + i0) {          // tile reaches past the first row's last key
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) > off + qi) sacc[kb][r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = sacc[kb][r] * a.scale_log2;
-        if (need_mask && kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) > off + qi) v = -INFINITY;
-        sacc[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = xor32_max(mx);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = xor32_max(mx) * a.scale_log2;
     const float m_new = fmaxf(m_run, mx);
     const bool raise = first || m_new > m_run + kRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -254,7 +257,7 @@ void prefill_kernel(Args a) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pr = __builtin_amdgcn_exp2f(sacc[ks >> 1][8 * (ks & 1) + e] - m_eff);
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks >> 1][8 * (ks & 1) + e], a.scale_log2, -m_eff));
         l_run += pr;
         pb[ks][e] = (__bf16)pr;
       }
