@@ -40,7 +40,8 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kDNope = 128, kDRope = 64, kDK = kDNope + kDRope, kDVh = 128;
 constexpr int kTile = 64;                    // keys per tile
-constexpr int kRowsWg = 128;                 // query rows per workgroup
+constexpr int kRB = 1;                        // row blocks of 32 per wave (RB = 2 measured slower: 1 wave per SIMD, AGPR copies, coarser causal blocks)
+constexpr int kRowsWg = 4 * 32 * kRB;          // query rows per workgroup
 constexpr int kThreads = 256;
 constexpr int kLineGroup = 8192;             // one 128-byte line of 64 keys
 constexpr int kKBytes = kTile * kDK * 2;     // 24576
@@ -117,8 +118,13 @@ struct TilePlan {
   uint32_t pos16[2];             // 16 * (in-line chunk of this lane's slot), per key parity
 };
 
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+// RB = query row blocks of 32 per wave: RB = 1 gives 128 rows per workgroup
+// and two workgroups per CU; RB = 2 gives 256 rows per workgroup, one per CU,
+// and halves the LDS bytes per MFMA (each K or V fragment feeds two MFMAs).
+template <int RB>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3 - RB, 3 - RB)))
 void prefill_kernel(Args a) {
+  constexpr int ROWS_WG = 4 * 32 * RB;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
   LDS_AS uint8_t* const stage0 = (LDS_AS uint8_t*)smem;
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -129,29 +135,35 @@ void prefill_kernel(Args a) {
   const int qb = uniform(a.nblk - 1 - (int)blockIdx.x % a.nblk);
   const int q0 = uniform(a.cu_q[b]), N = uniform(a.cu_q[b + 1] - q0);
   const int k0 = uniform(a.cu_k[b]), L = uniform(a.cu_k[b + 1] - k0);
-  const int i0 = qb * kRowsWg;               // first query index of the block
+  const int i0 = qb * ROWS_WG;               // first query index of the block
   if (i0 >= N) return;
   const int H = a.H;
   const int off = L - N;                     // query i sees keys j <= off + i
-  const int last_key = off + min(N, i0 + kRowsWg) - 1;
+  const int last_key = off + min(N, i0 + ROWS_WG) - 1;
   const int ntiles = last_key >= 0 ? last_key / kTile + 1 : 0;
-  const int qi = i0 + 32 * wave + n;         // this lane's query (PV/softmax row)
-  const bool row_live = qi < N;
+  int qi[RB];                                // this lane's queries (row n of each row block)
+  bool row_live[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    qi[rb] = i0 + 32 * (RB * wave + rb) + n;
+    row_live[rb] = qi[rb] < N;
+  }
 
   // ---- query rows: B operand of S^T = K Q^T, k-step c holds dims 16c + 8h..+7
-  bf16x8 qreg[12];
-  {
-    const bf16x8* qrow = (const bf16x8*)(a.q + ((size_t)(q0 + min(qi, N - 1)) * H + head) * kDK);
+  bf16x8 qreg[RB][12];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const bf16x8* qrow = (const bf16x8*)(a.q + ((size_t)(q0 + min(qi[rb], N - 1)) * H + head) * kDK);
 #pragma unroll
     for (int c = 0; c < 12; ++c) {
       const bf16x8 v = qrow[2 * c + h];
-      qreg[c] = row_live ? v : bf16x8{};
+      qreg[rb][c] = row_live[rb] ? v : bf16x8{};
     }
   }
 
-  // ---- load plan (per lane, fixed across tiles)
+  // ---- loads of one key tile (see TilePlan)
   const size_t rowK = (size_t)H * kDNope * 2;   // bytes between keys in k_nope / v
-  uint32_t lds_k0 = (uint32_t)uniform((int)(uintptr_t)(stage0 + (tid & ~63) * 16));
+  const uint32_t lds_k0 = (uint32_t)uniform((int)(uintptr_t)(stage0 + (tid & ~63) * 16));
   auto issue = [&](int t, int stage) {
     const int kt0 = t * kTile;
     const int nvalid = min(kTile, L - kt0);
@@ -193,10 +205,17 @@ void prefill_kernel(Args a) {
                               8 * (j & 1);
   }
 
-  f32x16 o[4];
+  f32x16 o[RB][4];
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb) o[fb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) o[rb][fb] = f32x16{};
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+  }
   bool first = true;
 
   if (ntiles > 0) issue(0, 0);
@@ -205,8 +224,10 @@ void prefill_kernel(Args a) {
     wait_loads();
     if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
 
-    // ---- QK: S^T[64 keys, 32 rows]
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    // ---- QK: S^T[64 keys, 32 rows] per row block; each K fragment feeds RB MFMAs
+    f32x16 sacc[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sacc[rb][0] = sacc[rb][1] = f32x16{};
     {
       auto kaddr = [&](int i) {
         const int c = i >> 1, kb = i & 1;
@@ -220,76 +241,98 @@ void prefill_kernel(Args a) {
       for (int i = 0; i < NQ; ++i) {
         const bf16x8 av = ring[i % D];
         if (i + D < NQ) ring[i % D] = ld128(kaddr(i + D));
-        sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[i >> 1], sacc[i & 1], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sacc[rb][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[rb][i >> 1], sacc[rb][i & 1], 0, 0, 0);
       }
     }
 
-    // ---- softmax: row qi, keys 64t + 32kb + 8(r/4) + 4h + r%4. The max is
+    // ---- softmax: row qi[rb], keys 64t + 32kb + 8(r/4) + 4h + r%4. The max is
     //      taken on the raw scores (the scale is positive), and the scale is
     //      folded into the exponent: P = 2^(s * c - m).
     const int kt0 = t * kTile;
-    if (kt0 + kTile - 1 > off + i0) {          // tile reaches past the first row's last key
+    if (kt0 + kTile - 1 > off + i0) {          // tile reaches past the block's first row's last key
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) > off + qi[rb]) sacc[rb][kb][r] = -INFINITY;
+    }
+    float alpha[RB];
+    bool any_raise = first;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) > off + qi) sacc[kb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][kb][r]);
+      mx = xor32_max(mx) * a.scale_log2;
+      const float m_new = fmaxf(m_run[rb], mx);
+      const bool raise = first || m_new > m_run[rb] + kRescaleThreshold;
+      alpha[rb] = first ? 0.0f : raise ? __builtin_amdgcn_exp2f(m_run[rb] - m_new) : 1.0f;
+      if (raise) m_run[rb] = m_new;
+      any_raise |= raise;
     }
-    float mx = -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(any_raise)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = xor32_max(mx) * a.scale_log2;
-    const float m_new = fmaxf(m_run, mx);
-    const bool raise = first || m_new > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float alpha = first ? 0.0f : raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      if (raise) m_run = m_new;
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb) o[fb] *= alpha;
-      l_run *= alpha;
+        for (int fb = 0; fb < 4; ++fb) o[rb][fb] *= alpha[rb];
+        l_run[rb] *= alpha[rb];
+      }
     }
     first = false;
-    const float m_eff = m_run == -INFINITY ? 0.0f : m_run;
-    bf16x8 pb[4];                             // PV k-step ks = 2kb + s: S registers 8s..8s+7 of block kb
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks >> 1][8 * (ks & 1) + e], a.scale_log2, -m_eff));
-        l_run += pr;
-        pb[ks][e] = (__bf16)pr;
-      }
 
-    // ---- PV: O^T[128 dims, 32 rows] += V^T . P^T
+    // ---- PV: O^T[128 dims, 32 rows] += V^T . P^T; P for k-step ks = 2kb + s is
+    //      the S registers 8s..8s+7 of block kb; each V fragment feeds RB MFMAs
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 pb[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m_eff = m_run[rb] == -INFINITY ? 0.0f : m_run[rb];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pr =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][ks >> 1][8 * (ks & 1) + e], a.scale_log2, -m_eff));
+          l_run[rb] += pr;
+          pb[rb][e] = (__bf16)pr;
+        }
+      }
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
         const LDS_AS uint8_t* base = cur + (fb >> 1) * kLineGroup + ks * 2048;
         const bf16x4 r0 = tr_read(base + v_lane[0][fb & 1]);
         const bf16x4 r1 = tr_read(base + v_lane[1][fb & 1]);
         const bf16x8 av = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[fb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[rb], o[rb][fb], 0, 0, 0);
       }
+    }
   }
 
   // ---- epilogue: O / l, LSE = (m + log2 l) ln 2
-  const float l_row = xor32_sum(l_run);
-  if (!row_live) return;
-  const bool live = l_row > 0.f;
-  const float inv = live ? 1.0f / l_row : 0.f;
-  const size_t row = (size_t)(q0 + qi) * H + head;
-  float* dst = a.out + row * kDVh;
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_row = xor32_sum(l_run[rb]);
+    if (!row_live[rb]) continue;
+    const bool live = l_row > 0.f;
+    const float inv = live ? 1.0f / l_row : 0.f;
+    const size_t row = (size_t)(q0 + qi[rb]) * H + head;
+    float* dst = a.out + row * kDVh;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      f32x4 v = {o[fb][4 * jj], o[fb][4 * jj + 1], o[fb][4 * jj + 2], o[fb][4 * jj + 3]};
-      *(f32x4*)(dst + 32 * fb + 8 * jj + 4 * h) = v * inv;
-    }
-  if (h == 0) a.lse[row] = live ? (m_run + __builtin_amdgcn_logf(l_row)) * kLn2 : -INFINITY;
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4 v = {o[rb][fb][4 * jj], o[rb][fb][4 * jj + 1], o[rb][fb][4 * jj + 2], o[rb][fb][4 * jj + 3]};
+        *(f32x4*)(dst + 32 * fb + 8 * jj + 4 * h) = v * inv;
+      }
+    if (h == 0) a.lse[row] = live ? (m_run[rb] + __builtin_amdgcn_logf(l_row)) * kLn2 : -INFINITY;
+  }
 }
 
 }  // namespace prefill
@@ -314,7 +357,7 @@ hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint1
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   dim3 grid(batch * a.nblk, num_heads);
   // the events (may be null) are recorded by the dispatch itself
-  hipExtLaunchKernelGGL(prefill::prefill_kernel, grid, dim3(prefill::kThreads), 0, s, ev_start, ev_stop, 0, a);
+  hipExtLaunchKernelGGL(prefill::prefill_kernel<prefill::kRB>, grid, dim3(prefill::kThreads), 0, s, ev_start, ev_stop, 0, a);
   return hipGetLastError();
 }
 
