@@ -185,6 +185,12 @@ def bench_prefill(args):
     out = torch.empty((Tq, H, 128), dtype=torch.float32, device=dev)
     lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
     max_q = int(w.q_lens.max())
+    if args.calib_copy_mib:
+        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     def step():
         mla.prefill(q, kn, kr, v, cq, ck, max_q, w.softmax_scale, out=out, lse=lse)
