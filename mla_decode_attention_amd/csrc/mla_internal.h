@@ -41,6 +41,7 @@ struct DecodeParams {
   int batch, q_len, num_heads;
   int rows;                   // rows per sequence (q_len * H; the largest one with cu_q)
   int q_rows;                 // rows held by q (B * rows, or T * H with cu_q)
+  int grid_units;             // work units of the launch (set by launch_decode)
   int max_pages;
   float scale_log2;           // softmax_scale * log2(e)
 };

@@ -110,6 +110,19 @@ __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint3
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// 64-row kernels: (unit, row block) of this workgroup. Workgroups are handed
+// to the 8 XCDs round-robin by their linear id, so the row blocks of one unit
+// (which read the same pages) take ids that are equal mod 8 and share that
+// XCD's L2. The grid is padded to a multiple of 8 units; padding workgroups
+// get a unit past the last and exit.
+struct WgCoord {
+  int unit, rb;
+};
+__device__ __forceinline__ WgCoord wg_coord(int row_blocks) {
+  const int l = blockIdx.x, xcd = l & 7, k = l >> 3;
+  return WgCoord{(k / row_blocks) * 8 + xcd, k % row_blocks};
+}
 // x, hidden from the optimiser: values derived from it are recomputed where
 // they are used instead of being hoisted out of the tile loop into registers.
 __device__ __forceinline__ int opaque(int x) {
@@ -1250,9 +1263,11 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   const int rh = wave & 1, fh = (wave >> 1) & 1, kh = wave >> 2;
   const int kq = 2 * kh + fh;                // key quarter this wave owns after the exchange
   const int R = p.rows;
-  const int row0 = blockIdx.y * ROWS_WG;
+  const WgCoord wc = wg_coord((R + ROWS_WG - 1) / ROWS_WG);
+  if (wc.unit >= p.grid_units) return;
+  const int row0 = wc.rb * ROWS_WG;
   const int row_qk = row0 + 32 * rh + n;
-  const int u = blockIdx.x;
+  const int u = wc.unit;
 
   Unit unit;
   if (!unit.init(a, u)) {
@@ -1676,10 +1691,12 @@ void decode_kernel_q8(DecodeParams p_, const int32_t* __restrict__ md_, const in
   const int n16 = lane & 15, g = lane >> 4;      // QK / softmax lane roles
   const int n = lane & 31, h = lane >> 5;        // PV lane roles
   const int R = p.rows;
-  const int row0 = blockIdx.y * ROWS_WG;
+  const WgCoord wc = wg_coord((R + ROWS_WG - 1) / ROWS_WG);
+  if (wc.unit >= p.grid_units) return;
+  const int row0 = wc.rb * ROWS_WG;
   const int rs = 16 * rq + n16;                   // softmax row within the workgroup
   const int row_qk = row0 + rs;
-  const int u = blockIdx.x;
+  const int u = wc.unit;
 
   Unit unit;
   if (!unit.init(a, u)) {
@@ -2147,9 +2164,12 @@ int variant_rows(int variant) { return variant == VAR_NARROW16 ? 16 : 64; }   //
 hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s,
                          hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int rb = (p.rows + variant_rows(variant) - 1) / variant_rows(variant);
-  dim3 grid(grid_units, rb);
+  // 64-row kernels: 1-D grid, units padded to a multiple of 8 (see wg_coord)
+  const bool wide = variant == VAR_WIDE64X || variant == VAR_Q8;
+  dim3 grid = wide ? dim3(((grid_units + 7) / 8) * 8 * rb) : dim3(grid_units, rb);
   KernelArgs a;
   a.p = p;
+  a.p.grid_units = grid_units;
   a.md = p.md;
   a.prefix = p.md ? p.md + MD_HEADER : nullptr;
   a.split_off = p.md ? a.prefix + p.batch + 1 : nullptr;
