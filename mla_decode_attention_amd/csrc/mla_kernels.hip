@@ -1977,6 +1977,339 @@ void decode_kernel_q8(DecodeParams p_, const int32_t* __restrict__ md_, const in
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// WIDE64X on an fp8 cache without widening the page in LDS: the E4M3 tile
+// stays in LDS (the Q8 layout), and each MFMA operand is widened exactly to
+// bf16 in registers right after its LDS read (v_cvt_scalef32_pk_bf16_fp8,
+// scale 1). K: one 16-byte read feeds two k-steps. V^T: ds_read_b64_tr_b8
+// gives a lane 8 consecutive keys of one feature, so the PV k-slot 8h + e is
+// key 16ks + 8h + e and P is stored in that order. Otherwise as the bf16
+// wide kernel above (same split, exchange, softmax and epilogue).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8 widen8(unsigned lo, unsigned hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
+    const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
+    const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
+    const uint8_t* __restrict__ kv_) {
+  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
+  constexpr int ROWS_WG = 64;
+  constexpr int NQ = kDqk / 32;              // 18 QK MFMAs per wave and tile (k-steps of one feature half)
+
+  constexpr bool FP8 = true;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kQ8TileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kQ8TileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t xchg[kXchgBytes];
+  LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
+  LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
+  LDS_AS uint8_t* const xb = (LDS_AS uint8_t*)(xchg);
+
+  const DecodeParams& p = a.p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = uniform(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int rh = wave & 1, fh = (wave >> 1) & 1, kh = wave >> 2;
+  const int kq = 2 * kh + fh;                // key quarter this wave owns after the exchange
+  const int R = p.rows;
+  const WgCoord wc = wg_coord((R + ROWS_WG - 1) / ROWS_WG);
+  if (wc.unit >= p.grid_units) return;
+  const int row0 = wc.rb * ROWS_WG;
+  const int row_qk = row0 + 32 * rh + n;
+  const int u = wc.unit;
+
+  Unit unit;
+  if (!unit.init(a, u)) {
+    if (!a.md) write_empty(p, unit.b0, row0, row0 + ROWS_WG, kThreadsX / 64);
+    return;
+  }
+
+  // ---- per-lane constant LDS offsets (E4M3 tile, 64-byte line groups)
+  // QK: one 16-byte read per two k-steps. Lane (n, h) reads chunk
+  // 18fh + h + 2j of key 32kh + n (j = 0..8): bytes 0-7 feed k-step 2j, bytes
+  // 8-15 k-step 2j+1 (the query registers use the same feature order).
+  // Chunks 2 apart are one line group (4096 bytes) apart with the same swizzle.
+  int k_lane[2];
+#pragma unroll
+  for (int jp = 0; jp < 2; ++jp) k_lane[jp] = lds8_byte(32 * kh + n, 18 * fh + h + 2 * jp);
+  // V^T: ds_read_b64_tr_b8 in 16-lane groups gi: lane i of the group, as a
+  // source, reads 8 bytes (half i%2 of chunk 4w + 2fb + gi%2) of key
+  // 16ks + 8h + i/2, and receives 8 keys 16ks + 8h + 0..7 of feature
+  // 64w + 32fb + 16(gi%2) + i; +1024 bytes per k-step of 16 keys.
+  int v_lane[2];   // [fb]
+  {
+    const int gi = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+      v_lane[fb] = lds8_byte(8 * h + (i >> 1), 4 * wave + 2 * fb + (gi & 1)) + 8 * (i & 1);
+  }
+  // exchange area: partial scores [wave][2 x 16 B][lane]; a wave reads its
+  // partner's (w ^ 2) block
+  LDS_AS uint8_t* const x_give = xb + (wave * 2 * 64 + lane) * 16;
+  const LDS_AS uint8_t* const x_take = xb + ((wave ^ 2) * 2 * 64 + lane) * 16;
+
+  bf16x8 qreg[NQ];
+  f32x16 o[2][2];                            // [feature block][row half]
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb) {
+    o[fb][0] = f32x16{};
+    o[fb][1] = f32x16{};
+  }
+  float m_run[2] = {-INFINITY, -INFINITY};   // running max of rows row0 + n, row0 + 32 + n
+  float l_run = 0.f;                         // partial row sum of row_qk (this key quarter, lane half)
+  bool restart = true;                       // next rescale zeroes O and l (a sequence starts)
+  int row_tok = 0;                           // query token of row_qk in the current sequence
+
+  TileDmaQ8 dma;
+  TileInfo next = unit.prepare(a, unit.f_begin, buf0, nullptr, tid, dma);
+  // a row block past a sequence's rows (per-sequence q_len) skips its tiles:
+  // no loads, no compute
+  if (row0 < next.rows) dma_all(dma);
+
+  // cur: E4M3 tile (codes, then the 64 scales) of this step; nxt: where the
+  // next tile's loads go
+  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
+    const LDS_AS float* const sbc = (const LDS_AS float*)(cur + kFp8TileBytes);
+    const TileInfo ti = next;
+    const int t = ti.t, L = ti.L;
+    const bool skip = row0 >= ti.rows;
+
+    if (ti.first && !skip) {
+      const int rr = row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0);
+      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {
+        bf16x8 v = qrow[36 * fh + 4 * (c >> 1) + 2 * h + (c & 1)];
+        qreg[c] = row_qk < ti.rows ? v : bf16x8{};
+      }
+      // O and l restart through the rescale below (alpha = 0), so the
+      // accumulators are never reset outside the one rescale path
+      m_run[0] = m_run[1] = -INFINITY;
+      restart = true;
+      row_tok = rr / p.num_heads;
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    }
+    const bool final_out = ti.final_out;
+    const int slot = ti.slot;
+
+    // the next tile's facts and load plan (addresses only) are set up while
+    // this tile's loads may still be landing
+    const bool more = f + 1 < unit.f_end;
+    if (more) next = unit.prepare(a, f + 1, nxt, nullptr, tid, dma);
+    wait_tile();
+    const bool load_next = more && row0 < next.rows;
+    if (skip) {
+      if (load_next) dma_all(dma);
+      return;
+    }
+
+    // ---- QK GEMM: partial S^T[32 keys of half kh, 32 rows of half rh] over feature half fh
+    f32x16 sacc = f32x16{};
+    // one copy of the loop with the next tile's loads and one without, so
+    // the load slots need no per-slot branch
+    auto qk = [&](auto with_loads) {
+      constexpr int NJ = NQ / 2, D = 3;
+      auto kaddr = [&](int j) { return cur + k_lane[j & 1] + (j >> 1) * 4096; };
+      u32x4 ring[D];
+#pragma unroll
+      for (int j = 0; j < D; ++j) ring[j] = *(const LDS_AS u32x4*)kaddr(j);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const u32x4 w = ring[j % D];
+        if (j + D < NJ) ring[j % D] = *(const LDS_AS u32x4*)kaddr(j + D);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bf16x8 av = widen8(w[2 * e], w[2 * e + 1]);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[2 * j + e], sacc, 0, 0, 0);
+        }
+        if constexpr (decltype(with_loads)::value) dma_slot_ct<NJ>(dma, j);
+        sched_fence();
+      }
+    };
+    if (load_next) qk(std::true_type{});
+    else qk(std::false_type{});
+
+    // ---- add the two feature halves: keep registers 8fh..8fh+7 (keys
+    //      16kq + 0..15), give registers 8(1-fh).. to the partner. fh is
+    //      wave-uniform: a scalar branch with constant register indices
+    //      (a select on fh would become a per-element indexed extract).
+    float sv[8];
+    if (fh) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = sacc[8 + e];
+      *(LDS_AS f32x4*)(x_give) = f32x4{sacc[0], sacc[1], sacc[2], sacc[3]};
+      *(LDS_AS f32x4*)(x_give + 1024) = f32x4{sacc[4], sacc[5], sacc[6], sacc[7]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = sacc[e];
+      *(LDS_AS f32x4*)(x_give) = f32x4{sacc[8], sacc[9], sacc[10], sacc[11]};
+      *(LDS_AS f32x4*)(x_give + 1024) = f32x4{sacc[12], sacc[13], sacc[14], sacc[15]};
+    }
+    lds_barrier();
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      const f32x4 v = *(const LDS_AS f32x4*)(x_take + part * 1024);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[4 * part + e] += v[e];
+    }
+
+    // ---- softmax. P is computed against the running max before the tile
+    //      maxima of the other waves are known: with the lazy rescale the
+    //      running max moves only when some row's tile max exceeds it by more
+    //      than the threshold (so P <= 2^threshold otherwise). The quarter
+    //      maxima are published with P; after the barrier every wave checks
+    //      all 64 rows (the same decision in every wave) and, on the rare tiles
+    //      that raise a row's max (always on a sequence's first tile), rescales
+    //      O and l and rewrites P behind one more barrier.
+    LDS_AS float* const smax = (LDS_AS float*)(cur + 8 * 4096);   // rope line group: [key quarter][row]
+    const int key0 = t * kPage + 16 * kq + 4 * h;
+    // keys at or past vis are masked (causal rule / cache tail); only the
+    // tiles that reach past L - qlen + 1 can hold such keys
+    const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
+    f32x4 ksc[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+      ksc[jj] = FP8 ? *(const LDS_AS f32x4*)(sbc + 16 * kq + 8 * jj + 4 * h) : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sv[r] *= FP8 ? ksc[r >> 2][r & 3] * p.scale_log2 : p.scale_log2;
+    if (__builtin_expect(need_mask, 0)) {
+      const int vis = L - ti.qlen + row_tok + 1;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if ((key0 + 8 * (r >> 2) + (r & 3)) >= vis) sv[r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sv[r]);
+    mx = max_xor32(mx);
+    if (h == 0) smax[kq * 64 + 32 * rh + n] = mx;
+    // A wave that sees a row max past the threshold stamps the tile index
+    // into the flag word (left over values of other tiles never match f; a
+    // stray match would only take the exact slow path below).
+    LDS_AS int* const raise_flag = (LDS_AS int*)(smax + 256);
+    if (!restart && __builtin_amdgcn_ballot_w64(mx > m_run[rh] + kRescaleThreshold) && lane == 0)
+      *raise_flag = f;
+    // P operand [k-step][row half][lane (n, h)] in the exchange area (the
+    // partial scores there were consumed before the barrier above): reader
+    // lane (n, h) holds keys 16ks + 8h + 0..7, so this lane's keys 4h + 0..3
+    // go to reader half 0 and keys 8 + 4h + 0..3 to reader half 1, at byte 8h
+    LDS_AS uint8_t* const p_out = xb + ((kq * 2 + rh) * 64 + n) * 16 + 8 * h;
+    float l_tile = 0.f;
+    auto make_p = [&](float m_ref) {
+      bf16x4 pa, pc;
+      l_tile = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = exp2_fast(sv[e] - m_ref);
+        l_tile += pr;
+        const __bf16 v = (__bf16)(pr * ksc[e >> 2][e & 3]);
+        if (e < 4) pa[e] = v;
+        else pc[e - 4] = v;
+      }
+      *(LDS_AS bf16x4*)p_out = pa;
+      *(LDS_AS bf16x4*)(p_out + 32 * 16) = pc;
+    };
+    // (a row whose keys were all masked so far keeps m = -inf: reference 0, P = 0)
+    if (!restart) make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
+    lds_barrier();
+
+    if (restart || uniform(*raise_flag) == f) {
+      // some row's max moved (or a sequence starts): every wave derives the
+      // new running max of all 64 rows from the quarter maxima
+      float alpha[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float tmax = fmaxf(fmaxf(smax[32 * rb + n], smax[64 + 32 * rb + n]),
+                                 fmaxf(smax[128 + 32 * rb + n], smax[192 + 32 * rb + n]));
+        const float m_new = fmaxf(m_run[rb], tmax);
+        const bool raise = m_new > m_run[rb] + kRescaleThreshold;
+        alpha[rb] = restart ? 0.0f : raise ? exp2_fast(m_run[rb] - m_new) : 1.0f;
+        if (raise) m_run[rb] = m_new;
+      }
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb) {
+        o[fb][0] *= alpha[0];
+        o[fb][1] *= alpha[1];
+      }
+      l_run *= alpha[rh];
+      make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
+      lds_barrier();
+    }
+    restart = false;
+    l_run += l_tile;
+
+    // ---- PV GEMM: O^T[64 features of this wave, 64 rows] += V^T . P^T, V^T
+    //      through the transposed byte read and widened in registers
+    {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 pb0 = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 0) * 64 + lane) * 16);
+        const bf16x8 pb1 = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 1) * 64 + lane) * 16);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) {
+          const i32x2 x = tr8_read(cur + v_lane[fb] + ks * 1024);
+          const bf16x8 av = widen8((unsigned)x[0], (unsigned)x[1]);
+          o[fb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb0, o[fb][0], 0, 0, 0);
+          o[fb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb1, o[fb][1], 0, 0, 0);
+        }
+      }
+    }
+
+    // The next step's first barrier orders this PV's LDS reads before any
+    // write into `cur` or the exchange area; only the epilogue needs one here.
+    if (!ti.last) return;
+    lds_barrier();   // every wave is done reading P from the exchange area
+
+    // ---- epilogue for this sequence: full row sums, then O / l and LSE
+    LDS_AS float* const ssum = (LDS_AS float*)xb;   // [key quarter][row]
+    const float lh = sum_xor32(l_run);
+    if (h == 0) ssum[kq * 64 + 32 * rh + n] = lh;
+    lds_barrier();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = row0 + 32 * rb + n;
+      const float l_row = (ssum[32 * rb + n] + ssum[64 + 32 * rb + n]) +
+                          (ssum[128 + 32 * rb + n] + ssum[192 + 32 * rb + n]);
+      const bool live = l_row > 0.f;
+      const float inv = live ? 1.0f / l_row : 0.f;
+      if (row < ti.rows) {
+        float* dst_o;
+        float* dst_l;
+        if (final_out) {
+          dst_o = p.out + ((size_t)ti.qrow0 + row) * kDv;
+          dst_l = p.lse + (size_t)ti.qrow0 + row;
+        } else {
+          dst_o = p.ws_out + ((size_t)slot * R + row) * kDv;
+          dst_l = p.ws_lse + (size_t)slot * R + row;
+        }
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            f32x4 v = {o[fb][rb][4 * jj], o[fb][rb][4 * jj + 1], o[fb][rb][4 * jj + 2], o[fb][rb][4 * jj + 3]};
+            *(f32x4*)(dst_o + 64 * wave + 32 * fb + 8 * jj + 4 * h) = v * inv;
+          }
+        }
+        if (wave == 0 && h == 0)
+          *dst_l = live ? (m_run[rb] + log2_fast(l_row)) * kLn2 : -INFINITY;
+      }
+    }
+  };
+
+  for (int f = unit.f_begin; f < unit.f_end; f += 2) {
+    step(f, buf0, buf1);
+    if (f + 1 < unit.f_end) step(f + 1, buf1, buf0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Split schedule (one workgroup). Integer only; matches the definition in the
 // header: equal tile counts per unit over the flattened (sequence, tile) space.
@@ -2189,7 +2522,7 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
   } else if (variant == VAR_Q8) {
     MLA_LAUNCH(decode_kernel_q8, kThreadsX);
   } else {
-    if (fp8) MLA_LAUNCH((decode_kernel_x<true>), kThreadsX);
+    if (fp8) MLA_LAUNCH(decode_kernel_xf, kThreadsX);
     else MLA_LAUNCH((decode_kernel_x<false>), kThreadsX);
   }
 #undef MLA_LAUNCH
