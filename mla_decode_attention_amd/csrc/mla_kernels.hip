@@ -34,8 +34,14 @@
 //                        features for PV (16x16 MFMA).
 //   NARROW16   (R <= 16, fp8):  4 waves split each tile's 64 keys, partial
 //                        states merged at the end (16x16 MFMA).
-//   WIDE64X    (R > 16): 64 rows; QK split 2x2 (row half x feature half) over
-//                        the waves, PV split by output columns (32x32 MFMA).
+//   WIDE64X    (R > 16): 64 rows, 8 waves; QK split by row half x feature
+//                        half x key half, PV by output columns (32x32 MFMA).
+//                        bf16 cache: decode_kernel_x; fp8 cache:
+//                        decode_kernel_xf (E4M3 tile in LDS, operands widened
+//                        in registers).
+//   Q8         (fp8 cache, mla_decode_fwd_fp8mma): queries and P in E4M3 on
+//                        fp8 MFMA, 64 rows, 8 waves.
+// (The prefill / extend kernel is in mla_prefill.hip.)
 //
 // Split-KV: work units of equal tile count over the flattened
 // (sequence, tile) space; sequences cut across units write partial (O, LSE)
@@ -1170,73 +1176,7 @@ struct TileDmaX<false> {
   __device__ __forceinline__ void load_ct() const { load(I); }
 };
 
-// fp8 page, 512 threads: a plain copy of the 36 KiB page into the staging
-// buffer (slot 512i + t; the last load is made by waves 0-3 only), plus the
-// 64 per-token scales (one 4-byte load per lane of wave 0).
-template <>
-struct TileDmaX<true> {
-  static constexpr int kLoads = kFp8LoadsX;
-  const uint8_t* page;
-  const uint8_t* scale;
-  uint32_t lds0, sc_lds, sc_off;
-  int nvalid, tid;
-  __device__ __forceinline__ void plan(const uint8_t* kv, const float* kv_scale, int page_id, int nv,
-                                       LDS_AS uint8_t* buf, LDS_AS float* sbuf, int t) {
-    page = kv + (size_t)page_id * kFp8TileBytes;
-    scale = (const uint8_t*)(kv_scale + (size_t)page_id * kPage);
-    nvalid = nv;
-    tid = t;
-    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
-    sc_lds = (uint32_t)uniform((int)(uintptr_t)sbuf);
-    const int lane = tid & 63;
-    sc_off = 4 * (lane < nvalid ? lane : nvalid - 1);
-  }
-  __device__ __forceinline__ void load(int i) const {
-    if (i * kThreadsX + (tid & ~63) >= kFp8SlotsX) return;   // wave-uniform
-    // lane offset recomputed per load (not hoisted into five registers)
-    const int sidx = i * kThreadsX + opaque(tid);
-    uint32_t voff = sidx * 16;
-    if (nvalid < kPage) {
-      // tail page: slots of keys at or past nvalid re-read the last valid key
-      const int key = sidx / 36;
-      if (key >= nvalid) voff = (nvalid - 1) * kFp8RowBytes + (sidx - key * 36) * 16;
-    }
-    dma16(voff, page, lds0 + i * kThreadsX * 16);
-    if (i == 0 && tid < 64) dma4(sc_off, scale, sc_lds);
-  }
-  template <int I>
-  __device__ __forceinline__ void load_ct() const { load(I); }
-};
 
-// fp8 staging page -> bf16 tile with 512 threads (see widen_fp8_tile).
-__device__ __forceinline__ void widen_fp8_tile_x(const LDS_AS uint8_t* stage, LDS_AS uint8_t* tile, int tid) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-#pragma unroll
-  for (int j = 0; j < kFp8LoadsX; ++j) {
-    const int sidx = j * kThreadsX + opaque(tid);
-    if (sidx >= kFp8SlotsX) break;
-    const int key = sidx / 36, c16 = sidx - key * 36;
-    const u32x4 w = *(const LDS_AS u32x4*)(stage + sidx * 16);
-    u32x4 lo, hi;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bf16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false);
-      const bf16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true);
-      const unsigned u0 = __builtin_bit_cast(unsigned, x0), u1 = __builtin_bit_cast(unsigned, x1);
-      if (e < 2) {
-        lo[2 * e] = u0;
-        lo[2 * e + 1] = u1;
-      } else {
-        hi[2 * (e - 2)] = u0;
-        hi[2 * (e - 2) + 1] = u1;
-      }
-    }
-    *(LDS_AS u32x4*)(tile + lds_byte(key, 2 * c16)) = lo;
-    *(LDS_AS u32x4*)(tile + lds_byte(key, 2 * c16 + 1)) = hi;
-  }
-}
-
-template <bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
     const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
@@ -1247,14 +1187,11 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   constexpr int NQ = kDqk / 32;              // 18 QK MFMAs per wave and tile (k-steps of one feature half)
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[FP8 ? kFp8TileBytes + 2 * kPage * 4 : kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t xchg[kXchgBytes];
   LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
   LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
   LDS_AS uint8_t* const xb = (LDS_AS uint8_t*)(xchg);
-  // fp8: page codes staged in smem1, per-token scales (double buffered) after them
-  LDS_AS float* const sb0 = (LDS_AS float*)(buf1 + kFp8TileBytes);
-  LDS_AS float* const sb1 = sb0 + kPage;
 
   const DecodeParams& p = a.p;
   const int tid = threadIdx.x;
@@ -1313,17 +1250,14 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   bool restart = true;                       // next rescale zeroes O and l (a sequence starts)
   int row_tok = 0;                           // query token of row_qk in the current sequence
 
-  TileDmaX<FP8> dma;
-  TileInfo next = unit.prepare(a, unit.f_begin, FP8 ? buf1 : buf0, sb0, tid, dma);
+  TileDmaX<false> dma;
+  TileInfo next = unit.prepare(a, unit.f_begin, buf0, nullptr, tid, dma);
   // a row block past a sequence's rows (per-sequence q_len) skips its tiles:
   // no loads, no compute
   if (row0 < next.rows) dma_all(dma);
 
-  // cur: bf16 tile computed in this step; nxt: where the next tile's loads go
-  // (fp8: the staging area again, free once the current page is widened);
-  // sbc / sbn: fp8 scales of this tile and of the next one.
-  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt,
-                  const LDS_AS float* const sbc, LDS_AS float* const sbn) {
+  // cur: tile computed in this step; nxt: where the next tile's loads go
+  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
     const TileInfo ti = next;
     const int t = ti.t, L = ti.L;
     const bool skip = row0 >= ti.rows;
@@ -1349,16 +1283,12 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     // the next tile's facts and load plan (addresses only) are set up while
     // this tile's loads may still be landing
     const bool more = f + 1 < unit.f_end;
-    if (more) next = unit.prepare(a, f + 1, nxt, sbn, tid, dma);
+    if (more) next = unit.prepare(a, f + 1, nxt, nullptr, tid, dma);
     wait_tile();
     const bool load_next = more && row0 < next.rows;
     if (skip) {
       if (load_next) dma_all(dma);
       return;
-    }
-    if constexpr (FP8) {
-      widen_fp8_tile_x(buf1, cur, tid);
-      lds_barrier();
     }
 
     // ---- QK GEMM: partial S^T[32 keys of half kh, 32 rows of half rh] over feature half fh
@@ -1419,12 +1349,8 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     // keys at or past vis are masked (causal rule / cache tail); only the
     // tiles that reach past L - qlen + 1 can hold such keys
     const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
-    f32x4 ksc[2];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-      ksc[jj] = FP8 ? *(const LDS_AS f32x4*)(sbc + 16 * kq + 8 * jj + 4 * h) : f32x4{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-    for (int r = 0; r < 8; ++r) sv[r] *= FP8 ? ksc[r >> 2][r & 3] * p.scale_log2 : p.scale_log2;
+    for (int r = 0; r < 8; ++r) sv[r] *= p.scale_log2;
     if (__builtin_expect(need_mask, 0)) {
       const int vis = L - ti.qlen + row_tok + 1;
 #pragma unroll
@@ -1453,7 +1379,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
       for (int e = 0; e < 8; ++e) {
         const float pr = exp2_fast(sv[e] - m_ref);
         l_tile += pr;
-        pb[e] = (__bf16)(FP8 ? pr * ksc[e >> 2][e & 3] : pr);
+        pb[e] = (__bf16)pr;
       }
       *p_out = pb;
     };
@@ -1560,13 +1486,8 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   };
 
   for (int f = unit.f_begin; f < unit.f_end; f += 2) {
-    if constexpr (FP8) {
-      step(f, buf0, buf1, sb0, sb1);
-      if (f + 1 < unit.f_end) step(f + 1, buf0, buf1, sb1, sb0);
-    } else {
-      step(f, buf0, buf1, nullptr, nullptr);
-      if (f + 1 < unit.f_end) step(f + 1, buf1, buf0, nullptr, nullptr);
-    }
+    step(f, buf0, buf1);
+    if (f + 1 < unit.f_end) step(f + 1, buf1, buf0);
   }
 }
 
@@ -2523,7 +2444,7 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
     MLA_LAUNCH(decode_kernel_q8, kThreadsX);
   } else {
     if (fp8) MLA_LAUNCH(decode_kernel_xf, kThreadsX);
-    else MLA_LAUNCH((decode_kernel_x<false>), kThreadsX);
+    else MLA_LAUNCH(decode_kernel_x, kThreadsX);
   }
 #undef MLA_LAUNCH
   return hipGetLastError();
