@@ -105,19 +105,6 @@ struct Args {
   float scale_log2;
 };
 
-// The loads of one key tile into one stage. Load i of thread t fills slot
-// 256i + t of a 64-key region: line group i/2, key 32(i%2) + t/8, in-line
-// position t%8; K loads 0-3 come from k_nope (chunks 0..15), 4-5 from k_rope
-// (chunks 16..23), V loads 0-3 from v. Keys at or past `nvalid` re-read the
-// last valid key.
-struct TilePlan {
-  const uint8_t* kn;        // k_nope row of key 0 of the tile, head h
-  const uint8_t* kr;        // k_rope row of key 0
-  const uint8_t* vv;        // v row of key 0, head h
-  uint32_t off_h[2], off_r[2];   // per key parity: row offsets (head-strided / rope)
-  uint32_t pos16[2];             // 16 * (in-line chunk of this lane's slot), per key parity
-};
-
 // RB = query row blocks of 32 per wave: RB = 1 gives 128 rows per workgroup
 // and two workgroups per CU; RB = 2 gives 256 rows per workgroup, one per CU,
 // and halves the LDS bytes per MFMA (each K or V fragment feeds two MFMAs).
@@ -161,31 +148,31 @@ void prefill_kernel(Args a) {
     }
   }
 
-  // ---- loads of one key tile (see TilePlan)
+  // ---- loads of one key tile
   const size_t rowK = (size_t)H * kDNope * 2;   // bytes between keys in k_nope / v
   const uint32_t lds_k0 = (uint32_t)uniform((int)(uintptr_t)(stage0 + (tid & ~63) * 16));
-  auto issue = [&](int t, int stage) {
+  // Load i (0..9) of key tile t into a stage. K load i (0-5) of thread t
+  // fills slot 256i + t of the K region: line group i/2, key 32(i%2) + t/8,
+  // in-line position t%8 -- loads 0-3 from k_nope (chunks 0..15), 4-5 from
+  // k_rope (chunks 16..23); V loads 6-9 fill the V region the same way. Keys
+  // at or past the sequence end re-read the last key.
+  auto issue_one = [&](int t, int stage, int i) {
     const int kt0 = t * kTile;
     const int nvalid = min(kTile, L - kt0);
-    const uint8_t* kn = a.k_nope + ((size_t)(k0 + kt0) * H + head) * (kDNope * 2);
-    const uint8_t* kr = a.k_rope + (size_t)(k0 + kt0) * (kDRope * 2);
-    const uint8_t* vv = a.v + ((size_t)(k0 + kt0) * H + head) * (kDVh * 2);
     const uint32_t lds = lds_k0 + stage * kStage;
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int key = 32 * (i & 1) + (tid >> 3);
-      const int src = key < nvalid ? key : nvalid - 1;
-      const int c = 8 * (i >> 1) + ((tid & 7) ^ swz3(key));
-      if (i < 4) dma16((uint32_t)(src * rowK + c * 16), kn, lds + i * 4096);
-      else dma16((uint32_t)(src * (kDRope * 2) + (c - 16) * 16), kr, lds + i * 4096);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 32 * (i & 1) + (tid >> 3);
-      const int src = key < nvalid ? key : nvalid - 1;
-      const int c = 8 * (i >> 1) + ((tid & 7) ^ swz3(key));
-      dma16((uint32_t)(src * rowK + c * 16), vv, lds + kKBytes + i * 4096);
-    }
+    const int ii = i < 6 ? i : i - 6;
+    const int key = 32 * (ii & 1) + (tid >> 3);
+    const int src = key < nvalid ? key : nvalid - 1;
+    const int c = 8 * (ii >> 1) + ((tid & 7) ^ swz3(key));
+    if (i < 4)
+      dma16((uint32_t)(src * rowK + c * 16), a.k_nope + ((size_t)(k0 + kt0) * H + head) * (kDNope * 2),
+            lds + i * 4096);
+    else if (i < 6)
+      dma16((uint32_t)(src * (kDRope * 2) + (c - 16) * 16), a.k_rope + (size_t)(k0 + kt0) * (kDRope * 2),
+            lds + i * 4096);
+    else
+      dma16((uint32_t)(src * rowK + c * 16), a.v + ((size_t)(k0 + kt0) * H + head) * (kDVh * 2),
+            lds + kKBytes + ii * 4096);
   };
 
   // per-lane LDS offsets: K operand (key 32kb + n, chunk 2c + h), V^T reads
@@ -218,11 +205,14 @@ void prefill_kernel(Args a) {
   }
   bool first = true;
 
-  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 0)
+#pragma unroll
+    for (int i = 0; i < 10; ++i) issue_one(0, 0, i);
   for (int t = 0; t < ntiles; ++t) {
     LDS_AS uint8_t* const cur = stage0 + (t & 1) * kStage;
     wait_loads();
-    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+    // the next tile's 10 loads go out one per even QK slot (not as a burst)
+    const bool load_next = t + 1 < ntiles;
 
     // ---- QK: S^T[64 keys, 32 rows] per row block; each K fragment feeds RB MFMAs
     f32x16 sacc[RB][2];
@@ -244,6 +234,7 @@ void prefill_kernel(Args a) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           sacc[rb][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[rb][i >> 1], sacc[rb][i & 1], 0, 0, 0);
+        if ((i & 1) == 0 && i < 20 && load_next) issue_one(t + 1, (t + 1) & 1, i >> 1);
       }
     }
 
