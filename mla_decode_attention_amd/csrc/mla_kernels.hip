@@ -1561,8 +1561,10 @@ struct TileDmaQ8 {
   }
   __device__ __forceinline__ void load(int i) const {
     if (i * kThreadsX + (tid & ~63) >= kFp8SlotsX) return;   // wave-uniform
-    dma16(voff, page + 128 * i, lds0 + i * kThreadsX * 16);
-    if (i == 0 && tid < 64) dma4(sc_off, scale, sc_lds);
+    // (readfirstlane: should the plan pass through a phi the compiler cannot
+    // prove uniform, M0's source stays scalar)
+    dma16(voff, page + 128 * i, (uint32_t)uniform((int)(lds0 + i * kThreadsX * 16)));
+    if (i == 0 && tid < 64) dma4(sc_off, scale, (uint32_t)uniform((int)sc_lds));
   }
   template <int I>
   __device__ __forceinline__ void load_ct() const { load(I); }
