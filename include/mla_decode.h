@@ -132,7 +132,8 @@ int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int num_unit
  *   metadata       NULL: one work unit per sequence, no partials, no merge
  *                  (workspace unused). Otherwise the buffer written by
  *                  mla_get_split_metadata for the same cache_seqlens, batch
- *                  and num_units.
+ *                  and num_units (checked on the device against the buffer's
+ *                  header: for another batch or num_units nothing is written).
  *   num_units      the value given to mla_get_split_metadata (ignored if
  *                  metadata is NULL)
  *   workspace      device buffer of >= mla_workspace_bytes(batch, q_len,
@@ -245,7 +246,8 @@ int mla_prefill_fwd(const void* q, const void* k_nope, const void* k_rope, const
  *   lse             device fp32 [batch, rows_per_seq]
  * Per row: M = max_k lse_k; lse = M + ln sum_k exp(lse_k - M);
  * out = sum_k exp(lse_k - lse) * part_out_k. Partials with lse_k = -inf weigh
- * 0; a sequence with no partial (or only -inf ones) gets out = 0, lse = -inf.
+ * 0 and their part_out values are not read into the result (NaN included); a
+ * sequence with no partial (or only -inf ones) gets out = 0, lse = -inf.
  */
 int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq_part_offsets,
                 int batch, int rows_per_seq, float* out, float* lse, void* stream);

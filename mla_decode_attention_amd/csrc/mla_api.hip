@@ -249,7 +249,8 @@ int decode_impl(const void* q, const int32_t* cu_q, int total_q, const void* kv_
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   if (metadata) {
     const int32_t* offsets = (const int32_t*)metadata + mla::MD_HEADER + batch + 1;
-    e = mla::launch_combine(p.ws_out, p.ws_lse, offsets, cu_q, num_heads, batch, p.rows, out, lse, 1, s);
+    e = mla::launch_combine(p.ws_out, p.ws_lse, offsets, cu_q, num_heads, batch, p.rows, out, lse, 1, s,
+                            p.md, num_units);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   }
   return ok();

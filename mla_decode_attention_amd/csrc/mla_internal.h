@@ -66,9 +66,12 @@ hipError_t launch_append(const uint16_t* latent, int batch, int new_tokens, cons
                          int num_pages, hipStream_t s);
 // cu_q (nullable): per-sequence query offsets; sequence b then owns rows
 // [0, (cu_q[b+1] - cu_q[b]) * num_heads) and writes out rows from cu_q[b] * num_heads.
+// md (nullable): split metadata the offsets come from; nothing is merged
+// unless its header names this batch and `units`.
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
                           const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
-                          float* lse, int skip_single, hipStream_t s);
+                          float* lse, int skip_single, hipStream_t s, const int32_t* md = nullptr,
+                          int units = 0);
 
 // Prefill / extend (un-absorbed MLA, head dim 192 = 128 + 64 shared rope, v 128).
 int prefill_rows_per_block();

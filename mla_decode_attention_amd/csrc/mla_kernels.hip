@@ -374,6 +374,14 @@ __device__ __forceinline__ int seq_qrow0(const DecodeParams& p, int b) {
   return p.cu_q ? uniform(p.cu_q[b]) * p.num_heads : b * p.rows;
 }
 
+// Metadata built for this launch's batch and unit count. A mismatch is a
+// caller error; the kernels then read no further metadata and write nothing
+// (a unit index past the metadata's units would read past its arrays).
+__device__ __forceinline__ bool md_matches(const DecodeParams& p) {
+  return uniform(p.md[MD_MAGIC]) == kMdMagic && uniform(p.md[MD_BATCH]) == p.batch &&
+         uniform(p.md[MD_UNITS]) == p.grid_units;
+}
+
 // Flattened tile range [f_begin, f_end) of unit u and the prefetch cursor.
 // Everything the tile stream needs per tile is held in scalar registers or in
 // one VGPR of cached page ids (lane i = page of tile pc_t0 + i), so loading a
@@ -393,6 +401,7 @@ struct Unit {
     payload = 1;
     if (a.md) {
       const int B = a.p.batch;
+      if (!md_matches(a.p)) return false;
       payload = a.md[MD_PAYLOAD];
       const int T = a.prefix[B];
       f_begin = u * payload;
@@ -2335,18 +2344,28 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
 // LSE merge of partials: one workgroup per (sequence, pair of rows), 128
 // threads x 4 features per row. One pass gives the max and the rescaled sum of
 // the partial LSEs; a second pass accumulates the weighted partial outputs,
-// four partials in flight per step.
+// four partials in flight per step. A partial with LSE -inf weighs nothing and
+// its values are not used (they may be anything, NaN included).
+// md (nullable): the decode's metadata; the merge does nothing unless it was
+// built for this batch and num_units (as the decode kernels check).
 // ---------------------------------------------------------------------------
+__constant__ int32_t kNoMetadataHeader[MD_HEADER] = {};
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_out,
                                                       const float* __restrict__ part_lse,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ cu_q, int num_heads,
                                                       int B, int R, float* __restrict__ out,
-                                                      float* __restrict__ lse, int skip_single) {
+                                                      float* __restrict__ lse, int skip_single,
+                                                      const int32_t* __restrict__ md, int units) {
   const int b = blockIdx.x;
   const int k0 = offsets[b];
   const int n = offsets[b + 1] - k0;
-  if (skip_single && n == 1) return;
+  // header words loaded unconditionally, together with the offsets (no extra round trip)
+  const int32_t* hdr = md ? md : kNoMetadataHeader;
+  const int h0 = hdr[MD_MAGIC], h1 = hdr[MD_BATCH], h2 = hdr[MD_UNITS];
+  const bool bad = md && ((h0 != kMdMagic) | (h1 != B) | (h2 != units));
+  if (bad | (skip_single && n == 1)) return;
   const int r = blockIdx.y * 2 + (threadIdx.x >> 7);
   // partial slots hold R rows; sequence b owns the first rows_b of them
   const int rows_b = cu_q ? (cu_q[b + 1] - cu_q[b]) * num_heads : R;
@@ -2399,7 +2418,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         ov[j] = *(const f32x4*)(po + (k + j) * ostride);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc += wk[j] * ov[j];
+      for (int j = 0; j < 4; ++j)
+        if (wk[j] != 0.f) acc += wk[j] * ov[j];
     }
     for (; k < n; ++k) {
       const float v = pl[k * lstride];
@@ -2460,10 +2480,10 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min
 
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
                           const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
-                          float* lse, int skip_single, hipStream_t s) {
+                          float* lse, int skip_single, hipStream_t s, const int32_t* md, int units) {
   dim3 grid(batch, (rows + 1) / 2);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, part_out, part_lse, offsets, cu_q, num_heads,
-                     batch, rows, out, lse, skip_single);
+                     batch, rows, out, lse, skip_single, md, units);
   return hipGetLastError();
 }
 

@@ -145,7 +145,9 @@ def test_combine_matches_oracle_merge(R):
     pl = (rng.standard_normal((N, R)) * 3).astype(np.float32)
     pl[0, :5] = -np.inf                      # some partials saw no visible key
     pl[3:8, 7] = -np.inf                     # a row with only -inf partials in sequence 3
-    out, lse = mla.combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+    po_gpu = po.copy()
+    po_gpu[np.isneginf(pl)] = np.nan         # values of -inf partials are never read into the result
+    out, lse = mla.combine(torch.from_numpy(po_gpu).cuda(), torch.from_numpy(pl).cuda(),
                            torch.from_numpy(offs).cuda())
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
