@@ -74,13 +74,18 @@ const char* mla_last_error(void);
  * Split-KV planning (host only, no device access).
  *
  * The split schedule cuts the flattened (sequence, 64-token tile) space into
- * `num_units` contiguous work units of equal tile count (FlashDecoding-style
+ * `num_units` contiguous work units of about equal cost (FlashDecoding-style
  * splitting of the cache, named among the attention features in PaddleNLP
  * issue #10157's overview; the cache is cut into partitions that are merged
  * afterwards in the Append Attention flags of the mhpq.cn article on PaddleNLP
- * inference flags). With T_b = ceil(L_b/64) and T = sum T_b:
- *   payload = max(ceil(T / num_units), min_tiles_per_unit, 1)
- *   unit u covers flattened tiles [u*payload, min((u+1)*payload, T)).
+ * inference flags). A sequence's start (its query rows, its epilogue, its
+ * metadata) is charged as 3 tiles. With T_b = ceil(L_b/64), T = sum T_b, and
+ * every sequence with tiles laid on a weighted line as 3 start positions then
+ * its T_b tiles (W positions in all):
+ *   payload = max(ceil(W / num_units), min_tiles_per_unit, 1)
+ *   unit u starts at the tile of weighted position u*payload (a sequence's
+ *   first tile if the position falls in its start, T past the end) and runs
+ *   to the next unit's start; a unit may hold no tile.
  * A sequence touched by k > 1 units is computed as k partials and merged.
  *
  * mla_default_num_units: a unit count that fills the current device for this

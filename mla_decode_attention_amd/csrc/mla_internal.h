@@ -12,19 +12,26 @@ constexpr int kDv = 512;          // value = first 512 entries of the row
 constexpr int kThreads = 256;     // 4 waves of 64 lanes per workgroup
 
 // Metadata layout (int32 words, device):
-//   [0] magic  [1] batch  [2] num_units  [3] payload  [4] total_partials
-//   [5] units_used  [6..7] reserved
-//   [8 .. 8+B]            prefix: first flattened tile of each sequence [B+1]
-//   [9+B .. 9+2B]         split_offset: first partial slot of each sequence [B+1]
-//   [10+2B .. 10+2B+U)    unit_first_seq: sequence holding each unit's first tile
-constexpr int kMdMagic = 0x4D4C4131;  // 'MLA1'
+//   [0] magic  [1] batch  [2] num_units  [3] payload (weighted)  [4] total_partials
+//   [5] units_used  [6] sequence start cost (tiles)  [7] reserved
+//   [8 .. 8+B]                 prefix: first flattened tile of each sequence [B+1]
+//   [9+B .. 9+2B]              split_offset: first partial slot of each sequence [B+1]
+//   [10+2B .. 10+2B+U)         unit_first_seq: sequence holding each unit's first tile
+//   [10+2B+U .. 11+2B+2U)      unit_begin: first flattened tile of each unit [U+1]
+//   [11+2B+2U .. 11+3B+2U)     seq_first_unit: unit holding each sequence's first tile
+constexpr int kMdMagic = 0x4D4C4132;  // 'MLA2'
 enum { MD_MAGIC = 0, MD_BATCH = 1, MD_UNITS = 2, MD_PAYLOAD = 3, MD_TOTAL_PARTIALS = 4,
-       MD_UNITS_USED = 5, MD_HEADER = 8 };
+       MD_UNITS_USED = 5, MD_SEQ_COST = 6, MD_HEADER = 8 };
 constexpr int kDefaultMinTiles = 8;
+// A sequence's start (query rows, epilogue, partial write, metadata) costs
+// about as much as this many 64-token tiles; the split schedule charges it.
+constexpr int kSeqCostTiles = 3;
 
 inline size_t metadata_words(int batch, int units) {
-  return (size_t)MD_HEADER + 2 * ((size_t)batch + 1) + (size_t)units;
+  return (size_t)MD_HEADER + 3 * (size_t)batch + 2 + 2 * (size_t)units + 1;
 }
+__host__ __device__ inline size_t md_unit_begin(int batch, int units) { return (size_t)MD_HEADER + 2 * ((size_t)batch + 1) + units; }
+__host__ __device__ inline size_t md_seq_first_unit(int batch, int units) { return md_unit_begin(batch, units) + units + 1; }
 
 struct DecodeParams {
   const uint16_t* q;          // bf16 bits [B, s, H, 576], or [T, H, 576] with cu_q

@@ -387,26 +387,36 @@ __device__ __forceinline__ bool md_matches(const DecodeParams& p) {
 // one VGPR of cached page ids (lane i = page of tile pc_t0 + i), so loading a
 // tile performs no metadata load; sequence changes (and every 64 tiles) reload
 // the cache.
-struct Unit {
-  int u, f_begin, f_end, b0, payload;
+// NX: load the next sequence's facts ahead (two more registers; off in the
+// kernels that have none to spare).
+template <bool NX>
+struct UnitT {
+  int u, f_begin, f_end, b0;
+  const int32_t* seq_first_unit;               // metadata: unit holding each sequence's first tile
   int bp, bp_first, bp_last, bp_L, bp_tiles;  // sequence of the prefetch cursor
   bool bp_final;
   int bp_slot;
   int bp_qlen, bp_qrow0;                       // query tokens and first q/out row
   int pc_t0, page_cache;
+  // facts of sequence nx_b = bp + 1, loaded when bp is entered so that the
+  // switch to it needs no memory round trip: lane 0 its length, lanes 1-2 its
+  // tile prefix, lanes 3-4 its partial offsets, lanes 5-6 its query offsets,
+  // lane 7 the unit holding its first tile;
+  // nx_pages lane i = its page of tile i (i < max_pages)
+  int nx_b, nx_facts, nx_pages;
 
   // false if the unit has no tiles
   __device__ __forceinline__ bool init(const KernelArgs& a, int unit) {
     u = unit;
-    payload = 1;
+    seq_first_unit = nullptr;
     if (a.md) {
       const int B = a.p.batch;
       if (!md_matches(a.p)) return false;
-      payload = a.md[MD_PAYLOAD];
-      const int T = a.prefix[B];
-      f_begin = u * payload;
-      if (f_begin >= T) return false;
-      f_end = min(f_begin + payload, T);
+      const int32_t* ub = a.md + md_unit_begin(B, a.p.grid_units);
+      seq_first_unit = a.md + md_seq_first_unit(B, a.p.grid_units);
+      f_begin = ub[u];
+      f_end = ub[u + 1];
+      if (f_begin >= f_end) return false;
       b0 = a.split_off[B + 1 + u];
     } else {
       b0 = u;
@@ -417,8 +427,8 @@ struct Unit {
     f_begin = uniform(f_begin);
     f_end = uniform(f_end);
     b0 = uniform(b0);
-    payload = uniform(payload);
     if (f_end <= f_begin) return false;
+    nx_b = -1;
     enter(a, b0, f_begin);
     return true;
   }
@@ -430,25 +440,65 @@ struct Unit {
     // drain here (rare path) so the per-tile readlane below needs no wait
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
   }
+  // Load the facts of sequence bp + 1 (split mode only: in unsplit mode a
+  // unit is one sequence). Nothing waits here; the first use waits.
+  __device__ __forceinline__ void prefetch_next(const KernelArgs& a) {
+    nx_b = -1;
+    if (!NX || !a.md || bp + 1 >= a.p.batch) return;
+    nx_b = bp + 1;
+    const int lane = threadIdx.x & 63;
+    const int32_t* src = a.seqlens + nx_b;
+    if (lane == 1 || lane == 2) src = a.prefix + nx_b + (lane - 1);
+    if (lane == 3 || lane == 4) src = a.split_off + nx_b + (lane - 3);
+    if (a.p.cu_q && (lane == 5 || lane == 6)) src = a.p.cu_q + nx_b + (lane - 5);
+    if (lane == 7) src = seq_first_unit + nx_b;
+    nx_facts = *src;
+    nx_pages = lane < a.p.max_pages ? a.block_table[(size_t)nx_b * a.p.max_pages + lane] : 0;
+  }
   // Make sequence bb (holding flattened tile f) the prefetch sequence.
   __device__ __forceinline__ void enter(const KernelArgs& a, int bb, int f) {
-    bp = uniform(bb);
-    bp_L = uniform(max(a.seqlens[bp], 0));
-    bp_tiles = (bp_L + kPage - 1) / kPage;
-    bp_qlen = seq_qlen(a.p, bp);
-    bp_qrow0 = seq_qrow0(a.p, bp);
-    bp_final = true;
-    bp_slot = 0;
-    if (a.md) {
-      bp_first = uniform(a.prefix[bp]);
-      bp_last = uniform(a.prefix[bp + 1]);
-      bp_final = uniform(a.split_off[bp + 1] - a.split_off[bp]) == 1;
-      bp_slot = uniform(a.split_off[bp] + (u - bp_first / payload));
+    bb = uniform(bb);
+    if (NX && bb == nx_b && f == uniform(__builtin_amdgcn_readlane(nx_facts, 1))) {
+      // entered at its first tile with its facts already loaded
+      bp = bb;
+      bp_L = max(uniform(__builtin_amdgcn_readlane(nx_facts, 0)), 0);
+      bp_tiles = (bp_L + kPage - 1) / kPage;
+      bp_first = f;
+      bp_last = uniform(__builtin_amdgcn_readlane(nx_facts, 2));
+      const int so0 = uniform(__builtin_amdgcn_readlane(nx_facts, 3));
+      const int so1 = uniform(__builtin_amdgcn_readlane(nx_facts, 4));
+      bp_final = so1 - so0 == 1;
+      bp_slot = so0 + (u - uniform(__builtin_amdgcn_readlane(nx_facts, 7)));
+      if (a.p.cu_q) {
+        const int c0 = uniform(__builtin_amdgcn_readlane(nx_facts, 5));
+        bp_qlen = uniform(__builtin_amdgcn_readlane(nx_facts, 6)) - c0;
+        bp_qrow0 = c0 * a.p.num_heads;
+      } else {
+        bp_qlen = a.p.q_len;
+        bp_qrow0 = bp * a.p.rows;
+      }
+      pc_t0 = 0;
+      page_cache = (int)(threadIdx.x & 63) < bp_tiles ? nx_pages : 0;
     } else {
-      bp_first = 0;
-      bp_last = f_end;
+      bp = bb;
+      bp_L = uniform(max(a.seqlens[bp], 0));
+      bp_tiles = (bp_L + kPage - 1) / kPage;
+      bp_qlen = seq_qlen(a.p, bp);
+      bp_qrow0 = seq_qrow0(a.p, bp);
+      bp_final = true;
+      bp_slot = 0;
+      if (a.md) {
+        bp_first = uniform(a.prefix[bp]);
+        bp_last = uniform(a.prefix[bp + 1]);
+        bp_final = uniform(a.split_off[bp + 1] - a.split_off[bp]) == 1;
+        bp_slot = uniform(a.split_off[bp] + (u - seq_first_unit[bp]));
+      } else {
+        bp_first = 0;
+        bp_last = f_end;
+      }
+      load_pages(a, f - bp_first);
     }
-    load_pages(a, f - bp_first);
+    if (bp_last < f_end) prefetch_next(a);
   }
   // Scalar facts of flattened tile f and the plan of its loads into `dst`.
   template <class Dma>
@@ -456,7 +506,10 @@ struct Unit {
                                               LDS_AS float* sdst, int tid, Dma& dma) {
     if (f >= bp_last) {
       int bb = bp + 1;
-      while (a.prefix[bb + 1] <= f) ++bb;   // skip sequences without tiles
+      // the prefetched sequence holds tile f unless sequences without tiles
+      // come between: then walk the prefix
+      if (!(NX && bb == nx_b && uniform(__builtin_amdgcn_readlane(nx_facts, 2)) > f))
+        while (a.prefix[bb + 1] <= f) ++bb;
       enter(a, bb, f);
     }
     TileInfo ti;
@@ -477,6 +530,7 @@ struct Unit {
     return ti;
   }
 };
+using Unit = UnitT<true>;
 
 // O = 0, LSE = -inf for rows [r0, r1) of an empty sequence (unsplit mode).
 // Called by waves 0..nwaves-1 of the block.
@@ -1266,6 +1320,20 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   if (row0 < next.rows) dma_all(dma);
 
   // cur: tile computed in this step; nxt: where the next tile's loads go
+  // query rows of this wave's row into registers (no wait: the first use
+  // waits); issued at a sequence's first tile, or right after the QK of the
+  // previous sequence's last tile when both are in the unit (q_ready)
+  bool q_ready = false;
+  auto load_q = [&](const TileInfo& tq) {
+    const int rr = row_qk < tq.rows ? row_qk : max(tq.rows - 1, 0);
+    const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(tq.qrow0 + rr, p.q_rows - 1) * kDqk);
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      bf16x8 v = qrow[36 * fh + 2 * c + h];
+      qreg[c] = row_qk < tq.rows ? v : bf16x8{};
+    }
+  };
+
   auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
     const TileInfo ti = next;
     const int t = ti.t, L = ti.L;
@@ -1273,12 +1341,8 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
     if (ti.first && !skip) {
       const int rr = row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0);
-      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) {
-        bf16x8 v = qrow[36 * fh + 2 * c + h];
-        qreg[c] = row_qk < ti.rows ? v : bf16x8{};
-      }
+      if (!q_ready) load_q(ti);
+      q_ready = false;
       // O and l restart through the rescale below (alpha = 0), so the
       // accumulators are never reset outside the one rescale path
       m_run[0] = m_run[1] = -INFINITY;
@@ -1320,6 +1384,11 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     };
     if (load_next) qk(std::true_type{});
     else qk(std::false_type{});
+    // the next tile starts a sequence of this unit: its query rows now (qreg is free)
+    if (ti.last && more && row0 < next.rows) {
+      load_q(next);
+      q_ready = true;
+    }
 
     // ---- add the two feature halves: keep registers 8fh..8fh+7 (keys
     //      16kq + 0..15), give registers 8(1-fh).. to the partner. fh is
@@ -1630,7 +1699,7 @@ void decode_kernel_q8(DecodeParams p_, const int32_t* __restrict__ md_, const in
   const int row_qk = row0 + rs;
   const int u = wc.unit;
 
-  Unit unit;
+  UnitT<false> unit;
   if (!unit.init(a, u)) {
     if (!a.md) write_empty(p, unit.b0, row0, row0 + ROWS_WG, kThreadsX / 64);
     return;
@@ -1958,7 +2027,7 @@ void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const in
   const int row_qk = row0 + 32 * rh + n;
   const int u = wc.unit;
 
-  Unit unit;
+  UnitT<false> unit;
   if (!unit.init(a, u)) {
     if (!a.md) write_empty(p, unit.b0, row0, row0 + ROWS_WG, kThreadsX / 64);
     return;
@@ -2008,6 +2077,20 @@ void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const in
 
   // cur: E4M3 tile (codes, then the 64 scales) of this step; nxt: where the
   // next tile's loads go
+  // query rows of this wave's row into registers (no wait: the first use
+  // waits); issued at a sequence's first tile, or right after the QK of the
+  // previous sequence's last tile when both are in the unit (q_ready)
+  bool q_ready = false;
+  auto load_q = [&](const TileInfo& tq) {
+    const int rr = row_qk < tq.rows ? row_qk : max(tq.rows - 1, 0);
+    const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(tq.qrow0 + rr, p.q_rows - 1) * kDqk);
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      bf16x8 v = qrow[36 * fh + 4 * (c >> 1) + 2 * h + (c & 1)];
+      qreg[c] = row_qk < tq.rows ? v : bf16x8{};
+    }
+  };
+
   auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
     const LDS_AS float* const sbc = (const LDS_AS float*)(cur + kFp8TileBytes);
     const TileInfo ti = next;
@@ -2016,12 +2099,8 @@ void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const in
 
     if (ti.first && !skip) {
       const int rr = row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0);
-      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) {
-        bf16x8 v = qrow[36 * fh + 4 * (c >> 1) + 2 * h + (c & 1)];
-        qreg[c] = row_qk < ti.rows ? v : bf16x8{};
-      }
+      if (!q_ready) load_q(ti);
+      q_ready = false;
       // O and l restart through the rescale below (alpha = 0), so the
       // accumulators are never reset outside the one rescale path
       m_run[0] = m_run[1] = -INFINITY;
@@ -2068,6 +2147,11 @@ void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const in
     };
     if (load_next) qk(std::true_type{});
     else qk(std::false_type{});
+    // the next tile starts a sequence of this unit: its query rows now (qreg is free)
+    if (ti.last && more && row0 < next.rows) {
+      load_q(next);
+      q_ready = true;
+    }
 
     // ---- add the two feature halves: keep registers 8fh..8fh+7 (keys
     //      16kq + 0..15), give registers 8(1-fh).. to the partner. fh is
@@ -2247,105 +2331,142 @@ void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const in
 // header: equal tile counts per unit over the flattened (sequence, tile) space.
 // ---------------------------------------------------------------------------
 
-// Exclusive prefix sum over the 1024 threads of the block; *total gets the sum.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
+// Exclusive prefix sums of two values over the 1024 threads of the block;
+// *total gets the sums. It communicates through LDS only.
+__device__ __forceinline__ int2 block_exclusive_scan2(int2 v, int* wave_tot, int2* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+  int2 x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
+    const int yx = __shfl_up(x.x, d), yy = __shfl_up(x.y, d);
+    if (lane >= d) {
+      x.x += yx;
+      x.y += yy;
+    }
   }
-  if (lane == 63) wave_tot[wave] = x;
-  __syncthreads();
+  if (lane == 63) {
+    wave_tot[wave] = x.x;
+    wave_tot[16 + wave] = x.y;
+  }
+  lds_barrier();
   if (wave == 0) {
-    int t = lane < 16 ? wave_tot[lane] : 0;
+    int tx = lane < 16 ? wave_tot[lane] : 0, ty = lane < 16 ? wave_tot[16 + lane] : 0;
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) {
-      const int y = __shfl_up(t, d);
-      if (lane >= d) t += y;
+      const int yx = __shfl_up(tx, d), yy = __shfl_up(ty, d);
+      if (lane >= d) {
+        tx += yx;
+        ty += yy;
+      }
     }
-    if (lane < 16) wave_tot[16 + lane] = t;   // inclusive per-wave offsets
+    if (lane < 16) {
+      wave_tot[32 + lane] = tx;   // inclusive per-wave offsets
+      wave_tot[48 + lane] = ty;
+    }
   }
-  __syncthreads();
-  const int base = wave ? wave_tot[16 + wave - 1] : 0;
-  if (total) *total = wave_tot[31];
-  const int r = base + x - v;
-  __syncthreads();
+  lds_barrier();
+  const int2 base = wave ? make_int2(wave_tot[32 + wave - 1], wave_tot[48 + wave - 1]) : make_int2(0, 0);
+  if (total) *total = make_int2(wave_tot[47], wave_tot[63]);
+  const int2 r = make_int2(base.x + x.x - v.x, base.y + x.y - v.y);
+  lds_barrier();
   return r;
 }
 
+// The split schedule in closed form. On the weighted line a sequence with
+// tiles occupies [wpre_b, wpre_b + c + T_b): c start positions, then its
+// tiles; the tile at position p belongs to unit floor(p / payload). So a
+// sequence's pieces are the units floor((wpre_b + c) / payload) ..
+// floor((wpre_b + c + T_b - 1) / payload), the units starting inside its
+// range start at its first tile or at the tile their position names, and a
+// sequence shares its first unit with the previous sequence with tiles iff
+// position wpre_b - 1 (that sequence's last tile) lies in the same unit.
+// One workgroup; sequences are split evenly over the threads.
 __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, int B, int units,
                                                         int min_tiles, int32_t* md) {
-  __shared__ int wave_tot[32];
+  __shared__ int wave_tot[64];
   const int tid = threadIdx.x;
   const int per = (B + 1023) / 1024;
   const int lo = min(tid * per, B), hi = min(lo + per, B);
+  constexpr int c = kSeqCostTiles;
   int32_t* prefix = md + MD_HEADER;
   int32_t* split_off = prefix + B + 1;
   int32_t* unit_seq = split_off + B + 1;
+  int32_t* unit_begin = md + md_unit_begin(B, units);
+  int32_t* first_unit = md + md_seq_first_unit(B, units);
 
   auto tiles = [&](int bb) { return (max(seqlens[bb], 0) + kPage - 1) / kPage; };
 
-  int acc = 0;
-  for (int bb = lo; bb < hi; ++bb) acc += tiles(bb);
-  int T = 0;
-  int run = block_exclusive_scan(acc, wave_tot, &T);
-  const int payload = max(max((T + units - 1) / units, min_tiles), 1);
+  // tile prefix and weighted prefix
+  int2 acc = make_int2(0, 0);
   for (int bb = lo; bb < hi; ++bb) {
-    prefix[bb] = run;
-    run += tiles(bb);
+    const int t = tiles(bb);
+    acc.x += t;
+    acc.y += t ? t + c : 0;
   }
-  if (tid == 0) prefix[B] = T;
+  int2 tot;
+  const int2 run = block_exclusive_scan2(acc, wave_tot, &tot);
+  const int T = tot.x, W = tot.y;
+  const int payload = max(max((W + units - 1) / units, min_tiles), 1);
 
-  acc = 0;
-  for (int bb = lo; bb < hi; ++bb) {
-    const int tb = tiles(bb);
-    const int pb = prefix[bb];
-    acc += tb ? ((pb + tb - 1) / payload - pb / payload + 1) : 0;
-  }
-  int total_partials = 0;
-  run = block_exclusive_scan(acc, wave_tot, &total_partials);
-  for (int bb = lo; bb < hi; ++bb) {
-    split_off[bb] = run;
-    const int tb = tiles(bb);
-    const int pb = prefix[bb];
-    run += tb ? ((pb + tb - 1) / payload - pb / payload + 1) : 0;
-  }
-  if (tid == 0) split_off[B] = total_partials;
-  __syncthreads();   // prefix[] complete before the searches below
-
-  for (int uu = tid; uu < units; uu += 1024) {
-    const long long f = (long long)uu * payload;
-    int res = B;
-    if (f < T) {
-      int lo2 = 0, hi2 = B;  // last bb with prefix[bb] <= f
-      while (hi2 - lo2 > 1) {
-        const int mid = (lo2 + hi2) >> 1;
-        if (prefix[mid] <= f) lo2 = mid; else hi2 = mid;
+  // pieces of each sequence, the units starting in it, and the first units
+  // shared with the previous sequence
+  auto pieces = [&](int wp, int t) { return t ? (wp + c + t - 1) / payload - (wp + c) / payload + 1 : 0; };
+  int2 acc2 = make_int2(0, 0);
+  {
+    int tp = run.x, wp = run.y;
+    for (int bb = lo; bb < hi; ++bb) {
+      const int t = tiles(bb);
+      prefix[bb] = tp;
+      first_unit[bb] = t ? (wp + c) / payload : 0;
+      if (t) {
+        acc2.x += pieces(wp, t);
+        acc2.y += (wp > 0 && (wp - 1) / payload == (wp + c) / payload) ? 1 : 0;
+        for (long long u = ((long long)wp + payload - 1) / payload; u * payload < (long long)wp + c + t; ++u) {
+          unit_begin[u] = tp + (int)max(0LL, u * payload - wp - c);
+          unit_seq[u] = bb;
+        }
       }
-      res = lo2;
+      tp += t;
+      wp += t ? t + c : 0;
     }
-    unit_seq[uu] = res;
+  }
+  int2 tot2;
+  const int2 run2 = block_exclusive_scan2(acc2, wave_tot, &tot2);
+  {
+    int so = run2.x, wp = run.y;
+    for (int bb = lo; bb < hi; ++bb) {
+      const int t = tiles(bb);
+      split_off[bb] = so;
+      so += pieces(wp, t);
+      wp += t ? t + c : 0;
+    }
+  }
+  // units past the weighted line start at T and hold no tile
+  for (int uu = tid; uu <= units; uu += 1024) {
+    if ((long long)uu * payload >= W) {
+      unit_begin[uu] = T;
+      if (uu < units) unit_seq[uu] = B;
+    }
   }
   if (tid == 0) {
+    prefix[B] = T;
+    split_off[B] = tot2.x;
     md[MD_MAGIC] = kMdMagic;
     md[MD_BATCH] = B;
     md[MD_UNITS] = units;
     md[MD_PAYLOAD] = payload;
-    md[MD_TOTAL_PARTIALS] = total_partials;
-    md[MD_UNITS_USED] = T ? (T + payload - 1) / payload : 0;
-    md[6] = 0;
+    md[MD_TOTAL_PARTIALS] = tot2.x;
+    md[MD_UNITS_USED] = tot2.x - tot2.y;
+    md[MD_SEQ_COST] = c;
     md[7] = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
 // LSE merge of partials: one workgroup per (sequence, pair of rows), 128
-// threads x 4 features per row. One pass gives the max and the rescaled sum of
-// the partial LSEs; a second pass accumulates the weighted partial outputs,
-// four partials in flight per step. A partial with LSE -inf weighs nothing and
-// its values are not used (they may be anything, NaN included).
+// threads x 4 features per row, one online pass over the partials (eight in
+// flight per step). A partial with LSE -inf weighs nothing and its values are
+// not used (they may be anything, NaN included).
 // md (nullable): the decode's metadata; the merge does nothing unless it was
 // built for this batch and num_units (as the decode kernels check).
 // ---------------------------------------------------------------------------
@@ -2376,57 +2497,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const float* po = part_out + ((size_t)k0 * R + r) * kDv + d;
   const size_t lstride = R, ostride = (size_t)R * kDv;
 
+  // One online pass: partial k enters with weight e^(LSE_k - M) against the
+  // running max M; the loads of kU partials are issued together, so a row
+  // with n partials costs about n / kU memory round trips. A partial whose
+  // LSE is -inf is skipped and its values never enter the sums.
+  constexpr int kU = 8;
   float M = -INFINITY, S = 0.f;
-  int k = 0;
-  for (; k + 4 <= n; k += 4) {
-    float v[4];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < n; k += kU) {
+    float v[kU];
+    f32x4 ov[kU];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = pl[(k + j) * lstride];
+    for (int j = 0; j < kU; ++j) {
+      const bool in = k + j < n;
+      v[j] = in ? pl[(k + j) * lstride] : -INFINITY;
+      ov[j] = in ? *(const f32x4*)(po + (k + j) * ostride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kU; ++j) {
       if (v[j] == -INFINITY) continue;
       if (v[j] > M) {
-        S = S * expf(M - v[j]) + 1.f;
+        const float c = expf(M - v[j]);   // 0 while M is -inf
+        S = S * c + 1.f;
+        acc = acc * c + ov[j];
         M = v[j];
       } else {
-        S += expf(v[j] - M);
+        const float wgt = expf(v[j] - M);
+        S += wgt;
+        acc += wgt * ov[j];
       }
     }
   }
-  for (; k < n; ++k) {
-    const float v = pl[k * lstride];
-    if (v == -INFINITY) continue;
-    if (v > M) {
-      S = S * expf(M - v) + 1.f;
-      M = v;
-    } else {
-      S += expf(v - M);
-    }
-  }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float lse_v = -INFINITY;
-  if (M != -INFINITY) {
-    lse_v = M + logf(S);
-    k = 0;
-    for (; k + 4 <= n; k += 4) {
-      float wk[4];
-      f32x4 ov[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = pl[(k + j) * lstride];
-        wk[j] = v == -INFINITY ? 0.f : expf(v - lse_v);
-        ov[j] = *(const f32x4*)(po + (k + j) * ostride);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (wk[j] != 0.f) acc += wk[j] * ov[j];
-    }
-    for (; k < n; ++k) {
-      const float v = pl[k * lstride];
-      if (v == -INFINITY) continue;
-      acc += expf(v - lse_v) * *(const f32x4*)(po + k * ostride);
-    }
-  }
+  const bool live = M != -INFINITY;
+  const float lse_v = live ? M + logf(S) : -INFINITY;
+  acc *= live ? 1.f / S : 0.f;
   *(f32x4*)(out + (out_row0 + r) * kDv + d) = acc;
   if (d == 0) lse[out_row0 + r] = lse_v;
 }

@@ -113,6 +113,8 @@ def test_split_and_unsplit_agree():
 @pytest.mark.parametrize("lens,units,mt", [
     ([256], 256, 0), ([4096] * 7, 16, 0), ([1, 63, 64, 65, 0, 700], 5, 1), ([0, 0], 4, 8),
     ([65536, 512, 3000, 70], 64, 0), ([130] * 3, 1000, 1), (list(range(0, 5000, 37)), 250, 0),
+    # too large for the kernel's LDS copies (2B + U + 2 > 16384 words): searches read the metadata
+    ([int(x) for x in np.random.default_rng(5).integers(0, 3000, 8000)], 400, 0),
 ])
 def test_metadata_matches_oracle_schedule(lens, units, mt):
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
@@ -120,19 +122,14 @@ def test_metadata_matches_oracle_schedule(lens, units, mt):
     md = plan.metadata.cpu().numpy()
     sch = oracle.split_schedule(lens, units, mt if mt else 8)
     B = len(lens)
-    assert md[0] == 0x4D4C4131 and md[1] == B and md[2] == units
+    assert md[0] == 0x4D4C4132 and md[1] == B and md[2] == units and md[6] == 3
     assert md[3] == sch["payload"] and md[4] == sch["total_partials"] and md[5] == sch["units_used"]
     assert list(md[8:8 + B + 1]) == sch["prefix"]
     assert list(md[9 + B:10 + 2 * B]) == sch["split_offset"]
-    # first sequence of each unit: the one holding flattened tile u * payload
-    first = md[10 + 2 * B:10 + 2 * B + units]
-    for u in range(units):
-        f = u * sch["payload"]
-        if f >= sch["prefix"][-1]:
-            assert first[u] == B
-        else:
-            b = max(i for i in range(B) if sch["prefix"][i] <= f)
-            assert first[u] == b and sch["prefix"][b + 1] > f
+    base = 10 + 2 * B
+    assert list(md[base:base + units]) == sch["unit_first_seq"]
+    assert list(md[base + units:base + 2 * units + 1]) == sch["unit_begin"]
+    assert list(md[base + 2 * units + 1:base + 2 * units + 1 + B]) == sch["seq_first_unit"]
 
 
 @pytest.mark.parametrize("R", [16, 256])

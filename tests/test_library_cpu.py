@@ -42,7 +42,7 @@ def test_abi_and_status_strings(lib):
 
 
 def test_sizes(lib):
-    assert lib.mla_metadata_bytes(64, 256) == 4 * (8 + 2 * 65 + 256)
+    assert lib.mla_metadata_bytes(64, 256) == 4 * (8 + 2 * 65 + 256 + 257 + 64)
     # (B + units) partial slots x rows x (512 + 1) fp32
     assert lib.mla_workspace_bytes(64, 1, 16, 256) == 320 * 16 * 512 * 4 + ((320 * 16 * 4 + 255) // 256) * 256
     assert lib.mla_metadata_bytes(0, 4) == 0

@@ -355,36 +355,65 @@ def test_fp8_rows_match_torch_dequant():
 
 # ----------------------------------------------------------------- schedule
 
-def _walk_schedule(seqlens, num_units, min_tiles):
-    """Brute force: hand tiles out one at a time, payload per unit."""
-    T_b = [-(-int(x) // 64) for x in seqlens]
-    T = sum(T_b)
-    payload = max(-(-T // max(num_units, 1)), min_tiles, 1)
-    owner = []   # (unit) per flattened tile
-    for f in range(T):
-        owner.append(f // payload)
+def _walk_schedule(seqlens, num_units, min_tiles, seq_cost=3):
+    """Brute force: lay the sequences on a weighted line tile by tile (each
+    sequence with tiles first takes seq_cost empty positions), and give every
+    tile to the unit floor(position / payload)."""
+    T_b = [-(-max(int(x), 0) // 64) for x in seqlens]
+    W = sum(t + seq_cost for t in T_b if t)
+    payload = max(-(-W // max(num_units, 1)), min_tiles, 1)
+    owner = []   # unit of each flattened tile
+    pos = 0
+    for t in T_b:
+        if t:
+            pos += seq_cost
+        for _ in range(t):
+            owner.append(pos // payload)
+            pos += 1
+    assert pos == W
     pieces = {}
     f = 0
     for b, t in enumerate(T_b):
-        units = sorted(set(owner[f:f + t]))
-        pieces[b] = units
+        pieces[b] = sorted(set(owner[f:f + t]))
         f += t
-    return payload, pieces
+    # a unit starts at its first tile; units without tiles start where the
+    # next tile owned by a later unit is (or at T)
+    begin = [next((i for i, o in enumerate(owner) if o >= u), len(owner)) for u in range(num_units + 1)]
+    return payload, pieces, begin, owner
 
 
 @pytest.mark.parametrize("seqlens,units,mt", [
     ([256], 256, 8), ([4096] * 7, 16, 8), ([1, 63, 64, 65, 0, 700], 5, 1),
     ([0, 0], 4, 8), ([65536, 512, 3000, 70], 64, 8), ([130] * 3, 1000, 1),
+    ([0, 512, 0, 0, 9000, 64, 0], 12, 1), ([700] * 40 + [65536], 128, 8),
 ])
 def test_split_schedule_matches_walk(seqlens, units, mt):
     sch = oracle.split_schedule(seqlens, units, mt)
-    payload, pieces = _walk_schedule(seqlens, units, mt)
+    payload, pieces, begin, owner = _walk_schedule(seqlens, units, mt)
     assert sch["payload"] == payload
+    assert sch["unit_begin"] == begin
     for b in range(len(seqlens)):
         assert sch["num_splits"][b] == len(pieces[b])
+        if pieces[b]:
+            assert sch["seq_first_unit"][b] == pieces[b][0]
+            # pieces of a sequence sit in consecutive units
+            assert pieces[b] == list(range(pieces[b][0], pieces[b][-1] + 1))
     assert sch["total_partials"] == sum(len(p) for p in pieces.values())
-    T = sum(-(-x // 64) for x in seqlens)
-    assert sch["units_used"] == (-(-T // payload) if T else 0)
+    assert sch["units_used"] == len(set(owner))
+    assert max(owner, default=0) < units
+
+
+def test_split_schedule_balances_sequence_starts():
+    # many short sequences and one long one: with the start cost charged, no
+    # unit's cost (tiles + 3 per sequence start in it) exceeds the payload
+    seqlens = [600] * 30 + [65536]
+    sch = oracle.split_schedule(seqlens, 64, 1)
+    T_b = [-(-x // 64) for x in seqlens]
+    ub = sch["unit_begin"]
+    starts = set(sch["prefix"][b] for b in range(len(seqlens)) if T_b[b])
+    for u in range(64):
+        cost = (ub[u + 1] - ub[u]) + 3 * sum(1 for f in starts if ub[u] <= f < ub[u + 1])
+        assert cost <= sch["payload"] + 3
 
 
 def test_workload_generators_are_seeded_and_shaped():
