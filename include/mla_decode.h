@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 #define MLA_PAGE_TOKENS 64   /* tokens per cache page */
 #define MLA_D_QK 576         /* query / latent row width: 512 latent + 64 rope */
 #define MLA_D_V 512          /* value width: the first 512 entries of the row */
@@ -79,13 +79,14 @@ const char* mla_last_error(void);
  * issue #10157's overview; the cache is cut into partitions that are merged
  * afterwards in the Append Attention flags of the mhpq.cn article on PaddleNLP
  * inference flags). A sequence's start (its query rows, its epilogue, its
- * metadata) is charged as 3 tiles. With T_b = ceil(L_b/64), T = sum T_b, and
- * every sequence with tiles laid on a weighted line as 3 start positions then
- * its T_b tiles (W positions in all):
- *   payload = max(ceil(W / num_units), min_tiles_per_unit, 1)
- *   unit u starts at the tile of weighted position u*payload (a sequence's
- *   first tile if the position falls in its start, T past the end) and runs
- *   to the next unit's start; a unit may hold no tile.
+ * metadata) is charged as c tiles: c = 1 when q_len * num_heads <= 16 (the
+ * 16-row kernel), else c = 3 (the 64-row kernels). With T_b = ceil(L_b/64),
+ * T = sum T_b, and every sequence with tiles laid on a weighted line as c
+ * start positions then its T_b tiles (W positions in all):
+ *   U' = max(1, min(num_units, floor(W / min_tiles_per_unit)))
+ *   the line is cut at floor(u * W / U'), u = 0..U'; unit u < U' starts at
+ *   the tile its cut names (a sequence's first tile if the cut falls in its
+ *   start) and runs to the next unit's start; units u >= U' hold no tile.
  * A sequence touched by k > 1 units is computed as k partials and merged.
  *
  * mla_default_num_units: a unit count that fills the current device for this
@@ -102,6 +103,9 @@ size_t mla_workspace_bytes(int batch, int q_len, int num_heads, int num_units);
  * mla_get_split_metadata: build the split schedule on the device.
  *   cache_seqlens  device int32 [batch], L_b >= 0 (negative values count as 0)
  *   batch          >= 1
+ *   q_len, num_heads  >= 1, the shape of the decode calls that will use the
+ *                  metadata (it selects the start cost c; any shape may still
+ *                  use the metadata, only the balance differs)
  *   num_units      >= 1, the number of work units (see above)
  *   min_tiles_per_unit  >= 0; 0 selects the default (8)
  *   metadata       device buffer of >= mla_metadata_bytes(batch, num_units)
@@ -110,8 +114,8 @@ size_t mla_workspace_bytes(int batch, int q_len, int num_heads, int num_units);
  * One small kernel, stream-ordered. Reuse the metadata for every layer of a
  * decode step that has the same cache_seqlens.
  */
-int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int num_units,
-                           int min_tiles_per_unit, void* metadata, size_t metadata_bytes,
+int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
+                           int num_units, int min_tiles_per_unit, void* metadata, size_t metadata_bytes,
                            void* stream);
 
 /*

@@ -57,7 +57,7 @@ def load_library():
         "mla_default_num_units": (c_int, [c_int, c_int, c_int]),
         "mla_metadata_bytes": (c_size, [c_int, c_int]),
         "mla_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int]),
-        "mla_get_split_metadata": (c_int, [vp, c_int, c_int, c_int, vp, c_size, vp]),
+        "mla_get_split_metadata": (c_int, [vp, c_int, c_int, c_int, c_int, c_int, vp, c_size, vp]),
         "mla_decode_fwd": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
                                    ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
         "mla_decode_fwd_fp8mma": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
@@ -151,8 +151,8 @@ def get_split_metadata(cache_seqlens: torch.Tensor, q_len: int, num_heads: int,
     wbytes = lib.mla_workspace_bytes(batch, q_len, num_heads, num_units)
     if workspace is None:
         workspace = torch.empty(wbytes, dtype=torch.uint8, device=cache_seqlens.device)
-    _check(lib.mla_get_split_metadata(_ptr(cache_seqlens), batch, num_units, min_tiles_per_unit,
-                                      _ptr(metadata), metadata.numel() * 4, _stream()),
+    _check(lib.mla_get_split_metadata(_ptr(cache_seqlens), batch, q_len, num_heads, num_units,
+                                      min_tiles_per_unit, _ptr(metadata), metadata.numel() * 4, _stream()),
            "mla_get_split_metadata")
     return SplitPlan(metadata, num_units, batch, q_len, num_heads, workspace)
 

@@ -132,11 +132,13 @@ size_t mla_workspace_bytes(int batch, int q_len, int num_heads, int num_units) {
   return workspace_need(batch, q_len, num_heads, num_units);
 }
 
-int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int num_units,
-                           int min_tiles_per_unit, void* metadata, size_t metadata_bytes,
+int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
+                           int num_units, int min_tiles_per_unit, void* metadata, size_t metadata_bytes,
                            void* stream) {
   if (!cache_seqlens || !metadata) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (q_len < 1 || num_heads < 1)
+    return fail(MLA_ERR_INVALID_ARG, "q_len and num_heads must be >= 1 (got %d, %d)", q_len, num_heads);
   if (num_units < 1) return fail(MLA_ERR_INVALID_ARG, "num_units must be >= 1 (got %d)", num_units);
   if (min_tiles_per_unit < 0)
     return fail(MLA_ERR_INVALID_ARG, "min_tiles_per_unit must be >= 0 (got %d)", min_tiles_per_unit);
@@ -149,7 +151,10 @@ int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int num_unit
   int st = device_info(&d);
   if (st != MLA_OK) return st;
   const int mt = min_tiles_per_unit == 0 ? mla::kDefaultMinTiles : min_tiles_per_unit;
-  hipError_t e = mla::launch_metadata(cache_seqlens, batch, num_units, mt, (int32_t*)metadata,
+  // a sequence's start costs what it does in the kernel this shape selects
+  const int rows = q_len * num_heads;
+  const int cost = mla::variant_for(rows) == mla::VAR_NARROW16 ? mla::kSeqCostNarrow : mla::kSeqCostWide;
+  hipError_t e = mla::launch_metadata(cache_seqlens, batch, num_units, mt, cost, (int32_t*)metadata,
                                       (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "metadata kernel launch: %s", hipGetErrorString(e));
   return ok();

@@ -12,7 +12,7 @@ constexpr int kDv = 512;          // value = first 512 entries of the row
 constexpr int kThreads = 256;     // 4 waves of 64 lanes per workgroup
 
 // Metadata layout (int32 words, device):
-//   [0] magic  [1] batch  [2] num_units  [3] payload (weighted)  [4] total_partials
+//   [0] magic  [1] batch  [2] num_units  [3] units cut (U')  [4] total_partials
 //   [5] units_used  [6] sequence start cost (tiles)  [7] reserved
 //   [8 .. 8+B]                 prefix: first flattened tile of each sequence [B+1]
 //   [9+B .. 9+2B]              split_offset: first partial slot of each sequence [B+1]
@@ -20,12 +20,14 @@ constexpr int kThreads = 256;     // 4 waves of 64 lanes per workgroup
 //   [10+2B+U .. 11+2B+2U)      unit_begin: first flattened tile of each unit [U+1]
 //   [11+2B+2U .. 11+3B+2U)     seq_first_unit: unit holding each sequence's first tile
 constexpr int kMdMagic = 0x4D4C4132;  // 'MLA2'
-enum { MD_MAGIC = 0, MD_BATCH = 1, MD_UNITS = 2, MD_PAYLOAD = 3, MD_TOTAL_PARTIALS = 4,
+enum { MD_MAGIC = 0, MD_BATCH = 1, MD_UNITS = 2, MD_UNITS_CUT = 3, MD_TOTAL_PARTIALS = 4,
        MD_UNITS_USED = 5, MD_SEQ_COST = 6, MD_HEADER = 8 };
 constexpr int kDefaultMinTiles = 8;
 // A sequence's start (query rows, epilogue, partial write, metadata) costs
 // about as much as this many 64-token tiles; the split schedule charges it.
-constexpr int kSeqCostTiles = 3;
+// Measured: ~1.4 tiles in the 16-row kernel, ~3.5 in the 64-row kernels.
+constexpr int kSeqCostNarrow = 1;
+constexpr int kSeqCostWide = 3;
 
 inline size_t metadata_words(int batch, int units) {
   return (size_t)MD_HEADER + 3 * (size_t)batch + 2 + 2 * (size_t)units + 1;
@@ -66,7 +68,7 @@ int variant_rows(int variant);
 // ev_start / ev_stop: optional events recorded by the kernel dispatch itself.
 hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s,
                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
-hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles,
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles, int seq_cost,
                            int32_t* md, hipStream_t s);
 hipError_t launch_append(const uint16_t* latent, int batch, int new_tokens, const int32_t* block_table,
                          int max_pages, const int32_t* seqlens, uint8_t* kv, float* kv_scale, int fp8,

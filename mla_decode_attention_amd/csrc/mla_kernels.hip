@@ -2374,20 +2374,20 @@ __device__ __forceinline__ int2 block_exclusive_scan2(int2 v, int* wave_tot, int
 
 // The split schedule in closed form. On the weighted line a sequence with
 // tiles occupies [wpre_b, wpre_b + c + T_b): c start positions, then its
-// tiles; the tile at position p belongs to unit floor(p / payload). So a
-// sequence's pieces are the units floor((wpre_b + c) / payload) ..
-// floor((wpre_b + c + T_b - 1) / payload), the units starting inside its
-// range start at its first tile or at the tile their position names, and a
-// sequence shares its first unit with the previous sequence with tiles iff
-// position wpre_b - 1 (that sequence's last tile) lies in the same unit.
-// One workgroup; sequences are split evenly over the threads.
+// tiles. The line is cut at floor(u * W / U') for u = 0..U', U' =
+// max(1, min(units, floor(W / min_tiles))) (units past U' are empty), so the
+// tile at position p belongs to unit owner(p) = floor(((p + 1) U' - 1) / W).
+// A sequence's pieces are the units owner(wpre_b + c) .. owner(wpre_b + c +
+// T_b - 1); the units starting inside its range start at its first tile or at
+// the tile their cut names; and it shares its first unit with the previous
+// sequence with tiles iff owner(wpre_b - 1) (that sequence's last tile) is the
+// same unit. One workgroup; sequences are split evenly over the threads.
 __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, int B, int units,
-                                                        int min_tiles, int32_t* md) {
+                                                        int min_tiles, int c, int32_t* md) {
   __shared__ int wave_tot[64];
   const int tid = threadIdx.x;
   const int per = (B + 1023) / 1024;
   const int lo = min(tid * per, B), hi = min(lo + per, B);
-  constexpr int c = kSeqCostTiles;
   int32_t* prefix = md + MD_HEADER;
   int32_t* split_off = prefix + B + 1;
   int32_t* unit_seq = split_off + B + 1;
@@ -2406,23 +2406,27 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
   int2 tot;
   const int2 run = block_exclusive_scan2(acc, wave_tot, &tot);
   const int T = tot.x, W = tot.y;
-  const int payload = max(max((W + units - 1) / units, min_tiles), 1);
+  const int ucut = max(1, min(units, W / max(min_tiles, 1)));
+  const long long Wl = W, Ul = ucut;
+  auto owner = [&](long long pos) { return (int)(((pos + 1) * Ul - 1) / Wl); };
+  auto cut = [&](long long u) { return u * Wl / Ul; };
 
   // pieces of each sequence, the units starting in it, and the first units
   // shared with the previous sequence
-  auto pieces = [&](int wp, int t) { return t ? (wp + c + t - 1) / payload - (wp + c) / payload + 1 : 0; };
+  auto pieces = [&](int wp, int t) { return t ? owner(wp + c + t - 1) - owner(wp + c) + 1 : 0; };
   int2 acc2 = make_int2(0, 0);
   {
     int tp = run.x, wp = run.y;
     for (int bb = lo; bb < hi; ++bb) {
       const int t = tiles(bb);
       prefix[bb] = tp;
-      first_unit[bb] = t ? (wp + c) / payload : 0;
+      first_unit[bb] = t ? owner(wp + c) : 0;
       if (t) {
         acc2.x += pieces(wp, t);
-        acc2.y += (wp > 0 && (wp - 1) / payload == (wp + c) / payload) ? 1 : 0;
-        for (long long u = ((long long)wp + payload - 1) / payload; u * payload < (long long)wp + c + t; ++u) {
-          unit_begin[u] = tp + (int)max(0LL, u * payload - wp - c);
+        acc2.y += (wp > 0 && owner(wp - 1) == owner(wp + c)) ? 1 : 0;
+        // units u with wp <= cut(u) < wp + c + t
+        for (long long u = ((long long)wp * Ul + Wl - 1) / Wl; cut(u) < (long long)wp + c + t; ++u) {
+          unit_begin[u] = tp + (int)max(0LL, cut(u) - wp - c);
           unit_seq[u] = bb;
         }
       }
@@ -2441,9 +2445,9 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
       wp += t ? t + c : 0;
     }
   }
-  // units past the weighted line start at T and hold no tile
+  // units from the last cut on start at T and hold no tile
   for (int uu = tid; uu <= units; uu += 1024) {
-    if ((long long)uu * payload >= W) {
+    if (W == 0 || uu >= ucut) {
       unit_begin[uu] = T;
       if (uu < units) unit_seq[uu] = B;
     }
@@ -2454,7 +2458,7 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
     md[MD_MAGIC] = kMdMagic;
     md[MD_BATCH] = B;
     md[MD_UNITS] = units;
-    md[MD_PAYLOAD] = payload;
+    md[MD_UNITS_CUT] = ucut;
     md[MD_TOTAL_PARTIALS] = tot2.x;
     md[MD_UNITS_USED] = tot2.x - tot2.y;
     md[MD_SEQ_COST] = c;
@@ -2576,9 +2580,10 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
   return hipGetLastError();
 }
 
-hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles, int32_t* md,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(1024), 0, s, seqlens, batch, units, min_tiles, md);
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles, int seq_cost,
+                           int32_t* md, hipStream_t s) {
+  hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(1024), 0, s, seqlens, batch, units, min_tiles, seq_cost,
+                     md);
   return hipGetLastError();
 }
 

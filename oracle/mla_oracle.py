@@ -221,28 +221,27 @@ def mla_decode(q_bits, cache, block_table, seqlens, softmax_scale, kv_dtype="bf1
 # Split-KV schedule (integer work; the GPU scheduler must match it exactly).
 # --------------------------------------------------------------------------
 
-SEQ_COST_TILES = 3
-
-
-def split_schedule(seqlens, num_units, min_tiles_per_unit=8, seq_cost=SEQ_COST_TILES):
+def split_schedule(seqlens, num_units, min_tiles_per_unit=8, seq_cost=3):
     """Cut the flattened (sequence, 64-token tile) space into contiguous units
-    of about equal cost, a sequence's start costing `seq_cost` tiles.
+    of about equal cost, a sequence's start costing `seq_cost` tiles (the
+    library charges 1 for shapes of at most 16 rows, 3 above).
 
     T_b = ceil(L_b / 64) tiles per sequence, prefix[b] = sum of T before b,
     T = prefix[B]. On a weighted line, a sequence with tiles occupies
     seq_cost + T_b positions (its start cost, then its tiles), from
     wpre[b] = sum over b' < b of (seq_cost + T_b' if T_b' else 0); W is the
-    total. payload = max(ceil(W / num_units), min_tiles_per_unit, 1) (at
-    least 1). Unit u starts at the flattened tile of weighted position
-    u * payload: the tile that position names, or the sequence's first tile
-    when it falls in the start cost, or T past the end; unit u covers tiles
-    [unit_begin[u], unit_begin[u + 1]) and may be empty. A sequence whose tiles
-    fall in k units is split into k partials; the piece in unit u is split
-    number u - seq_first_unit[b], seq_first_unit[b] being the unit holding its
-    first tile. A sequence with no tiles has 0 partials.
+    total. With U' = max(1, min(num_units, floor(W / max(min_tiles, 1)))), the
+    line is cut at cut[u] = floor(u * W / U') for u = 0..U'. Unit u < U'
+    starts at the flattened tile its cut names: the tile at that position, or
+    the sequence's first tile when the cut falls in the start cost; unit u
+    covers tiles [unit_begin[u], unit_begin[u + 1]) and may be empty; units
+    u >= U' start at T and are empty. A sequence whose tiles fall in k units
+    is split into k partials; the piece in unit u is split number
+    u - seq_first_unit[b], seq_first_unit[b] being the unit holding its first
+    tile. A sequence with no tiles has 0 partials.
 
     Returns a dict of plain Python ints/lists:
-      payload, units_used (units with at least one tile), prefix [B+1],
+      units_cut (U'), units_used (units with at least one tile), prefix [B+1],
       num_splits [B], split_offset [B+1] (cumulative), total_partials,
       unit_begin [num_units + 1], unit_first_seq [num_units] (the sequence
       holding each unit's first tile, B past the end), seq_first_unit [B]
@@ -258,7 +257,7 @@ def split_schedule(seqlens, num_units, min_tiles_per_unit=8, seq_cost=SEQ_COST_T
         wpre.append(wpre[-1] + (seq_cost + t if t else 0))
     T, W = prefix[-1], wpre[-1]
     units = max(int(num_units), 1)
-    payload = max(-(-W // units), int(min_tiles_per_unit), 1)
+    ucut = max(1, min(units, W // max(int(min_tiles_per_unit), 1)))
 
     def tile_at(v):
         if v >= W:
@@ -266,7 +265,7 @@ def split_schedule(seqlens, num_units, min_tiles_per_unit=8, seq_cost=SEQ_COST_T
         b = max(i for i in range(B) if wpre[i] <= v and T_b[i] > 0)
         return prefix[b] + max(0, v - wpre[b] - seq_cost)
 
-    unit_begin = [tile_at(u * payload) for u in range(units + 1)]
+    unit_begin = [tile_at(u * W // ucut) if (u < ucut and W > 0) else T for u in range(units + 1)]
 
     def holder(f):   # the unit whose range holds tile f
         return max(u for u in range(units) if unit_begin[u] <= f)
@@ -288,7 +287,7 @@ def split_schedule(seqlens, num_units, min_tiles_per_unit=8, seq_cost=SEQ_COST_T
     for k in num_splits:
         split_offset.append(split_offset[-1] + k)
     units_used = sum(1 for u in range(units) if unit_begin[u] < unit_begin[u + 1])
-    return dict(payload=payload, units_used=units_used, prefix=prefix, num_splits=num_splits,
+    return dict(units_cut=ucut, units_used=units_used, prefix=prefix, num_splits=num_splits,
                 split_offset=split_offset, total_partials=split_offset[-1], unit_begin=unit_begin,
                 unit_first_seq=unit_first_seq, seq_first_unit=seq_first_unit)
 

@@ -113,17 +113,18 @@ def test_split_and_unsplit_agree():
 @pytest.mark.parametrize("lens,units,mt", [
     ([256], 256, 0), ([4096] * 7, 16, 0), ([1, 63, 64, 65, 0, 700], 5, 1), ([0, 0], 4, 8),
     ([65536, 512, 3000, 70], 64, 0), ([130] * 3, 1000, 1), (list(range(0, 5000, 37)), 250, 0),
-    # too large for the kernel's LDS copies (2B + U + 2 > 16384 words): searches read the metadata
+    # a large batch: 8000 sequences over 400 units, several sequences per thread
     ([int(x) for x in np.random.default_rng(5).integers(0, 3000, 8000)], 400, 0),
 ])
-def test_metadata_matches_oracle_schedule(lens, units, mt):
+@pytest.mark.parametrize("q_len,heads,cost", [(1, 16, 1), (2, 128, 3)])
+def test_metadata_matches_oracle_schedule(lens, units, mt, q_len, heads, cost):
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    plan = mla.get_split_metadata(sl, 1, 16, num_units=units, min_tiles_per_unit=mt)
+    plan = mla.get_split_metadata(sl, q_len, heads, num_units=units, min_tiles_per_unit=mt)
     md = plan.metadata.cpu().numpy()
-    sch = oracle.split_schedule(lens, units, mt if mt else 8)
+    sch = oracle.split_schedule(lens, units, mt if mt else 8, cost)
     B = len(lens)
-    assert md[0] == 0x4D4C4132 and md[1] == B and md[2] == units and md[6] == 3
-    assert md[3] == sch["payload"] and md[4] == sch["total_partials"] and md[5] == sch["units_used"]
+    assert md[0] == 0x4D4C4132 and md[1] == B and md[2] == units and md[6] == cost
+    assert md[3] == sch["units_cut"] and md[4] == sch["total_partials"] and md[5] == sch["units_used"]
     assert list(md[8:8 + B + 1]) == sch["prefix"]
     assert list(md[9 + B:10 + 2 * B]) == sch["split_offset"]
     base = 10 + 2 * B

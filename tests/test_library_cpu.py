@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_and_status_strings(lib):
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     assert lib.mla_status_string(0) == b"MLA_OK"
     assert lib.mla_status_string(3) == b"MLA_ERR_WORKSPACE"
     assert lib.mla_status_string(99) == b"MLA_ERR_UNKNOWN"
@@ -86,11 +86,13 @@ def test_decode_argument_errors(lib, kw, expect):
 
 def test_metadata_argument_errors(lib):
     f = lib.mla_get_split_metadata
-    assert f(None, 4, 8, 0, FAKE, 1 << 20, None) == INVALID
-    assert f(FAKE, 0, 8, 0, FAKE, 1 << 20, None) == INVALID
-    assert f(FAKE, 4, 0, 0, FAKE, 1 << 20, None) == INVALID
-    assert f(FAKE, 4, 8, -1, FAKE, 1 << 20, None) == INVALID
-    assert f(FAKE, 4, 8, 0, FAKE, 16, None) == WORKSPACE
+    assert f(None, 4, 1, 16, 8, 0, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 0, 1, 16, 8, 0, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 0, 16, 8, 0, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 1, 0, 8, 0, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 1, 16, 0, 0, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 1, 16, 8, -1, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 1, 16, 8, 0, FAKE, 16, None) == WORKSPACE
 
 
 def test_combine_argument_errors(lib):
