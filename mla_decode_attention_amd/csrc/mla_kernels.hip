@@ -2384,7 +2384,9 @@ __device__ __forceinline__ int2 block_exclusive_scan2(int2 v, int* wave_tot, int
 // same unit. One workgroup; sequences are split evenly over the threads.
 __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, int B, int units,
                                                         int min_tiles, int c, int32_t* md) {
+  constexpr int kLdsSeqs = 4096;   // batches up to this size place units by a search in LDS
   __shared__ int wave_tot[64];
+  __shared__ int s_wpre[kLdsSeqs + 1], s_prefix[kLdsSeqs + 1];
   const int tid = threadIdx.x;
   const int per = (B + 1023) / 1024;
   const int lo = min(tid * per, B), hi = min(lo + per, B);
@@ -2408,26 +2410,54 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
   const int T = tot.x, W = tot.y;
   const int ucut = max(1, min(units, W / max(min_tiles, 1)));
   const long long Wl = W, Ul = ucut;
-  auto owner = [&](long long pos) { return (int)(((pos + 1) * Ul - 1) / Wl); };
-  auto cut = [&](long long u) { return u * Wl / Ul; };
+  // 32-bit arithmetic when every product fits (W * U' < 2^31); 64-bit integer
+  // division is a long software routine
+  const bool fits32 = Wl * Ul < (1LL << 31);
+  auto owner = [&](long long pos) {
+    return fits32 ? (int)(((unsigned)(pos + 1) * (unsigned)ucut - 1u) / (unsigned)W)
+                  : (int)(((pos + 1) * Ul - 1) / Wl);
+  };
+  auto cut = [&](long long u) {
+    return fits32 ? (long long)((unsigned)u * (unsigned)W / (unsigned)ucut) : u * Wl / Ul;
+  };
+  const long long wq = W / ucut, wr = W % ucut;
 
   // pieces of each sequence, the units starting in it, and the first units
   // shared with the previous sequence
   auto pieces = [&](int wp, int t) { return t ? owner(wp + c + t - 1) - owner(wp + c) + 1 : 0; };
+  const bool lds_search = B <= kLdsSeqs;
   int2 acc2 = make_int2(0, 0);
   {
     int tp = run.x, wp = run.y;
     for (int bb = lo; bb < hi; ++bb) {
       const int t = tiles(bb);
       prefix[bb] = tp;
+      if (lds_search) {
+        s_prefix[bb] = tp;
+        s_wpre[bb] = wp;
+      }
       first_unit[bb] = t ? owner(wp + c) : 0;
       if (t) {
         acc2.x += pieces(wp, t);
         acc2.y += (wp > 0 && owner(wp - 1) == owner(wp + c)) ? 1 : 0;
+      }
+      if (t && !lds_search) {
         // units u with wp <= cut(u) < wp + c + t
-        for (long long u = ((long long)wp * Ul + Wl - 1) / Wl; cut(u) < (long long)wp + c + t; ++u) {
-          unit_begin[u] = tp + (int)max(0LL, cut(u) - wp - c);
+        // cut(u + 1) = cut(u) + W / U' + (1 when the remainder wraps): one
+        // division for the first unit, then adds
+        const long long u0 = fits32 ? (long long)(((unsigned)wp * (unsigned)ucut + (unsigned)W - 1u) / (unsigned)W)
+                                    : ((long long)wp * Ul + Wl - 1) / Wl;
+        long long cu = cut(u0);
+        long long rem = u0 * Wl - cu * Ul;
+        for (long long u = u0; cu < (long long)wp + c + t; ++u) {
+          unit_begin[u] = tp + (int)max(0LL, cu - wp - c);
           unit_seq[u] = bb;
+          cu += wq;
+          rem += wr;
+          if (rem >= Ul) {
+            rem -= Ul;
+            ++cu;
+          }
         }
       }
       tp += t;
@@ -2435,7 +2465,21 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
     }
   }
   int2 tot2;
-  const int2 run2 = block_exclusive_scan2(acc2, wave_tot, &tot2);
+  const int2 run2 = block_exclusive_scan2(acc2, wave_tot, &tot2);   // its barriers also publish s_wpre, s_prefix
+  if (lds_search) {
+    // one unit per thread: the sequence holding position cut(u) is the last
+    // one whose weighted prefix is at or below it
+    for (int uu = tid; uu < ucut && W > 0; uu += 1024) {
+      const long long cu = cut(uu);
+      int lo2 = 0, hi2 = B;
+      while (hi2 - lo2 > 1) {
+        const int mid = (lo2 + hi2) >> 1;
+        if (s_wpre[mid] <= cu) lo2 = mid; else hi2 = mid;
+      }
+      unit_begin[uu] = s_prefix[lo2] + (int)max(0LL, cu - s_wpre[lo2] - c);
+      unit_seq[uu] = lo2;
+    }
+  }
   {
     int so = run2.x, wp = run.y;
     for (int bb = lo; bb < hi; ++bb) {
