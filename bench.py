@@ -10,7 +10,8 @@ previous few steps).
 
 Prints ONE JSON line (default workload: batch 64, 16 heads, q_len 1, seqlens
 U[1024,4096], bf16 cache) with:
-  value      effective KV GB/s of the whole step (KV bytes / step time)
+  value      effective KV GB/s of the whole step (KV bytes / step time), the
+             step replayed from a captured HIP graph (--eager: direct launches)
   roofline   the attention kernel alone: algorithmic bytes (HBM-bound shapes)
              or flops (MFMA-bound shapes) per launch / its mean launch time,
              timed with HIP events on its own stream, vs the MI355X peak
@@ -261,6 +262,9 @@ def main():
                     help="also run the cache append (mla_append_kv) of this many new tokens per sequence "
                          "in every step, before the decode (their rows are the last positions of each "
                          "sequence)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as direct launches (default: replay of a captured HIP graph of the "
+                         "step, as a serving loop runs a decode step)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -344,6 +348,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # attention kernel alone: direct launches, each recording HIP events with its own dispatch
     mla.profile_enable(True)
     mla.profile_read()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -358,6 +363,25 @@ def main():
     step_ms = t0.elapsed_time(t1) / args.steps
     main_ms_total, launches = mla.profile_read()
     main_ms = main_ms_total / max(launches, 1)
+
+    # whole step: one captured graph per pool copy (split schedule, attention,
+    # merge), replayed in turn
+    if not args.eager:
+        graphs = []
+        for k in range(sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % sets].replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            graphs[i % sets].replay()
+        t1.record()
+        torch.cuda.synchronize()
+        step_ms = t0.elapsed_time(t1) / args.steps
 
     step_s = step_ms * 1e-3
     main_s = main_ms * 1e-3
@@ -398,7 +422,8 @@ def main():
                    "heads": w.num_heads, "q_len": w.q_len if not w.varlen else "per-sequence, max %d" % w.q_len,
                    "query_tokens": int(sum(w.q_lens)), "kv_dtype": w.kv_dtype,
                    "tokens": alg["tokens"], "pages": alg["pages"], "num_units": units,
-                   "pool_copies": sets, "seed": 0, "append_tokens": args.append_tokens},
+                   "pool_copies": sets, "seed": 0, "append_tokens": args.append_tokens,
+                   "step_launch": "direct launches" if args.eager else "HIP graph replay"},
         "tflops": round(tflops, 2),
         "kv_gbps": round(kv_gbps, 1),
         "roofline": roof,

@@ -2606,10 +2606,17 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
   a.qptr = p.q;
   a.kv = p.kv;
   // The events (may be null) are recorded by the dispatch itself, so their
-  // interval is the kernel's execution alone.
-#define MLA_LAUNCH(kernel, threads) \
-  hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, ev_start, ev_stop, 0, a.p, a.md, a.prefix, \
-                        a.split_off, a.seqlens, a.block_table, a.qptr, a.kv)
+  // interval is the kernel's execution alone. Without events a plain launch
+  // (what a captured graph records).
+#define MLA_LAUNCH(kernel, threads)                                                                      \
+  do {                                                                                                  \
+    if (ev_start || ev_stop)                                                                            \
+      hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, ev_start, ev_stop, 0, a.p, a.md, a.prefix, \
+                            a.split_off, a.seqlens, a.block_table, a.qptr, a.kv);                        \
+    else                                                                                                \
+      hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, a.p, a.md, a.prefix, a.split_off, a.seqlens, \
+                         a.block_table, a.qptr, a.kv);                                                   \
+  } while (0)
   const bool fp8 = p.kv_scale != nullptr;
   if (variant == VAR_NARROW16) {
     if (fp8) MLA_LAUNCH((decode_kernel16<VAR_NARROW16, true>), kThreads);
