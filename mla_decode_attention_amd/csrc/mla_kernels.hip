@@ -1597,14 +1597,17 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 //   scale of block kb: lane (n, h) holds keys 16h..16h+15 (block 0) and
 //   32+16h.. (block 1), so block kb is exactly the 32 keys of key half kb.
 //   fp8 tile layout in LDS: chunk c (16 bytes, features 16c..16c+15) of key k
-//   at ((c/4) * 64 + k) * 64 + ((c%4) ^ swz2(k)) * 16, swz2(k) = (k/4)%4;
-//   16 consecutive keys at one chunk, and the 8 keys x 2 half-chunks of a
-//   transposed read, fall on distinct banks.
+//   at ((c/4) * 64 + k) * 64 + ((c%4) ^ swz2(k)) * 16, where swz2(k) holds
+//   bits 2 and 3 of k swapped (bit 3 -> bit 0, bit 2 -> bit 1): 16
+//   consecutive keys at one chunk fall on distinct banks (any bijection of
+//   k/4 does), and so do the 8 keys x 2 adjacent chunks of a transposed read
+//   (keys k and k + 4 must differ in bit 1 of the slot, or slot parity from
+//   the adjacent chunk collides with them).
 // ---------------------------------------------------------------------------
 constexpr int kQ8PStride = 80;     // bytes per row of the P8 buffer: 64 keys + pad (conflict-free rows)
 constexpr int kQ8TileBytes = kFp8TileBytes + kPage * 4;   // codes + per-token scales
 
-__device__ __forceinline__ int swz2(int key) { return (key >> 2) & 3; }
+__device__ __forceinline__ int swz2(int key) { return ((key >> 3) & 1) | (((key >> 2) & 1) << 1); }
 __device__ __forceinline__ int lds8_byte(int key, int chunk) {
   return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz2(key)) << 4);
 }
