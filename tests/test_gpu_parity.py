@@ -42,6 +42,18 @@ def test_heads_and_query_tokens(H, s):
     assert_parity(w, out, lse, ref_out, ref_lse, f"H={H} s={s}")
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("split", [False, True])
+def test_max_rows_per_sequence(kv_dtype, split):
+    # q_len * H = 4096 rows per sequence, the library's limit: 64 row blocks,
+    # causal over 32 query tokens, a sequence shorter than them
+    lens = [200, 32, 65]
+    w = make_workload("maxrows", len(lens), 128, 32, lens, kv_dtype=kv_dtype, seed=41)
+    out, lse, _ = run_gpu(w, split=split, num_units=5, min_tiles=1)
+    ref_out, ref_lse = reference(w)
+    assert_parity(w, out, lse, ref_out, ref_lse, f"max rows {kv_dtype} split={split}")
+
+
 @pytest.mark.parametrize("H,s", [(16, 1), (16, 3), (64, 2), (128, 2)])
 @pytest.mark.parametrize("split", [False, True])
 def test_fp8_cache_shapes(H, s, split):

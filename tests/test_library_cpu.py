@@ -66,6 +66,7 @@ def _decode(lib, **kw):
     (dict(s=0), INVALID),
     (dict(H=0), INVALID),
     (dict(s=6, H=1024), INVALID),            # rows over the limit
+    (dict(s=1, H=4097), INVALID),            # one row over the limit (4096 rows per sequence)
     (dict(pages=0), INVALID),
     (dict(maxp=0), INVALID),
     (dict(sm=float("nan")), INVALID),
