@@ -256,6 +256,8 @@ def main():
                          "the second workload (mla_prefill_fwd, un-absorbed MLA, value in TFLOP/s)")
     ap.add_argument("--sets", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--num-units", type=int, default=0, help="split work units (0 = library default)")
+    ap.add_argument("--min-tiles", type=int, default=0,
+                    help="minimum tiles per split unit (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append-tokens", type=int, default=0,
@@ -315,7 +317,7 @@ def main():
         out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.float32, device=dev)
         lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
     units = args.num_units or mla.default_num_units(w.batch, w.q_len, w.num_heads)
-    plan = mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units)
+    plan = mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units, min_tiles_per_unit=args.min_tiles)
 
     if args.calib_copy_mib:
         a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -422,6 +424,7 @@ def main():
                    "heads": w.num_heads, "q_len": w.q_len if not w.varlen else "per-sequence, max %d" % w.q_len,
                    "query_tokens": int(sum(w.q_lens)), "kv_dtype": w.kv_dtype,
                    "tokens": alg["tokens"], "pages": alg["pages"], "num_units": units,
+                   "min_tiles_per_unit": args.min_tiles or "library default",
                    "pool_copies": sets, "seed": 0, "append_tokens": args.append_tokens,
                    "step_launch": "direct launches" if args.eager else "HIP graph replay"},
         "tflops": round(tflops, 2),
