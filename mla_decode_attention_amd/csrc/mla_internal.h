@@ -55,10 +55,9 @@ struct DecodeParams {
   float scale_log2;           // softmax_scale * log2(e)
 };
 
-// Kernel variants: rows of one workgroup and how its 4 waves share a tile.
+// Kernel variants: rows of one workgroup and how its waves share a tile.
 enum Variant {
   VAR_NARROW16 = 0,   // 16 rows; each wave takes 16 of the tile's 64 keys
-  VAR_WIDE64 = 1,     // 64 rows, each wave 16 rows and all 64 keys (a shape of the 16-row template; not launched)
   VAR_WIDE64X = 2,    // 64 rows; QK split 2x2 (rows x keys), PV split by columns
   VAR_Q8 = 3,         // 64 rows, fp8 cache on fp8 MFMA (queries and P quantised to E4M3)
 };

@@ -552,37 +552,24 @@ __device__ __forceinline__ void wait_tile() {
 }
 
 // ---------------------------------------------------------------------------
-// 16-row MFMA variants (NARROW16, WIDE64): v_mfma_f32_16x16x32_bf16 for QK
-// (and PV of WIDE64), v_mfma_f32_16x16x16_bf16 for PV of NARROW16.
+// 16-row kernel for the fp8 cache (up to 16 rows per sequence): 4 waves, wave
+// w takes keys 16w..16w+15 of every page; v_mfma_f32_16x16x32_bf16 for QK,
+// v_mfma_f32_16x16x16_bf16 for PV; the four key quarters' softmax states are
+// merged in LDS at a sequence's end. The fp8 page is copied to a staging
+// buffer and widened to bf16 in LDS. (A bf16 cache at these row counts takes
+// decode_kernel_pc below.)
 // ---------------------------------------------------------------------------
-template <int VAR>
-struct Cfg;
-template <>
-struct Cfg<VAR_NARROW16> {
-  static constexpr int kKeysPerWave = 16;
-  static constexpr int kRowsWg = 16;
-};
-template <>
-struct Cfg<VAR_WIDE64> {
-  static constexpr int kKeysPerWave = 64;
-  static constexpr int kRowsWg = 64;
-};
 
 constexpr int kQkDepth = 6;   // LDS operand fetches in flight ahead of the QK MFMAs
 constexpr int kPvDepth = 4;   // ... ahead of the PV MFMAs
 
-template <int VAR, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
+void decode_kernel16_fp8(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
     const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
     const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
     const uint8_t* __restrict__ kv_) {
   const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
-  (void)a;
-  constexpr int KPW = Cfg<VAR>::kKeysPerWave;
-  constexpr int NKB = KPW / 16;              // 16-key blocks per wave
-  constexpr int ROWS_WG = Cfg<VAR>::kRowsWg;
-  constexpr bool NARROW = (VAR == VAR_NARROW16);
+  constexpr int ROWS_WG = 16;
   constexpr int kQChunks = kDqk / 32;        // 18 k-steps of 32 features
   constexpr int kFeatBlocks = kDv / 16;      // 32 output blocks of 16 features
 
@@ -592,7 +579,7 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
   __shared__ __attribute__((aligned(16))) float sbuf[2][kPage];   // fp8 per-token scales
   LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
   LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
-  // fp8: buf0 holds the widened bf16 tile, buf1 the two fp8 staging pages
+  // buf0 holds the widened bf16 tile, buf1 the two fp8 staging pages
   LDS_AS uint8_t* const stage0 = buf1;
   LDS_AS uint8_t* const stage1 = buf1 + kFp8TileBytes;
   LDS_AS float* const sb0 = (LDS_AS float*)(&sbuf[0][0]);
@@ -603,8 +590,8 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int R = p.rows;
-  const int row = blockIdx.y * ROWS_WG + (NARROW ? 0 : wave * 16) + li;
-  const int key_blk = NARROW ? wave : 0;     // first 16-key block of this wave
+  const int row = blockIdx.y * ROWS_WG + li;
+  const int key_blk = wave;                  // the 16-key block of this wave
   const int u = blockIdx.x;
 
   Unit unit;
@@ -614,8 +601,8 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
   }
 
   // ---- per-lane constant LDS offsets
-  // QK operand for k-step c: key 16(key_blk + kb) + li, chunk 4c + g
-  //   = (c/2) line groups + chunk 4(c%2) + g of the line; +2048 per 16 keys
+  // QK operand for k-step c: key 16 key_blk + li, chunk 4c + g
+  //   = (c/2) line groups + chunk 4(c%2) + g of the line
   int qk_lane[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) qk_lane[par] = lds_byte(16 * key_blk + li, 4 * par + g);
@@ -630,12 +617,13 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
   f32x4 o[kFeatBlocks];
   float m_run = -INFINITY, l_run = 0.f;
 
-  TileDma<FP8> dma;
-  TileInfo next = unit.prepare(a, unit.f_begin, FP8 ? stage0 : buf0, sb0, tid, dma);
+  TileDma<true> dma;
+  TileInfo next = unit.prepare(a, unit.f_begin, stage0, sb0, tid, dma);
   dma_all(dma);
 
-  // cur: bf16 tile computed in this step; nxt: where the next tile's loads go;
-  // stage / sbc / sbn: fp8 staging page of this tile and the scale buffers.
+  // cur: bf16 tile computed in this step; nxt: staging page the next tile's
+  // loads go to; stage / sbc / sbn: fp8 staging page of this tile and the
+  // scale buffers.
   auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt,
                   const LDS_AS uint8_t* const stage, const LDS_AS float* const sbc,
                   LDS_AS float* const sbn) {
@@ -665,59 +653,44 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
     const bool more = f + 1 < unit.f_end;
     wait_tile();
-    if constexpr (FP8) {
-      widen_fp8_tile(stage, cur, tid);
-      lds_barrier();
-    }
+    widen_fp8_tile(stage, cur, tid);
+    lds_barrier();
     if (more) next = unit.prepare(a, f + 1, nxt, sbn, tid, dma);
 
-    // ---- QK GEMM: S^T (keys x rows) for this wave's keys, K from LDS, Q^T in registers
-    constexpr int NACC = NKB == 1 ? 2 : NKB;      // split a lone chain in two
-    constexpr int NQK = kQChunks * NKB;
-    constexpr int NPV = NARROW ? kFeatBlocks : 2 * kFeatBlocks;   // PV MFMAs
-    f32x4 s[NACC];
-#pragma unroll
-    for (int x = 0; x < NACC; ++x) s[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- QK GEMM: S^T (keys x rows) for this wave's keys, K from LDS, Q^T in
+    //      registers; the k-steps alternate between two accumulators (two
+    //      independent MFMA chains), summed at the end
+    f32x4 s[2];
+    s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      auto kaddr = [&](int i) {
-        const int c = i / NKB, kb = i % NKB;
-        return cur + qk_lane[c & 1] + (c >> 1) * kLineGroupBytes + kb * 2048;
-      };
+      auto kaddr = [&](int c) { return cur + qk_lane[c & 1] + (c >> 1) * kLineGroupBytes; };
       bf16x8 ring[kQkDepth];
 #pragma unroll
       for (int i = 0; i < kQkDepth; ++i) ring[i] = ld128(kaddr(i));
 #pragma unroll
-      for (int i = 0; i < NQK; ++i) {
-        const int c = i / NKB, kb = i % NKB;
-        const bf16x8 av = ring[i % kQkDepth];
-        if (i + kQkDepth < NQK) ring[i % kQkDepth] = ld128(kaddr(i + kQkDepth));
-        const int acc = NKB == 1 ? (c & 1) : kb;
-        s[acc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[c], s[acc], 0, 0, 0);
-        dma_slot<NQK>(dma, more, i);
+      for (int c = 0; c < kQChunks; ++c) {
+        const bf16x8 av = ring[c % kQkDepth];
+        if (c + kQkDepth < kQChunks) ring[c % kQkDepth] = ld128(kaddr(c + kQkDepth));
+        s[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[c], s[c & 1], 0, 0, 0);
+        dma_slot<kQChunks>(dma, more, c);
         sched_fence();
       }
     }
-    if constexpr (NKB == 1) s[0] += s[1];
+    s[0] += s[1];
 
     // ---- online softmax (base 2)
     const int key0 = t * kPage + key_blk * 16;
     const int vis = L - ti.qlen + (row < ti.rows ? row : max(ti.rows - 1, 0)) / p.num_heads + 1;
     const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
-    // fp8: per-token scales of this lane's keys (folded into scores and P)
-    f32x4 ksc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      ksc[kb] = FP8 ? *(const LDS_AS f32x4*)(sbc + 16 * (key_blk + kb) + 4 * g) : f32x4{1.f, 1.f, 1.f, 1.f};
+    // per-token scales of this lane's keys (folded into scores and P)
+    const f32x4 ksc = *(const LDS_AS f32x4*)(sbc + 16 * key_blk + 4 * g);
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = s[kb][r] * (FP8 ? ksc[kb][r] * p.scale_log2 : p.scale_log2);
-        if (need_mask && (key0 + kb * 16 + 4 * g + r) >= vis) v = -INFINITY;
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
+    for (int r = 0; r < 4; ++r) {
+      float v = s[0][r] * (ksc[r] * p.scale_log2);
+      if (need_mask && (key0 + 4 * g + r) >= vis) v = -INFINITY;
+      s[0][r] = v;
+      mx = fmaxf(mx, v);
     }
     mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m_run, mx);
@@ -731,64 +704,28 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
     }
     const float m_eff = (m_run == -INFINITY) ? 0.0f : m_run;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = exp2_fast(s[kb][r] - m_eff);
-        s[kb][r] = FP8 ? pr * ksc[kb][r] : pr;   // PV weight of the unscaled fp8 row
-        l_run += pr;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const float pr = exp2_fast(s[0][r] - m_eff);
+      s[0][r] = pr * ksc[r];   // PV weight of the unscaled fp8 row
+      l_run += pr;
     }
 
     // ---- PV GEMM: O^T (features x rows) += V^T . P^T, V^T read transposed from LDS
     {
-      auto vaddr = [&](int fb, int kblk) {
-        return cur + v_lane[fb & 3] + (fb >> 2) * kLineGroupBytes + kblk * 2048;
-      };
-      if constexpr (NARROW) {
-        bf16x4 pb;
+      auto vaddr = [&](int fb) { return cur + v_lane[fb & 3] + (fb >> 2) * kLineGroupBytes; };
+      bf16x4 pb;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pb[r] = (__bf16)s[0][r];
-        const i16x4 pbs = __builtin_bit_cast(i16x4, pb);
-        bf16x4 ring[kPvDepth];
+      for (int r = 0; r < 4; ++r) pb[r] = (__bf16)s[0][r];
+      const i16x4 pbs = __builtin_bit_cast(i16x4, pb);
+      bf16x4 ring[kPvDepth];
 #pragma unroll
-        for (int i = 0; i < kPvDepth; ++i) ring[i] = tr_read(vaddr(i, 0));
+      for (int i = 0; i < kPvDepth; ++i) ring[i] = tr_read(vaddr(i));
 #pragma unroll
-        for (int fb = 0; fb < kFeatBlocks; ++fb) {
-          const bf16x4 v = ring[fb % kPvDepth];
-          if (fb + kPvDepth < kFeatBlocks) ring[fb % kPvDepth] = tr_read(vaddr(fb + kPvDepth, 0));
-          o[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v), pbs, o[fb],
-                                                            0, 0, 0);
-          sched_fence();
-        }
-      } else {
-        bf16x8 pb[2];
-#pragma unroll
-        for (int c32 = 0; c32 < 2; ++c32) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pb[c32][r] = (__bf16)s[2 * c32][r];
-            pb[c32][4 + r] = (__bf16)s[2 * c32 + 1][r];
-          }
-        }
-        bf16x4 r0[kPvDepth], r1[kPvDepth];
-#pragma unroll
-        for (int i = 0; i < kPvDepth; ++i) {
-          r0[i] = tr_read(vaddr(i % kFeatBlocks, 2 * (i / kFeatBlocks)));
-          r1[i] = tr_read(vaddr(i % kFeatBlocks, 2 * (i / kFeatBlocks) + 1));
-        }
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-          const int c32 = i / kFeatBlocks, fb = i % kFeatBlocks;
-          const bf16x8 av = __builtin_shufflevector(r0[i % kPvDepth], r1[i % kPvDepth], 0, 1, 2, 3, 4, 5, 6, 7);
-          if (i + kPvDepth < NPV) {
-            const int j = i + kPvDepth;
-            r0[i % kPvDepth] = tr_read(vaddr(j % kFeatBlocks, 2 * (j / kFeatBlocks)));
-            r1[i % kPvDepth] = tr_read(vaddr(j % kFeatBlocks, 2 * (j / kFeatBlocks) + 1));
-          }
-          o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[c32], o[fb], 0, 0, 0);
-          sched_fence();
-        }
+      for (int fb = 0; fb < kFeatBlocks; ++fb) {
+        const bf16x4 v = ring[fb % kPvDepth];
+        if (fb + kPvDepth < kFeatBlocks) ring[fb % kPvDepth] = tr_read(vaddr(fb + kPvDepth));
+        o[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v), pbs, o[fb], 0, 0, 0);
+        sched_fence();
       }
     }
 
@@ -800,7 +737,7 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
     float l_row = sum_xor32(sum_xor16(l_run));
     float m_row = m_run;
 
-    if constexpr (NARROW) {
+    {
       // merge the 4 waves' key quarters of the same 16 rows (fixed order)
       if (g == 0) {
         mrg[0][wave][li] = m_run;
@@ -845,7 +782,7 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
       m_row = M;
     }
 
-    if (!NARROW || wave == 0) {
+    if (wave == 0) {
       const bool live = l_row > 0.f;
       const float inv = live ? 1.0f / l_row : 0.f;
       const float lse_v = live ? (m_row + log2_fast(l_row)) * kLn2 : -INFINITY;
@@ -864,18 +801,13 @@ void decode_kernel16(DecodeParams p_, const int32_t* __restrict__ md_, const int
         if (g == 0) *dst_l = lse_v;
       }
     }
-    if constexpr (NARROW) lds_barrier();  // `cur` is the next prefetch target
+    lds_barrier();  // `cur` is widened into again by the next step
   };
 
-  // Two copies of the step with the buffers fixed at compile time.
+  // Two copies of the step with the staging buffers fixed at compile time.
   for (int f = unit.f_begin; f < unit.f_end; f += 2) {
-    if constexpr (FP8) {
-      step(f, buf0, stage1, stage0, sb0, sb1);
-      if (f + 1 < unit.f_end) step(f + 1, buf0, stage0, stage1, sb1, sb0);
-    } else {
-      step(f, buf0, buf1, nullptr, nullptr, nullptr);
-      if (f + 1 < unit.f_end) step(f + 1, buf1, buf0, nullptr, nullptr, nullptr);
-    }
+    step(f, buf0, stage1, stage0, sb0, sb1);
+    if (f + 1 < unit.f_end) step(f + 1, buf0, stage0, stage1, sb1, sb0);
   }
 }
 
@@ -1011,7 +943,7 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
     return;
   }
 
-  // consumer LDS offsets (see decode_kernel16): QK operand of key 16cw + li,
+  // consumer LDS offsets (as in decode_kernel16_fp8): QK operand of key 16cw + li,
   // chunk 4c + g; transposed V operand of keys 4g + li/4 (+ 16 per key block)
   int qk_lane[2];
 #pragma unroll
@@ -2622,7 +2554,7 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
   } while (0)
   const bool fp8 = p.kv_scale != nullptr;
   if (variant == VAR_NARROW16) {
-    if (fp8) MLA_LAUNCH((decode_kernel16<VAR_NARROW16, true>), kThreads);
+    if (fp8) MLA_LAUNCH(decode_kernel16_fp8, kThreads);
     else MLA_LAUNCH(decode_kernel_pc, 2 * kThreads);
   } else if (variant == VAR_Q8) {
     MLA_LAUNCH(decode_kernel_q8, kThreadsX);
