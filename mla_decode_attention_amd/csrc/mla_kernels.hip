@@ -1254,16 +1254,16 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   // cur: tile computed in this step; nxt: where the next tile's loads go
   // query rows of this wave's row into registers (no wait: the first use
   // waits); issued at a sequence's first tile, or right after the QK of the
-  // previous sequence's last tile when both are in the unit (q_ready)
+  // previous sequence's last tile when both are in the unit (q_ready). A row
+  // past the sequence's rows takes its last row: the values go into qreg
+  // untouched (a select on them would wait for the loads at once), and such
+  // rows are never stored.
   bool q_ready = false;
   auto load_q = [&](const TileInfo& tq) {
     const int rr = row_qk < tq.rows ? row_qk : max(tq.rows - 1, 0);
     const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(tq.qrow0 + rr, p.q_rows - 1) * kDqk);
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) {
-      bf16x8 v = qrow[36 * fh + 2 * c + h];
-      qreg[c] = row_qk < tq.rows ? v : bf16x8{};
-    }
+    for (int c = 0; c < NQ; ++c) qreg[c] = qrow[36 * fh + 2 * c + h];
   };
 
   auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
@@ -1289,6 +1289,11 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     // this tile's loads may still be landing
     const bool more = f + 1 < unit.f_end;
     if (more) next = unit.prepare(a, f + 1, nxt, nullptr, tid, dma);
+    // the same wait as wait_tile's, as a builtin the compiler tracks: it then
+    // knows that query rows prefetched after the previous tile's QK have
+    // landed and puts no waits of its own into this tile's QK loop (where
+    // they would also wait for the next tile's direct-to-LDS loads)
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
     wait_tile();
     const bool load_next = more && row0 < next.rows;
     if (skip) {
