@@ -318,7 +318,7 @@ def main():
     else:
         out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.float32, device=dev)
         lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
-    units = args.num_units or mla.default_num_units(w.batch, w.q_len, w.num_heads)
+    units = args.num_units or mla.default_num_units(w.batch, w.q_len, w.num_heads, varlen=w.varlen)
     plan = mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units, min_tiles_per_unit=args.min_tiles)
 
     if args.calib_copy_mib:

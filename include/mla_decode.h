@@ -90,12 +90,21 @@ const char* mla_last_error(void);
  * A sequence touched by k > 1 units is computed as k partials and merged.
  *
  * mla_default_num_units: a unit count that fills the current device for this
- *   shape (0 if the device cannot be queried).
+ *   shape (0 if the device cannot be queried): 8 k for the 8 XCDs, with k the
+ *   smallest multiple of c / gcd(c, rb) not below c / rb (c = CUs per XCD,
+ *   rb = row blocks per sequence), so that the k rb workgroups an XCD runs
+ *   fill whole rounds of its CUs.
+ * mla_default_num_units_varlen: the same for mla_decode_fwd_varlen with up
+ *   to max_q_len query tokens per sequence, with k also at least
+ *   ceil(batch / 8) (about one unit per sequence: row blocks that sequences
+ *   with fewer query tokens leave idle end their unit early and free their
+ *   CU). Pass max_q_len as the q_len of mla_get_split_metadata.
  * mla_metadata_bytes: size of the metadata buffer for (batch, num_units).
  * mla_workspace_bytes: size of the partials workspace for the shape:
  *   (batch + num_units) * q_len * num_heads * (512 + 1) * 4 bytes, rounded up.
  */
 int mla_default_num_units(int batch, int q_len, int num_heads);
+int mla_default_num_units_varlen(int batch, int max_q_len, int num_heads);
 size_t mla_metadata_bytes(int batch, int num_units);
 size_t mla_workspace_bytes(int batch, int q_len, int num_heads, int num_units);
 

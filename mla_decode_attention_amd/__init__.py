@@ -55,6 +55,7 @@ def load_library():
         "mla_status_string": (ctypes.c_char_p, [c_int]),
         "mla_last_error": (ctypes.c_char_p, []),
         "mla_default_num_units": (c_int, [c_int, c_int, c_int]),
+        "mla_default_num_units_varlen": (c_int, [c_int, c_int, c_int]),
         "mla_metadata_bytes": (c_size, [c_int, c_int]),
         "mla_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int]),
         "mla_get_split_metadata": (c_int, [vp, c_int, c_int, c_int, c_int, c_int, vp, c_size, vp]),
@@ -110,8 +111,11 @@ def abi_version() -> int:
     return load_library().mla_abi_version()
 
 
-def default_num_units(batch: int, q_len: int, num_heads: int) -> int:
-    return load_library().mla_default_num_units(batch, q_len, num_heads)
+def default_num_units(batch: int, q_len: int, num_heads: int, varlen: bool = False) -> int:
+    """Library default unit count (varlen: for decode_varlen, q_len = max_q_len)."""
+    lib = load_library()
+    f = lib.mla_default_num_units_varlen if varlen else lib.mla_default_num_units
+    return f(batch, q_len, num_heads)
 
 
 def metadata_bytes(batch: int, num_units: int) -> int:
@@ -136,13 +140,17 @@ class SplitPlan:
 def get_split_metadata(cache_seqlens: torch.Tensor, q_len: int, num_heads: int,
                        num_units: Optional[int] = None, min_tiles_per_unit: int = 0,
                        metadata: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None) -> SplitPlan:
-    """Build the split-KV schedule for one decode step (reusable across layers)."""
+                       workspace: Optional[torch.Tensor] = None, varlen: bool = False) -> SplitPlan:
+    """Build the split-KV schedule for one decode step (reusable across layers).
+
+    varlen: the plan is for decode_varlen (q_len = max_q_len); only changes
+    the default unit count."""
     lib = load_library()
     _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
     batch = cache_seqlens.shape[0]
     if num_units is None:
-        num_units = lib.mla_default_num_units(batch, q_len, num_heads)
+        num_units = (lib.mla_default_num_units_varlen if varlen else lib.mla_default_num_units)(
+            batch, q_len, num_heads)
         if num_units < 1:
             raise MLAError(f"mla_default_num_units failed: {lib.mla_last_error().decode()}")
     nbytes = lib.mla_metadata_bytes(batch, num_units)

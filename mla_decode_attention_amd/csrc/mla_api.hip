@@ -91,6 +91,33 @@ size_t workspace_need(int batch, int q_len, int num_heads, int units) {
   return o_bytes + ((l_bytes + 255) & ~(size_t)255);
 }
 
+
+// One 147 KiB-LDS workgroup per CU. Workgroups are dealt to the 8 XCDs round
+// robin, and the rb row blocks of a unit share one XCD (they read the same
+// pages through its L2), so an XCD runs k units as k * rb workgroups on its
+// CUs. k is the smallest multiple of per_xcd / gcd(per_xcd, rb) that is at
+// least max(per_xcd / rb, k_floor, 1): k * rb then fills whole rounds of the
+// XCD's CUs, never leaving a second round a few workgroups deep (e.g. rb =
+// 12: k = 8, three full rounds, where k = 2 or 3 would leave 8 CUs idle or
+// run 4 workgroups in a second round). Returns 8k, or 0 on a device error.
+int units_in_whole_rounds(int batch, int q_len, int num_heads, int k_floor) {
+  if (batch < 1 || q_len < 1 || num_heads < 1) return 0;
+  DevInfo d;
+  if (device_info(&d) != MLA_OK) return 0;
+  const int rows = q_len * num_heads;
+  const int var = mla::variant_for(rows);
+  const int rb = (rows + mla::variant_rows(var) - 1) / mla::variant_rows(var);
+  constexpr int kXcds = 8;
+  const int per_xcd = d.cus / kXcds > 0 ? d.cus / kXcds : 1;
+  int g = per_xcd, r = rb;
+  while (r) { const int t = g % r; g = r; r = t; }
+  const int step = per_xcd / g;
+  int k0 = per_xcd / rb;
+  if (k0 < k_floor) k0 = k_floor;
+  if (k0 < 1) k0 = 1;
+  const int k = ((k0 + step - 1) / step) * step;
+  return k * kXcds;
+}
 }  // namespace
 
 extern "C" {
@@ -110,16 +137,16 @@ const char* mla_status_string(int status) {
 
 const char* mla_last_error(void) { return g_err; }
 
+
 int mla_default_num_units(int batch, int q_len, int num_heads) {
-  if (batch < 1 || q_len < 1 || num_heads < 1) return 0;
-  DevInfo d;
-  if (device_info(&d) != MLA_OK) return 0;
-  const int rows = q_len * num_heads;
-  const int var = mla::variant_for(rows);
-  const int rb = (rows + mla::variant_rows(var) - 1) / mla::variant_rows(var);
-  // one 147 KiB-LDS workgroup per CU; spread the row blocks of a unit over CUs
-  int units = d.cus / rb;
-  return units < 1 ? 1 : units;
+  return units_in_whole_rounds(batch, q_len, num_heads, 0);
+}
+
+int mla_default_num_units_varlen(int batch, int max_q_len, int num_heads) {
+  // about one unit per sequence: the row blocks that a sequence with fewer
+  // query tokens leaves idle then end their unit early and free their CU for
+  // the next workgroup, instead of idling beside a longer neighbour
+  return units_in_whole_rounds(batch, max_q_len, num_heads, (batch + 7) / 8);
 }
 
 size_t mla_metadata_bytes(int batch, int num_units) {

@@ -65,3 +65,27 @@ def test_mismatched_metadata_writes_nothing(H, s, units_call):
     mla.decode(d["q"], d["kv"], d["block_table"], d["seqlens"], w.softmax_scale, plan=plan, out=out, lse=lse)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0) and torch.all(lse == 7.0)
+
+
+@pytest.mark.parametrize("batch,q_len,heads", [(64, 1, 16), (128, 2, 128), (128, 3, 64), (128, 3, 128),
+                                               (128, 6, 128), (32, 1, 128), (1, 32, 128), (1000, 5, 64)])
+def test_default_unit_counts_fill_whole_rounds(batch, q_len, heads):
+    """Default unit counts: a multiple of the 8 XCDs, and each XCD's units x
+    row blocks fill whole rounds of its CUs (row blocks of a unit share an
+    XCD); the varlen default also gives about one unit per sequence."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    per_xcd = cus // 8
+    rows = q_len * heads
+    rb = 1 if rows <= 16 else (rows + 63) // 64
+    for varlen in (False, True):
+        u = mla.default_num_units(batch, q_len, heads, varlen=varlen)
+        assert u > 0 and u % 8 == 0, (u, varlen)
+        k = u // 8
+        assert (k * rb) % per_xcd == 0, (u, rb, varlen)
+        assert k >= max(1, per_xcd // rb)
+        if varlen:
+            assert u >= batch
+        # and a plan with that many units runs (metadata sized for it)
+        sl = torch.full((batch,), 300, dtype=torch.int32, device="cuda")
+        plan = mla.get_split_metadata(sl, q_len, heads, varlen=varlen)
+        assert plan.num_units == u
