@@ -116,10 +116,16 @@ void prefill_kernel(Args a) {
   LDS_AS uint8_t* const stage0 = (LDS_AS uint8_t*)smem;
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int head = blockIdx.y;
-  // longest query blocks first (causal work grows with the block index)
-  const int b = uniform((int)blockIdx.x / a.nblk);
-  const int qb = uniform(a.nblk - 1 - (int)blockIdx.x % a.nblk);
+  // Longest query blocks first (causal work grows with the block index),
+  // across the whole grid: workgroups are dispatched in linear-id order, so
+  // the linear id runs over (query block, descending) x sequence x head and
+  // every sequence's and head's longest blocks start in the first round.
+  const int nseq = (int)gridDim.x / a.nblk;
+  const int lin = (int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x;
+  const int rank = lin / (nseq * a.H), rem = lin - rank * (nseq * a.H);
+  const int head = uniform(rem % a.H);
+  const int b = uniform(rem / a.H);
+  const int qb = uniform(a.nblk - 1 - rank);
   const int q0 = uniform(a.cu_q[b]), N = uniform(a.cu_q[b + 1] - q0);
   const int k0 = uniform(a.cu_k[b]), L = uniform(a.cu_k[b + 1] - k0);
   const int i0 = qb * ROWS_WG;               // first query index of the block
