@@ -157,7 +157,12 @@ __device__ __forceinline__ void dma4(uint32_t voff, const uint8_t* sbase, uint32
 template <bool FP8>
 struct TileDma;
 
-// bf16 page: 18 loads per thread straight into the tile layout.
+// bf16 page, 256 threads: 18 loads per thread straight into the tile layout.
+// Load i of thread t fills line group i/2 of key 32(i%2) + t/8, in-line
+// position t%8 (the lane fetches the chunk that belongs there, so the 8 lanes
+// of an octet read one whole 128-byte line of one key row); keys at or past
+// `nvalid` re-read the last valid key. The 64-row kernel issues these from
+// its waves 0-3; the 16-row bf16 kernel uses only the plan.
 template <>
 struct TileDma<false> {
   static constexpr int kLoads = kLoadsPerThread;
@@ -178,6 +183,8 @@ struct TileDma<false> {
   __device__ __forceinline__ void load(int i) const {
     dma16(voff[i & 1] + 128 * (i >> 1), page, lds0 + i * 4096);
   }
+  template <int I>
+  __device__ __forceinline__ void load_ct() const { load(I); }
 };
 
 // fp8 page: a plain copy of the 36 KiB page into a staging buffer (9 loads per
@@ -1139,38 +1146,8 @@ constexpr int kThreadsX = 512;
 constexpr int kQkDepthX = 4;
 constexpr int kPvDepthX = 4;
 constexpr int kXchgBytes = 16384;
-constexpr int kLoadsX = kTileBytes / (kThreadsX * 16);                         // 9
 constexpr int kFp8SlotsX = kFp8TileBytes / 16;                                 // 2304
 constexpr int kFp8LoadsX = (kFp8SlotsX + kThreadsX - 1) / kThreadsX;           // 5
-static_assert(kLoadsX * kThreadsX * 16 == kTileBytes, "tile must split evenly");
-
-template <bool FP8>
-struct TileDmaX;
-
-// bf16 page, 512 threads: load i of thread t fills LDS slot 512i + t, i.e.
-// line group i, key t/8, in-line position t%8; the lane fetches the chunk
-// that belongs there, so the 8 lanes of an octet read one whole 128-byte line
-// of one key row. Keys at or past `nvalid` re-read the last valid key.
-template <>
-struct TileDmaX<false> {
-  static constexpr int kLoads = kLoadsX;
-  const uint8_t* page;
-  uint32_t voff, lds0;
-  __device__ __forceinline__ void plan(const uint8_t* kv, const float* /*kv_scale*/, int page_id,
-                                       int nvalid, LDS_AS uint8_t* buf, LDS_AS float* /*sbuf*/,
-                                       int tid) {
-    page = kv + (size_t)page_id * kTileBytes;
-    const int key = tid >> 3;
-    const int src_key = key < nvalid ? key : nvalid - 1;
-    voff = src_key * kRowBytes + 16 * ((tid & 7) ^ swz3(key));
-    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
-  }
-  // the per-load offset goes into the scalar base, so the lane offset is one register
-  __device__ __forceinline__ void load(int i) const { dma16(voff, page + 128 * i, lds0 + i * 8192); }
-  template <int I>
-  __device__ __forceinline__ void load_ct() const { load(I); }
-};
-
 
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
@@ -1245,11 +1222,15 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   bool restart = true;                       // next rescale zeroes O and l (a sequence starts)
   int row_tok = 0;                           // query token of row_qk in the current sequence
 
-  TileDmaX<false> dma;
+  // Waves 0-3 (one per SIMD) issue the page's direct-to-LDS loads, 18 each,
+  // one after every QK MFMA (the 256-thread plan of TileDma<false>); waves
+  // 4-7 issue none, so while a loading wave waits on the vector-memory queue
+  // its SIMD partner keeps issuing MFMAs.
+  TileDma<false> dma;
   TileInfo next = unit.prepare(a, unit.f_begin, buf0, nullptr, tid, dma);
   // a row block past a sequence's rows (per-sequence q_len) skips its tiles:
   // no loads, no compute
-  if (row0 < next.rows) dma_all(dma);
+  if (row0 < next.rows && wave < 4) dma_all(dma);
 
   // cur: tile computed in this step; nxt: where the next tile's loads go
   // query rows of this wave's row into registers (no wait: the first use
@@ -1297,7 +1278,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     wait_tile();
     const bool load_next = more && row0 < next.rows;
     if (skip) {
-      if (load_next) dma_all(dma);
+      if (load_next && wave < 4) dma_all(dma);
       return;
     }
 
@@ -1319,7 +1300,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
         sched_fence();
       }
     };
-    if (load_next) qk(std::true_type{});
+    if (load_next && wave < 4) qk(std::true_type{});
     else qk(std::false_type{});
     // the next tile starts a sequence of this unit: its query rows now (qreg is free)
     if (ti.last && more && row0 < next.rows) {
