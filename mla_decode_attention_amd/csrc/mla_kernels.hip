@@ -1569,6 +1569,39 @@ struct TileDmaQ8 {
   __device__ __forceinline__ void load_ct() const { load(I); }
 };
 
+// The same page layout from 256 threads (waves 0-3 of the 64-row fp8 kernel):
+// load j of thread t fills LDS slot 256j + t, i.e. line group j, key
+// (t/4)%64, position t%4, so the thread's key and position are fixed and load
+// j reads bytes 64j.. of that key's row. Wave 0 also loads the 64 per-token
+// scales with its first load.
+struct TileDmaQ8Half {
+  static constexpr int kLoads = kFp8TileBytes / (256 * 16);   // 9
+  const uint8_t* page;
+  const uint8_t* scale;
+  uint32_t voff, lds0, sc_lds, sc_off;
+  int tid;
+  __device__ __forceinline__ void plan(const uint8_t* kv, const float* kv_scale, int page_id, int nvalid,
+                                       LDS_AS uint8_t* buf, LDS_AS float* /*sbuf*/, int t) {
+    page = kv + (size_t)page_id * kFp8TileBytes;
+    scale = (const uint8_t*)(kv_scale + (size_t)page_id * kPage);
+    tid = t;
+    const int key = (t >> 2) & 63, pos = t & 3;
+    const int src_key = key < nvalid ? key : nvalid - 1;
+    voff = src_key * kFp8RowBytes + 16 * (pos ^ swz2(key));
+    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (t & ~63) * 16));
+    sc_lds = (uint32_t)uniform((int)(uintptr_t)(buf + kFp8TileBytes));
+    const int lane = t & 63;
+    sc_off = 4 * (lane < nvalid ? lane : nvalid - 1);
+  }
+  __device__ __forceinline__ void load(int j) const {
+    dma16(voff, page + 64 * j, (uint32_t)uniform((int)(lds0 + j * 4096)));
+    if (j == 0 && tid < 64) dma4(sc_off, scale, (uint32_t)uniform((int)sc_lds));
+  }
+  template <int I>
+  __device__ __forceinline__ void load_ct() const { load(I); }
+};
+static_assert(TileDmaQ8Half::kLoads * 256 * 16 == kFp8TileBytes, "fp8 tile must split evenly");
+
 __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
@@ -1990,11 +2023,13 @@ void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const in
   bool restart = true;                       // next rescale zeroes O and l (a sequence starts)
   int row_tok = 0;                           // query token of row_qk in the current sequence
 
-  TileDmaQ8 dma;
+  // waves 0-3 issue the page's loads (9 each), waves 4-7 none, as in the
+  // bf16 kernel
+  TileDmaQ8Half dma;
   TileInfo next = unit.prepare(a, unit.f_begin, buf0, nullptr, tid, dma);
   // a row block past a sequence's rows (per-sequence q_len) skips its tiles:
   // no loads, no compute
-  if (row0 < next.rows) dma_all(dma);
+  if (row0 < next.rows && wave < 4) dma_all(dma);
 
   // cur: E4M3 tile (codes, then the 64 scales) of this step; nxt: where the
   // next tile's loads go
@@ -2039,7 +2074,7 @@ void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const in
     wait_tile();
     const bool load_next = more && row0 < next.rows;
     if (skip) {
-      if (load_next) dma_all(dma);
+      if (load_next && wave < 4) dma_all(dma);
       return;
     }
 
@@ -2066,7 +2101,7 @@ void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const in
         sched_fence();
       }
     };
-    if (load_next) qk(std::true_type{});
+    if (load_next && wave < 4) qk(std::true_type{});
     else qk(std::false_type{});
     // the next tile starts a sequence of this unit: its query rows now (qreg is free)
     if (ti.last && more && row0 < next.rows) {
