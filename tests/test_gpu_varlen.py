@@ -17,8 +17,9 @@ def run_varlen(w, split=True, num_units=None, min_tiles=0, out=None, lse=None):
     cu = torch.from_numpy(w.cu_q).cuda()
     plan = None
     if split:
+        # (default unit count: the varlen one, as the benchmark launches it)
         plan = mla.get_split_metadata(d["seqlens"], w.q_len, w.num_heads, num_units=num_units,
-                                      min_tiles_per_unit=min_tiles)
+                                      min_tiles_per_unit=min_tiles, varlen=True)
     o, l = mla.decode_varlen(q, cu, w.q_len, d["kv"], d["block_table"], d["seqlens"], w.softmax_scale,
                              kv_scale=d["kv_scale"], plan=plan, out=out, lse=lse)
     torch.cuda.synchronize()
