@@ -1383,6 +1383,20 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
     if (!restart) make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
     lds_barrier();
 
+    // the first V^T fragments of the PV GEMM, read before the raise check
+    // (a raise rewrites P, never V)
+    auto vaddr = [&](int i, int second) {
+      const int ks = i >> 1, fb = i & 1;
+      return cur + v_lane[second][fb] + ks * 2048;
+    };
+    constexpr int NPV = 8;   // (k-step, feature block) pairs; each feeds 2 row halves
+    bf16x4 r0[kPvDepthX], r1[kPvDepthX];
+#pragma unroll
+    for (int i = 0; i < kPvDepthX; ++i) {
+      r0[i] = tr_read(vaddr(i, 0));
+      r1[i] = tr_read(vaddr(i, 1));
+    }
+
     if (restart || uniform(*raise_flag) == f) {
       // some row's max moved (or a sequence starts): every wave derives the
       // new running max of all 64 rows from the quarter maxima
@@ -1410,17 +1424,6 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
     // ---- PV GEMM: O^T[64 features of this wave, 64 rows] += V^T . P^T
     {
-      auto vaddr = [&](int i, int second) {
-        const int ks = i >> 1, fb = i & 1;
-        return cur + v_lane[second][fb] + ks * 2048;
-      };
-      constexpr int NPV = 8;   // (k-step, feature block) pairs; each feeds 2 row halves
-      bf16x4 r0[kPvDepthX], r1[kPvDepthX];
-#pragma unroll
-      for (int i = 0; i < kPvDepthX; ++i) {
-        r0[i] = tr_read(vaddr(i, 0));
-        r1[i] = tr_read(vaddr(i, 1));
-      }
       bf16x8 pbr[2];
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
