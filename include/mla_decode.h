@@ -138,8 +138,13 @@ int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int q_len, i
  *   kv_dtype       mla_kv_dtype_t
  *   num_pages      pages in the pool (>= 1)
  *   block_table    device int32 [batch, max_pages_per_seq]; entries
- *                  [0, ceil(L_b/64)) of row b must be valid page ids < num_pages;
- *                  later entries are never read
+ *                  [0, ceil(L_b/64)) of row b must be valid page ids < num_pages.
+ *                  The kernels may also load (and then ignore) other entries
+ *                  of the table -- in split mode up to the first
+ *                  min(64, max_pages_per_seq) of the row after a sequence's --
+ *                  so the whole [batch, max_pages_per_seq] table must be
+ *                  readable device memory; the values of entries past
+ *                  ceil(L_b/64) never matter
  *   max_pages_per_seq  row stride of block_table (>= 1)
  *   cache_seqlens  device int32 [batch]; caller contract:
  *                  ceil(L_b/64) <= max_pages_per_seq
@@ -254,7 +259,13 @@ int mla_prefill_fwd(const void* q, const void* k_nope, const void* k_rope, const
                     int num_heads, float softmax_scale, float* out, float* lse, void* stream);
 
 /*
- * mla_combine: merge per-sequence partials by their log-sum-exp.
+ * mla_combine: merge per-sequence partials by their log-sum-exp, the merge
+ * step of split-KV decoding (FlashDecoding, named among the attention
+ * features in PaddleNLP issue #10157's overview; the cache partitions of
+ * Append Attention that are computed apart and merged, mhpq.cn article on
+ * PaddleNLP inference flags, Append Attention section). Partials of disjoint
+ * key sets combine exactly: each is renormalised by exp(lse_k - lse) of the
+ * softmax over their union.
  *   part_out        device fp32 [num_partials, rows_per_seq, 512], 16-byte aligned
  *   part_lse        device fp32 [num_partials, rows_per_seq] (natural log)
  *   seq_part_offsets device int32 [batch + 1], non-decreasing; sequence b owns

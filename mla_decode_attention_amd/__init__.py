@@ -20,7 +20,8 @@ from typing import Optional
 import torch
 
 __all__ = ["load_library", "library_path", "abi_version", "default_num_units", "metadata_bytes",
-           "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "get_split_metadata", "decode", "decode_varlen", "combine", "append_kv",
+           "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "get_split_metadata", "decode",
+           "decode_varlen", "combine", "append_kv", "prefill",
            "MLAError", "KV_BF16", "KV_FP8_E4M3", "PAGE_TOKENS", "D_QK", "D_V"]
 
 PAGE_TOKENS = 64
@@ -94,17 +95,49 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtypes, ndim=None):
+def _need(t: torch.Tensor, name: str, dtypes, ndim=None, shape=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _plan_buffers(plan, dev):
+    """(metadata, workspace, num_units, workspace bytes) of a plan, checked."""
+    _need(plan.metadata, "plan.metadata", (torch.int32,), 1, device=dev)
+    _need(plan.workspace, "plan.workspace", (torch.uint8,), 1, device=dev)
+    return plan.metadata, plan.workspace, plan.num_units, _nbytes(plan.workspace)
+
+
+def _check_cache(kv_cache, kv_scale, dev):
+    """(kv_dtype, num_pages) of a [P, 64, 576] cache, with its scales checked."""
+    fp8_types = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+    _need(kv_cache, "kv_cache", (torch.bfloat16,) + fp8_types, 3, device=dev)
+    if tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_QK):
+        raise ValueError(f"kv_cache must be [pages, {PAGE_TOKENS}, {D_QK}]")
+    P = kv_cache.shape[0]
+    kv_dtype = KV_BF16 if kv_cache.dtype == torch.bfloat16 else KV_FP8_E4M3
+    if kv_dtype == KV_FP8_E4M3:
+        if kv_scale is None:
+            raise ValueError("fp8 cache needs kv_scale")
+        _need(kv_scale, "kv_scale", (torch.float32,), 2, shape=(P, PAGE_TOKENS), device=dev)
+    elif kv_scale is not None:
+        raise ValueError("kv_scale is only for an fp8 cache")
+    return kv_dtype, P
 
 
 def abi_version() -> int:
@@ -153,14 +186,17 @@ def get_split_metadata(cache_seqlens: torch.Tensor, q_len: int, num_heads: int,
             batch, q_len, num_heads)
         if num_units < 1:
             raise MLAError(f"mla_default_num_units failed: {lib.mla_last_error().decode()}")
+    dev = cache_seqlens.device
     nbytes = lib.mla_metadata_bytes(batch, num_units)
     if metadata is None:
-        metadata = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=cache_seqlens.device)
+        metadata = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=dev)
+    _need(metadata, "metadata", (torch.int32,), 1, device=dev)
     wbytes = lib.mla_workspace_bytes(batch, q_len, num_heads, num_units)
     if workspace is None:
-        workspace = torch.empty(wbytes, dtype=torch.uint8, device=cache_seqlens.device)
+        workspace = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), 1, device=dev)
     _check(lib.mla_get_split_metadata(_ptr(cache_seqlens), batch, q_len, num_heads, num_units,
-                                      min_tiles_per_unit, _ptr(metadata), metadata.numel() * 4, _stream()),
+                                      min_tiles_per_unit, _ptr(metadata), _nbytes(metadata), _stream()),
            "mla_get_split_metadata")
     return SplitPlan(metadata, num_units, batch, q_len, num_heads, workspace)
 
@@ -179,36 +215,29 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
     """
     lib = load_library()
     _need(q, "q", (torch.bfloat16,), 4)
+    dev = q.device
     B, s, H, d = q.shape
     if d != D_QK:
         raise ValueError(f"q last dim must be {D_QK}")
-    fp8_types = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
-    _need(kv_cache, "kv_cache", (torch.bfloat16,) + fp8_types, 3)
-    if tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_QK):
-        raise ValueError(f"kv_cache must be [pages, {PAGE_TOKENS}, {D_QK}]")
-    kv_dtype = KV_BF16 if kv_cache.dtype == torch.bfloat16 else KV_FP8_E4M3
-    if kv_dtype == KV_FP8_E4M3:
-        if kv_scale is None:
-            raise ValueError("fp8 cache needs kv_scale")
-        _need(kv_scale, "kv_scale", (torch.float32,), 2)
-    _need(block_table, "block_table", (torch.int32,), 2)
-    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
-    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+    kv_dtype, P = _check_cache(kv_cache, kv_scale, dev)
+    _need(block_table, "block_table", (torch.int32,), 2, device=dev)
+    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1, shape=(B,), device=dev)
+    if block_table.shape[0] != B:
         raise ValueError("block_table / cache_seqlens batch mismatch")
     if out is None:
-        out = torch.empty((B, s, H, D_V), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, s, H, D_V), dtype=torch.float32, device=dev)
     if lse is None:
-        lse = torch.empty((B, s, H), dtype=torch.float32, device=q.device)
-    _need(out, "out", (torch.float32,), 4)
-    _need(lse, "lse", (torch.float32,), 3)
+        lse = torch.empty((B, s, H), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), 4, shape=(B, s, H, D_V), device=dev)
+    _need(lse, "lse", (torch.float32,), 3, shape=(B, s, H), device=dev)
     md = ws = None
     units, wbytes = 0, 0
     if plan is not None:
         if (plan.batch, plan.q_len, plan.num_heads) != (B, s, H):
             raise ValueError("plan was built for another shape")
-        md, ws, units, wbytes = plan.metadata, plan.workspace, plan.num_units, plan.workspace.numel()
+        md, ws, units, wbytes = _plan_buffers(plan, dev)
     name = "mla_decode_fwd_fp8mma" if fp8_mma else "mla_decode_fwd"
-    _check(getattr(lib, name)(_ptr(q), _ptr(kv_cache), _ptr(kv_scale), kv_dtype, kv_cache.shape[0],
+    _check(getattr(lib, name)(_ptr(q), _ptr(kv_cache), _ptr(kv_scale), kv_dtype, P,
                               _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), B, s, H,
                               float(softmax_scale), _ptr(out), _ptr(lse), _ptr(md), units, _ptr(ws),
                               wbytes, _stream()), name)
@@ -229,23 +258,24 @@ def prefill(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torc
     Tq, H, d = q.shape
     if d != 192:
         raise ValueError("q last dim must be 192")
-    _need(k_nope, "k_nope", (torch.bfloat16,), 3)
-    _need(k_rope, "k_rope", (torch.bfloat16,), 2)
-    _need(v, "v", (torch.bfloat16,), 3)
+    dev = q.device
+    _need(k_nope, "k_nope", (torch.bfloat16,), 3, device=dev)
+    _need(k_rope, "k_rope", (torch.bfloat16,), 2, device=dev)
+    _need(v, "v", (torch.bfloat16,), 3, device=dev)
     Tk = k_nope.shape[0]
     if tuple(k_nope.shape) != (Tk, H, 128) or tuple(k_rope.shape) != (Tk, 64) or tuple(v.shape) != (Tk, H, 128):
         raise ValueError("k_nope [Tk,H,128], k_rope [Tk,64], v [Tk,H,128] expected")
-    _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,), 1)
-    _need(cu_seqlens_k, "cu_seqlens_k", (torch.int32,), 1)
+    _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,), 1, device=dev)
+    _need(cu_seqlens_k, "cu_seqlens_k", (torch.int32,), 1, device=dev)
     B = cu_seqlens_q.shape[0] - 1
     if B < 1 or cu_seqlens_k.shape[0] != B + 1:
         raise ValueError("cu_seqlens_q / cu_seqlens_k must both have batch + 1 entries")
     if out is None:
-        out = torch.empty((Tq, H, 128), dtype=torch.float32, device=q.device)
+        out = torch.empty((Tq, H, 128), dtype=torch.float32, device=dev)
     if lse is None:
-        lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
-    _need(out, "out", (torch.float32,), 3)
-    _need(lse, "lse", (torch.float32,), 2)
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), 3, shape=(Tq, H, 128), device=dev)
+    _need(lse, "lse", (torch.float32,), 2, shape=(Tq, H), device=dev)
     _check(lib.mla_prefill_fwd(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(cu_seqlens_q),
                                _ptr(cu_seqlens_k), B, int(max_q_len), H, float(softmax_scale), _ptr(out),
                                _ptr(lse), _stream()), "mla_prefill_fwd")
@@ -267,35 +297,28 @@ def decode_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, max_q_len: int, k
     T, H, d = q.shape
     if d != D_QK:
         raise ValueError(f"q last dim must be {D_QK}")
-    _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,), 1)
+    dev = q.device
+    _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,), 1, device=dev)
     B = cu_seqlens_q.shape[0] - 1
-    fp8_types = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
-    _need(kv_cache, "kv_cache", (torch.bfloat16,) + fp8_types, 3)
-    if tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_QK):
-        raise ValueError(f"kv_cache must be [pages, {PAGE_TOKENS}, {D_QK}]")
-    kv_dtype = KV_BF16 if kv_cache.dtype == torch.bfloat16 else KV_FP8_E4M3
-    if kv_dtype == KV_FP8_E4M3:
-        if kv_scale is None:
-            raise ValueError("fp8 cache needs kv_scale")
-        _need(kv_scale, "kv_scale", (torch.float32,), 2)
-    _need(block_table, "block_table", (torch.int32,), 2)
-    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
-    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+    kv_dtype, P = _check_cache(kv_cache, kv_scale, dev)
+    _need(block_table, "block_table", (torch.int32,), 2, device=dev)
+    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1, shape=(B,), device=dev)
+    if block_table.shape[0] != B:
         raise ValueError("block_table / cache_seqlens batch mismatch")
     if out is None:
-        out = torch.empty((T, H, D_V), dtype=torch.float32, device=q.device)
+        out = torch.empty((T, H, D_V), dtype=torch.float32, device=dev)
     if lse is None:
-        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    _need(out, "out", (torch.float32,), 3)
-    _need(lse, "lse", (torch.float32,), 2)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), 3, shape=(T, H, D_V), device=dev)
+    _need(lse, "lse", (torch.float32,), 2, shape=(T, H), device=dev)
     md = ws = None
     units, wbytes = 0, 0
     if plan is not None:
         if (plan.batch, plan.q_len, plan.num_heads) != (B, max_q_len, H):
             raise ValueError("plan was built for another shape")
-        md, ws, units, wbytes = plan.metadata, plan.workspace, plan.num_units, plan.workspace.numel()
+        md, ws, units, wbytes = _plan_buffers(plan, dev)
     _check(lib.mla_decode_fwd_varlen(_ptr(q), _ptr(cu_seqlens_q), T, int(max_q_len), _ptr(kv_cache),
-                                     _ptr(kv_scale), kv_dtype, kv_cache.shape[0], _ptr(block_table),
+                                     _ptr(kv_scale), kv_dtype, P, _ptr(block_table),
                                      block_table.shape[1], _ptr(cache_seqlens), B, H, float(softmax_scale),
                                      _ptr(out), _ptr(lse), _ptr(md), units, _ptr(ws), wbytes, _stream()),
            "mla_decode_fwd_varlen")
@@ -319,14 +342,21 @@ def combine(part_out: torch.Tensor, part_lse: torch.Tensor, seq_part_offsets: to
     """LSE-merge partials: part_out [N, R, 512], part_lse [N, R], offsets int32 [B+1]."""
     lib = load_library()
     _need(part_out, "part_out", (torch.float32,), 3)
-    _need(part_lse, "part_lse", (torch.float32,), 2)
-    _need(seq_part_offsets, "seq_part_offsets", (torch.int32,), 1)
-    R = part_out.shape[1]
+    dev = part_out.device
+    N, R = part_out.shape[0], part_out.shape[1]
+    if part_out.shape[2] != D_V:
+        raise ValueError(f"part_out must be [partials, rows, {D_V}]")
+    _need(part_lse, "part_lse", (torch.float32,), 2, shape=(N, R), device=dev)
+    _need(seq_part_offsets, "seq_part_offsets", (torch.int32,), 1, device=dev)
     B = seq_part_offsets.shape[0] - 1
+    if B < 1:
+        raise ValueError("seq_part_offsets must have batch + 1 >= 2 entries")
     if out is None:
-        out = torch.empty((B, R, D_V), dtype=torch.float32, device=part_out.device)
+        out = torch.empty((B, R, D_V), dtype=torch.float32, device=dev)
     if lse is None:
-        lse = torch.empty((B, R), dtype=torch.float32, device=part_out.device)
+        lse = torch.empty((B, R), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), 3, shape=(B, R, D_V), device=dev)
+    _need(lse, "lse", (torch.float32,), 2, shape=(B, R), device=dev)
     _check(lib.mla_combine(_ptr(part_out), _ptr(part_lse), _ptr(seq_part_offsets), B, R, _ptr(out),
                            _ptr(lse), _stream()), "mla_combine")
     return out, lse
@@ -343,23 +373,16 @@ def append_kv(latent: torch.Tensor, block_table: torch.Tensor, cache_seqlens: to
     """
     lib = load_library()
     _need(latent, "latent", (torch.bfloat16,), 3)
+    dev = latent.device
     B, s, d = latent.shape
     if d != D_QK:
         raise ValueError(f"latent last dim must be {D_QK}")
-    fp8_types = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
-    _need(kv_cache, "kv_cache", (torch.bfloat16,) + fp8_types, 3)
-    if tuple(kv_cache.shape[1:]) != (PAGE_TOKENS, D_QK):
-        raise ValueError(f"kv_cache must be [pages, {PAGE_TOKENS}, {D_QK}]")
-    kv_dtype = KV_BF16 if kv_cache.dtype == torch.bfloat16 else KV_FP8_E4M3
-    if kv_dtype == KV_FP8_E4M3:
-        if kv_scale is None:
-            raise ValueError("fp8 cache needs kv_scale")
-        _need(kv_scale, "kv_scale", (torch.float32,), 2)
-    _need(block_table, "block_table", (torch.int32,), 2)
-    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
-    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+    kv_dtype, P = _check_cache(kv_cache, kv_scale, dev)
+    _need(block_table, "block_table", (torch.int32,), 2, device=dev)
+    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1, shape=(B,), device=dev)
+    if block_table.shape[0] != B:
         raise ValueError("block_table / cache_seqlens batch mismatch")
     _check(lib.mla_append_kv(_ptr(latent), B, s, _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
-                             _ptr(kv_cache), _ptr(kv_scale), kv_dtype, kv_cache.shape[0], _stream()),
+                             _ptr(kv_cache), _ptr(kv_scale), kv_dtype, P, _stream()),
            "mla_append_kv")
     return kv_cache, kv_scale

@@ -334,7 +334,9 @@ int mla_prefill_fwd(const void* q, const void* k_nope, const void* k_rope, const
                 max_q_len, num_heads);
   if (num_heads > 65535) return fail(MLA_ERR_INVALID_ARG, "num_heads must be <= 65535");
   const long long nblk = ((long long)max_q_len + mla::prefill_rows_per_block() - 1) / mla::prefill_rows_per_block();
-  if (nblk * batch > INT32_MAX) return fail(MLA_ERR_INVALID_ARG, "batch * query blocks exceeds the grid");
+  // the kernel's linear workgroup id runs over (query block, sequence, head) in an int
+  if (nblk * batch * num_heads > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARG, "batch * query blocks * num_heads exceeds the 32-bit grid index");
   if (!isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
   if (!aligned(q, 16) || !aligned(k_nope, 16) || !aligned(k_rope, 16) || !aligned(v, 16) || !aligned(out, 16))
     return fail(MLA_ERR_INVALID_ARG, "q, k_nope, k_rope, v and out must be 16-byte aligned");

@@ -105,13 +105,15 @@ __device__ __forceinline__ void lds_barrier() {
 // destination lds_addr + 16 * lane (lds_addr wave-uniform, in M0). Written as
 // inline asm so the compiler does not treat it as an LDS store it must wait on:
 // the kernel orders these loads itself with explicit vmcnt waits + barriers.
+// The LDS address is an M0 operand, so the compiler writes M0 itself and knows
+// it is in use; the s_nop is the wait state the hardware needs between an M0
+// write and a load into LDS, which the compiler cannot see inside the asm.
 __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "v"(voff), "s"(sbase), "{m0}"(lds_addr)
       : "memory");
 }
 
@@ -146,11 +148,10 @@ __device__ __forceinline__ int opaque(int x) {
 // 4-byte direct-to-LDS load per lane (used for the fp8 per-token scales).
 __device__ __forceinline__ void dma4(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dword %0, %1"
       :
-      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "v"(voff), "s"(sbase), "{m0}"(lds_addr)
       : "memory");
 }
 

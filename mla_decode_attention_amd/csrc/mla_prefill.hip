@@ -60,11 +60,10 @@ __device__ __forceinline__ int lds_byte(int key, int chunk) {
 
 __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "v"(voff), "s"(sbase), "{m0}"(lds_addr)
       : "memory");
 }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

@@ -24,7 +24,7 @@ from .mla_oracle import (  # noqa: F401
     PAGE_TOKENS, D_QK, D_V,
     bf16_bits_to_f64, e4m3fn_value, E4M3FN_TABLE, decode_e4m3fn,
     sequence_rows, visible_counts, attend, attend_partials, lse_merge,
-    mla_decode, mla_decode_sequence, mla_decode_varlen, split_schedule,
+    mla_decode, mla_decode_sequence, mla_decode_varlen,
     E4M3FN_MAX, encode_e4m3fn, quantize_token_e4m3, append_kv, quantize_query_rows_e4m3,
     D_NOPE, D_ROPE, D_QK_PREFILL, D_V_PREFILL, mla_prefill,
 )

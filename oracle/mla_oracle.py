@@ -218,81 +218,6 @@ def mla_decode(q_bits, cache, block_table, seqlens, softmax_scale, kv_dtype="bf1
 
 
 # --------------------------------------------------------------------------
-# Split-KV schedule (integer work; the GPU scheduler must match it exactly).
-# --------------------------------------------------------------------------
-
-def split_schedule(seqlens, num_units, min_tiles_per_unit=8, seq_cost=3):
-    """Cut the flattened (sequence, 64-token tile) space into contiguous units
-    of about equal cost, a sequence's start costing `seq_cost` tiles (the
-    library charges 1 for shapes of at most 16 rows, 3 above).
-
-    T_b = ceil(L_b / 64) tiles per sequence, prefix[b] = sum of T before b,
-    T = prefix[B]. On a weighted line, a sequence with tiles occupies
-    seq_cost + T_b positions (its start cost, then its tiles), from
-    wpre[b] = sum over b' < b of (seq_cost + T_b' if T_b' else 0); W is the
-    total. With U' = max(1, min(num_units, floor(W / max(min_tiles, 1)))), the
-    line is cut at cut[u] = floor(u * W / U') for u = 0..U'. Unit u < U'
-    starts at the flattened tile its cut names: the tile at that position, or
-    the sequence's first tile when the cut falls in the start cost; unit u
-    covers tiles [unit_begin[u], unit_begin[u + 1]) and may be empty; units
-    u >= U' start at T and are empty. A sequence whose tiles fall in k units
-    is split into k partials; the piece in unit u is split number
-    u - seq_first_unit[b], seq_first_unit[b] being the unit holding its first
-    tile. A sequence with no tiles has 0 partials.
-
-    Returns a dict of plain Python ints/lists:
-      units_cut (U'), units_used (units with at least one tile), prefix [B+1],
-      num_splits [B], split_offset [B+1] (cumulative), total_partials,
-      unit_begin [num_units + 1], unit_first_seq [num_units] (the sequence
-      holding each unit's first tile, B past the end), seq_first_unit [B]
-      (0 for a sequence without tiles).
-    """
-    L = [max(int(x), 0) for x in seqlens]
-    B = len(L)
-    T_b = [(x + PAGE_TOKENS - 1) // PAGE_TOKENS for x in L]
-    prefix = [0]
-    wpre = [0]
-    for t in T_b:
-        prefix.append(prefix[-1] + t)
-        wpre.append(wpre[-1] + (seq_cost + t if t else 0))
-    T, W = prefix[-1], wpre[-1]
-    units = max(int(num_units), 1)
-    ucut = max(1, min(units, W // max(int(min_tiles_per_unit), 1)))
-
-    def tile_at(v):
-        if v >= W:
-            return T
-        b = max(i for i in range(B) if wpre[i] <= v and T_b[i] > 0)
-        return prefix[b] + max(0, v - wpre[b] - seq_cost)
-
-    unit_begin = [tile_at(u * W // ucut) if (u < ucut and W > 0) else T for u in range(units + 1)]
-
-    def holder(f):   # the unit whose range holds tile f
-        return max(u for u in range(units) if unit_begin[u] <= f)
-
-    unit_first_seq = []
-    for u in range(units):
-        f = unit_begin[u]
-        unit_first_seq.append(B if f >= T else max(i for i in range(B) if prefix[i] <= f))
-    num_splits, seq_first_unit = [], []
-    for b, t in enumerate(T_b):
-        if t == 0:
-            num_splits.append(0)
-            seq_first_unit.append(0)
-        else:
-            first = holder(prefix[b])
-            num_splits.append(holder(prefix[b] + t - 1) - first + 1)
-            seq_first_unit.append(first)
-    split_offset = [0]
-    for k in num_splits:
-        split_offset.append(split_offset[-1] + k)
-    units_used = sum(1 for u in range(units) if unit_begin[u] < unit_begin[u + 1])
-    return dict(units_cut=ucut, units_used=units_used, prefix=prefix, num_splits=num_splits,
-                split_offset=split_offset, total_partials=split_offset[-1], unit_begin=unit_begin,
-                unit_first_seq=unit_first_seq, seq_first_unit=seq_first_unit)
-
-
-# --------------------------------------------------------------------------
 # Appending new tokens' latent rows to the cache (the step before attention
 # in a decode step; cache quantisation C8 of PaddleNLP issue #10157's
 # overview, read as OCP E4M3FN codes with one fp32 scale per token).

@@ -7,6 +7,7 @@ import oracle
 import mla_decode_attention_amd as mla
 from workloads import config, make_workload, PAGE_TOKENS
 from _gpu_util import to_device, run_gpu, reference, assert_parity
+from _split_contract import check_metadata, schedule_words
 
 pytestmark = pytest.mark.gpu
 
@@ -122,27 +123,58 @@ def test_split_and_unsplit_agree():
 
 # ----------------------------------------------------------------- scheduler + combine
 
-@pytest.mark.parametrize("lens,units,mt", [
+METADATA_CASES = [
     ([256], 256, 0), ([4096] * 7, 16, 0), ([1, 63, 64, 65, 0, 700], 5, 1), ([0, 0], 4, 8),
     ([65536, 512, 3000, 70], 64, 0), ([130] * 3, 1000, 1), (list(range(0, 5000, 37)), 250, 0),
     # a large batch: 8000 sequences over 400 units, several sequences per thread
     ([int(x) for x in np.random.default_rng(5).integers(0, 3000, 8000)], 400, 0),
-])
-@pytest.mark.parametrize("q_len,heads,cost", [(1, 16, 1), (2, 128, 3)])
-def test_metadata_matches_oracle_schedule(lens, units, mt, q_len, heads, cost):
+]
+
+
+def _device_metadata(lens, units, mt, q_len, heads):
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
     plan = mla.get_split_metadata(sl, q_len, heads, num_units=units, min_tiles_per_unit=mt)
-    md = plan.metadata.cpu().numpy()
-    sch = oracle.split_schedule(lens, units, mt if mt else 8, cost)
-    B = len(lens)
-    assert md[0] == 0x4D4C4132 and md[1] == B and md[2] == units and md[6] == cost
-    assert md[3] == sch["units_cut"] and md[4] == sch["total_partials"] and md[5] == sch["units_used"]
-    assert list(md[8:8 + B + 1]) == sch["prefix"]
-    assert list(md[9 + B:10 + 2 * B]) == sch["split_offset"]
-    base = 10 + 2 * B
-    assert list(md[base:base + units]) == sch["unit_first_seq"]
-    assert list(md[base + units:base + 2 * units + 1]) == sch["unit_begin"]
-    assert list(md[base + 2 * units + 1:base + 2 * units + 1 + B]) == sch["seq_first_unit"]
+    return plan.metadata.cpu().numpy()
+
+
+@pytest.mark.parametrize("lens,units,mt", METADATA_CASES)
+@pytest.mark.parametrize("q_len,heads,cost", [(1, 16, 1), (2, 128, 3)])
+def test_metadata_is_a_valid_schedule(lens, units, mt, q_len, heads, cost):
+    """Properties every valid split schedule has, whatever its balance rule:
+    each tile in exactly one unit, contiguous unit ranges, consecutive units
+    per sequence, offsets and first units that agree with the ranges, and
+    every unit's cost within one sequence start of an even share."""
+    md = _device_metadata(lens, units, mt, q_len, heads)
+    check_metadata(md, lens, units, mt if mt else 8, cost)
+
+
+def test_metadata_is_valid_on_random_batches():
+    rng = np.random.default_rng(123)
+    for _ in range(24):
+        B = int(rng.choice([1, 3, 32, 129, 1000]))
+        kind = rng.integers(0, 3)
+        if kind == 0:
+            lens = rng.integers(0, 5000, B)
+        elif kind == 1:
+            lens = np.exp(rng.uniform(np.log(1), np.log(70000), B)).astype(int)
+        else:
+            lens = rng.choice([0, 1, 64, 65, 4096], B)
+        lens = [int(x) for x in lens]
+        units = int(rng.choice([1, 7, 64, 256, 1024]))
+        mt = int(rng.choice([0, 1, 3, 8, 100]))
+        q_len, heads, cost = [(1, 16, 1), (2, 128, 3)][int(rng.integers(0, 2))]
+        md = _device_metadata(lens, units, mt, q_len, heads)
+        check_metadata(md, lens, units, mt if mt else 8, cost)
+
+
+@pytest.mark.parametrize("lens,units,mt", METADATA_CASES)
+@pytest.mark.parametrize("q_len,heads,cost", [(1, 16, 1), (2, 128, 3)])
+def test_metadata_matches_header_definition(lens, units, mt, q_len, heads, cost):
+    """The device metadata is word for word the rule include/mla_decode.h
+    states (the library's own contract; not part of what the method computes)."""
+    md = _device_metadata(lens, units, mt, q_len, heads)
+    want = schedule_words(lens, units, mt if mt else 8, cost)
+    assert [int(x) for x in md[:len(want)]] == want
 
 
 @pytest.mark.parametrize("R", [16, 256])
@@ -175,16 +207,27 @@ def test_combine_matches_oracle_merge(R):
 
 # ----------------------------------------------------------------- full sizes, sampled
 
+# every sequence of the smaller workloads; at least 16 of the two largest
+FULL_SIZE_SAMPLE = {"tiny": None, "share16": None, "ragged": None, "mtp": 16, "fp8": 16}
+
+
 @pytest.mark.parametrize("name", ["tiny", "share16", "mtp", "ragged", "fp8"])
-def test_full_size_sampled(name):
+def test_full_size(name):
     """Whole-batch run in the launch configuration the benchmark times (default
-    split plan), checked against the oracle on a sample of sequences."""
+    split plan), compared with the oracle on every sequence of tiny, share16
+    and ragged, and on 16 sequences (the first, the last and 14 drawn) of mtp
+    and fp8."""
     w = config(name, seed=0)
     out, lse, _ = run_gpu(w, split=True)
     B = w.batch
-    sample = sorted({0, B - 1, int(np.argmax(w.seqlens)), B // 2})
+    k = FULL_SIZE_SAMPLE[name]
+    if k is None:
+        sample = list(range(B))
+    else:
+        rng = np.random.default_rng(99)
+        sample = sorted({0, B - 1} | set(int(x) for x in rng.choice(np.arange(1, B - 1), k - 2, replace=False)))
     ref_out, ref_lse = reference(w, batch_indices=sample)
-    assert_parity(w, out[sample], lse[sample], ref_out, ref_lse, f"{name} full, sample {sample}")
+    assert_parity(w, out[sample], lse[sample], ref_out, ref_lse, f"{name} full, {len(sample)} sequences")
 
 
 # ------------------------------------------------------- lazy-rescale coverage

@@ -155,6 +155,8 @@ def test_prefill_argument_errors(lib):
     assert call(mq=0) == INVALID
     assert call(H=0) == INVALID
     assert call(H=70000) == INVALID
+    # (query blocks x sequences x heads) past the 32-bit workgroup index
+    assert call(B=40000, mq=1 << 15, H=256) == INVALID
     assert call(sm=float("nan")) == INVALID
     assert call(q=FAKE_ODD) == INVALID
     assert call(out=FAKE_ODD) == INVALID

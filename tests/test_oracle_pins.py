@@ -353,75 +353,6 @@ def test_fp8_rows_match_torch_dequant():
     assert np.array_equal(rows, ref)
 
 
-# ----------------------------------------------------------------- schedule
-
-def _walk_schedule(seqlens, num_units, min_tiles, seq_cost=3):
-    """Brute force: lay the sequences on a weighted line tile by tile (each
-    sequence with tiles first takes seq_cost empty positions), list the cut
-    points, and give every tile to the last unit whose cut is at or before
-    its position."""
-    T_b = [-(-max(int(x), 0) // 64) for x in seqlens]
-    W = sum(t + seq_cost for t in T_b if t)
-    ucut = max(1, min(num_units, W // max(min_tiles, 1)))
-    cuts = [u * W // ucut for u in range(ucut)]
-    owner = []   # unit of each flattened tile
-    pos = 0
-    for t in T_b:
-        if t:
-            pos += seq_cost
-        for _ in range(t):
-            owner.append(max(u for u in range(ucut) if cuts[u] <= pos))
-            pos += 1
-    assert pos == W
-    pieces = {}
-    f = 0
-    for b, t in enumerate(T_b):
-        pieces[b] = sorted(set(owner[f:f + t]))
-        f += t
-    # a unit starts at its first tile; units without tiles start where the
-    # next tile owned by a later unit is (or at T)
-    begin = [next((i for i, o in enumerate(owner) if o >= u), len(owner)) for u in range(num_units + 1)]
-    return ucut, pieces, begin, owner
-
-
-@pytest.mark.parametrize("seqlens,units,mt,cost", [
-    ([256], 256, 8, 3), ([4096] * 7, 16, 8, 3), ([1, 63, 64, 65, 0, 700], 5, 1, 1),
-    ([0, 0], 4, 8, 3), ([65536, 512, 3000, 70], 64, 8, 3), ([130] * 3, 1000, 1, 1),
-    ([0, 512, 0, 0, 9000, 64, 0], 12, 1, 3), ([700] * 40 + [65536], 128, 8, 3),
-    ([2500] * 64, 256, 8, 1), ([3000, 1, 1, 1, 5000], 7, 2, 1),
-])
-def test_split_schedule_matches_walk(seqlens, units, mt, cost):
-    sch = oracle.split_schedule(seqlens, units, mt, cost)
-    ucut, pieces, begin, owner = _walk_schedule(seqlens, units, mt, cost)
-    assert sch["units_cut"] == ucut
-    assert sch["unit_begin"] == begin
-    for b in range(len(seqlens)):
-        assert sch["num_splits"][b] == len(pieces[b])
-        if pieces[b]:
-            assert sch["seq_first_unit"][b] == pieces[b][0]
-            # pieces of a sequence sit in consecutive units
-            assert pieces[b] == list(range(pieces[b][0], pieces[b][-1] + 1))
-    assert sch["total_partials"] == sum(len(p) for p in pieces.values())
-    assert sch["units_used"] == len(set(owner))
-    assert max(owner, default=0) < units
-
-
-def test_split_schedule_balances_sequence_starts():
-    # many short sequences and one long one: with the start cost charged, every
-    # unit's cost (tiles + 3 per sequence start in it) is within one start of
-    # W / units, and every unit holds work
-    seqlens = [600] * 30 + [65536]
-    sch = oracle.split_schedule(seqlens, 64, 1, 3)
-    T_b = [-(-x // 64) for x in seqlens]
-    W = sum(t + 3 for t in T_b)
-    ub = sch["unit_begin"]
-    starts = set(sch["prefix"][b] for b in range(len(seqlens)) if T_b[b])
-    for u in range(64):
-        cost = (ub[u + 1] - ub[u]) + 3 * sum(1 for f in starts if ub[u] <= f < ub[u + 1])
-        assert cost <= -(-W // 64) + 3
-    assert sch["units_used"] == 64
-
-
 def test_workload_generators_are_seeded_and_shaped():
     a = config("share16", small=True, seed=3)
     b = config("share16", small=True, seed=3)
