@@ -3,19 +3,29 @@
 
 One step = one pass of the whole path over one batch: split schedule
 (mla_get_split_metadata), then mla_decode_fwd (attention kernel + LSE merge of
-split sequences). Inputs are seeded synthetic data already resident in HBM.
-To keep the 256 MB Infinity Cache from serving repeat reads, steps rotate over
-several copies of the page pool (each step reads a copy it did not read in the
-previous few steps).
+split sequences); the tiny workload (one sequence of four pages) runs the
+unsplit single-launch path. Inputs are seeded synthetic data already resident
+in HBM. To keep the 256 MB Infinity Cache from serving repeat reads, steps
+rotate over several copies of the page pool.
 
-Prints ONE JSON line (default workload: batch 64, 16 heads, q_len 1, seqlens
-U[1024,4096], bf16 cache) with:
-  value      effective KV GB/s of the whole step (KV bytes / step time), the
-             step replayed from a captured HIP graph (--eager: direct launches)
-  roofline   the attention kernel alone: algorithmic bytes (HBM-bound shapes)
-             or flops (MFMA-bound shapes) per launch / its mean launch time,
-             timed with HIP events on its own stream, vs the MI355X peak
-  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
+By default the five decode workloads are measured and ONE JSON line is printed.
+Its headline (value, ms_per_step, roofline, cpu_baseline) is the largest one,
+fp8 (batch 128, 128 heads, q_len 2 causal, 8192 cached tokens, fp8 cache), and
+its `configs` array holds every workload:
+  step_ms     whole step, replayed from captured HIP graphs: median, min and
+              mean over the timed steps (each step bracketed by events)
+  kernel_ms   each kernel of the step alone (attention, metadata, combine),
+              from HIP events recorded by the kernel dispatches: median, min,
+              mean over >= 50 launches
+  tflops, kv_gbps, frac_step   the whole step against the binding roofline
+  frac_kernel                  the attention kernel alone (mean launch)
+  traffic                      HBM bytes per attention launch from the
+                               committed rocprofv3 counters (null if the
+                               kernel source changed since)
+`clocks` holds the graphics clock of each XCD and the memory clock read with
+amd-smi while the headline workload runs.
+
+--config NAME measures one workload (also varlen, fp8mma, prefill, extend).
 """
 from __future__ import annotations
 
@@ -23,6 +33,9 @@ import argparse
 import json
 import math
 import os
+import re
+import statistics
+import subprocess
 import sys
 import time
 
@@ -33,7 +46,12 @@ if ROOT not in sys.path:
 METRIC = "MLA decode TFLOP/s + effective KV GB/s, % of roofline, per batch/heads/q_len"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
-PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA (context for the fp8 cache)
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
+DECODE_CONFIGS = ["tiny", "share16", "mtp", "ragged", "fp8"]
+HEADLINE = "fp8"
+# the tiny workload's four pages are one work unit either way: one launch,
+# no schedule, no merge
+UNSPLIT = {"tiny"}
 
 
 def algorithmic(w):
@@ -62,7 +80,6 @@ def kernel_source_digest() -> str:
     """SHA-256 of the attention kernel sources with comments and blank space
     removed, so that editing a comment does not count as changing a kernel."""
     import hashlib
-    import re
     src = ""
     for name in ("mla_kernels.hip", "mla_prefill.hip"):
         with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", name)) as f:
@@ -88,16 +105,18 @@ def measured_traffic(config_name: str):
     return int(t["configs"][config_name]["bytes"])
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle as it stands, on whole sequences in batch order (starting
     over after the last) until `seconds` pass."""
-    import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     e, f = (2, 0) if w.kv_dtype == "bf16" else (1, 4)
     done, kv, flops = 0, 0, 0
     t0 = time.perf_counter()
@@ -117,16 +136,310 @@ def cpu_baseline(w, seconds: float):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    tflops = flops / dt / 1e12
+    mfma_bound = w.num_heads * int(max(w.q_lens)) > 16
+    return {"value": round(tflops, 6) if mfma_bound else round(kv / dt / 1e9, 4),
+            "unit": "TFLOP/s" if mfma_bound else "GB/s", "cores": int(blas_threads()), "kind": "oracle",
             "sample": f"{done} whole-sequence evaluations in batch order ({done / w.batch:.2f} passes over "
-                      f"the {w.batch} sequences), {dt:.1f} s wall, fp64 numpy", "tflops": flops / dt / 1e12,
-            "seconds": round(dt, 2)}
+                      f"the {w.batch} sequences), {dt:.1f} s wall, fp64 numpy",
+            "tflops": round(tflops, 6), "kv_gbps": round(kv / dt / 1e9, 4), "seconds": round(dt, 2)}
+
+
+def stats(ms):
+    """median / min / mean of a list of times (ms), rounded."""
+    if not ms:
+        return None
+    return {"median": round(statistics.median(ms), 5), "min": round(min(ms), 5),
+            "mean": round(sum(ms) / len(ms), 5), "n": len(ms)}
+
+
+def read_clocks(busy):
+    """Graphics clock of each XCD and the memory clock (MHz) from amd-smi,
+    read while `busy()` keeps the GPU working; None if amd-smi is missing."""
+    try:
+        p = subprocess.Popen(["amd-smi", "metric", "-c"], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                             text=True)
+    except OSError:
+        return None
+    t0 = time.time()
+    while p.poll() is None and time.time() - t0 < 20:
+        busy()
+    if p.poll() is None:
+        p.kill()
+        return None
+    out = p.stdout.read()
+    gfx = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out)]
+    mem = [int(m) for m in re.findall(r"MEM_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out)]
+    if not gfx:
+        return None
+    return {"sclk_mhz": gfx, "mclk_mhz": mem, "source": "amd-smi metric -c during graph replays"}
+
+
+def roofline_for(alg, fp8_mma):
+    """(bound, T_roof seconds) of one step's algorithmic work."""
+    t_hbm = alg["bytes"] / (PEAK_HBM_GBPS * 1e9)
+    peak = PEAK_FP8_TFLOPS if fp8_mma else PEAK_BF16_TFLOPS
+    t_mfma = alg["flops"] / (peak * 1e12)
+    return ("hbm", t_hbm, peak) if t_hbm >= t_mfma else ("mfma", t_mfma, peak)
+
+
+class DecodeRun:
+    """One decode workload on the device: inputs, plan, step, timings."""
+
+    def __init__(self, name, args, fp8_mma=False):
+        import numpy as np
+        import torch
+        import mla_decode_attention_amd as mla
+        from workloads import config, CONFIG_TEXT
+        self.mla, self.torch = mla, torch
+        self.name = name
+        self.fp8_mma = fp8_mma
+        self.wname = "fp8" if fp8_mma else name
+        t_gen = time.perf_counter()
+        self.w = w = config(self.wname, seed=0)
+        self.alg = algorithmic(w)
+        self.text = CONFIG_TEXT[self.wname] + (
+            "; queries and P in E4M3 on fp8 MFMA (mla_decode_fwd_fp8mma)" if fp8_mma else "")
+        print(f"[bench] {name}: generated in {time.perf_counter() - t_gen:.1f} s; "
+              f"KV {self.alg['kv_bytes'] / 1e6:.1f} MB, {self.alg['flops'] / 1e9:.1f} GFLOP",
+              file=sys.stderr, flush=True)
+        dev = torch.device("cuda:0")
+        self.q = torch.from_numpy(w.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        if w.kv_dtype == "bf16":
+            kv0 = torch.from_numpy(w.cache.view(np.int16)).to(dev).view(torch.bfloat16)
+            scale0 = None
+        else:
+            kv0 = torch.from_numpy(w.cache).to(dev)
+            scale0 = torch.from_numpy(w.kv_scale).to(dev)
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        self.sl = torch.from_numpy(w.seqlens).to(dev)
+        pool_bytes = kv0.numel() * kv0.element_size()
+        self.sets = args.sets or max(1, min(8, math.ceil(768e6 / max(pool_bytes, 1))))
+        self.kvs = [kv0] + [kv0.clone() for _ in range(self.sets - 1)]
+        self.scales = [scale0] + [None if scale0 is None else scale0.clone() for _ in range(self.sets - 1)]
+        if w.varlen:
+            self.cu_q = torch.from_numpy(w.cu_q).to(dev)
+            T = int(w.cu_q[-1])
+            self.out = torch.empty((T, w.num_heads, 512), dtype=torch.float32, device=dev)
+            self.lse = torch.empty((T, w.num_heads), dtype=torch.float32, device=dev)
+        else:
+            self.out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.float32, device=dev)
+            self.lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
+        self.split = not (name in UNSPLIT and not args.num_units)
+        self.units = 0
+        self.plan = None
+        if self.split:
+            self.units = args.num_units or mla.default_num_units(w.batch, w.q_len, w.num_heads, varlen=w.varlen)
+            self.plan = mla.get_split_metadata(self.sl, w.q_len, w.num_heads, num_units=self.units,
+                                               min_tiles_per_unit=args.min_tiles, varlen=w.varlen)
+        self.min_tiles = args.min_tiles
+        self.latent = None
+        if args.append_tokens:
+            g = torch.Generator(device="cpu").manual_seed(1)
+            lat32 = torch.randn((w.batch, args.append_tokens, 576), generator=g)
+            self.latent = lat32.to(torch.bfloat16).to(dev)
+        self.graphs = None
+
+    def step(self, i):
+        mla, w = self.mla, self.w
+        k = i % self.sets
+        if self.latent is not None:
+            mla.append_kv(self.latent, self.bt, self.sl, self.kvs[k], self.scales[k])
+        if self.split:
+            mla.get_split_metadata(self.sl, w.q_len, w.num_heads, num_units=self.units,
+                                   min_tiles_per_unit=self.min_tiles, metadata=self.plan.metadata,
+                                   workspace=self.plan.workspace, varlen=w.varlen)
+        if w.varlen:
+            mla.decode_varlen(self.q, self.cu_q, w.q_len, self.kvs[k], self.bt, self.sl, w.softmax_scale,
+                              kv_scale=self.scales[k], plan=self.plan, out=self.out, lse=self.lse)
+        else:
+            mla.decode(self.q, self.kvs[k], self.bt, self.sl, w.softmax_scale, kv_scale=self.scales[k],
+                       plan=self.plan, out=self.out, lse=self.lse, fp8_mma=self.fp8_mma)
+
+    def time_kernels(self, reps):
+        """Each kernel of the step alone: events recorded by its dispatches."""
+        mla, torch = self.mla, self.torch
+        torch.cuda.synchronize()
+        mla.profile_enable(True)
+        for k in (mla.PROFILE_ATTENTION, mla.PROFILE_METADATA, mla.PROFILE_COMBINE):
+            mla.profile_read_launches(k, capacity=0)
+        for i in range(reps):
+            self.step(i)
+        torch.cuda.synchronize()
+        mla.profile_enable(False)
+        return {kind: mla.profile_read_launches(k, capacity=reps + 8)
+                for kind, k in (("attention", mla.PROFILE_ATTENTION), ("metadata", mla.PROFILE_METADATA),
+                                ("combine", mla.PROFILE_COMBINE))}
+
+    def capture(self, eager):
+        torch = self.torch
+        if eager:
+            return
+        self.graphs = []
+        for k in range(self.sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(k)
+            self.graphs.append(g)
+
+    def run_step(self, i):
+        if self.graphs is None:
+            self.step(i)
+        else:
+            self.graphs[i % self.sets].replay()
+
+    def time_steps(self, steps, warmup):
+        """K steps back to back, an event between consecutive steps: per-step
+        times and the mean over the bracketed region."""
+        torch = self.torch
+        for i in range(warmup):
+            self.run_step(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            self.run_step(i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return per, ev[0].elapsed_time(ev[steps]) / steps
+
+    def entry(self, kern, per_step, mean_step, traffic_name):
+        """The config's record for the JSON line."""
+        w, alg = self.w, self.alg
+        bound, t_roof, peak = roofline_for(alg, self.fp8_mma)
+        st = stats(per_step)
+        attn = stats(kern["attention"])
+        step_med_s = st["median"] * 1e-3
+        kv_gbps = alg["kv_bytes"] / step_med_s / 1e9
+        tflops = alg["flops"] / step_med_s / 1e12
+        traffic = measured_traffic(traffic_name)
+        return {
+            "name": self.name,
+            "workload": self.text,
+            "batch": w.batch, "heads": w.num_heads,
+            "q_len": w.q_len if not w.varlen else "per-sequence, max %d" % w.q_len,
+            "kv_dtype": w.kv_dtype, "tokens": alg["tokens"], "pages": alg["pages"],
+            "path": "split (metadata + attention + merge)" if self.split else "unsplit (one attention launch)",
+            "num_units": self.units if self.split else None,
+            "pool_copies": self.sets,
+            "algorithmic_bytes": alg["bytes"], "algorithmic_flops": alg["flops"], "kv_bytes": alg["kv_bytes"],
+            "bound": bound, "t_roof_us": round(t_roof * 1e6, 2), "peak": peak,
+            "step_ms": st, "step_ms_bracketed_mean": round(mean_step, 5),
+            "kernel_ms": {"attention": attn, "metadata": stats(kern["metadata"]),
+                          "combine": stats(kern["combine"])},
+            "tflops": round(tflops, 2), "kv_gbps": round(kv_gbps, 1),
+            "frac_step": round(t_roof / step_med_s, 4),
+            "frac_kernel": round(t_roof / (attn["mean"] * 1e-3), 4),
+            "frac_kernel_median": round(t_roof / (attn["median"] * 1e-3), 4),
+            "traffic_bytes": traffic,
+            "traffic_ratio": None if traffic is None else round(traffic / alg["bytes"], 3),
+        }
+
+
+def roofline_object(e, kernel_name):
+    """The contract's roofline object for the dominant (attention) kernel:
+    algorithmic work per launch over its mean dispatch-timed launch."""
+    attn_s = e["kernel_ms"]["attention"]["mean"] * 1e-3
+    if e["bound"] == "hbm":
+        achieved, unit = e["algorithmic_bytes"] / attn_s / 1e9, "GB/s"
+        peak = PEAK_HBM_GBPS
+    else:
+        achieved, unit = e["algorithmic_flops"] / attn_s / 1e12, "TFLOP/s"
+        peak = e["peak"]
+    return {"bound": e["bound"], "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": e["traffic_bytes"],
+            "kernel": kernel_name, "kernel_ms": e["kernel_ms"]["attention"]["mean"],
+            "kernel_ms_median": e["kernel_ms"]["attention"]["median"],
+            "launches": e["kernel_ms"]["attention"]["n"],
+            "frac_step": e["frac_step"],
+            "algorithmic_bytes": e["algorithmic_bytes"], "algorithmic_flops": e["algorithmic_flops"],
+            "t_roof_us": e["t_roof_us"]}
+
+
+KERNEL_NAMES = {"tiny": "decode_kernel_pc", "share16": "decode_kernel_pc", "mtp": "decode_kernel_x",
+                "ragged": "decode_kernel_x", "fp8": "decode_kernel_xf", "varlen": "decode_kernel_x",
+                "fp8mma": "decode_kernel_q8"}
+
+
+def bench_decode(args):
+    import torch
+    torch.cuda.set_device(torch.device("cuda:0"))
+    names = DECODE_CONFIGS if args.config == "all" else [args.config]
+    headline = HEADLINE if args.config == "all" else args.config
+    reps = max(args.reps, 50)
+    entries, head = [], None
+    clocks = None
+    for name in names:
+        run = DecodeRun(name, args, fp8_mma=(name == "fp8mma"))
+        if args.calib_copy_mib:
+            a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+            b = torch.empty_like(a)
+            b.copy_(a)
+            torch.cuda.synchronize()
+            del a, b
+        for i in range(args.warmup):
+            run.step(i)
+        kern = run.time_kernels(reps)
+        run.capture(args.eager)
+        per, mean = run.time_steps(args.steps if name == headline else max(args.steps, 50), args.warmup)
+        e = run.entry(kern, per, mean, name)
+        entries.append(e)
+        print(f"[bench] {name}: step median {e['step_ms']['median'] * 1e3:.1f} us, attention kernel mean "
+              f"{e['kernel_ms']['attention']['mean'] * 1e3:.1f} us, frac_step {e['frac_step']:.3f}, "
+              f"frac_kernel {e['frac_kernel']:.3f}", file=sys.stderr, flush=True)
+        if name == headline:
+            head = (run, e, mean)
+            if not args.no_clocks:
+                i_box = [0]
+
+                def busy():
+                    for _ in range(20):
+                        run.run_step(i_box[0])
+                        i_box[0] += 1
+                    torch.cuda.synchronize()
+                clocks = read_clocks(busy)
+        if name != headline:
+            del run
+            torch.cuda.empty_cache()
+
+    run, e, mean = head
+    alg = run.alg
+    step_s = mean * 1e-3
+    value = alg["flops"] / step_s / 1e12 if e["bound"] == "mfma" else alg["kv_bytes"] / step_s / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2 if e["bound"] == "mfma" else 1),
+        "unit": "TFLOP/s" if e["bound"] == "mfma" else "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if run.fp8_mma else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{e['name']}: {e['workload']}", "batch": e["batch"], "heads": e["heads"],
+                   "q_len": e["q_len"], "kv_dtype": e["kv_dtype"], "tokens": e["tokens"], "pages": e["pages"],
+                   "path": e["path"], "num_units": e["num_units"], "pool_copies": e["pool_copies"], "seed": 0,
+                   "append_tokens": args.append_tokens,
+                   "step_launch": "direct launches" if args.eager else "HIP graph replay"},
+        "tflops": round(alg["flops"] / step_s / 1e12, 2),
+        "kv_gbps": round(alg["kv_bytes"] / step_s / 1e9, 1),
+        "roofline": roofline_object(e, KERNEL_NAMES.get(e["name"], "decode_kernel")),
+        "clocks": clocks,
+        "configs": entries,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(run.w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
 
 
 def prefill_algorithmic(w):
     """Flops (QK 192 + PV 128 multiply-adds per visible (row, key) pair per
     head) and bytes (q, k_nope, k_rope, v once; out and lse) of one call."""
-    import numpy as np
     vis = 0
     for N, L in zip(w.q_lens, w.k_lens):
         N, L = int(N), int(L)
@@ -144,11 +457,6 @@ def prefill_cpu_baseline(w, seconds: float):
     count until `seconds` pass."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     N0, L0 = int(w.q_lens[0]), int(w.k_lens[0])
     n, flops, dt = 16, 0, 0.0
     t0 = time.perf_counter()
@@ -164,7 +472,7 @@ def prefill_cpu_baseline(w, seconds: float):
         if n == N0 or time.perf_counter() - t0 >= seconds or dt_i * 4 > seconds:
             break
         n *= 2
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
             "sample": f"first {n} of {N0} queries of sequence 0 (an extend over its first {p_end} keys), "
                       f"{dt:.1f} s wall for that call, fp64 numpy", "seconds": round(dt, 2)}
 
@@ -201,25 +509,28 @@ def bench_prefill(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    reps = max(args.reps, 50)
     mla.profile_enable(True)
-    mla.profile_read()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
+    mla.profile_read_launches(mla.PROFILE_ATTENTION, capacity=0)
+    for _ in range(reps):
         step()
-    t1.record()
     torch.cuda.synchronize()
     mla.profile_enable(False)
-    step_ms = t0.elapsed_time(t1) / args.steps
-    k_total, launches = mla.profile_read()
-    k_ms = k_total / max(launches, 1)
+    kern = stats(mla.profile_read_launches(mla.PROFILE_ATTENTION, capacity=reps + 8))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = stats([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    step_ms = ev[0].elapsed_time(ev[args.steps]) / args.steps
     tflops = alg["flops"] / (step_ms * 1e-3) / 1e12
-    achieved = alg["flops"] / (k_ms * 1e-3) / 1e12
+    achieved = alg["flops"] / (kern["mean"] * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.config),
-            "kernel": "prefill_kernel", "kernel_ms": round(k_ms, 5), "launches": launches,
+            "kernel": "prefill_kernel", "kernel_ms": kern["mean"], "kernel_ms_median": kern["median"],
+            "launches": kern["n"], "frac_step": round(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12) / (per["median"] * 1e-3), 4),
             "algorithmic_bytes": alg["bytes"], "algorithmic_flops": alg["flops"],
             "t_roof_us": round(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e6, 2)}
     line = {
@@ -238,6 +549,7 @@ def bench_prefill(args):
         "config": {"workload": f"{args.config}: {PREFILL_TEXT[args.config]}", "batch": w.batch, "heads": H,
                    "query_tokens": Tq, "key_tokens": int(w.cu_k[-1]), "visible_pairs": alg["visible_pairs"],
                    "seed": 0},
+        "step_ms": per,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -249,19 +561,22 @@ def bench_prefill(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100, help="timed steps of the headline workload")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="share16",
-                    choices=["tiny", "share16", "mtp", "ragged", "fp8", "varlen", "fp8mma", "prefill", "extend"],
-                    help="workload; fp8mma = the fp8 workload on mla_decode_fwd_fp8mma (queries and P in "
-                         "E4M3, fp8 matrix cores; an approximation of the default path); prefill / extend = "
-                         "the second workload (mla_prefill_fwd, un-absorbed MLA, value in TFLOP/s)")
+    ap.add_argument("--reps", type=int, default=100, help="kernel launches timed per workload (at least 50)")
+    ap.add_argument("--config", default="all",
+                    choices=["all", "tiny", "share16", "mtp", "ragged", "fp8", "varlen", "fp8mma", "prefill",
+                             "extend"],
+                    help="all = the five decode workloads, headline fp8; fp8mma = the fp8 workload on "
+                         "mla_decode_fwd_fp8mma (queries and P in E4M3, fp8 matrix cores; an approximation of "
+                         "the default path); prefill / extend = the second workload (mla_prefill_fwd)")
     ap.add_argument("--sets", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--num-units", type=int, default=0, help="split work units (0 = library default)")
     ap.add_argument("--min-tiles", type=int, default=0,
                     help="minimum tiles per split unit (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true", help="do not read the clocks with amd-smi")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="also run the cache append (mla_append_kv) of this many new tokens per sequence "
                          "in every step, before the decode (their rows are the last positions of each "
@@ -278,165 +593,12 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): this build "
               "has no multi-GPU path; the per-GPU kernel is the whole computation.", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1:
+        ap.error("--steps must be >= 1")
 
     if args.config in ("prefill", "extend"):
         return bench_prefill(args)
-
-    import numpy as np
-    import torch
-    import mla_decode_attention_amd as mla
-    from workloads import config, CONFIG_TEXT
-
-    fp8_mma = args.config == "fp8mma"
-    wname = "fp8" if fp8_mma else args.config
-    t_gen = time.perf_counter()
-    w = config(wname, seed=0)
-    alg = algorithmic(w)
-    print(f"[bench] {args.config}: generated in {time.perf_counter() - t_gen:.1f} s; "
-          f"KV {alg['kv_bytes'] / 1e6:.1f} MB, {alg['flops'] / 1e9:.1f} GFLOP", file=sys.stderr, flush=True)
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    q = torch.from_numpy(w.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    if w.kv_dtype == "bf16":
-        kv0 = torch.from_numpy(w.cache.view(np.int16)).to(dev).view(torch.bfloat16)
-        scale0 = None
-    else:
-        kv0 = torch.from_numpy(w.cache).to(dev)
-        scale0 = torch.from_numpy(w.kv_scale).to(dev)
-    bt = torch.from_numpy(w.block_table).to(dev)
-    sl = torch.from_numpy(w.seqlens).to(dev)
-    pool_bytes = kv0.numel() * kv0.element_size()
-    sets = args.sets or max(1, min(8, math.ceil(768e6 / max(pool_bytes, 1))))
-    kvs = [kv0] + [kv0.clone() for _ in range(sets - 1)]
-    scales = [scale0] + [None if scale0 is None else scale0.clone() for _ in range(sets - 1)]
-    if w.varlen:
-        cu_q = torch.from_numpy(w.cu_q).to(dev)
-        T = int(w.cu_q[-1])
-        out = torch.empty((T, w.num_heads, 512), dtype=torch.float32, device=dev)
-        lse = torch.empty((T, w.num_heads), dtype=torch.float32, device=dev)
-    else:
-        out = torch.empty((w.batch, w.q_len, w.num_heads, 512), dtype=torch.float32, device=dev)
-        lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
-    units = args.num_units or mla.default_num_units(w.batch, w.q_len, w.num_heads, varlen=w.varlen)
-    plan = mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units, min_tiles_per_unit=args.min_tiles)
-
-    if args.calib_copy_mib:
-        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-
-    latent = None
-    if args.append_tokens:
-        g = torch.Generator(device="cpu").manual_seed(1)
-        lat32 = torch.randn((w.batch, args.append_tokens, 576), generator=g)
-        latent = lat32.to(torch.bfloat16).to(dev)
-
-    def step(i):
-        if latent is not None:
-            k = i % sets
-            mla.append_kv(latent, bt, sl, kvs[k], scales[k])
-        mla.get_split_metadata(sl, w.q_len, w.num_heads, num_units=units, metadata=plan.metadata,
-                               workspace=plan.workspace)
-        k = i % sets
-        if w.varlen:
-            mla.decode_varlen(q, cu_q, w.q_len, kvs[k], bt, sl, w.softmax_scale, kv_scale=scales[k], plan=plan,
-                              out=out, lse=lse)
-        else:
-            mla.decode(q, kvs[k], bt, sl, w.softmax_scale, kv_scale=scales[k], plan=plan, out=out, lse=lse,
-                       fp8_mma=fp8_mma)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # attention kernel alone: direct launches, each recording HIP events with its own dispatch
-    mla.profile_enable(True)
-    mla.profile_read()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    mla.profile_enable(False)
-    step_ms = t0.elapsed_time(t1) / args.steps
-    main_ms_total, launches = mla.profile_read()
-    main_ms = main_ms_total / max(launches, 1)
-
-    # whole step: one captured graph per pool copy (split schedule, attention,
-    # merge), replayed in turn
-    if not args.eager:
-        graphs = []
-        for k in range(sets):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(k)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % sets].replay()
-        torch.cuda.synchronize()
-        t0.record()
-        for i in range(args.steps):
-            graphs[i % sets].replay()
-        t1.record()
-        torch.cuda.synchronize()
-        step_ms = t0.elapsed_time(t1) / args.steps
-
-    step_s = step_ms * 1e-3
-    main_s = main_ms * 1e-3
-    kv_gbps = alg["kv_bytes"] / step_s / 1e9
-    tflops = alg["flops"] / step_s / 1e12
-    t_hbm = alg["bytes"] / (PEAK_HBM_GBPS * 1e9)
-    peak_mfma = PEAK_FP8_TFLOPS if fp8_mma else PEAK_BF16_TFLOPS   # the contraction dtype's peak
-    t_mfma = alg["flops"] / (peak_mfma * 1e12)
-    if t_hbm >= t_mfma:
-        achieved = alg["bytes"] / main_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
-    else:
-        achieved = alg["flops"] / main_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_mfma,
-                "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4), "traffic": None}
-    roof["traffic"] = measured_traffic(args.config)
-    roof.update({"kernel": "decode_kernel", "kernel_ms": round(main_ms, 5), "launches": launches,
-                 "algorithmic_bytes": alg["bytes"], "algorithmic_flops": alg["flops"],
-                 "t_roof_us": round(max(t_hbm, t_mfma) * 1e6, 2)})
-
-    line = {
-        "metric": METRIC,
-        "value": round(kv_gbps, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8" if fp8_mma else "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{args.config}: {CONFIG_TEXT[wname]}" + (
-                       "; queries and P in E4M3 on fp8 MFMA (mla_decode_fwd_fp8mma)" if fp8_mma else ""),
-                   "batch": w.batch,
-                   "heads": w.num_heads, "q_len": w.q_len if not w.varlen else "per-sequence, max %d" % w.q_len,
-                   "query_tokens": int(sum(w.q_lens)), "kv_dtype": w.kv_dtype,
-                   "tokens": alg["tokens"], "pages": alg["pages"], "num_units": units,
-                   "min_tiles_per_unit": args.min_tiles or "library default",
-                   "pool_copies": sets, "seed": 0, "append_tokens": args.append_tokens,
-                   "step_launch": "direct launches" if args.eager else "HIP graph replay"},
-        "tflops": round(tflops, 2),
-        "kv_gbps": round(kv_gbps, 1),
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    return bench_decode(args)
 
 
 if __name__ == "__main__":

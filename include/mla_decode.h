@@ -313,17 +313,29 @@ int mla_append_kv(const void* latent, int batch, int new_tokens, const int32_t* 
 
 /*
  * Measurement hook (diagnostics, not part of the computation).
- * mla_profile_enable(1): from now on every launch of the main attention
- *   kernel (the attention pass of mla_decode_fwd and its variants, not the
- *   merge; the kernel of mla_prefill_fwd) is bracketed by a pair of HIP events
- *   recorded by the dispatch on the caller's stream. Event pairs come from
- *   a pool the library creates on first use (host-side HIP event objects; no
- *   device memory). mla_profile_enable(0) stops recording.
- * mla_profile_read: waits for the recorded events, returns the summed elapsed
- *   time (ms) and the number of recorded launches, and clears the record.
+ * mla_profile_enable(1): from now on every kernel launch of the library is
+ *   bracketed by a pair of HIP events recorded by the dispatch itself on the
+ *   caller's stream, so each interval is that kernel's execution (no launch
+ *   latency). Launches are recorded per kind:
+ *     MLA_PROFILE_ATTENTION  the attention kernel of mla_decode_fwd and its
+ *                            variants, and the kernel of mla_prefill_fwd
+ *     MLA_PROFILE_METADATA   the kernel of mla_get_split_metadata
+ *     MLA_PROFILE_COMBINE    the LSE merge (of a split decode or mla_combine)
+ *   Event pairs come from a pool the library creates on first use (host-side
+ *   HIP event objects; no device memory). mla_profile_enable(0) stops
+ *   recording.
+ * mla_profile_read_launches: waits for the recorded events of one kind, writes
+ *   the elapsed time (ms) of each recorded launch in launch order to
+ *   ms[0 .. min(count, capacity)), sets *count to the number recorded, and
+ *   clears that kind's record. capacity may be 0 (ms may then be NULL).
+ * mla_profile_read: the same for MLA_PROFILE_ATTENTION, as the summed time.
  * Not thread-safe with concurrent decode calls on other threads.
  */
+#define MLA_PROFILE_ATTENTION 0
+#define MLA_PROFILE_METADATA 1
+#define MLA_PROFILE_COMBINE 2
 int mla_profile_enable(int enable);
+int mla_profile_read_launches(int kernel, float* ms, int capacity, int* count);
 int mla_profile_read(double* total_ms, int* launches);
 
 #ifdef __cplusplus

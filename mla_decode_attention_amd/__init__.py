@@ -20,7 +20,8 @@ from typing import Optional
 import torch
 
 __all__ = ["load_library", "library_path", "abi_version", "default_num_units", "metadata_bytes",
-           "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "get_split_metadata", "decode",
+           "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "profile_read_launches",
+           "PROFILE_ATTENTION", "PROFILE_METADATA", "PROFILE_COMBINE", "get_split_metadata", "decode",
            "decode_varlen", "combine", "append_kv", "prefill",
            "MLAError", "KV_BF16", "KV_FP8_E4M3", "PAGE_TOKENS", "D_QK", "D_V"]
 
@@ -71,6 +72,8 @@ def load_library():
                                           c_int, ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
         "mla_profile_enable": (c_int, [c_int]),
         "mla_profile_read": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]),
+        "mla_profile_read_launches": (c_int, [c_int, ctypes.POINTER(ctypes.c_float), c_int,
+                                              ctypes.POINTER(c_int)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -335,6 +338,19 @@ def profile_read():
     ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
     _check(load_library().mla_profile_read(ctypes.byref(ms), ctypes.byref(n)), "mla_profile_read")
     return ms.value, n.value
+
+
+PROFILE_ATTENTION, PROFILE_METADATA, PROFILE_COMBINE = 0, 1, 2
+
+
+def profile_read_launches(kernel: int = PROFILE_ATTENTION, capacity: int = 4096):
+    """Elapsed ms of each recorded launch of one kernel kind (attention,
+    metadata or combine), in launch order; clears that kind's record."""
+    lib = load_library()
+    n = ctypes.c_int(0)
+    buf = (ctypes.c_float * capacity)()
+    _check(lib.mla_profile_read_launches(int(kernel), buf, capacity, ctypes.byref(n)), "mla_profile_read_launches")
+    return [float(buf[i]) for i in range(min(n.value, capacity))]
 
 
 def combine(part_out: torch.Tensor, part_lse: torch.Tensor, seq_part_offsets: torch.Tensor,

@@ -63,12 +63,14 @@ int device_info(DevInfo* out) {
   return MLA_OK;
 }
 
-// Measurement hook state (see mla_profile_enable).
+// Measurement hook state (see mla_profile_enable): per kernel kind, the
+// (start, stop) event pairs recorded by the dispatches, in launch order.
+constexpr int kProfKinds = 3;   // MLA_PROFILE_ATTENTION, _METADATA, _COMBINE
 struct Profile {
   std::mutex mu;
   bool on = false;
-  std::vector<hipEvent_t> pool;                             // free events
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded;  // (start, stop)
+  std::vector<hipEvent_t> pool;                                         // free events
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded[kProfKinds];  // (start, stop)
 };
 Profile g_prof;
 
@@ -81,6 +83,32 @@ hipEvent_t take_event() {
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
+}
+
+// An event pair for the next launch when recording is on (else nulls).
+void prof_begin(hipEvent_t* ev0, hipEvent_t* ev1) {
+  *ev0 = *ev1 = nullptr;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.on) return;
+  *ev0 = take_event();
+  *ev1 = take_event();
+  if (!*ev0 || !*ev1) {
+    if (*ev0) g_prof.pool.push_back(*ev0);
+    if (*ev1) g_prof.pool.push_back(*ev1);
+    *ev0 = *ev1 = nullptr;
+  }
+}
+
+// Keep the pair of a launch that was made (return it to the pool otherwise).
+void prof_end(int kind, hipEvent_t ev0, hipEvent_t ev1, bool launched) {
+  if (!ev0 || !ev1) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (launched) {
+    g_prof.recorded[kind].emplace_back(ev0, ev1);
+  } else {
+    g_prof.pool.push_back(ev0);
+    g_prof.pool.push_back(ev1);
+  }
 }
 
 size_t workspace_need(int batch, int q_len, int num_heads, int units) {
@@ -181,8 +209,11 @@ int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int q_len, i
   // a sequence's start costs what it does in the kernel this shape selects
   const int rows = q_len * num_heads;
   const int cost = mla::variant_for(rows) == mla::VAR_NARROW16 ? mla::kSeqCostNarrow : mla::kSeqCostWide;
+  hipEvent_t ev0, ev1;
+  prof_begin(&ev0, &ev1);
   hipError_t e = mla::launch_metadata(cache_seqlens, batch, num_units, mt, cost, (int32_t*)metadata,
-                                      (hipStream_t)stream);
+                                      (hipStream_t)stream, ev0, ev1);
+  prof_end(MLA_PROFILE_METADATA, ev0, ev1, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "metadata kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -260,29 +291,17 @@ int decode_impl(const void* q, const int32_t* cu_q, int total_q, const void* kv_
 
   const int var = fp8_mma ? mla::VAR_Q8 : mla::variant_for(p.rows);
   hipStream_t s = (hipStream_t)stream;
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  {
-    std::lock_guard<std::mutex> lk(g_prof.mu);
-    if (g_prof.on) {
-      ev0 = take_event();
-      ev1 = take_event();
-      if (!ev0 || !ev1) {
-        if (ev0) g_prof.pool.push_back(ev0);
-        if (ev1) g_prof.pool.push_back(ev1);
-        ev0 = ev1 = nullptr;
-      }
-    }
-  }
+  hipEvent_t ev0, ev1;
+  prof_begin(&ev0, &ev1);
   hipError_t e = mla::launch_decode(p, var, metadata ? num_units : batch, s, ev0, ev1);
-  if (ev0 && ev1) {
-    std::lock_guard<std::mutex> lk(g_prof.mu);
-    g_prof.recorded.emplace_back(ev0, ev1);
-  }
+  prof_end(MLA_PROFILE_ATTENTION, ev0, ev1, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   if (metadata) {
     const int32_t* offsets = (const int32_t*)metadata + mla::MD_HEADER + batch + 1;
+    prof_begin(&ev0, &ev1);
     e = mla::launch_combine(p.ws_out, p.ws_lse, offsets, cu_q, num_heads, batch, p.rows, out, lse, 1, s,
-                            p.md, num_units);
+                            p.md, num_units, ev0, ev1);
+    prof_end(MLA_PROFILE_COMBINE, ev0, ev1, e == hipSuccess);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   }
   return ok();
@@ -345,26 +364,12 @@ int mla_prefill_fwd(const void* q, const void* k_nope, const void* k_rope, const
   DevInfo d;
   int st = device_info(&d);
   if (st != MLA_OK) return st;
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  {
-    std::lock_guard<std::mutex> lk(g_prof.mu);
-    if (g_prof.on) {
-      ev0 = take_event();
-      ev1 = take_event();
-      if (!ev0 || !ev1) {
-        if (ev0) g_prof.pool.push_back(ev0);
-        if (ev1) g_prof.pool.push_back(ev1);
-        ev0 = ev1 = nullptr;
-      }
-    }
-  }
+  hipEvent_t ev0, ev1;
+  prof_begin(&ev0, &ev1);
   hipError_t e = mla::launch_prefill((const uint16_t*)q, (const uint16_t*)k_nope, (const uint16_t*)k_rope,
                                      (const uint16_t*)v, cu_seqlens_q, cu_seqlens_k, batch, max_q_len, num_heads,
                                      softmax_scale, out, lse, (hipStream_t)stream, ev0, ev1);
-  if (ev0 && ev1) {
-    std::lock_guard<std::mutex> lk(g_prof.mu);
-    g_prof.recorded.emplace_back(ev0, ev1);
-  }
+  prof_end(MLA_PROFILE_ATTENTION, ev0, ev1, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -382,8 +387,11 @@ int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq
   DevInfo d;
   int st = device_info(&d);
   if (st != MLA_OK) return st;
+  hipEvent_t ev0, ev1;
+  prof_begin(&ev0, &ev1);
   hipError_t e = mla::launch_combine(part_out, part_lse, seq_part_offsets, nullptr, 1, batch, rows_per_seq,
-                                     out, lse, 0, (hipStream_t)stream);
+                                     out, lse, 0, (hipStream_t)stream, nullptr, 0, ev0, ev1);
+  prof_end(MLA_PROFILE_COMBINE, ev0, ev1, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -421,29 +429,45 @@ int mla_profile_enable(int enable) {
   return ok();
 }
 
-int mla_profile_read(double* total_ms, int* launches) {
-  if (!total_ms || !launches) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+int mla_profile_read_launches(int kernel, float* ms, int capacity, int* count) {
+  if (!count || (capacity > 0 && !ms)) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (kernel < 0 || kernel >= kProfKinds) return fail(MLA_ERR_INVALID_ARG, "unknown kernel kind %d", kernel);
+  if (capacity < 0) return fail(MLA_ERR_INVALID_ARG, "capacity must be >= 0");
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  double sum = 0.0;
   int n = 0;
   int st = MLA_OK;
-  for (auto& pr : g_prof.recorded) {
-    float ms = 0.f;
+  for (auto& pr : g_prof.recorded[kernel]) {
+    float t = 0.f;
     hipError_t e = hipEventSynchronize(pr.second);
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, pr.first, pr.second);
     if (e != hipSuccess) {
       st = fail(MLA_ERR_HIP, "profile event: %s", hipGetErrorString(e));
     } else {
-      sum += ms;
+      if (n < capacity) ms[n] = t;
       ++n;
     }
     g_prof.pool.push_back(pr.first);
     g_prof.pool.push_back(pr.second);
   }
-  g_prof.recorded.clear();
-  *total_ms = sum;
-  *launches = n;
+  g_prof.recorded[kernel].clear();
+  *count = n;
   return st == MLA_OK ? ok() : st;
+}
+
+int mla_profile_read(double* total_ms, int* launches) {
+  if (!total_ms || !launches) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  std::vector<float> t;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    t.resize(g_prof.recorded[MLA_PROFILE_ATTENTION].size());
+  }
+  int n = 0;
+  const int st = mla_profile_read_launches(MLA_PROFILE_ATTENTION, t.data(), (int)t.size(), &n);
+  double sum = 0.0;
+  for (int i = 0; i < n && i < (int)t.size(); ++i) sum += t[i];
+  *total_ms = sum;
+  *launches = n < (int)t.size() ? n : (int)t.size();
+  return st;
 }
 
 }  // extern "C"

@@ -68,7 +68,8 @@ int variant_rows(int variant);
 hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s,
                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles, int seq_cost,
-                           int32_t* md, hipStream_t s);
+                           int32_t* md, hipStream_t s, hipEvent_t ev_start = nullptr,
+                           hipEvent_t ev_stop = nullptr);
 hipError_t launch_append(const uint16_t* latent, int batch, int new_tokens, const int32_t* block_table,
                          int max_pages, const int32_t* seqlens, uint8_t* kv, float* kv_scale, int fp8,
                          int num_pages, hipStream_t s);
@@ -79,7 +80,7 @@ hipError_t launch_append(const uint16_t* latent, int batch, int new_tokens, cons
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
                           const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
                           float* lse, int skip_single, hipStream_t s, const int32_t* md = nullptr,
-                          int units = 0);
+                          int units = 0, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Prefill / extend (un-absorbed MLA, head dim 192 = 128 + 64 shared rope, v 128).
 int prefill_rows_per_block();

@@ -2592,18 +2592,27 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
 }
 
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles, int seq_cost,
-                           int32_t* md, hipStream_t s) {
-  hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(1024), 0, s, seqlens, batch, units, min_tiles, seq_cost,
-                     md);
+                           int32_t* md, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (ev_start || ev_stop)
+    hipExtLaunchKernelGGL(metadata_kernel, dim3(1), dim3(1024), 0, s, ev_start, ev_stop, 0, seqlens, batch,
+                          units, min_tiles, seq_cost, md);
+  else
+    hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(1024), 0, s, seqlens, batch, units, min_tiles, seq_cost,
+                       md);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
                           const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
-                          float* lse, int skip_single, hipStream_t s, const int32_t* md, int units) {
+                          float* lse, int skip_single, hipStream_t s, const int32_t* md, int units,
+                          hipEvent_t ev_start, hipEvent_t ev_stop) {
   dim3 grid(batch, (rows + 1) / 2);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, part_out, part_lse, offsets, cu_q, num_heads,
-                     batch, rows, out, lse, skip_single, md, units);
+  if (ev_start || ev_stop)
+    hipExtLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, ev_start, ev_stop, 0, part_out, part_lse,
+                          offsets, cu_q, num_heads, batch, rows, out, lse, skip_single, md, units);
+  else
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, part_out, part_lse, offsets, cu_q, num_heads,
+                       batch, rows, out, lse, skip_single, md, units);
   return hipGetLastError();
 }
 

@@ -78,9 +78,10 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
   return hipSuccess;
 }
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles, int seq_cost, int32_t* md,
-                           hipStream_t) {
+                           hipStream_t, hipEvent_t e0, hipEvent_t e1) {
   Launch l;
   l.kind = 2;
+  l.events = e0 && e1;
   l.a = seqlens;
   l.b = md;
   l.batch = batch;
@@ -100,9 +101,10 @@ hipError_t launch_append(const uint16_t*, int batch, int, const int32_t*, int, c
 }
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t*, const int32_t*, int,
                           int batch, int rows, float*, float*, int skip_single, hipStream_t, const int32_t*,
-                          int units) {
+                          int units, hipEvent_t e0, hipEvent_t e1) {
   Launch l;
   l.kind = 4;
+  l.events = e0 && e1;
   l.a = part_out;
   l.b = part_lse;
   l.batch = batch;
@@ -386,6 +388,29 @@ static void check_profile_hook() {
   CHECK(mla_profile_enable(0) == MLA_OK);
   CHECK(g_events == created);   // events come back to the pool and are reused
   CHECK(mla_profile_read(&ms, &n) == MLA_OK && n == 1);
+  // per-kind records: a split call records the attention kernel and the
+  // merge, the planner its kernel; each kind is read and cleared on its own
+  static std::vector<unsigned char> ws(mla_workspace_bytes(2, 1, 16, 4) + 256);
+  c.md = g_buf[6];
+  c.units = 4;
+  c.ws = (void*)(((uintptr_t)ws.data() + 255) & ~(uintptr_t)255);
+  c.wsb = mla_workspace_bytes(2, 1, 16, 4);
+  CHECK(mla_profile_enable(1) == MLA_OK);
+  g_launches.clear();
+  CHECK(c.run() == MLA_OK && c.run() == MLA_OK);
+  CHECK(mla_get_split_metadata(c.sl, 2, 1, 16, 4, 0, g_buf[6], mla_metadata_bytes(2, 4), nullptr) == MLA_OK);
+  CHECK(mla_profile_enable(0) == MLA_OK);
+  CHECK(g_launches.size() == 5);
+  for (const Launch& l : g_launches) CHECK(l.events);
+  float t[4] = {0, 0, 0, 0};
+  CHECK(mla_profile_read_launches(MLA_PROFILE_COMBINE, t, 1, &n) == MLA_OK && n == 2 && t[0] == 0.5f && t[1] == 0);
+  CHECK(mla_profile_read_launches(MLA_PROFILE_METADATA, t, 4, &n) == MLA_OK && n == 1);
+  CHECK(mla_profile_read_launches(MLA_PROFILE_ATTENTION, nullptr, 0, &n) == MLA_OK && n == 2);
+  CHECK(mla_profile_read_launches(MLA_PROFILE_ATTENTION, t, 4, &n) == MLA_OK && n == 0);
+  CHECK(mla_profile_read_launches(3, t, 4, &n) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_profile_read_launches(0, nullptr, 4, &n) == MLA_ERR_INVALID_ARG);
+  // the pool grows only to the most pairs held at once (5 launches here)
+  CHECK(g_events <= 10);
 }
 
 int main() {

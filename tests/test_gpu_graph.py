@@ -73,3 +73,26 @@ def test_graph_replay_follows_new_lengths():
         w.seqlens = np.array(lens, dtype=np.int32)
         ref_out, ref_lse = reference(w)
         assert_parity(w, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, f"lens={lens}")
+
+
+def test_profile_hook_records_every_kernel_kind():
+    """The measurement hook gives one dispatch-timed interval per launch of
+    each kernel kind (attention, metadata, merge), in launch order."""
+    w = config("share16", small=True, seed=8)
+    d = to_device(w)
+    plan = mla.get_split_metadata(d["seqlens"], w.q_len, w.num_heads, num_units=5, min_tiles_per_unit=1)
+    torch.cuda.synchronize()
+    mla.profile_enable(True)
+    for k in (mla.PROFILE_ATTENTION, mla.PROFILE_METADATA, mla.PROFILE_COMBINE):
+        mla.profile_read_launches(k, capacity=0)
+    for _ in range(3):
+        mla.get_split_metadata(d["seqlens"], w.q_len, w.num_heads, num_units=5, min_tiles_per_unit=1,
+                               metadata=plan.metadata, workspace=plan.workspace)
+        mla.decode(d["q"], d["kv"], d["block_table"], d["seqlens"], w.softmax_scale, plan=plan)
+    mla.profile_enable(False)
+    att = mla.profile_read_launches(mla.PROFILE_ATTENTION)
+    md = mla.profile_read_launches(mla.PROFILE_METADATA)
+    cb = mla.profile_read_launches(mla.PROFILE_COMBINE)
+    assert len(att) == 3 and len(md) == 3 and len(cb) == 3
+    assert all(0.0 < t < 100.0 for t in att + md + cb)
+    assert mla.profile_read_launches(mla.PROFILE_ATTENTION) == []
