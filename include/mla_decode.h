@@ -312,6 +312,38 @@ int mla_append_kv(const void* latent, int batch, int new_tokens, const int32_t* 
                   int kv_dtype, int num_pages, void* stream);
 
 /*
+ * mla_decode_fwd_noalloc: mla_decode_fwd for callers that cannot allocate
+ * device memory -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. One call builds the split schedule and
+ * runs the split decode and the merge, with the schedule and the partials in
+ * a static device buffer of MLA_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each device it runs on until the process ends (its device address is
+ * looked up once per device on the first call there). The call allocates
+ * nothing and takes no workspace.
+ *   num_units      >= 0; 0 selects mla_default_num_units(batch, q_len, num_heads)
+ *   min_tiles_per_unit  >= 0; 0 selects the default (8)
+ *   every other argument as for mla_decode_fwd.
+ * Limit: mla_noalloc_scratch_need(batch, q_len, num_heads, units) must not
+ * exceed MLA_NOALLOC_SCRATCH_BYTES (metadata rounded up to 256 bytes plus
+ * mla_workspace_bytes for the shape); larger calls fail with
+ * MLA_ERR_WORKSPACE before anything is launched.
+ * All calls on one device share its buffer: calls that overlap in time on
+ * that device (other streams, other threads) race and must be serialised by
+ * the caller. Nothing in the buffer needs clearing between calls: every word
+ * a call reads was written earlier by the same call. Results equal
+ * mla_decode_fwd's with a plan of the same unit count, bit for bit.
+ * mla_noalloc_scratch_need: the bytes a call of this shape uses (0 for
+ * invalid sizes).
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+size_t mla_noalloc_scratch_need(int batch, int q_len, int num_heads, int num_units);
+int mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                           int num_pages, const int32_t* block_table, int max_pages_per_seq,
+                           const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
+                           float softmax_scale, float* out, float* lse, int num_units, int min_tiles_per_unit,
+                           void* stream);
+
+/*
  * Measurement hook (diagnostics, not part of the computation).
  * mla_profile_enable(1): from now on every kernel launch of the library is
  *   bracketed by a pair of HIP events recorded by the dispatch itself on the

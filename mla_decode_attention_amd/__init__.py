@@ -22,7 +22,7 @@ import torch
 __all__ = ["load_library", "library_path", "abi_version", "default_num_units", "metadata_bytes",
            "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "profile_read_launches",
            "PROFILE_ATTENTION", "PROFILE_METADATA", "PROFILE_COMBINE", "get_split_metadata", "decode",
-           "decode_varlen", "combine", "append_kv", "prefill",
+           "decode_varlen", "decode_noalloc", "combine", "append_kv", "prefill",
            "MLAError", "KV_BF16", "KV_FP8_E4M3", "PAGE_TOKENS", "D_QK", "D_V"]
 
 PAGE_TOKENS = 64
@@ -70,6 +70,9 @@ def load_library():
         "mla_append_kv": (c_int, [vp, c_int, c_int, vp, c_int, vp, vp, vp, c_int, c_int, vp]),
         "mla_decode_fwd_varlen": (c_int, [vp, vp, c_int, c_int, vp, vp, c_int, c_int, vp, c_int, vp, c_int,
                                           c_int, ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
+        "mla_decode_fwd_noalloc": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
+                                           ctypes.c_float, vp, vp, c_int, c_int, vp]),
+        "mla_noalloc_scratch_need": (c_size, [c_int, c_int, c_int, c_int]),
         "mla_profile_enable": (c_int, [c_int]),
         "mla_profile_read": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]),
         "mla_profile_read_launches": (c_int, [c_int, ctypes.POINTER(ctypes.c_float), c_int,
@@ -244,6 +247,37 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                               _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), B, s, H,
                               float(softmax_scale), _ptr(out), _ptr(lse), _ptr(md), units, _ptr(ws),
                               wbytes, _stream()), name)
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                   cache_seqlens: torch.Tensor, softmax_scale: float, kv_scale: Optional[torch.Tensor] = None,
+                   num_units: int = 0, min_tiles_per_unit: int = 0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None):
+    """Split decode whose schedule and partials live in the library's static
+    device buffer (mla_decode_fwd_noalloc): no workspace, no allocation in the
+    library (out / lse are allocated here only when not given)."""
+    lib = load_library()
+    _need(q, "q", (torch.bfloat16,), 4)
+    dev = q.device
+    B, s, H, d = q.shape
+    if d != D_QK:
+        raise ValueError(f"q last dim must be {D_QK}")
+    kv_dtype, P = _check_cache(kv_cache, kv_scale, dev)
+    _need(block_table, "block_table", (torch.int32,), 2, device=dev)
+    _need(cache_seqlens, "cache_seqlens", (torch.int32,), 1, shape=(B,), device=dev)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    if out is None:
+        out = torch.empty((B, s, H, D_V), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, s, H), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), 4, shape=(B, s, H, D_V), device=dev)
+    _need(lse, "lse", (torch.float32,), 3, shape=(B, s, H), device=dev)
+    _check(lib.mla_decode_fwd_noalloc(_ptr(q), _ptr(kv_cache), _ptr(kv_scale), kv_dtype, P, _ptr(block_table),
+                                      block_table.shape[1], _ptr(cache_seqlens), B, s, H, float(softmax_scale),
+                                      _ptr(out), _ptr(lse), int(num_units), int(min_tiles_per_unit), _stream()),
+           "mla_decode_fwd_noalloc")
     return out, lse
 
 

@@ -222,6 +222,13 @@ int mla_get_split_metadata(const int32_t* cache_seqlens, int batch, int q_len, i
 
 namespace {
 
+// Split-schedule build that decode_impl launches itself, after its argument
+// checks (mla_decode_fwd_noalloc).
+struct MetadataLaunch {
+  int min_tiles;
+  int seq_cost;
+};
+
 // Shared body of mla_decode_fwd (cu_q == nullptr: q_len query tokens per
 // sequence) and mla_decode_fwd_varlen (cu_q: per-sequence offsets, q_len is
 // the largest count, q holds total_q tokens).
@@ -229,7 +236,8 @@ int decode_impl(const void* q, const int32_t* cu_q, int total_q, const void* kv_
                 int kv_dtype, int num_pages, const int32_t* block_table, int max_pages_per_seq,
                 const int32_t* cache_seqlens, int batch, int q_len, int num_heads, float softmax_scale,
                 float* out, float* lse, const void* metadata, int num_units, void* workspace,
-                size_t workspace_bytes, void* stream, bool fp8_mma = false) {
+                size_t workspace_bytes, void* stream, bool fp8_mma = false,
+                const MetadataLaunch* build_metadata = nullptr) {
   if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !lse)
     return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   if (fp8_mma && kv_dtype != MLA_KV_FP8_E4M3)
@@ -292,6 +300,14 @@ int decode_impl(const void* q, const int32_t* cu_q, int total_q, const void* kv_
   const int var = fp8_mma ? mla::VAR_Q8 : mla::variant_for(p.rows);
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t ev0, ev1;
+  if (build_metadata) {
+    // the schedule into `metadata`, stream-ordered before the attention kernel
+    prof_begin(&ev0, &ev1);
+    hipError_t e = mla::launch_metadata(cache_seqlens, batch, num_units, build_metadata->min_tiles,
+                                        build_metadata->seq_cost, (int32_t*)metadata, s, ev0, ev1);
+    prof_end(MLA_PROFILE_METADATA, ev0, ev1, e == hipSuccess);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "metadata kernel launch: %s", hipGetErrorString(e));
+  }
   prof_begin(&ev0, &ev1);
   hipError_t e = mla::launch_decode(p, var, metadata ? num_units : batch, s, ev0, ev1);
   prof_end(MLA_PROFILE_ATTENTION, ev0, ev1, e == hipSuccess);
@@ -468,6 +484,62 @@ int mla_profile_read(double* total_ms, int* launches) {
   *total_ms = sum;
   *launches = n < (int)t.size() ? n : (int)t.size();
   return st;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// No-allocation decode: the split schedule and the partials live in the
+// library's static device buffer (mla_scratch.hip) instead of caller buffers.
+// ---------------------------------------------------------------------------
+extern "C" {
+
+size_t mla_noalloc_scratch_need(int batch, int q_len, int num_heads, int num_units) {
+  if (batch < 1 || q_len < 1 || num_heads < 1 || num_units < 1) return 0;
+  const size_t md = (mla_metadata_bytes(batch, num_units) + 255) & ~(size_t)255;
+  return md + workspace_need(batch, q_len, num_heads, num_units);
+}
+
+int mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const float* kv_scale, int kv_dtype,
+                           int num_pages, const int32_t* block_table, int max_pages_per_seq,
+                           const int32_t* cache_seqlens, int batch, int q_len, int num_heads,
+                           float softmax_scale, float* out, float* lse, int num_units, int min_tiles_per_unit,
+                           void* stream) {
+  if (batch < 1 || q_len < 1 || num_heads < 1)
+    return fail(MLA_ERR_INVALID_ARG, "batch, q_len, num_heads must be >= 1 (got %d, %d, %d)", batch, q_len,
+                num_heads);
+  if (num_units < 0) return fail(MLA_ERR_INVALID_ARG, "num_units must be >= 0 (got %d)", num_units);
+  if (min_tiles_per_unit < 0)
+    return fail(MLA_ERR_INVALID_ARG, "min_tiles_per_unit must be >= 0 (got %d)", min_tiles_per_unit);
+  if ((long long)q_len * num_heads > MLA_MAX_ROWS)
+    return fail(MLA_ERR_INVALID_ARG, "q_len * num_heads = %lld exceeds %d", (long long)q_len * num_heads,
+                MLA_MAX_ROWS);
+  int units = num_units;
+  if (units == 0) {
+    units = mla_default_num_units(batch, q_len, num_heads);
+    if (units < 1) {
+      char why[sizeof(g_err)];
+      snprintf(why, sizeof(why), "%s", g_err);
+      return fail(MLA_ERR_HIP, "no default unit count: %s", why);
+    }
+  }
+  const size_t need = mla_noalloc_scratch_need(batch, q_len, num_heads, units);
+  if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE, "schedule and partials need %zu bytes; the static scratch holds %zu", need,
+                (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  void* base = nullptr;
+  e = mla::scratch_address(dev, &base);
+  if (e != hipSuccess || !base) return fail(MLA_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+  const size_t md_bytes = (mla_metadata_bytes(batch, units) + 255) & ~(size_t)255;
+  const int rows = q_len * num_heads;
+  const MetadataLaunch ml{min_tiles_per_unit == 0 ? mla::kDefaultMinTiles : min_tiles_per_unit,
+                          mla::variant_for(rows) == mla::VAR_NARROW16 ? mla::kSeqCostNarrow : mla::kSeqCostWide};
+  return decode_impl(q, nullptr, 0, kv_cache, kv_scale, kv_dtype, num_pages, block_table, max_pages_per_seq,
+                     cache_seqlens, batch, q_len, num_heads, softmax_scale, out, lse, base, units,
+                     (uint8_t*)base + md_bytes, need - md_bytes, stream, false, &ml);
 }
 
 }  // extern "C"

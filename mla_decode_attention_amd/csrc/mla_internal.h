@@ -82,6 +82,10 @@ hipError_t launch_combine(const float* part_out, const float* part_lse, const in
                           float* lse, int skip_single, hipStream_t s, const int32_t* md = nullptr,
                           int units = 0, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
+// Device address of device `dev`'s static scratch (MLA_NOALLOC_SCRATCH_BYTES),
+// looked up on the first call for that device, which must be current then.
+hipError_t scratch_address(int dev, void** out);
+
 // Prefill / extend (un-absorbed MLA, head dim 192 = 128 + 64 shared rope, v 128).
 int prefill_rows_per_block();
 hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,

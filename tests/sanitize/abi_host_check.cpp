@@ -61,6 +61,9 @@ struct Launch {
   bool events = false;
 };
 static std::vector<Launch> g_launches;
+// host stand-in for the static device buffer of the no-allocation entry point
+alignas(256) static unsigned char g_scratch[1 << 20];
+static int g_scratch_lookups = 0;
 
 namespace mla {
 int variant_for(int rows) { return rows <= 16 ? VAR_NARROW16 : VAR_WIDE64X; }
@@ -123,6 +126,11 @@ hipError_t launch_prefill(const uint16_t*, const uint16_t*, const uint16_t*, con
   l.events = e0 && e1;
   g_launches.push_back(l);
   return hipSuccess;
+}
+hipError_t scratch_address(int dev, void** out) {
+  ++g_scratch_lookups;
+  *out = dev == g_dev ? g_scratch : nullptr;
+  return dev == g_dev ? hipSuccess : hipErrorInvalidDevice;
 }
 }  // namespace mla
 
@@ -413,6 +421,47 @@ static void check_profile_hook() {
   CHECK(g_events <= 10);
 }
 
+// The no-allocation entry point: size limit checked before any launch; the
+// schedule and the partials are carved from the scratch without overlap.
+static void check_noalloc() {
+  DecodeCall c;
+  CHECK(mla_noalloc_scratch_need(0, 1, 16, 8) == 0);
+  const size_t need = mla_noalloc_scratch_need(2, 1, 16, 8);
+  CHECK(need == ((mla_metadata_bytes(2, 8) + 255) & ~(size_t)255) + mla_workspace_bytes(2, 1, 16, 8));
+  // the fp8 workload at the default unit count fits; a much larger shape does not
+  CHECK(mla_noalloc_scratch_need(128, 2, 128, 64) <= (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  g_launches.clear();
+  CHECK(mla_decode_fwd_noalloc(c.q, c.kv, nullptr, 0, 8, c.bt, 4, c.sl, 1024, 8, 128, 0.072f, c.out, c.lse, 0, 0,
+                               nullptr) == MLA_ERR_WORKSPACE);
+  CHECK(mla_decode_fwd_noalloc(c.q, c.kv, nullptr, 0, 8, c.bt, 4, c.sl, 2, 1, 16, 0.072f, c.out, c.lse, -1, 0,
+                               nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_decode_fwd_noalloc(c.q, c.kv, nullptr, 0, 8, c.bt, 4, c.sl, 2, 1, 16, 0.072f, c.out, c.lse, 8, -1,
+                               nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_decode_fwd_noalloc(nullptr, c.kv, nullptr, 0, 8, c.bt, 4, c.sl, 2, 1, 16, 0.072f, c.out, c.lse, 8, 0,
+                               nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(g_launches.empty());   // nothing launched on an error
+  CHECK(mla_decode_fwd_noalloc(c.q, c.kv, nullptr, 0, 8, c.bt, 4, c.sl, 2, 1, 16, 0.072f, c.out, c.lse, 8, 0,
+                               nullptr) == MLA_OK);
+  CHECK(g_launches.size() == 3);
+  if (g_launches.size() == 3) {
+    const Launch& m = g_launches[0];
+    const Launch& d = g_launches[1];
+    const Launch& cb = g_launches[2];
+    CHECK(m.kind == 2 && d.kind == 1 && cb.kind == 4);
+    CHECK(m.b == (const void*)g_scratch && d.p.md == (const int32_t*)g_scratch);
+    CHECK(m.units == 8 && d.grid_units == 8 && m.min_tiles == mla::kDefaultMinTiles);
+    const unsigned char* o0 = (const unsigned char*)d.p.ws_out;
+    CHECK(o0 >= g_scratch + mla_metadata_bytes(2, 8) && ((uintptr_t)o0 % 256) == 0);
+    CHECK((const unsigned char*)d.p.ws_lse + (size_t)10 * 16 * 4 <= g_scratch + need);
+  }
+  // default unit count on the 256-CU device
+  g_launches.clear();
+  CHECK(mla_decode_fwd_noalloc(c.q, c.kv, nullptr, 0, 8, c.bt, 4, c.sl, 64, 1, 16, 0.072f, c.out, c.lse, 0, 3,
+                               nullptr) == MLA_OK);
+  CHECK(g_launches.size() == 3 && g_launches[1].grid_units == 256 && g_launches[0].min_tiles == 3);
+  CHECK(g_scratch_lookups >= 2);
+}
+
 int main() {
   check_sizes_and_defaults();
   check_decode_errors();
@@ -427,6 +476,7 @@ int main() {
   check_unsupported_device();
   check_metadata_and_others();
   check_profile_hook();
+  check_noalloc();
   if (g_fail) {
     fprintf(stderr, "%d check(s) failed\n", g_fail);
     return 1;
