@@ -81,7 +81,7 @@ def kernel_source_digest() -> str:
     removed, so that editing a comment does not count as changing a kernel."""
     import hashlib
     src = ""
-    for name in ("mla_kernels.hip", "mla_prefill.hip"):
+    for name in ("mla_device.h", "mla_kernels.hip", "mla_decode_so.hip", "mla_prefill.hip"):
         with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", name)) as f:
             src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
@@ -357,8 +357,8 @@ def roofline_object(e, kernel_name):
             "t_roof_us": e["t_roof_us"]}
 
 
-KERNEL_NAMES = {"tiny": "decode_kernel_pc", "share16": "decode_kernel_pc", "mtp": "decode_kernel_x",
-                "ragged": "decode_kernel_x", "fp8": "decode_kernel_xf", "varlen": "decode_kernel_x",
+KERNEL_NAMES = {"tiny": "decode_kernel_pc", "share16": "decode_kernel_pc", "mtp": "decode_kernel_so<false>",
+                "ragged": "decode_kernel_so<false>", "fp8": "decode_kernel_so<true>", "varlen": "decode_kernel_x",
                 "fp8mma": "decode_kernel_q8"}
 
 

@@ -1,0 +1,720 @@
+// 64-row MLA decode kernel with score waves and output waves (gfx950).
+//
+// The four steps of one MLA pass -- data load, QK GEMM, online softmax update
+// with the probabilities staged from registers to shared memory, PV GEMM
+// (PaddleNLP issue #10157, "Multi-head Latent Attention (MLA) operator",
+// overview) -- split over two kinds of wave, so that on every SIMD one wave's
+// softmax runs under the other wave's matrix work (the overlap of PV with the
+// softmax update that the pages' second scheme aims at, done here with one
+// wave of each kind per SIMD):
+//
+//   score waves 0-3   S^T = K . Q^T for 16 keys x 32 rows over all 576
+//                     features (v_mfma_f32_16x16x32_bf16, the 32 query rows of
+//                     the wave in registers), then the softmax of those
+//                     scores, and the probabilities P (bf16) into LDS in the
+//                     B-operand layout of the PV GEMM.
+//   output waves 4-7  O^T[128 features, 64 rows] += V^T . P^T
+//                     (v_mfma_f32_32x32x16_bf16, V^T read transposed from the
+//                     same LDS tile), and the page loads.
+//
+// A step is half a page (32 keys) for the bf16 cache and a whole page (64
+// keys) for the fp8 cache. In iteration k the score waves work on step k while
+// the output waves work on step k - 1, and one workgroup barrier ends the
+// iteration: it publishes step k's P and row references to the output waves
+// and frees step k - 2's buffer for the loads of a later step. Steps land in a
+// ring of LDS buffers (4 x 36 KiB for the bf16 cache, 3 x 40 KiB for the fp8
+// cache), so the loads of a step are issued two iterations (bf16) or one
+// iteration (fp8, at its start) before it is used.
+//
+// Online softmax without a per-step agreement. Each score wave keeps its own
+// running row maximum m (base 2) and partial row sum l over its half of the
+// keys of every step, raised lazily (only when a step's maximum exceeds m by more than
+// 2^8, so P <= 2^8) and, one step later, raised to its partner's maximum (the
+// other key half of the same rows), so the two halves agree again after a
+// raise. With each step's P the wave publishes the reference m it used. The
+// output waves keep their own reference M per row: when the two halves'
+// references equal M (nearly every step) the PV GEMM runs as is; otherwise O is
+// rescaled to the largest reference and the lower half's P is scaled down in
+// registers before its MFMAs. At a sequence's end the row sum is
+// l_0 2^(m_0 - M) + l_1 2^(m_1 - M), so O / l and LSE = M + log2 l are exact
+// for any interleaving of raises.
+//
+// fp8 cache: the E4M3 codes stay in LDS; the K operand is widened to bf16 in
+// registers after a 16-byte read that serves two k-steps (the query registers
+// follow the same feature order), V^T comes from the transposed byte read, the
+// token's scale multiplies its score and its probability (P_j s_j goes into
+// the PV GEMM, P_j into the row sum).
+//
+// Used for uniform q_len (no per-sequence query counts); q_len * heads > 16.
+#include "mla_device.h"
+
+namespace mla {
+namespace so {
+
+// LDS operand reads in flight ahead of the MFMAs: K in the score waves, V^T
+// in the output waves
+#ifndef SO_KD
+#define SO_KD 8
+#endif
+#ifndef SO_VD
+#define SO_VD 8
+#endif
+constexpr int kThreadsSo = 512;
+constexpr int kRowsSo = 64;
+constexpr int kNq = kDqk / 32;     // 18 k-steps of 32 features in the QK GEMM
+
+template <bool FP8>
+struct Cfg;
+
+// bf16: steps of 32 keys. Chunk c (8 features) of key k (0..31) at byte
+// ((c / 8) * 256 + k * 8 + ((c ^ swz3(k)) % 8)) * 16: line groups of 4 KiB
+// (one 128-byte line of all 32 keys), conflict-free for 16 consecutive keys at
+// one chunk (K operand) and for 4 keys x 4 chunks (transposed V read).
+template <>
+struct Cfg<false> {
+  static constexpr int kKeys = 32;
+  static constexpr int kBufBytes = kKeys * kRowBytes;      // 36864
+  static constexpr int kBufs = 4;
+  static constexpr int kLoads = kBufBytes / (256 * 16);    // 9 per output-wave lane
+  static constexpr int kLineGroup = kKeys * 128;           // 4096
+  __device__ static int byte(int key, int chunk) {
+    return ((chunk >> 3) * 256 + key * 8 + ((chunk ^ swz3(key)) & 7)) * 16;
+  }
+};
+
+// fp8: steps of 64 keys (a page). Chunk c (16 codes) of key k at byte
+// ((c / 4) * 64 + k) * 64 + ((c % 4) ^ swz2(k)) * 16 (64-byte line groups of
+// 4 KiB); the 64 per-token scales follow the codes, then padding up to 10
+// loads x 256 lanes x 16 bytes.
+template <>
+struct Cfg<true> {
+  static constexpr int kKeys = 64;
+  static constexpr int kCodeBytes = kKeys * kFp8RowBytes;  // 36864
+  static constexpr int kBufBytes = 10 * 256 * 16;          // 40960
+  static constexpr int kBufs = 3;
+  static constexpr int kLoads = 10;
+  static constexpr int kLineGroup = kKeys * 64;            // 4096
+  __device__ static int byte(int key, int chunk) {
+    return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz2(key)) << 4);
+  }
+};
+
+// Exchange area after the buffers: P [parity][k-step][row half][lane] x 16 B
+// (k-steps of 16 keys), the references M [parity][key half][row] and row sums
+// L [parity][key half][row] of the score waves.
+constexpr int kMBytes = 2 * 2 * 64 * 4;        // 1024
+
+// s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt untouched (gfx9
+// encoding: vmcnt bits 3:0 and 15:14).
+constexpr int vm_imm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
+
+// Wait until at most `steps` steps' worth of page loads (L per lane each) are
+// in flight: the loads of older steps have landed.
+template <int L>
+__device__ __forceinline__ void wait_steps_in_flight(int steps) {
+  if (steps <= 0) __builtin_amdgcn_s_waitcnt(vm_imm(0));
+  else if (steps == 1) __builtin_amdgcn_s_waitcnt(vm_imm(L));
+  else __builtin_amdgcn_s_waitcnt(vm_imm(2 * L));
+}
+
+// Scalar load (s_load) of a word the kernel never writes, at a uniform index.
+#define CONST_AS __attribute__((address_space(4)))
+__device__ __forceinline__ int sld(const int32_t* p, size_t i) { return ((const CONST_AS int32_t*)p)[i]; }
+
+// Page walk of one work unit (uniform q_len): the flattened tiles
+// [f_begin, f_end) of the unit, one page record at a time, every fact in
+// scalar registers (read with scalar loads on a sequence change). PAGES: also
+// the page ids, from a vector register of 64 cached ids (lane i = tile
+// pc_t0 + i). Each role of wave walks the unit at its own pace: the page loads
+// ahead, the score waves at their step, the output waves one step behind.
+template <bool PAGES>
+struct Walk {
+  int u, f, f_begin, f_end;
+  int b, bfirst, blast, L;   // sequence of page f, its first flattened tile, the next sequence's, its length
+  int final_out, slot;
+  int pc_t0, page_cache;     // lane i of page_cache: the page of tile pc_t0 + i of sequence b
+
+  // page ids of tiles t0 .. t0 + 63 of sequence b into page_cache (a vector
+  // load, waited for here: on a sequence change and every 64 pages)
+  __device__ __forceinline__ void load_pages(const KernelArgs& a, int t0) {
+    if (!PAGES) return;
+    const DecodeParams& p = a.p;
+    pc_t0 = t0;
+    const int t = t0 + (int)(threadIdx.x & 63);
+    const int tiles = (L + kPage - 1) / kPage;
+    page_cache = t < tiles ? p.block_table[(size_t)b * p.max_pages + t] : 0;
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  }
+
+  // false if the unit has no tiles (or the metadata was not built for this call)
+  __device__ __forceinline__ bool init(const KernelArgs& a, int unit) {
+    u = unit;
+    const DecodeParams& p = a.p;
+    if (a.md) {
+      const int B = p.batch;
+      if (sld(a.md, MD_MAGIC) != kMdMagic || sld(a.md, MD_BATCH) != B || sld(a.md, MD_UNITS) != p.grid_units)
+        return false;
+      const size_t ub = md_unit_begin(B, p.grid_units);
+      f_begin = sld(a.md, ub + u);
+      f_end = sld(a.md, ub + u + 1);
+      if (f_begin >= f_end) return false;
+      f = f_begin;
+      enter(a, sld(a.split_off, B + 1 + u));   // the sequence holding the unit's first tile
+    } else {
+      f_begin = f = 0;
+      f_end = (max(sld(p.seqlens, u), 0) + kPage - 1) / kPage;
+      if (f_end <= 0) return false;
+      enter(a, u);
+    }
+    return true;
+  }
+  __device__ __forceinline__ void enter(const KernelArgs& a, int bb) {
+    const DecodeParams& p = a.p;
+    b = bb;
+    L = max(sld(p.seqlens, b), 0);
+    if (a.md) {
+      bfirst = sld(a.prefix, b);
+      blast = sld(a.prefix, b + 1);
+      const int so0 = sld(a.split_off, b), so1 = sld(a.split_off, b + 1);
+      final_out = so1 - so0 == 1;
+      slot = so0 + (u - sld(a.md, md_seq_first_unit(p.batch, p.grid_units) + b));
+    } else {
+      bfirst = 0;
+      blast = f_end;
+      final_out = 1;
+      slot = 0;
+    }
+    load_pages(a, f - bfirst);
+  }
+  // the record of page f (and with PAGES its page id and valid tokens); then
+  // the next page
+  __device__ __forceinline__ TileInfo next(const KernelArgs& a) {
+    int page, nvalid;
+    return next(a, page, nvalid);
+  }
+  __device__ __forceinline__ TileInfo next(const KernelArgs& a, int& page, int& nvalid) {
+    const DecodeParams& p = a.p;
+    if (f >= blast) {
+      int bb = b + 1;
+      while (sld(a.prefix, bb + 1) <= f) ++bb;   // sequences without tiles in between
+      enter(a, bb);
+    }
+    TileInfo ti;
+    ti.b = b;
+    ti.t = f - bfirst;
+    ti.L = L;
+    ti.first = f == f_begin || ti.t == 0;
+    ti.last = f + 1 == f_end || f + 1 == blast;
+    ti.final_out = final_out != 0;
+    ti.slot = slot;
+    ti.qlen = p.q_len;
+    ti.rows = p.rows;
+    ti.qrow0 = b * p.rows;
+    page = 0;
+    if (PAGES) {
+      if (ti.t - pc_t0 >= 64) load_pages(a, ti.t);
+      page = uniform(__builtin_amdgcn_readlane(page_cache, ti.t - pc_t0));
+    }
+    nvalid = min(kPage, L - ti.t * kPage);
+    ++f;
+    return ti;
+  }
+};
+
+template <bool FP8>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void decode_kernel_so(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
+                      const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
+                      const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
+                      const uint8_t* __restrict__ kv_) {
+  using C = Cfg<FP8>;
+  constexpr int NB = C::kBufs;
+  constexpr int SPP = kPage / C::kKeys;     // steps per page
+  constexpr int KB = C::kKeys / 32;         // 16-key blocks of a score wave per step
+  constexpr int NKS = C::kKeys / 16;        // PV k-steps (16 keys) per step
+  constexpr int kPBytes = 2 * NKS * 2 * 64 * 16;
+  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * C::kBufBytes + kPBytes + 2 * kMBytes];
+  LDS_AS uint8_t* const bufs = (LDS_AS uint8_t*)smem;
+  LDS_AS uint8_t* const pbuf = bufs + NB * C::kBufBytes;
+  LDS_AS float* const mpub = (LDS_AS float*)(pbuf + kPBytes);
+  LDS_AS float* const lpub = mpub + kMBytes / 4;
+
+  const DecodeParams& p = a.p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = uniform(tid >> 6);
+  const int R = p.rows;
+  const WgCoord wc = wg_coord((R + kRowsSo - 1) / kRowsSo);
+  if (wc.unit >= p.grid_units) return;
+  const int row0 = wc.rb * kRowsSo;
+  const int u = wc.unit;
+
+  Walk<false> walk;   // this wave's own step (score waves) or the step behind (output waves)
+  if (!walk.init(a, u)) {
+    if (!a.md) write_empty(p, u, row0, row0 + kRowsSo, kThreadsSo / 64);
+    return;
+  }
+  const int n_steps = SPP * (walk.f_end - walk.f_begin);
+  auto buf = [&](int k) { return bufs + (k % NB) * C::kBufBytes; };
+
+  if (wave >= 4) {
+    // ======================================================== output waves
+    const int ow = wave - 4;                 // features 128 ow .. 128 ow + 127
+    const int tt = tid - 256;                // 0..255: lane of the page loads
+    const int n = lane & 31, h = lane >> 5;
+
+    // ---- page loads. Step j (page f_begin + j / SPP, part j % SPP) goes to
+    // buf(j); load i of lane tt fills LDS slot 256 i + tt (one KiB per wave
+    // and load).
+    Walk<true> wload;   // the page loads' walk, ahead of every other
+    wload.init(a, u);
+    int plan_page = 0, plan_nvalid = 1, plan_hh = 0;
+    uint32_t voff = 0;
+    const uint8_t* src = nullptr;
+    auto plan_step = [&](int j) {
+      plan_hh = j % SPP;
+      if (plan_hh == 0) wload.next(a, plan_page, plan_nvalid);
+      if constexpr (!FP8) {
+        // line group i, key tt / 8, position tt % 8
+        const int key = tt >> 3, pos = tt & 7;
+        const int src_key = min(32 * plan_hh + key, plan_nvalid - 1);
+        src = a.kv + (size_t)plan_page * kTileBytes;
+        voff = src_key * kRowBytes + 16 * (pos ^ swz3(key));
+      } else {
+        // line group i, key tt / 4, position tt % 4
+        const int key = tt >> 2, pos = tt & 3;
+        const int src_key = min(key, plan_nvalid - 1);
+        src = a.kv + (size_t)plan_page * kFp8TileBytes;
+        voff = src_key * kFp8RowBytes + 16 * (pos ^ swz2(key));
+      }
+    };
+    auto load = [&](int j, int i) {
+      const uint32_t dst = (uint32_t)uniform((int)(uintptr_t)(buf(j) + (4 * i + ow) * 1024));
+      if constexpr (!FP8) {
+        dma16(voff + 128 * i, src, dst);
+      } else {
+        if (i < 9) {
+          dma16(voff + 64 * i, src, dst);
+        } else {
+          // the page's 64 scales (lanes 0-15 of wave 4); the rest re-read
+          // them into the padding
+          const uint8_t* sc = (const uint8_t*)(p.kv_scale + (size_t)plan_page * kPage);
+          dma16(16 * (lane & 15), sc, dst);
+        }
+      }
+    };
+    auto load_all = [&](int j) {
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i) load(j, i);
+    };
+
+    static_assert(NB - 3 <= 2 && 2 * C::kLoads <= 63, "wait counts");
+    // prologue: steps 0 .. NB-3 in flight, step 0 landed
+    for (int j = 0; j < NB - 2 && j < n_steps; ++j) {
+      plan_step(j);
+      load_all(j);
+    }
+    wait_steps_in_flight<C::kLoads>(min(NB - 3, n_steps - 1));
+    lds_barrier();
+
+    // ---- V^T operand addresses (32x32x16 A operand, keys in natural order:
+    // k-slot 8h + e of k-step ks is key 16 ks + 8h + e)
+    int v_lane[2][2];    // bf16: [second][fb & 1]
+    int v8_lane[4];      // fp8: [fb]
+    {
+      const int q = lane >> 4, j = lane & 15;
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int second = 0; second < 2; ++second)
+#pragma unroll
+          for (int fb1 = 0; fb1 < 2; ++fb1)
+            v_lane[second][fb1] = C::byte(8 * h + 4 * second + (j >> 2), 4 * fb1 + 2 * (q & 1) + ((j & 3) >> 1)) +
+                                  8 * (j & 1);
+      } else {
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+          v8_lane[fb] = C::byte(8 * h + (j >> 1), 8 * ow + 2 * fb + (q & 1)) + 8 * (j & 1);
+      }
+    }
+
+    f32x16 o[4][2];   // [feature block][row half]
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) o[fb][0] = o[fb][1] = f32x16{};
+    float M[2] = {-INFINITY, -INFINITY};
+    // epilogue of a finished sequence, stored at the start of the next
+    // iteration (before that iteration's page loads)
+    bool pend = false;
+    float pend_inv[2] = {0.f, 0.f}, pend_lse[2] = {0.f, 0.f};
+    TileInfo pend_ti{};
+
+    auto flush = [&]() {
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        const int row = row0 + 32 * rh + n;
+        if (row < pend_ti.rows) {
+          float* dst_o;
+          float* dst_l;
+          if (pend_ti.final_out) {
+            dst_o = p.out + ((size_t)pend_ti.qrow0 + row) * kDv;
+            dst_l = p.lse + (size_t)pend_ti.qrow0 + row;
+          } else {
+            dst_o = p.ws_out + ((size_t)pend_ti.slot * R + row) * kDv;
+            dst_l = p.ws_lse + (size_t)pend_ti.slot * R + row;
+          }
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const f32x4 v = {o[fb][rh][4 * jj], o[fb][rh][4 * jj + 1], o[fb][rh][4 * jj + 2],
+                               o[fb][rh][4 * jj + 3]};
+              *(f32x4*)(dst_o + 128 * ow + 32 * fb + 8 * jj + 4 * h) = v * pend_inv[rh];
+            }
+          if (ow == 0 && h == 0) *dst_l = pend_lse[rh];
+        }
+      }
+      // O restarts through the rescale of the next sequence's first step
+      // (alpha = 0 while M is -inf), so O itself is not touched here
+      M[0] = M[1] = -INFINITY;
+      pend = false;
+    };
+
+    // iteration 0: the score waves take step 0, the output waves only load
+    if (NB - 2 < n_steps) {
+      plan_step(NB - 2);
+      load_all(NB - 2);
+    }
+    wait_steps_in_flight<C::kLoads>(min(NB - 2, n_steps - 1) - 1);
+    lds_barrier();
+    TileInfo ti{};
+    for (int k = 1; k <= n_steps; ++k) {
+      const int t = k - 1;   // the step computed here
+      const int par = t & 1;
+      const LDS_AS uint8_t* cur = buf(t);
+      const int j_load = k + NB - 2;
+      const bool do_load = j_load < n_steps;
+      // with three buffers a step's loads have one iteration to land: all of
+      // them go out first
+      constexpr bool kLoadsFirst = NB == 3;
+      if (do_load) plan_step(j_load);
+      if (kLoadsFirst && do_load) load_all(j_load);
+      // LDS reads that depend on nothing else, issued first: the references
+      // of the two key halves for this lane's rows, the P operands, and the
+      // first V^T operands
+      float r[2][2];   // [key half][row half]
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) r[kh][rh] = mpub[(par * 2 + kh) * 64 + 32 * rh + n];
+      bf16x8 pb[NKS][2];   // [k-step][row half]
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh)
+          pb[ks][rh] = *(const LDS_AS bf16x8*)(pbuf + (((par * NKS + ks) * 2 + rh) * 64 + lane) * 16);
+      // V^T operand of (k-step, feature block) pair i = 4 ks + fb
+      constexpr int NPAIRS = 4 * NKS;
+      constexpr int D = SO_VD < NPAIRS ? SO_VD : NPAIRS;
+      using VOp = typename std::conditional<FP8, i32x2, bf16x8>::type;
+      auto vread = [&](int i) -> VOp {
+        const int ks = i >> 2, fb = i & 3;
+        if constexpr (!FP8) {
+          const LDS_AS uint8_t* vb = cur + (2 * ow + (fb >> 1)) * C::kLineGroup + ks * 2048;
+          const bf16x4 x0 = tr_read(vb + v_lane[0][fb & 1]);
+          const bf16x4 x1 = tr_read(vb + v_lane[1][fb & 1]);
+          return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          return tr8_read(cur + v8_lane[fb] + ks * 1024);
+        }
+      };
+      VOp vr[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) vr[i] = vread(i);
+
+      if (pend) flush();
+      if (t % SPP == 0) ti = walk.next(a);
+      const bool last_step = ti.last && (t % SPP == SPP - 1);
+
+      // (a row whose reference is still -inf takes the rescale path, which
+      // zeroes O until the row has a visible key: a sequence's restart)
+      const bool odd = (r[0][0] != M[0]) | (r[1][0] != M[0]) | (r[0][1] != M[1]) | (r[1][1] != M[1]) |
+                       (M[0] == -INFINITY) | (M[1] == -INFINITY);
+      if (__builtin_amdgcn_ballot_w64(odd) != 0) {
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) {
+          const float mn = fmaxf(M[rh], fmaxf(r[0][rh], r[1][rh]));
+          const float alpha = M[rh] == -INFINITY ? 0.f : exp2_fast(M[rh] - mn);
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb) o[fb][rh] *= alpha;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            // P of key half ks / KB down to the new reference
+            const int kh = ks / KB;
+            const float fk = mn == -INFINITY ? 1.f : exp2_fast(r[kh][rh] - mn);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[ks][rh][e] = (__bf16)((float)pb[ks][rh][e] * fk);
+          }
+          M[rh] = mn;
+        }
+      }
+
+      // ---- PV GEMM; the loads of step j_load (when not issued above) go
+      //      after MFMA pairs floor(i * pairs / loads)
+#pragma unroll
+      for (int i = 0; i < NPAIRS; ++i) {
+        const int ks = i >> 2, fb = i & 3;
+        bf16x8 av;
+        if constexpr (!FP8) av = vr[i % D];
+        else av = widen8((unsigned)vr[i % D][0], (unsigned)vr[i % D][1]);
+        if (i + D < NPAIRS) vr[i % D] = vread(i + D);
+        o[fb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks][0], o[fb][0], 0, 0, 0);
+        o[fb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks][1], o[fb][1], 0, 0, 0);
+        if constexpr (!kLoadsFirst) {
+#pragma unroll
+          for (int l = 0; l < C::kLoads; ++l)
+            if ((l * NPAIRS) / C::kLoads == i && do_load) load(j_load, l);
+        }
+        sched_fence();
+      }
+
+      if (last_step) {
+        // row sums of the two key halves, in this lane's reference
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) {
+          float l = 0.f;
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            const float lk = lpub[(par * 2 + kh) * 64 + 32 * rh + n];
+            if (r[kh][rh] != -INFINITY) l += lk * exp2_fast(r[kh][rh] - M[rh]);
+          }
+          const bool live = l > 0.f;
+          pend_inv[rh] = live ? 1.0f / l : 0.f;
+          pend_lse[rh] = live ? (M[rh] + log2_fast(l)) * kLn2 : -INFINITY;
+        }
+        pend_ti = ti;
+        pend = true;
+      }
+      // step k + 1 has landed: the loads issued after its own (steps k + 2
+      // .. k + NB - 2 that exist) may still be in flight
+      wait_steps_in_flight<C::kLoads>(min(k + NB - 2, n_steps - 1) - (k + 1));
+      lds_barrier();
+    }
+    if (pend) flush();
+    return;
+  }
+
+  // ========================================================== score waves
+  const int rh = wave & 1, kh = wave >> 1;
+  const int c = lane & 15, g = lane >> 4;
+  // K operand offsets (16x16x32 A operand: lane (c, g) holds key 16 b + c of
+  // key block b = KB kh + kb, features 8g..8g+7 of the k-step)
+  int k_lane[KB][2];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = 16 * (KB * kh + kb) + c;
+    if constexpr (!FP8) {
+      // k-step j: chunk 4j + g = line group j/2, chunk-in-line 4(j%2) + g
+#pragma unroll
+      for (int e = 0; e < 2; ++e) k_lane[kb][e] = C::byte(key, 4 * e + g);
+    } else {
+      // k-steps 2jj, 2jj+1: one 16-byte read of chunk 4jj + g (bytes 0-7, 8-15)
+      k_lane[kb][0] = C::byte(key, g);
+      k_lane[kb][1] = 0;
+    }
+  }
+  bf16x8 q[2][kNq];         // [row block][k-step]
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  int row_tok[2] = {0, 0};
+
+  auto load_q = [&](const TileInfo& tq) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int rr = min(row0 + 32 * rh + 16 * rb + c, max(tq.rows - 1, 0));
+      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(tq.qrow0 + rr, p.q_rows - 1) * kDqk);
+#pragma unroll
+      for (int j = 0; j < kNq; ++j) {
+        if constexpr (!FP8) q[rb][j] = qrow[4 * j + g];
+        else q[rb][j] = qrow[8 * (j >> 1) + 2 * g + (j & 1)];
+      }
+    }
+  };
+
+  TileInfo ti = walk.next(a);   // page of step 0
+  load_q(ti);
+  lds_barrier();   // the prologue's loads of step 0 have landed
+  for (int k = 0; k <= n_steps; ++k) {
+    if (k < n_steps) {
+      const int par = k & 1;
+      const int hh = k % SPP;
+      const bool first_step = ti.first && hh == 0;
+      const bool last_step = ti.last && hh == SPP - 1;
+      const LDS_AS uint8_t* cur = buf(k);
+      if (first_step) {
+        // its query rows were loaded before the loop or after the previous
+        // step's QK
+        m_run[0] = m_run[1] = -INFINITY;
+        l_run[0] = l_run[1] = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          row_tok[rb] = min(row0 + 32 * rh + 16 * rb + c, max(ti.rows - 1, 0)) / p.num_heads;
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      }
+      // the partner's reference of the previous step, read ahead of its use
+      float pm[2] = {-INFINITY, -INFINITY};
+      if (!first_step) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) pm[rb] = mpub[((par ^ 1) * 2 + (kh ^ 1)) * 64 + 32 * rh + 16 * rb + c];
+      }
+      // ---- QK GEMM: S^T[16 keys of each block kb, 32 rows of half rh]
+      f32x4 s[KB][2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (!FP8) {
+        constexpr int NR = kNq;   // one 16-byte read per k-step
+        constexpr int D = SO_KD < NR ? SO_KD : NR;
+        auto kaddr = [&](int j) { return cur + k_lane[0][j & 1] + (j >> 1) * C::kLineGroup; };
+        bf16x8 kr[D];
+#pragma unroll
+        for (int i = 0; i < D; ++i) kr[i] = ld128(kaddr(i));
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+          const bf16x8 av = kr[j % D];
+          if (j + D < NR) kr[j % D] = ld128(kaddr(j + D));
+          s[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, q[0][j], s[0][0], 0, 0, 0);
+          s[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, q[1][j], s[0][1], 0, 0, 0);
+          sched_fence();
+        }
+      } else {
+        // read r = KB jj + kb: key block kb, k-steps 2jj and 2jj + 1
+        constexpr int NR = KB * (kNq / 2);
+        constexpr int D = SO_KD < NR ? SO_KD : NR;
+        auto kaddr = [&](int r) { return cur + k_lane[r % KB][0] + (r / KB) * C::kLineGroup; };
+        u32x4 kr[D];
+#pragma unroll
+        for (int i = 0; i < D; ++i) kr[i] = *(const LDS_AS u32x4*)kaddr(i);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const u32x4 w = kr[r % D];
+          if (r + D < NR) kr[r % D] = *(const LDS_AS u32x4*)kaddr(r + D);
+          const int kb = r % KB, jj = r / KB;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const bf16x8 av = widen8(w[2 * e], w[2 * e + 1]);
+            s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, q[0][2 * jj + e], s[kb][0], 0, 0, 0);
+            s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, q[1][2 * jj + e], s[kb][1], 0, 0, 0);
+          }
+          sched_fence();
+        }
+      }
+      // the next step starts another sequence of this unit: its query rows
+      // now (the registers are free once the MFMAs above have read them)
+      TileInfo nti = ti;
+      if (hh == SPP - 1 && k + 1 < n_steps) {
+        nti = walk.next(a);   // the next page
+        if (last_step) load_q(nti);
+      }
+
+      // ---- softmax of this wave's keys (lane (c, g) of block kb: keys
+      //      16 b + 4g + i, b = KB kh + kb)
+      const int step_key0 = ti.t * kPage + C::kKeys * hh;
+      const bool need_mask = (step_key0 + C::kKeys) > (ti.L - ti.qlen + 1);
+      f32x4 ksc[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        ksc[kb] = f32x4{1.f, 1.f, 1.f, 1.f};
+        if constexpr (FP8)
+          ksc[kb] = *(const LDS_AS f32x4*)(cur + C::kCodeBytes + (16 * (KB * kh + kb) + 4 * g) * 4);
+      }
+      float sv[KB][2][4];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sv[kb][rb][i] = s[kb][rb][i] * (FP8 ? ksc[kb][i] * p.scale_log2 : p.scale_log2);
+      if (__builtin_expect(need_mask, 0)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int vis = ti.L - ti.qlen + row_tok[rb] + 1;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (step_key0 + 16 * (KB * kh + kb) + 4 * g + i >= vis) sv[kb][rb][i] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          mx = fmaxf(mx, fmaxf(fmaxf(sv[kb][rb][0], sv[kb][rb][1]), fmaxf(sv[kb][rb][2], sv[kb][rb][3])));
+        mx = max_xor32(max_xor16(mx));
+        const int row = 32 * rh + 16 * rb + c;
+        // adopt the partner's reference of the previous step (same sequence)
+        const float base = fmaxf(m_run[rb], pm[rb]);
+        const float m_new = (mx > base + kRescaleThreshold) ? mx : base;
+        if (m_new != m_run[rb]) {
+          l_run[rb] = m_run[rb] == -INFINITY ? 0.f : l_run[rb] * exp2_fast(m_run[rb] - m_new);
+          m_run[rb] = m_new;
+        }
+        const float m_ref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          bf16x4 pq;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = exp2_fast(sv[kb][rb][i] - m_ref);
+            l_run[rb] += pr;
+            if constexpr (FP8) {
+              // masked keys may carry any scale (NaN in a page's unused tail)
+              pq[i] = (__bf16)(sv[kb][rb][i] == -INFINITY ? 0.f : pr * ksc[kb][i]);
+            } else {
+              pq[i] = (__bf16)pr;
+            }
+          }
+          const int b = KB * kh + kb;   // the PV k-step of this key block
+          *(LDS_AS bf16x4*)(pbuf + ((par * NKS + b) * 2 + rh) * 1024 + (16 * rb + c + 32 * (g >> 1)) * 16 +
+                            8 * (g & 1)) = pq;
+        }
+        if (g == 0) mpub[(par * 2 + kh) * 64 + row] = m_run[rb];
+        if (last_step) {
+          const float lt = sum_xor32(sum_xor16(l_run[rb]));
+          if (g == 0) lpub[(par * 2 + kh) * 64 + row] = lt;
+        }
+      }
+      ti = nti;
+    }
+    lds_barrier();
+  }
+}
+
+}  // namespace so
+
+hipError_t launch_decode_so(const DecodeParams& p, int grid_units, hipStream_t s, hipEvent_t ev_start,
+                            hipEvent_t ev_stop) {
+  const int rb = (p.rows + so::kRowsSo - 1) / so::kRowsSo;
+  dim3 grid(((grid_units + 7) / 8) * 8 * rb);
+  KernelArgs a;
+  a.p = p;
+  a.p.grid_units = grid_units;
+  a.md = p.md;
+  a.prefix = p.md ? p.md + MD_HEADER : nullptr;
+  a.split_off = p.md ? a.prefix + p.batch + 1 : nullptr;
+  a.seqlens = p.seqlens;
+  a.block_table = p.block_table;
+  a.qptr = p.q;
+  a.kv = p.kv;
+  const bool fp8 = p.kv_scale != nullptr;
+  auto kern = fp8 ? so::decode_kernel_so<true> : so::decode_kernel_so<false>;
+  if (ev_start || ev_stop)
+    hipExtLaunchKernelGGL(kern, grid, dim3(so::kThreadsSo), 0, s, ev_start, ev_stop, 0, a.p, a.md, a.prefix,
+                          a.split_off, a.seqlens, a.block_table, a.qptr, a.kv);
+  else
+    hipLaunchKernelGGL(kern, grid, dim3(so::kThreadsSo), 0, s, a.p, a.md, a.prefix, a.split_off, a.seqlens,
+                       a.block_table, a.qptr, a.kv);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -67,6 +67,9 @@ int variant_rows(int variant);
 // ev_start / ev_stop: optional events recorded by the kernel dispatch itself.
 hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s,
                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+// 64-row kernel with score and output waves (mla_decode_so.hip), uniform q_len.
+hipError_t launch_decode_so(const DecodeParams& p, int grid_units, hipStream_t s, hipEvent_t ev_start = nullptr,
+                            hipEvent_t ev_stop = nullptr);
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles, int seq_cost,
                            int32_t* md, hipStream_t s, hipEvent_t ev_start = nullptr,
                            hipEvent_t ev_stop = nullptr);

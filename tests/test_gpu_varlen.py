@@ -66,7 +66,12 @@ def test_varlen_leaves_foreign_rows_alone():
 
 
 @pytest.mark.parametrize("H,s", [(16, 1), (128, 2)])
-def test_varlen_with_equal_counts_is_bitwise_the_batched_call(H, s):
+def test_varlen_with_equal_counts_matches_the_batched_call(H, s):
+    """Uniform counts through the varlen entry: bit for bit the batched call
+    where both run the same kernel (up to 16 rows); with more rows the batched
+    call runs the score/output-wave kernel and the varlen call the kernel
+    with per-sequence query counts, so both meet the oracle bar and agree
+    within it."""
     w = make_workload("eq", 4, H, s, [300, 64, 1, 1000], seed=6)
     d = to_device(w)
     plan = mla.get_split_metadata(d["seqlens"], s, H, num_units=5, min_tiles_per_unit=1)
@@ -75,7 +80,16 @@ def test_varlen_with_equal_counts_is_bitwise_the_batched_call(H, s):
     o2, l2 = mla.decode_varlen(d["q"].reshape(4 * s, H, 576), cu, s, d["kv"], d["block_table"], d["seqlens"],
                                w.softmax_scale, plan=plan)
     torch.cuda.synchronize()
-    assert torch.equal(o1.reshape(4 * s, H, 512), o2) and torch.equal(l1.reshape(4 * s, H), l2)
+    o1, l1 = o1.reshape(4 * s, H, 512), l1.reshape(4 * s, H)
+    if s * H <= 16:
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        return
+    ref_out, ref_lse = oracle.mla_decode(w.q_bits, w.cache, w.block_table, w.seqlens, w.softmax_scale)
+    ref_out, ref_lse = ref_out.reshape(4 * s, H, 512), ref_lse.reshape(4 * s, H)
+    for o, l, what in ((o1, l1, "batched"), (o2, l2, "varlen")):
+        assert_parity(w, o.cpu().numpy(), l.cpu().numpy(), ref_out, ref_lse, what)
+    scale = float(np.abs(ref_out).max())
+    assert float((o1 - o2).abs().max()) <= 1e-2 * scale
 
 
 def test_full_size_varlen_sampled():
