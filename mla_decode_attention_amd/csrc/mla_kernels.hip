@@ -1951,76 +1951,120 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
 }
 
 // ---------------------------------------------------------------------------
-// LSE merge of partials: one workgroup per (sequence, pair of rows), 128
-// threads x 4 features per row, one online pass over the partials (eight in
-// flight per step). A partial with LSE -inf weighs nothing and its values are
-// not used (they may be anything, NaN included).
+// LSE merge of partials: one workgroup per (sequence, row), 4 groups of 64
+// threads per row, 8 features per thread (d..d+3 and 256+d..256+d+3, so each
+// load of a wave covers 1 KiB contiguous). Group g takes the partials
+// k = g, g + 4, ... in one online pass (running max, rescaled sum and output;
+// the loads of four partials issued together), so a sequence cut into many
+// partials (a long context over many units) costs about a quarter of the
+// memory round trips of one pass over all of them; the group states are then
+// merged through LDS. A partial with LSE -inf weighs nothing and its values
+// are not used (they may be anything, NaN included).
 // md (nullable): the decode's metadata; the merge does nothing unless it was
-// built for this batch and num_units (as the decode kernels check).
+// built for this batch and num_units (as the decode kernels check). The
+// header is read before the offsets, which sit in the metadata at positions
+// this call's batch sets (metadata built for a smaller batch is shorter).
 // ---------------------------------------------------------------------------
-__constant__ int32_t kNoMetadataHeader[MD_HEADER] = {};
+constexpr int kCombineRows = 1;      // rows per workgroup
+constexpr int kCombineGroups = 4;    // partial groups per row
+constexpr int kCombineInFlight = 4;  // partials per group whose loads are issued together
+constexpr int kCombineThreads = kCombineRows * kCombineGroups * 64;
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_out,
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part_out,
                                                       const float* __restrict__ part_lse,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ cu_q, int num_heads,
                                                       int B, int R, float* __restrict__ out,
                                                       float* __restrict__ lse, int skip_single,
                                                       const int32_t* __restrict__ md, int units) {
+  __shared__ float s_ms[kCombineRows][kCombineGroups][2];               // (max, sum)
+  __shared__ f32x4 s_acc[kCombineRows][kCombineGroups - 1][2][64];       // groups 1.., two halves
   const int b = blockIdx.x;
+  if (md && ((md[MD_MAGIC] != kMdMagic) | (md[MD_BATCH] != B) | (md[MD_UNITS] != units))) return;
   const int k0 = offsets[b];
   const int n = offsets[b + 1] - k0;
-  // header words loaded unconditionally, together with the offsets (no extra round trip)
-  const int32_t* hdr = md ? md : kNoMetadataHeader;
-  const int h0 = hdr[MD_MAGIC], h1 = hdr[MD_BATCH], h2 = hdr[MD_UNITS];
-  const bool bad = md && ((h0 != kMdMagic) | (h1 != B) | (h2 != units));
-  if (bad | (skip_single && n == 1)) return;
-  const int r = blockIdx.y * 2 + (threadIdx.x >> 7);
+  if (skip_single && n == 1) return;
+  const int half = threadIdx.x / (kCombineGroups * 64);         // row of the workgroup
+  const int grp = (threadIdx.x >> 6) % kCombineGroups;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.y * kCombineRows + half;
   // partial slots hold R rows; sequence b owns the first rows_b of them
   const int rows_b = cu_q ? (cu_q[b + 1] - cu_q[b]) * num_heads : R;
   const size_t out_row0 = cu_q ? (size_t)cu_q[b] * num_heads : (size_t)b * R;
-  if (r >= rows_b) return;
-  const int d = (threadIdx.x & 127) * 4;
+  const bool row_ok = r < rows_b;
+  const int d = lane * 4;                                        // features d.. and 256 + d..
   const float* pl = part_lse + (size_t)k0 * R + r;
   const float* po = part_out + ((size_t)k0 * R + r) * kDv + d;
   const size_t lstride = R, ostride = (size_t)R * kDv;
 
-  // One online pass: partial k enters with weight e^(LSE_k - M) against the
-  // running max M; the loads of kU partials are issued together, so a row
-  // with n partials costs about n / kU memory round trips. A partial whose
-  // LSE is -inf is skipped and its values never enter the sums.
-  constexpr int kU = 8;
+  constexpr int kU = kCombineInFlight;
   float M = -INFINITY, S = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < n; k += kU) {
-    float v[kU];
-    f32x4 ov[kU];
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  if (row_ok) {
+    for (int k = grp; k < n; k += kCombineGroups * kU) {
+      float v[kU];
+      f32x4 o0[kU], o1[kU];
 #pragma unroll
-    for (int j = 0; j < kU; ++j) {
-      const bool in = k + j < n;
-      v[j] = in ? pl[(k + j) * lstride] : -INFINITY;
-      ov[j] = in ? *(const f32x4*)(po + (k + j) * ostride) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int j = 0; j < kU; ++j) {
+        const int kk = k + j * kCombineGroups;
+        const bool in = kk < n;
+        v[j] = in ? pl[kk * lstride] : -INFINITY;
+        o0[j] = in ? *(const f32x4*)(po + kk * ostride) : f32x4{0.f, 0.f, 0.f, 0.f};
+        o1[j] = in ? *(const f32x4*)(po + kk * ostride + 256) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-    for (int j = 0; j < kU; ++j) {
-      if (v[j] == -INFINITY) continue;
-      if (v[j] > M) {
-        const float c = expf(M - v[j]);   // 0 while M is -inf
-        S = S * c + 1.f;
-        acc = acc * c + ov[j];
-        M = v[j];
-      } else {
-        const float wgt = expf(v[j] - M);
-        S += wgt;
-        acc += wgt * ov[j];
+      for (int j = 0; j < kU; ++j) {
+        if (v[j] == -INFINITY) continue;
+        if (v[j] > M) {
+          const float c = expf(M - v[j]);   // 0 while M is -inf
+          S = S * c + 1.f;
+          acc0 = acc0 * c + o0[j];
+          acc1 = acc1 * c + o1[j];
+          M = v[j];
+        } else {
+          const float w = expf(v[j] - M);
+          S += w;
+          acc0 += w * o0[j];
+          acc1 += w * o1[j];
+        }
       }
     }
   }
-  const bool live = M != -INFINITY;
-  const float lse_v = live ? M + logf(S) : -INFINITY;
-  acc *= live ? 1.f / S : 0.f;
-  *(f32x4*)(out + (out_row0 + r) * kDv + d) = acc;
-  if (d == 0) lse[out_row0 + r] = lse_v;
+  if (lane == 0) {
+    s_ms[half][grp][0] = M;
+    s_ms[half][grp][1] = S;
+  }
+  if (grp > 0) {
+    s_acc[half][grp - 1][0][lane] = acc0;
+    s_acc[half][grp - 1][1][lane] = acc1;
+  }
+  __syncthreads();
+  if (grp != 0 || !row_ok) return;
+  float Mt = M;
+#pragma unroll
+  for (int g = 1; g < kCombineGroups; ++g) Mt = fmaxf(Mt, s_ms[half][g][0]);
+  const bool live = Mt != -INFINITY;
+  float St = 0.f;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  if (live) {
+    const float c0 = M == -INFINITY ? 0.f : expf(M - Mt);
+    St = S * c0;
+    a0 = acc0 * c0;
+    a1 = acc1 * c0;
+#pragma unroll
+    for (int g = 1; g < kCombineGroups; ++g) {
+      const float mg = s_ms[half][g][0];
+      const float cg = mg == -INFINITY ? 0.f : expf(mg - Mt);
+      St += s_ms[half][g][1] * cg;
+      a0 += cg * s_acc[half][g - 1][0][lane];
+      a1 += cg * s_acc[half][g - 1][1][lane];
+    }
+  }
+  const float inv = live ? 1.f / St : 0.f;
+  float* dst = out + (out_row0 + r) * kDv + d;
+  *(f32x4*)dst = a0 * inv;
+  *(f32x4*)(dst + 256) = a1 * inv;
+  if (lane == 0) lse[out_row0 + r] = live ? Mt + logf(St) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -2088,12 +2132,12 @@ hipError_t launch_combine(const float* part_out, const float* part_lse, const in
                           const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
                           float* lse, int skip_single, hipStream_t s, const int32_t* md, int units,
                           hipEvent_t ev_start, hipEvent_t ev_stop) {
-  dim3 grid(batch, (rows + 1) / 2);
+  dim3 grid(batch, (rows + kCombineRows - 1) / kCombineRows);
   if (ev_start || ev_stop)
-    hipExtLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, ev_start, ev_stop, 0, part_out, part_lse,
+    hipExtLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, ev_start, ev_stop, 0, part_out, part_lse,
                           offsets, cu_q, num_heads, batch, rows, out, lse, skip_single, md, units);
   else
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, part_out, part_lse, offsets, cu_q, num_heads,
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, part_out, part_lse, offsets, cu_q, num_heads,
                        batch, rows, out, lse, skip_single, md, units);
   return hipGetLastError();
 }
