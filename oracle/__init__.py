@@ -28,3 +28,4 @@ from .mla_oracle import (  # noqa: F401
     E4M3FN_MAX, encode_e4m3fn, quantize_token_e4m3, append_kv, quantize_query_rows_e4m3,
     D_NOPE, D_ROPE, D_QK_PREFILL, D_V_PREFILL, mla_prefill,
 )
+from . import prefill_quant  # noqa: F401,E402
