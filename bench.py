@@ -81,7 +81,7 @@ def kernel_source_digest() -> str:
     removed, so that editing a comment does not count as changing a kernel."""
     import hashlib
     src = ""
-    for name in ("mla_device.h", "mla_kernels.hip", "mla_decode_so.hip", "mla_prefill.hip"):
+    for name in ("mla_device.h", "mla_kernels.hip", "mla_decode_so.hip", "mla_prefill.hip", "mla_prefill_q8.hip"):
         with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", name)) as f:
             src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
@@ -483,7 +483,9 @@ def bench_prefill(args):
     import mla_decode_attention_amd as mla
     from workloads import prefill_config, PREFILL_TEXT
 
-    w = prefill_config(args.config, seed=0)
+    quant = args.config.endswith("_q8")
+    wname = args.config[:-3] if quant else args.config
+    w = prefill_config(wname, seed=0)
     alg = prefill_algorithmic(w)
     print(f"[bench] {args.config}: {alg['flops'] / 1e12:.2f} TFLOP per call", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
@@ -503,8 +505,13 @@ def bench_prefill(args):
         torch.cuda.synchronize()
         del a, b
 
+    qkv = mla.prefill_quantize_kv(kn, kr, v, ck) if quant else None
+
     def step():
-        mla.prefill(q, kn, kr, v, cq, ck, max_q, w.softmax_scale, out=out, lse=lse)
+        if quant:   # the dynamic quantisation of K and V is part of every call
+            mla.prefill_quant(q, kn, kr, v, cq, ck, max_q, w.softmax_scale, out=out, lse=lse, qkv=qkv)
+        else:
+            mla.prefill(q, kn, kr, v, cq, ck, max_q, w.softmax_scale, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -512,11 +519,13 @@ def bench_prefill(args):
     reps = max(args.reps, 50)
     mla.profile_enable(True)
     mla.profile_read_launches(mla.PROFILE_ATTENTION, capacity=0)
+    mla.profile_read_launches(mla.PROFILE_QUANTIZE, capacity=0)
     for _ in range(reps):
         step()
     torch.cuda.synchronize()
     mla.profile_enable(False)
     kern = stats(mla.profile_read_launches(mla.PROFILE_ATTENTION, capacity=reps + 8))
+    qkern = stats(mla.profile_read_launches(mla.PROFILE_QUANTIZE, capacity=reps + 8)) if quant else None
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     ev[0].record()
     for i in range(args.steps):
@@ -527,12 +536,23 @@ def bench_prefill(args):
     step_ms = ev[0].elapsed_time(ev[args.steps]) / args.steps
     tflops = alg["flops"] / (step_ms * 1e-3) / 1e12
     achieved = alg["flops"] / (kern["mean"] * 1e-3) / 1e12
-    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.config),
-            "kernel": "prefill_kernel", "kernel_ms": kern["mean"], "kernel_ms_median": kern["median"],
-            "launches": kern["n"], "frac_step": round(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12) / (per["median"] * 1e-3), 4),
+    # the quantised path contracts INT8 x INT8 (QK) and FP8 x FP8 (PV): both
+    # dense peaks are 5.0 POP/s / PFLOP/s on MI355X
+    peak = PEAK_FP8_TFLOPS if quant else PEAK_BF16_TFLOPS
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.config),
+            "kernel": "prefill_q8_kernel" if quant else "prefill_kernel", "kernel_ms": kern["mean"],
+            "kernel_ms_median": kern["median"], "launches": kern["n"],
+            "frac_step": round(alg["flops"] / (peak * 1e12) / (per["median"] * 1e-3), 4),
             "algorithmic_bytes": alg["bytes"], "algorithmic_flops": alg["flops"],
-            "t_roof_us": round(alg["flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e6, 2)}
+            "t_roof_us": round(alg["flops"] / (peak * 1e12) * 1e6, 2)}
+    if quant:
+        Tk = int(w.cu_k[-1])
+        slots = Tk // 64 + w.batch
+        qbytes = Tk * H * (128 + 128) * 2 + Tk * 64 * 2 + slots * H * (12288 + 8192 + 256 + 4)
+        roof["quantizer"] = {"kernel": "quant_kv_kernel", "ms_mean": qkern["mean"], "ms_median": qkern["median"],
+                             "launches": qkern["n"], "algorithmic_bytes": qbytes,
+                             "GB/s": round(qbytes / (qkern["mean"] * 1e-3) / 1e9, 1)}
     line = {
         "metric": METRIC,
         "value": round(tflops, 1),
@@ -544,9 +564,11 @@ def bench_prefill(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "int8+fp8" if quant else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: {PREFILL_TEXT[args.config]}", "batch": w.batch, "heads": H,
+        "config": {"workload": f"{args.config}: {PREFILL_TEXT[wname]}"
+                               + ("; INT8 Q.K^T, FP8 P.V, K/V quantised in every call" if quant else ""),
+                   "batch": w.batch, "heads": H,
                    "query_tokens": Tq, "key_tokens": int(w.cu_k[-1]), "visible_pairs": alg["visible_pairs"],
                    "seed": 0},
         "step_ms": per,
@@ -566,10 +588,12 @@ def main():
     ap.add_argument("--reps", type=int, default=100, help="kernel launches timed per workload (at least 50)")
     ap.add_argument("--config", default="all",
                     choices=["all", "tiny", "share16", "mtp", "ragged", "fp8", "varlen", "fp8mma", "prefill",
-                             "extend"],
+                             "extend", "prefill_q8", "extend_q8"],
                     help="all = the five decode workloads, headline fp8; fp8mma = the fp8 workload on "
                          "mla_decode_fwd_fp8mma (queries and P in E4M3, fp8 matrix cores; an approximation of "
-                         "the default path); prefill / extend = the second workload (mla_prefill_fwd)")
+                         "the default path); prefill / extend = the second workload (mla_prefill_fwd); "
+                         "prefill_q8 / extend_q8 = the same on the quantised path (mla_prefill_quantize_kv + "
+                         "mla_prefill_quant_fwd)")
     ap.add_argument("--sets", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--num-units", type=int, default=0, help="split work units (0 = library default)")
     ap.add_argument("--min-tiles", type=int, default=0,
@@ -596,7 +620,7 @@ def main():
     if args.steps < 1:
         ap.error("--steps must be >= 1")
 
-    if args.config in ("prefill", "extend"):
+    if args.config in ("prefill", "extend", "prefill_q8", "extend_q8"):
         return bench_prefill(args)
     return bench_decode(args)
 

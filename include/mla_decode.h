@@ -259,6 +259,62 @@ int mla_prefill_fwd(const void* q, const void* k_nope, const void* k_rope, const
                     int num_heads, float softmax_scale, float* out, float* lse, void* stream);
 
 /*
+ * Quantised prefill / extend: the dynamic quantisation of PaddleNLP issue
+ * #10157's quantization section (SageAttention, DeepSeek head dim 192) --
+ * Q and K quantised to INT8, V to FP8; the INT32 products Q.K^T turned into
+ * FP32 and dequantised, an online softmax over them, its P quantised to FP8
+ * and multiplied with the FP8 V, the product dequantised once. Same inputs,
+ * outputs and causal rule as mla_prefill_fwd. The pages fix no block sizes or
+ * scale rules; this library's:
+ *   Q: INT8 per (query token, head): scale = max|q| / 127 over the 192
+ *      features (fp32), code = clamp(rint(q * (127 / max|q|)), +-127);
+ *   K: INT8 per (sequence, 64-key tile counted from the sequence's first key,
+ *      head), the same rule over the tile's valid keys x 192 features
+ *      (features 0-127: the head's k_nope, 128-191: k_rope);
+ *   V: E4M3FN per (sequence, 32-key block, head, feature) with the scale
+ *      2^e, e the smallest integer with max|v| <= 448 * 2^e (clamped to
+ *      [-127, 127]; 0 for an all-zero block), code = nearest-even E4M3FN of
+ *      v * 2^-e (exact);
+ *   P: the online softmax raises its running max to every 64-key tile's max
+ *      (so P <= 1) and quantises P * 2^8 to E4M3FN; the row sum adds the
+ *      unquantised P.
+ * A row with no visible key gets O = 0, LSE = -inf.
+ *
+ * mla_prefill_quant_kv_bytes: size of the quantised K/V buffer ("qkv") for
+ *   total_k keys (= cu_seqlens_k[batch]); 0 for invalid sizes. Host-only.
+ *   Layout (for tests and tools; n = total_k / 64 + batch tile slots, the
+ *   tile t of sequence b in slot T = cu_k[b] / 64 + b + t, record R = T * H + h):
+ *     k8 at 0: 12288 bytes per record; byte f*1024 + l*16 + i is the INT8
+ *        code of K[key 64t + 32(f/6) + l%32][feature 32(f%6) + 16(l/32) + i];
+ *     v8 at round256(n*H*12288): 8192 bytes per record; byte
+ *        (2g + q)*1024 + l*16 + i is the E4M3FN code of V[key 64t + 32q +
+ *        8(i/4) + 4(l/32) + i%4][feature 32g + l%32];
+ *     vs after v8 (each array starts 256-aligned): 256 bytes per record; byte
+ *        4l + g = 127 + e of (feature 32g + l%32, 32-key block 2t + l/32);
+ *     ks after vs: one fp32 K scale per record.
+ *   Keys past the sequence end hold code 0; slots between sequences are not
+ *   written.
+ * mla_prefill_quantize_kv: fills qkv from the bf16 k_nope [total_k, H, 128],
+ *   k_rope [total_k, 64], v [total_k, H, 128] (16-byte aligned) and
+ *   cu_seqlens_k [batch + 1] (non-decreasing, cu_k[batch] = total_k: caller
+ *   contract, not read on the host). qkv: device, 256-byte aligned,
+ *   >= mla_prefill_quant_kv_bytes bytes, else MLA_ERR_WORKSPACE.
+ * mla_prefill_quant_fwd: attention of q [total_q, H, 192] bf16 (quantised
+ *   in the kernel) over a qkv filled by mla_prefill_quantize_kv for the same
+ *   cu_seqlens_k, batch, total_k and num_heads; out [total_q, H, 128] fp32,
+ *   lse [total_q, H] (natural log); rows of sequences with N_b = 0 are not
+ *   written. The library allocates nothing. Errors: MLA_ERR_INVALID_ARG for
+ *   NULL or misaligned pointers and out-of-range sizes (num_heads <= 65535),
+ *   MLA_ERR_WORKSPACE for a short qkv, MLA_ERR_HIP for a failed launch.
+ */
+size_t mla_prefill_quant_kv_bytes(int batch, int64_t total_k, int num_heads);
+int mla_prefill_quantize_kv(const void* k_nope, const void* k_rope, const void* v, const int32_t* cu_seqlens_k,
+                            int batch, int64_t total_k, int num_heads, void* qkv, size_t qkv_bytes, void* stream);
+int mla_prefill_quant_fwd(const void* q, const void* qkv, size_t qkv_bytes, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, int batch, int max_q_len, int64_t total_k, int num_heads,
+                          float softmax_scale, float* out, float* lse, void* stream);
+
+/*
  * mla_combine: merge per-sequence partials by their log-sum-exp, the merge
  * step of split-KV decoding (FlashDecoding, named among the attention
  * features in PaddleNLP issue #10157's overview; the cache partitions of
@@ -350,9 +406,11 @@ int mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const float* kv_
  *   caller's stream, so each interval is that kernel's execution (no launch
  *   latency). Launches are recorded per kind:
  *     MLA_PROFILE_ATTENTION  the attention kernel of mla_decode_fwd and its
- *                            variants, and the kernel of mla_prefill_fwd
+ *                            variants, and the kernels of mla_prefill_fwd and
+ *                            mla_prefill_quant_fwd
  *     MLA_PROFILE_METADATA   the kernel of mla_get_split_metadata
  *     MLA_PROFILE_COMBINE    the LSE merge (of a split decode or mla_combine)
+ *     MLA_PROFILE_QUANTIZE   the K/V quantiser of mla_prefill_quantize_kv
  *   Event pairs come from a pool the library creates on first use (host-side
  *   HIP event objects; no device memory). mla_profile_enable(0) stops
  *   recording.
@@ -366,6 +424,7 @@ int mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const float* kv_
 #define MLA_PROFILE_ATTENTION 0
 #define MLA_PROFILE_METADATA 1
 #define MLA_PROFILE_COMBINE 2
+#define MLA_PROFILE_QUANTIZE 3
 int mla_profile_enable(int enable);
 int mla_profile_read_launches(int kernel, float* ms, int capacity, int* count);
 int mla_profile_read(double* total_ms, int* launches);

@@ -22,7 +22,8 @@ import torch
 __all__ = ["load_library", "library_path", "abi_version", "default_num_units", "metadata_bytes",
            "workspace_bytes", "SplitPlan", "profile_enable", "profile_read", "profile_read_launches",
            "PROFILE_ATTENTION", "PROFILE_METADATA", "PROFILE_COMBINE", "get_split_metadata", "decode",
-           "decode_varlen", "decode_noalloc", "combine", "append_kv", "prefill",
+           "decode_varlen", "decode_noalloc", "combine", "append_kv", "prefill", "PROFILE_QUANTIZE",
+           "prefill_quant_kv_bytes", "prefill_quantize_kv", "prefill_quant",
            "MLAError", "KV_BF16", "KV_FP8_E4M3", "PAGE_TOKENS", "D_QK", "D_V"]
 
 PAGE_TOKENS = 64
@@ -67,6 +68,10 @@ def load_library():
                                           ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
         "mla_combine": (c_int, [vp, vp, vp, c_int, c_int, vp, vp, vp]),
         "mla_prefill_fwd": (c_int, [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, ctypes.c_float, vp, vp, vp]),
+        "mla_prefill_quant_kv_bytes": (c_size, [c_int, ctypes.c_int64, c_int]),
+        "mla_prefill_quantize_kv": (c_int, [vp, vp, vp, vp, c_int, ctypes.c_int64, c_int, vp, c_size, vp]),
+        "mla_prefill_quant_fwd": (c_int, [vp, vp, c_size, vp, vp, c_int, c_int, ctypes.c_int64, c_int,
+                                          ctypes.c_float, vp, vp, vp]),
         "mla_append_kv": (c_int, [vp, c_int, c_int, vp, c_int, vp, vp, vp, c_int, c_int, vp]),
         "mla_decode_fwd_varlen": (c_int, [vp, vp, c_int, c_int, vp, vp, c_int, c_int, vp, c_int, vp, c_int,
                                           c_int, ctypes.c_float, vp, vp, vp, c_int, vp, c_size, vp]),
@@ -319,6 +324,74 @@ def prefill(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torc
     return out, lse
 
 
+def _prefill_kv_args(k_nope, k_rope, v, cu_seqlens_k, H=None):
+    dev = k_nope.device
+    _need(k_nope, "k_nope", (torch.bfloat16,), 3)
+    Tk = k_nope.shape[0]
+    H = k_nope.shape[1] if H is None else H
+    _need(k_nope, "k_nope", (torch.bfloat16,), 3, shape=(Tk, H, 128), device=dev)
+    _need(k_rope, "k_rope", (torch.bfloat16,), 2, shape=(Tk, 64), device=dev)
+    _need(v, "v", (torch.bfloat16,), 3, shape=(Tk, H, 128), device=dev)
+    _need(cu_seqlens_k, "cu_seqlens_k", (torch.int32,), 1, device=dev)
+    B = cu_seqlens_k.shape[0] - 1
+    if B < 1:
+        raise ValueError("cu_seqlens_k must have batch + 1 >= 2 entries")
+    return Tk, H, B
+
+
+def prefill_quant_kv_bytes(batch: int, total_k: int, num_heads: int) -> int:
+    """Bytes of the quantised K/V buffer of prefill_quantize_kv."""
+    return int(load_library().mla_prefill_quant_kv_bytes(int(batch), int(total_k), int(num_heads)))
+
+
+def prefill_quantize_kv(k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                        qkv: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """K to INT8 and V to FP8 for prefill_quant (layout in include/mla_decode.h).
+    Returns the uint8 buffer (allocated when qkv is None)."""
+    lib = load_library()
+    Tk, H, B = _prefill_kv_args(k_nope, k_rope, v, cu_seqlens_k)
+    nbytes = prefill_quant_kv_bytes(B, Tk, H)
+    if qkv is None:
+        qkv = torch.empty(nbytes, dtype=torch.uint8, device=k_nope.device)
+    _need(qkv, "qkv", (torch.uint8,), 1, device=k_nope.device)
+    _check(lib.mla_prefill_quantize_kv(_ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(cu_seqlens_k), B, Tk, H,
+                                       _ptr(qkv), _nbytes(qkv), _stream()), "mla_prefill_quantize_kv")
+    return qkv
+
+
+def prefill_quant(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
+                  cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_q_len: int, softmax_scale: float,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  qkv: Optional[torch.Tensor] = None, quantize: bool = True):
+    """Quantised prefill / extend (INT8 Q.K^T, FP8 P.V). Arguments as prefill();
+    K and V are quantised into qkv first (skipped with quantize=False, for a
+    qkv that prefill_quantize_kv already filled from the same K, V and
+    cu_seqlens_k). Returns (out fp32 [Tq,H,128], lse fp32 [Tq,H])."""
+    lib = load_library()
+    _need(q, "q", (torch.bfloat16,), 3)
+    Tq, H, d = q.shape
+    if d != 192:
+        raise ValueError("q last dim must be 192")
+    dev = q.device
+    Tk, _, B = _prefill_kv_args(k_nope, k_rope, v, cu_seqlens_k, H)
+    _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,), 1, shape=(B + 1,), device=dev)
+    if quantize:
+        qkv = prefill_quantize_kv(k_nope, k_rope, v, cu_seqlens_k, qkv)
+    elif qkv is None:
+        raise ValueError("quantize=False needs a filled qkv")
+    _need(qkv, "qkv", (torch.uint8,), 1, device=dev)
+    if out is None:
+        out = torch.empty((Tq, H, 128), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), 3, shape=(Tq, H, 128), device=dev)
+    _need(lse, "lse", (torch.float32,), 2, shape=(Tq, H), device=dev)
+    _check(lib.mla_prefill_quant_fwd(_ptr(q), _ptr(qkv), _nbytes(qkv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B,
+                                     int(max_q_len), Tk, H, float(softmax_scale), _ptr(out), _ptr(lse), _stream()),
+           "mla_prefill_quant_fwd")
+    return out, lse
+
+
 def decode_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, max_q_len: int, kv_cache: torch.Tensor,
                   block_table: torch.Tensor, cache_seqlens: torch.Tensor, softmax_scale: float,
                   kv_scale: Optional[torch.Tensor] = None, plan: Optional[SplitPlan] = None,
@@ -374,7 +447,7 @@ def profile_read():
     return ms.value, n.value
 
 
-PROFILE_ATTENTION, PROFILE_METADATA, PROFILE_COMBINE = 0, 1, 2
+PROFILE_ATTENTION, PROFILE_METADATA, PROFILE_COMBINE, PROFILE_QUANTIZE = 0, 1, 2, 3
 
 
 def profile_read_launches(kernel: int = PROFILE_ATTENTION, capacity: int = 4096):

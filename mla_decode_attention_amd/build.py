@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmla_decode.so"
 SOURCES = ["csrc/mla_kernels.hip", "csrc/mla_append.hip", "csrc/mla_prefill.hip", "csrc/mla_api.hip",
-           "csrc/mla_scratch.hip", "csrc/mla_decode_so.hip"]
+           "csrc/mla_scratch.hip", "csrc/mla_decode_so.hip", "csrc/mla_prefill_q8.hip"]
 ARCH = "gfx950"
 
 

@@ -65,7 +65,7 @@ int device_info(DevInfo* out) {
 
 // Measurement hook state (see mla_profile_enable): per kernel kind, the
 // (start, stop) event pairs recorded by the dispatches, in launch order.
-constexpr int kProfKinds = 3;   // MLA_PROFILE_ATTENTION, _METADATA, _COMBINE
+constexpr int kProfKinds = 4;   // MLA_PROFILE_ATTENTION, _METADATA, _COMBINE, _QUANTIZE
 struct Profile {
   std::mutex mu;
   bool on = false;
@@ -387,6 +387,80 @@ int mla_prefill_fwd(const void* q, const void* k_nope, const void* k_rope, const
                                      softmax_scale, out, lse, (hipStream_t)stream, ev0, ev1);
   prof_end(MLA_PROFILE_ATTENTION, ev0, ev1, e == hipSuccess);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t mla_prefill_quant_kv_bytes(int batch, int64_t total_k, int num_heads) {
+  if (batch < 1 || total_k < 0 || num_heads < 1) return 0;
+  return mla::qkv_layout(batch, total_k, num_heads).bytes;
+}
+
+namespace {
+int check_quant_sizes(int batch, int64_t total_k, int num_heads) {
+  if (batch < 1 || num_heads < 1 || total_k < 0)
+    return fail(MLA_ERR_INVALID_ARG, "batch >= 1, num_heads >= 1, total_k >= 0 required (got %d, %d, %lld)", batch,
+                num_heads, (long long)total_k);
+  if (num_heads > 65535) return fail(MLA_ERR_INVALID_ARG, "num_heads must be <= 65535");
+  // one quantiser workgroup per tile index: total_k / 64 + batch of them
+  if (total_k / 64 + batch > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARG, "total_k / 64 + batch exceeds the 32-bit grid");
+  return MLA_OK;
+}
+}  // namespace
+
+int mla_prefill_quantize_kv(const void* k_nope, const void* k_rope, const void* v, const int32_t* cu_seqlens_k,
+                            int batch, int64_t total_k, int num_heads, void* qkv, size_t qkv_bytes, void* stream) {
+  if (!k_nope || !k_rope || !v || !cu_seqlens_k || !qkv) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  int st = check_quant_sizes(batch, total_k, num_heads);
+  if (st != MLA_OK) return st;
+  if (!aligned(k_nope, 16) || !aligned(k_rope, 16) || !aligned(v, 16) || !aligned(qkv, 256))
+    return fail(MLA_ERR_INVALID_ARG, "k_nope, k_rope, v must be 16-byte and qkv 256-byte aligned");
+  if (!aligned(cu_seqlens_k, 4)) return fail(MLA_ERR_INVALID_ARG, "cu_seqlens_k must be 4-byte aligned");
+  const size_t need = mla::qkv_layout(batch, total_k, num_heads).bytes;
+  if (qkv_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "qkv buffer too small: %zu bytes, need %zu", qkv_bytes, need);
+  DevInfo d;
+  st = device_info(&d);
+  if (st != MLA_OK) return st;
+  hipEvent_t ev0, ev1;
+  prof_begin(&ev0, &ev1);
+  hipError_t e = mla::launch_quant_kv((const uint16_t*)k_nope, (const uint16_t*)k_rope, (const uint16_t*)v,
+                                      cu_seqlens_k, batch, total_k, num_heads, (uint8_t*)qkv, (hipStream_t)stream,
+                                      ev0, ev1);
+  prof_end(MLA_PROFILE_QUANTIZE, ev0, ev1, e == hipSuccess);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "quantiser launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int mla_prefill_quant_fwd(const void* q, const void* qkv, size_t qkv_bytes, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, int batch, int max_q_len, int64_t total_k, int num_heads,
+                          float softmax_scale, float* out, float* lse, void* stream) {
+  if (!q || !qkv || !cu_seqlens_q || !cu_seqlens_k || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  int st = check_quant_sizes(batch, total_k, num_heads);
+  if (st != MLA_OK) return st;
+  if (max_q_len < 1) return fail(MLA_ERR_INVALID_ARG, "max_q_len must be >= 1 (got %d)", max_q_len);
+  const long long nblk = ((long long)max_q_len + mla::prefill_q8_rows_per_block() - 1) / mla::prefill_q8_rows_per_block();
+  if (nblk * batch * num_heads > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARG, "batch * query blocks * num_heads exceeds the 32-bit grid index");
+  if (!isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(qkv, 256))
+    return fail(MLA_ERR_INVALID_ARG, "q and out must be 16-byte and qkv 256-byte aligned");
+  if (!aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return fail(MLA_ERR_INVALID_ARG, "lse and the offsets must be 4-byte aligned");
+  const size_t need = mla::qkv_layout(batch, total_k, num_heads).bytes;
+  if (qkv_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "qkv buffer too small: %zu bytes, need %zu", qkv_bytes, need);
+  DevInfo d;
+  st = device_info(&d);
+  if (st != MLA_OK) return st;
+  hipEvent_t ev0, ev1;
+  prof_begin(&ev0, &ev1);
+  hipError_t e = mla::launch_prefill_q8((const uint16_t*)q, (const uint8_t*)qkv, cu_seqlens_q, cu_seqlens_k, batch,
+                                        max_q_len, total_k, num_heads, softmax_scale, out, lse, (hipStream_t)stream,
+                                        ev0, ev1);
+  prof_end(MLA_PROFILE_ATTENTION, ev0, ev1, e == hipSuccess);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "quantised prefill launch: %s", hipGetErrorString(e));
   return ok();
 }
 

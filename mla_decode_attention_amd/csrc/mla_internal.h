@@ -90,6 +90,33 @@ hipError_t launch_combine(const float* part_out, const float* part_lse, const in
 hipError_t scratch_address(int dev, void** out);
 
 // Prefill / extend (un-absorbed MLA, head dim 192 = 128 + 64 shared rope, v 128).
+// Quantised prefill (mla_prefill_q8.hip): byte offsets of the quantised K,
+// V, V scales and K scales inside one buffer, and its size.
+struct QkvLayout {
+  size_t k8, v8, vs, ks, bytes;
+};
+// total_k / 64 + batch tile slots per head; per (slot, head) record 12288
+// bytes of K codes, 8192 of V codes, 256 E8M0 bytes and one fp32 K scale,
+// each array starting 256-byte aligned.
+inline QkvLayout qkv_layout(int batch, long long total_k, int num_heads) {
+  auto r256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t recs = (size_t)(total_k / 64 + batch) * (size_t)num_heads;
+  QkvLayout l;
+  l.k8 = 0;
+  l.v8 = r256(recs * 12288);
+  l.vs = l.v8 + r256(recs * 8192);
+  l.ks = l.vs + r256(recs * 256);
+  l.bytes = l.ks + r256(recs * sizeof(float));
+  return l;
+}
+hipError_t launch_quant_kv(const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v, const int32_t* cu_k,
+                           int batch, long long total_k, int num_heads, uint8_t* qkv, hipStream_t s,
+                           hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+int prefill_q8_rows_per_block();
+hipError_t launch_prefill_q8(const uint16_t* q, const uint8_t* qkv, const int32_t* cu_q, const int32_t* cu_k,
+                             int batch, int max_q_len, long long total_k, int num_heads, float softmax_scale,
+                             float* out, float* lse, hipStream_t s, hipEvent_t ev_start = nullptr,
+                             hipEvent_t ev_stop = nullptr);
 int prefill_rows_per_block();
 hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,
                           const int32_t* cu_q, const int32_t* cu_k, int batch, int max_q_len, int num_heads,

@@ -123,7 +123,7 @@ TIE_WINDOW = 2.0 ** -14
 
 
 def prefill_quant(q_bits, k_nope_bits, k_rope_bits, v_bits, cu_q, cu_k, softmax_scale,
-                  batch_indices=None, rows=None, return_slack=False):
+                  batch_indices=None, rows=None, return_slack=False, tile_dot_rel=0.0):
     """Quantised causal prefill / extend. Shapes and visibility as the
     unquantised prefill: sequence b owns queries cu_q[b]..cu_q[b+1] (N_b, the
     last N_b of its L_b tokens) and keys cu_k[b]..cu_k[b+1]; query i sees keys
@@ -134,7 +134,10 @@ def prefill_quant(q_bits, k_nope_bits, k_rope_bits, v_bits, cu_q, cu_k, softmax_
     return_slack: also return slack [Tq, H, 128], a bound on how far out may
     move when P codes whose input P * 2^8 lies within TIE_WINDOW (relative)
     of a rounding tie take the other of their two candidate codes -- the
-    codes an fp32 evaluation of these steps may legitimately pick.
+    codes an fp32 evaluation of these steps may legitimately pick -- plus,
+    when tile_dot_rel > 0, an error of up to tile_dot_rel times the largest
+    |P8_j V8_jd| term in each tile's P.V sum (for arithmetic that rounds
+    those sums more coarsely than the exact products).
     """
     q_codes, q_scale = quantize_query(q_bits)
     kv = quantize_kv(k_nope_bits, k_rope_bits, v_bits, cu_k)
@@ -183,6 +186,8 @@ def prefill_quant(q_bits, k_nope_bits, k_rope_bits, v_bits, cu_q, cu_k, softmax_
                     lo = decode_e4m3fn(encode_e4m3fn(y * (1 - TIE_WINDOW)))
                     hi = decode_e4m3fn(encode_e4m3fn(np.minimum(y * (1 + TIE_WINDOW), E4M3FN_MAX)))
                     sl = sl * alpha[:, None] + ((hi - lo) * 2.0 ** -P_SHIFT) @ np.abs(V8)
+                    if tile_dot_rel > 0:
+                        sl += tile_dot_rel * (P8[:, :, None] * np.abs(V8)[None]).max(axis=1)
                 m = np.where(live, m_new, m)
             live = l > 0
             rows_out = q0 + sel

@@ -53,7 +53,7 @@ hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) {
 
 // ------------------------------------------------------------------ fake launchers
 struct Launch {
-  int kind = 0;   // 1 decode, 2 metadata, 3 append, 4 combine, 5 prefill
+  int kind = 0;   // 1 decode, 2 metadata, 3 append, 4 combine, 5 prefill, 6 quantiser, 7 quantised prefill
   mla::DecodeParams p{};
   int variant = 0, grid_units = 0, batch = 0, units = 0, rows = 0, skip_single = 0, min_tiles = 0, cost = 0;
   const void* a = nullptr;
@@ -123,6 +123,30 @@ hipError_t launch_prefill(const uint16_t*, const uint16_t*, const uint16_t*, con
   Launch l;
   l.kind = 5;
   l.batch = batch;
+  l.events = e0 && e1;
+  g_launches.push_back(l);
+  return hipSuccess;
+}
+int prefill_q8_rows_per_block() { return 128; }
+hipError_t launch_quant_kv(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int batch,
+                           long long total_k, int, uint8_t* qkv, hipStream_t, hipEvent_t e0, hipEvent_t e1) {
+  Launch l;
+  l.kind = 6;
+  l.batch = batch;
+  l.units = (int)total_k;
+  l.a = qkv;
+  l.events = e0 && e1;
+  g_launches.push_back(l);
+  return hipSuccess;
+}
+hipError_t launch_prefill_q8(const uint16_t*, const uint8_t* qkv, const int32_t*, const int32_t*, int batch, int,
+                             long long total_k, int, float, float*, float*, hipStream_t, hipEvent_t e0,
+                             hipEvent_t e1) {
+  Launch l;
+  l.kind = 7;
+  l.batch = batch;
+  l.units = (int)total_k;
+  l.a = qkv;
   l.events = e0 && e1;
   g_launches.push_back(l);
   return hipSuccess;
@@ -374,6 +398,35 @@ static void check_metadata_and_others() {
                         nullptr) == MLA_ERR_INVALID_ARG);
   CHECK(mla_prefill_fwd(q, q, q, q, sl, sl, 2, 1024, 70000, 0.072f, (float*)g_buf[4], (float*)g_buf[5],
                         nullptr) == MLA_ERR_INVALID_ARG);
+
+  // quantised prefill: buffer size, layout bound, errors
+  // 100 keys, 2 sequences -> 100/64 + 2 = 3 slots per head
+  const size_t need = mla_prefill_quant_kv_bytes(2, 100, 2);
+  CHECK(need == 3 * 2 * 12288 + 3 * 2 * 8192 + 3 * 2 * 256 + 256);
+  CHECK(mla_prefill_quant_kv_bytes(0, 100, 2) == 0 && mla_prefill_quant_kv_bytes(2, -1, 2) == 0);
+  void* qkv = g_buf[6];
+  g_launches.clear();
+  CHECK(mla_prefill_quantize_kv(q, q, q, sl, 2, 100, 2, qkv, need - 1, nullptr) == MLA_ERR_WORKSPACE);
+  CHECK(mla_prefill_quantize_kv(q, q, q, sl, 1, 10, 1, qkv, mla_prefill_quant_kv_bytes(1, 10, 1), nullptr) == MLA_OK);
+  CHECK(g_launches.size() == 1 && g_launches[0].kind == 6 && g_launches[0].units == 10 && g_launches[0].a == qkv);
+  CHECK(mla_prefill_quantize_kv(q, q, q, sl, 1, 10, 1, qkv, mla_prefill_quant_kv_bytes(1, 10, 1) - 1, nullptr) ==
+        MLA_ERR_WORKSPACE);
+  CHECK(mla_prefill_quantize_kv(q, q, q, sl, 1, 10, 1, (char*)qkv + 16, 1 << 15, nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_prefill_quantize_kv(q, q, q, sl, 1, 10, 70000, qkv, 1 << 15, nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_prefill_quantize_kv(q, q, q, sl, 1, (int64_t)1 << 40, 1, qkv, 1 << 15, nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_prefill_quantize_kv(nullptr, q, q, sl, 1, 10, 1, qkv, 1 << 15, nullptr) == MLA_ERR_INVALID_ARG);
+  const size_t n1 = mla_prefill_quant_kv_bytes(1, 10, 1);
+  CHECK(mla_prefill_quant_fwd(q, qkv, n1, sl, sl, 1, 10, 10, 1, 0.072f, (float*)g_buf[4], (float*)g_buf[5],
+                              nullptr) == MLA_OK);
+  CHECK(g_launches.back().kind == 7 && g_launches.back().units == 10);
+  CHECK(mla_prefill_quant_fwd(q, qkv, n1 - 1, sl, sl, 1, 10, 10, 1, 0.072f, (float*)g_buf[4], (float*)g_buf[5],
+                              nullptr) == MLA_ERR_WORKSPACE);
+  CHECK(mla_prefill_quant_fwd(q, qkv, n1, sl, sl, 1, 0, 10, 1, 0.072f, (float*)g_buf[4], (float*)g_buf[5],
+                              nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_prefill_quant_fwd(q, qkv, 1 << 30, sl, sl, 40000, 1 << 15, 10, 256, 0.072f, (float*)g_buf[4],
+                              (float*)g_buf[5], nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_prefill_quant_fwd(q, qkv, n1, sl, sl, 1, 10, 10, 1, INFINITY, (float*)g_buf[4], (float*)g_buf[5],
+                              nullptr) == MLA_ERR_INVALID_ARG);
 }
 
 static void check_profile_hook() {
@@ -415,7 +468,7 @@ static void check_profile_hook() {
   CHECK(mla_profile_read_launches(MLA_PROFILE_METADATA, t, 4, &n) == MLA_OK && n == 1);
   CHECK(mla_profile_read_launches(MLA_PROFILE_ATTENTION, nullptr, 0, &n) == MLA_OK && n == 2);
   CHECK(mla_profile_read_launches(MLA_PROFILE_ATTENTION, t, 4, &n) == MLA_OK && n == 0);
-  CHECK(mla_profile_read_launches(3, t, 4, &n) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_profile_read_launches(4, t, 4, &n) == MLA_ERR_INVALID_ARG);
   CHECK(mla_profile_read_launches(0, nullptr, 4, &n) == MLA_ERR_INVALID_ARG);
   // the pool grows only to the most pairs held at once (5 launches here)
   CHECK(g_events <= 10);
