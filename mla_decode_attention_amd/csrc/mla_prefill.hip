@@ -101,7 +101,8 @@ struct Args {
   float* out;               // [Tq, H, 128]
   float* lse;               // [Tq, H]
   int H, nblk;
-  float scale_log2;
+  float scale_log2;         // |softmax_scale| * log2 e
+  uint32_t q_sign;          // 0x80008000 when softmax_scale < 0: q enters negated
 };
 
 // RB = query row blocks of 32 per wave: RB = 1 gives 128 rows per workgroup
@@ -148,7 +149,10 @@ void prefill_kernel(Args a) {
     const bf16x8* qrow = (const bf16x8*)(a.q + ((size_t)(q0 + min(qi[rb], N - 1)) * H + head) * kDK);
 #pragma unroll
     for (int c = 0; c < 12; ++c) {
-      const bf16x8 v = qrow[2 * c + h];
+      // with a negative softmax scale the scores use -q and |scale|, so that
+      // the row max below can be taken on the raw dot products
+      typedef __attribute__((ext_vector_type(4))) uint32_t u32x4v;
+      const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4v, qrow[2 * c + h]) ^ a.q_sign);
       qreg[rb][c] = row_live[rb] ? v : bf16x8{};
     }
   }
@@ -244,8 +248,8 @@ void prefill_kernel(Args a) {
     }
 
     // ---- softmax: row qi[rb], keys 64t + 32kb + 8(r/4) + 4h + r%4. The max is
-    //      taken on the raw scores (the scale is positive), and the scale is
-    //      folded into the exponent: P = 2^(s * c - m).
+    //      taken on the raw scores (the scale c is positive; q carries its
+    //      sign), and the scale is folded into the exponent: P = 2^(s * c - m).
     const int kt0 = t * kTile;
     if (kt0 + kTile - 1 > off + i0) {          // tile reaches past the block's first row's last key
 #pragma unroll
@@ -350,7 +354,8 @@ hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint1
   a.lse = lse;
   a.H = num_heads;
   a.nblk = (max_q_len + prefill::kRowsWg - 1) / prefill::kRowsWg;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.scale_log2 = fabsf(softmax_scale) * 1.4426950408889634f;
+  a.q_sign = softmax_scale < 0.f ? 0x80008000u : 0u;
   dim3 grid(batch * a.nblk, num_heads);
   // the events (may be null) are recorded by the dispatch itself
   hipExtLaunchKernelGGL(prefill::prefill_kernel<prefill::kRB>, grid, dim3(prefill::kThreads), 0, s, ev_start, ev_stop, 0, a);

@@ -20,7 +20,7 @@
 // order the attention kernel's MFMA operands take them; prefill_q8_kernel has
 // the bf16 prefill kernel's shape (128 query rows of one (sequence, head) per
 // workgroup, 4 waves x 32 rows, 64-key tiles through LDS, double buffered,
-// direct global->LDS loads) with
+// direct global->LDS loads; three workgroups per CU) with
 //   the query rows quantised in registers at the start (B operand of
 //       S^T = K Q^T: k-step c holds features 32c + 16h .. +15 of row n);
 //   QK on v_mfma_i32_32x32x32_i8, 12 per tile and wave, dequantised by one
@@ -207,15 +207,39 @@ struct Args {
   float scale_log2;
 };
 
-__device__ __forceinline__ void wait_loads() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// K/V stages in LDS: the loads of tile t + kStages - 1 go out during tile t.
+// Two stages (41.5 KiB) leave room for three workgroups per CU, which
+// measured faster than three stages at two workgroups per CU.
+#ifndef Q8_STAGES
+#define Q8_STAGES 2
+#endif
+constexpr int kStages = Q8_STAGES;
+static_assert(kStages == 2 || kStages == 3, "waits below cover up to one younger tile");
+
+// Wait until this wave's loads of the current tile have landed (younger: the
+// loads of the one later tile issued after them, 0 or nload of them; the
+// hardware counts vector memory operations in issue order), then make every
+// wave's loads visible.
+__device__ __forceinline__ void wait_tile(bool younger, bool wave0) {
+  if (!younger) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (wave0) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   lds_barrier();
 }
+#define CONST_AS __attribute__((address_space(4)))
+__device__ __forceinline__ float sldf(const float* p, size_t i) { return ((const CONST_AS float*)p)[i]; }
 __device__ __forceinline__ i32x4 ld128i(const LDS_AS uint8_t* p) { return *(const LDS_AS i32x4*)p; }
+__device__ __forceinline__ int max_xor32_i(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return max((int)r[0], (int)r[1]);
+}
 
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+#ifndef Q8_WAVES
+#define Q8_WAVES 3     // waves per SIMD: three workgroups of four waves per CU (<= 168 VGPRs)
+#endif
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(Q8_WAVES, Q8_WAVES)))
 void prefill_q8_kernel(Args a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
   LDS_AS uint8_t* const stage0 = (LDS_AS uint8_t*)smem;
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
@@ -256,7 +280,10 @@ void prefill_q8_kernel(Args a) {
       }
     }
     am = max_xor32(am);
-    const float inv = am > 0.f ? 127.f / am : 0.f;
+    // codes of -q for a negative softmax scale (rint and the clamp are odd
+    // functions, so these are exactly the negated codes of q), so that the
+    // score scale c below is positive and the row max can be taken on the dots
+    const float inv = (am > 0.f ? 127.f / am : 0.f) * (a.scale_log2 < 0.f ? -1.f : 1.f);
     const float sq = am > 0.f ? am / 127.f : 1.f;
 #pragma unroll
     for (int c = 0; c < 6; ++c)
@@ -267,7 +294,7 @@ void prefill_q8_kernel(Args a) {
                               (i8code(bf16f(u1 & 0xFFFF), inv) << 16) | (i8code(bf16f(u1 >> 16), inv) << 24);
         q8[c][w] = row_live ? (int)word : 0;
       }
-    rowc = sq * a.scale_log2;
+    rowc = sq * fabsf(a.scale_log2);
   }
 
   // ---- loads of one tile: K fragments wave + 4i (i < 3), V fragments wave +
@@ -293,13 +320,16 @@ void prefill_q8_kernel(Args a) {
   for (int fb = 0; fb < 4; ++fb) o[fb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (ntiles > 0)
-    for (int i = 0; i < nload; ++i) issue(0, 0, i);
+  for (int t0 = 0; t0 < kStages - 1 && t0 < ntiles; ++t0)
+    for (int i = 0; i < nload; ++i) issue(t0, t0, i);
+  int st_cur = 0;                              // stage of tile t
   for (int t = 0; t < ntiles; ++t) {
-    LDS_AS uint8_t* const cur = stage0 + (t & 1) * kStage;
-    const float kscale = a.ks[(size_t)(tbase + t) * H + head];
-    wait_loads();
-    const bool load_next = t + 1 < ntiles;
+    LDS_AS uint8_t* const cur = stage0 + st_cur * kStage;
+    const float kscale = sldf(a.ks, (size_t)(tbase + t) * H + head);
+    wait_tile(kStages == 3 && t + 1 < ntiles, wave == 0);
+    const int t_load = t + kStages - 1;        // its stage held tile t - 1, read by every wave before the barrier
+    const bool load_next = t_load < ntiles;
+    const int st_load = st_cur == 0 ? kStages - 1 : st_cur - 1;
 
     // ---- QK: S^T[64 keys, 32 rows] = K Q^T, k-step i: features 32(i/2).., key block i%2
     i32x16 sacc[2];
@@ -315,33 +345,34 @@ void prefill_q8_kernel(Args a) {
         const i32x4 av = ring[i % D];
         if (i + D < NQ) ring[i % D] = ld128i(kaddr(i + D));
         sacc[i & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, q8[i >> 1], sacc[i & 1], 0, 0, 0);
-        if ((i & 1) == 0 && (i >> 1) < nload && load_next) issue(t + 1, (t + 1) & 1, i >> 1);
+        if ((i & 1) == 0 && (i >> 1) < nload && load_next) issue(t_load, st_load, i >> 1);
       }
     }
 
-    // ---- dequantise, mask: lane (n, h) register r of block kb is key
-    //      64t + 32kb + 8(r/4) + 4h + r%4 of row qi
-    const float c = rowc * kscale;
-    float s[2][16];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = (float)sacc[kb][r] * c;
+    // ---- mask (tiles that reach past the block's first row's last key): lane
+    //      (n, h) register r of block kb is key 64t + 32kb + 8(r/4) + 4h + r%4
+    //      of row qi; a masked dot becomes INT_MIN, below every real one
+    //      (|dot| <= 192 * 127^2)
     const int kt0 = t * kTile;
-    if (kt0 + kTile - 1 > off + i0) {
+    const bool diag = kt0 + kTile - 1 > off + i0;
+    if (diag) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) > off + qi) s[kb][r] = -INFINITY;
+          if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) > off + qi) sacc[kb][r] = INT_MIN;
     }
-    // ---- online softmax, running max raised to every tile's max
-    float mx = -INFINITY;
+    // ---- online softmax on S * log2 e = dot * c (c > 0: the query codes carry
+    //      the sign of the softmax scale), the row max taken on the integer
+    //      dots; the running max is raised to every tile's max
+    const float c = rowc * kscale;
+    int mi = INT_MIN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_xor32(mx);
+      for (int r = 0; r < 16; ++r) mi = max(mi, sacc[kb][r]);
+    mi = max_xor32_i(mi);
+    const float mx = mi == INT_MIN ? -INFINITY : (float)mi * c;
     const float m_new = fmaxf(m_run, mx);
     const bool raise = m_new > m_run;
     if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -351,7 +382,19 @@ void prefill_q8_kernel(Args a) {
       l_run *= alpha;
     }
     m_run = m_new;
-    const float mo = (m_run == -INFINITY ? 0.f : m_run) - (float)kPShift;   // exp2(s - mo) = P * 2^8
+    const float mo = (m_run == -INFINITY ? 0.f : m_run) - (float)kPShift;   // exp2(dot * c - mo) = P * 2^8
+    float x[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[kb][r] = __builtin_fmaf((float)sacc[kb][r], c, -mo);
+    if (diag) {   // masked scores to -inf (their INT_MIN dots need not give exp2 = 0)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) > off + qi) x[kb][r] = -INFINITY;
+    }
     i32x8 p8;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -360,7 +403,7 @@ void prefill_q8_kernel(Args a) {
         float y[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          y[j] = exp2_fast(s[kb][4 * w + j] - mo);
+          y[j] = exp2_fast(x[kb][4 * w + j]);
           l_run += y[j];
         }
         int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
@@ -383,6 +426,7 @@ void prefill_q8_kernel(Args a) {
         default: o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, p8, o[3], 0, 0, 3, (int)vsw, 0, 127); break;
       }
     }
+    st_cur = st_cur + 1 == kStages ? 0 : st_cur + 1;
   }
 
   // ---- epilogue: O / l, LSE = (m + log2 l - 8) ln 2

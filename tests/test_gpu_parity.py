@@ -270,3 +270,13 @@ def test_rising_scores_rescale(kv_dtype, H, s, split):
     # sits far above their first tile's
     assert float(np.max(ref_lse)) > 20.0
     assert_parity(w, out, lse, ref_out, ref_lse, f"ramp {kv_dtype} H={H} s={s} split={split}")
+
+
+@pytest.mark.parametrize("kv_dtype,H,s", [("bf16", 16, 1), ("bf16", 128, 2), ("fp8_e4m3", 128, 2)])
+def test_negative_softmax_scale(kv_dtype, H, s):
+    """Any finite scale is accepted; a negative one turns the row max into the
+    most negative dot product (every decode kernel scales before its max)."""
+    w = make_workload("neg", 3, H, s, np.array([1, 200, 700]), kv_dtype=kv_dtype, seed=9, softmax_scale=-0.05)
+    for split in (False, True):
+        out, lse, _ = run_gpu(w, split=split)
+        assert_parity(w, out, lse, *reference(w), what=f"negative scale split={split}")

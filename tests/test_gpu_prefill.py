@@ -97,3 +97,12 @@ def test_full_size_sampled(name):
                                         np.array([0, 1], np.int32), np.array([0, p + 1], np.int32),
                                         w.softmax_scale)
             check(out[q0 + i:q0 + i + 1], lse[q0 + i:q0 + i + 1], ro, rl, f"{name} b={b} i={i}")
+
+
+def test_negative_softmax_scale():
+    """The API takes any finite scale: with a negative one the row max is the
+    most negative dot product, which the kernel handles by negating q."""
+    w = make_prefill_workload("neg", [1, 127, 129, 40], [1, 127, 129, 200], 4, seed=6)
+    w.softmax_scale = -0.11
+    out, lse = run(w)
+    check(out, lse, *reference(w), "negative scale")

@@ -233,3 +233,12 @@ def test_full_size_sampled_rows():
         pick |= set(int(x) for x in rng.integers(0, N, 6))
         rows[b] = sorted(x for x in pick if 0 <= x < N)
     check_vs_quant_oracle(out, lse, w, rows=rows, what="full size")
+
+
+def test_negative_softmax_scale():
+    """A negative scale enters as negated query codes (the INT8 rule is odd),
+    so the result matches the oracle's steps with the scale as given."""
+    w = make_prefill_workload("neg", [1, 127, 129, 40], [1, 127, 129, 200], 4, seed=6)
+    w.softmax_scale = -0.11
+    out, lse = run(w)
+    check_vs_quant_oracle(out, lse, w, what="negative scale")
