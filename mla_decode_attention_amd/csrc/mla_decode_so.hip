@@ -83,9 +83,15 @@ struct Cfg<false> {
 };
 
 // fp8: steps of 64 keys (a page). Chunk c (16 codes) of key k at byte
-// ((c / 4) * 64 + k) * 64 + ((c % 4) ^ swz2(k)) * 16 (64-byte line groups of
+// ((c / 4) * 64 + k) * 64 + ((c % 4) ^ swz2s(k)) * 16 (64-byte line groups of
 // 4 KiB); the 64 per-token scales follow the codes, then padding up to 10
-// loads x 256 lanes x 16 bytes.
+// loads x 256 lanes x 16 bytes. swz2s(k) = (k2, k0) (high to low bit): of the
+// two-bit functions of the key bits, one of those under which both operand
+// reads of this kernel -- 16 consecutive keys x 4 chunks (K, 16-byte reads)
+// and 8 keys x 2 chunks x 2 halves (V^T, transposed 8-byte reads) -- measure
+// free of LDS bank conflicts on gfx950 (the LDS hashes address bits into its
+// bank selection, so the plain row/column analysis does not predict this).
+__device__ __forceinline__ int swz2s(int key) { return (((key >> 2) & 1) << 1) | (key & 1); }
 template <>
 struct Cfg<true> {
   static constexpr int kKeys = 64;
@@ -95,7 +101,7 @@ struct Cfg<true> {
   static constexpr int kLoads = 10;
   static constexpr int kLineGroup = kKeys * 64;            // 4096
   __device__ static int byte(int key, int chunk) {
-    return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz2(key)) << 4);
+    return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz2s(key)) << 4);
   }
 };
 
@@ -285,7 +291,7 @@ void decode_kernel_so(DecodeParams p_, const int32_t* __restrict__ md_, const in
         const int key = tt >> 2, pos = tt & 3;
         const int src_key = min(key, plan_nvalid - 1);
         src = a.kv + (size_t)plan_page * kFp8TileBytes;
-        voff = src_key * kFp8RowBytes + 16 * (pos ^ swz2(key));
+        voff = src_key * kFp8RowBytes + 16 * (pos ^ swz2s(key));
       }
     };
     auto load = [&](int j, int i) {

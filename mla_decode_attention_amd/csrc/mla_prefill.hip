@@ -52,6 +52,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // chunk c (8 bf16) of key k: [line group c/8][key][c%8 permuted by the key]
 __device__ __forceinline__ int swz3(int key) {
+  // (k1, k0^k2, k0^k3): with this kernel's operand reads (32 consecutive keys
+  // at one chunk per half-wave) the LDS measures free of bank conflicts with
+  // the k3 term, unlike the decode kernels' reads of 16 keys x 4 chunks
   return (((key >> 1) & 1) << 2) | (((key ^ (key >> 2)) & 1) << 1) | ((key ^ (key >> 3)) & 1);
 }
 __device__ __forceinline__ int lds_byte(int key, int chunk) {
