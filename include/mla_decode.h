@@ -400,6 +400,19 @@ int mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const float* kv_
                            void* stream);
 
 /*
+ * mla_debug_page_violations: page-id bounds checks (diagnostics). The decode
+ * entry points trust block_table (caller contract above). A library built
+ * with MLA_DEBUG_BOUNDS (libmla_decode_debug.so) checks every page id its
+ * decode kernels use against [0, num_pages): an id outside is counted and
+ * replaced by page 0, so no read leaves the pool (the result is then not
+ * meaningful). This call waits for the device, returns the number of
+ * violations counted since the last reset in *count (per page use, summed
+ * over the kernels), and clears the counters when reset != 0. Without
+ * MLA_DEBUG_BOUNDS it returns MLA_ERR_UNSUPPORTED.
+ */
+int mla_debug_page_violations(int reset, uint64_t* count);
+
+/*
  * Measurement hook (diagnostics, not part of the computation).
  * mla_profile_enable(1): from now on every kernel launch of the library is
  *   bracketed by a pair of HIP events recorded by the dispatch itself on the

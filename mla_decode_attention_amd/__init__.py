@@ -24,6 +24,7 @@ __all__ = ["load_library", "library_path", "abi_version", "default_num_units", "
            "PROFILE_ATTENTION", "PROFILE_METADATA", "PROFILE_COMBINE", "get_split_metadata", "decode",
            "decode_varlen", "decode_noalloc", "combine", "append_kv", "prefill", "PROFILE_QUANTIZE",
            "prefill_quant_kv_bytes", "prefill_quantize_kv", "prefill_quant",
+           "use_debug_library", "debug_page_violations",
            "MLAError", "KV_BF16", "KV_FP8_E4M3", "PAGE_TOKENS", "D_QK", "D_V"]
 
 PAGE_TOKENS = 64
@@ -32,7 +33,9 @@ D_V = 512
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
 _LIB_NAME = "libmla_decode.so"
+_DEBUG_LIB_NAME = "libmla_decode_debug.so"
 _lib = None
+_use_debug = False
 
 
 class MLAError(RuntimeError):
@@ -40,7 +43,18 @@ class MLAError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+    name = _DEBUG_LIB_NAME if _use_debug else _LIB_NAME
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), name)
+
+
+def use_debug_library(enable: bool) -> None:
+    """Route every later call through libmla_decode_debug.so (built with
+    MLA_DEBUG_BOUNDS: page ids checked against the pool) or back through the
+    release library."""
+    global _lib, _use_debug
+    if bool(enable) != _use_debug:
+        _use_debug = bool(enable)
+        _lib = None
 
 
 def load_library():
@@ -78,6 +92,7 @@ def load_library():
         "mla_decode_fwd_noalloc": (c_int, [vp, vp, vp, c_int, c_int, vp, c_int, vp, c_int, c_int, c_int,
                                            ctypes.c_float, vp, vp, c_int, c_int, vp]),
         "mla_noalloc_scratch_need": (c_size, [c_int, c_int, c_int, c_int]),
+        "mla_debug_page_violations": (c_int, [c_int, ctypes.POINTER(ctypes.c_uint64)]),
         "mla_profile_enable": (c_int, [c_int]),
         "mla_profile_read": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]),
         "mla_profile_read_launches": (c_int, [c_int, ctypes.POINTER(ctypes.c_float), c_int,
@@ -448,6 +463,17 @@ def profile_read():
 
 
 PROFILE_ATTENTION, PROFILE_METADATA, PROFILE_COMBINE, PROFILE_QUANTIZE = 0, 1, 2, 3
+
+
+def debug_page_violations(reset: bool = True) -> int:
+    """Page ids outside the pool seen by the decode kernels since the last
+    reset (libmla_decode_debug.so only; MLAError otherwise). Waits for the
+    device."""
+    lib = load_library()
+    torch.cuda.synchronize()
+    n = ctypes.c_uint64(0)
+    _check(lib.mla_debug_page_violations(1 if reset else 0, ctypes.byref(n)), "mla_debug_page_violations")
+    return int(n.value)
 
 
 def profile_read_launches(kernel: int = PROFILE_ATTENTION, capacity: int = 4096):

@@ -11,6 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmla_decode.so"
+DEBUG_LIB_NAME = "libmla_decode_debug.so"   # MLA_DEBUG_BOUNDS: page ids checked against the pool
 SOURCES = ["csrc/mla_kernels.hip", "csrc/mla_append.hip", "csrc/mla_prefill.hip", "csrc/mla_api.hip",
            "csrc/mla_scratch.hip", "csrc/mla_decode_so.hip", "csrc/mla_prefill_q8.hip"]
 ARCH = "gfx950"
@@ -23,8 +24,8 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = True) -> str:
-    out = os.path.join(HERE, LIB_NAME)
+def build(verbose: bool = True, debug_bounds: bool = False) -> str:
+    out = os.path.join(HERE, DEBUG_LIB_NAME if debug_bounds else LIB_NAME)
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # no packed-fp32 VALU forms (v_pk_fma_f32 & co.) in device code
@@ -34,6 +35,8 @@ def build(verbose: bool = True) -> str:
            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wno-unused-result",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    if debug_bounds:
+        cmd += ["-DMLA_DEBUG_BOUNDS"]
     cmd += [os.path.join(HERE, s) for s in SOURCES]
     cmd += ["-o", tmp]
     if verbose:
@@ -49,7 +52,12 @@ def build(verbose: bool = True) -> str:
     return out
 
 
+def build_all(verbose: bool = True):
+    """The release library and the MLA_DEBUG_BOUNDS one."""
+    return build(verbose), build(verbose, debug_bounds=True)
+
+
 if __name__ == "__main__":
-    path = build()
-    print(path)
+    for path in (build_all() if "--debug" in sys.argv else (build(),)):
+        print(path)
     sys.exit(0)

@@ -292,6 +292,7 @@ int decode_impl(const void* q, const int32_t* cu_q, int total_q, const void* kv_
   p.rows = q_len * num_heads;
   p.q_rows = cu_q ? total_q * num_heads : batch * p.rows;
   p.max_pages = max_pages_per_seq;
+  p.num_pages = num_pages;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   const size_t slots = (size_t)batch + (size_t)num_units;
   p.ws_out = metadata ? (float*)workspace : nullptr;
@@ -516,6 +517,17 @@ int mla_append_kv(const void* latent, int batch, int new_tokens, const int32_t* 
 int mla_profile_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.on = enable != 0;
+  return ok();
+}
+
+int mla_debug_page_violations(int reset, uint64_t* count) {
+  if (!count) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  unsigned a = 0, b = 0;
+  hipError_t e = mla::page_violations_kernels(&a, reset != 0);
+  if (e == hipErrorNotSupported) return fail(MLA_ERR_UNSUPPORTED, "library built without MLA_DEBUG_BOUNDS");
+  if (e == hipSuccess) e = mla::page_violations_so(&b, reset != 0);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "page-violation counters: %s", hipGetErrorString(e));
+  *count = (uint64_t)a + b;
   return ok();
 }
 

@@ -148,7 +148,7 @@ struct Walk {
     pc_t0 = t0;
     const int t = t0 + (int)(threadIdx.x & 63);
     const int tiles = (L + kPage - 1) / kPage;
-    page_cache = t < tiles ? p.block_table[(size_t)b * p.max_pages + t] : 0;
+    page_cache = table_page(p.block_table + (size_t)b * p.max_pages, t, tiles, p.max_pages);
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
   }
 
@@ -219,7 +219,7 @@ struct Walk {
     page = 0;
     if (PAGES) {
       if (ti.t - pc_t0 >= 64) load_pages(a, ti.t);
-      page = uniform(__builtin_amdgcn_readlane(page_cache, ti.t - pc_t0));
+      page = checked_page(uniform(__builtin_amdgcn_readlane(page_cache, ti.t - pc_t0)), p.num_pages);
     }
     nvalid = min(kPage, L - ti.t * kPage);
     ++f;
@@ -697,6 +697,8 @@ void decode_kernel_so(DecodeParams p_, const int32_t* __restrict__ md_, const in
 }
 
 }  // namespace so
+
+MLA_PAGE_VIOLATIONS_ACCESSOR(page_violations_so)
 
 hipError_t launch_decode_so(const DecodeParams& p, int grid_units, hipStream_t s, hipEvent_t ev_start,
                             hipEvent_t ev_stop) {

@@ -80,6 +80,43 @@ __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint3
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Page ids come from the caller's block table, which release builds trust (a
+// documented caller contract). A MLA_DEBUG_BOUNDS build checks each page id
+// the decode kernels use against [0, num_pages): an id outside is counted in
+// this translation unit's counter and replaced by page 0, so the kernel still
+// reads only pool memory. `page` is wave-uniform.
+#ifdef MLA_DEBUG_BOUNDS
+static __device__ unsigned int g_page_violations;
+__device__ __forceinline__ int checked_page(int page, int num_pages) {
+  const bool bad = (unsigned)page >= (unsigned)num_pages;
+  if (bad && (threadIdx.x & 63) == 0) atomicAdd(&g_page_violations, 1u);
+  return uniform(bad ? 0 : page);   // stays a scalar (the loads take it as a base)
+}
+// block-table entry t of a sequence with tiles entries: beyond the table's
+// row (max_pages) it is an id of -1, which the check above counts
+__device__ __forceinline__ int table_page(const int32_t* row, int t, int tiles, int max_pages) {
+  return t < tiles ? (t < max_pages ? row[t] : -1) : 0;
+}
+#define MLA_PAGE_VIOLATIONS_ACCESSOR(name)                                              \
+  hipError_t name(unsigned* count, bool reset) {                                        \
+    hipError_t e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_page_violations), sizeof(unsigned), 0, \
+                                       hipMemcpyDeviceToHost);                          \
+    if (e == hipSuccess && reset) {                                                     \
+      const unsigned zero = 0;                                                          \
+      e = hipMemcpyToSymbol(HIP_SYMBOL(g_page_violations), &zero, sizeof(unsigned), 0,  \
+                            hipMemcpyHostToDevice);                                     \
+    }                                                                                   \
+    return e;                                                                           \
+  }
+#else
+__device__ __forceinline__ int checked_page(int page, int) { return page; }
+__device__ __forceinline__ int table_page(const int32_t* row, int t, int tiles, int) {
+  return t < tiles ? row[t] : 0;
+}
+#define MLA_PAGE_VIOLATIONS_ACCESSOR(name) \
+  hipError_t name(unsigned* count, bool) { *count = 0; return hipErrorNotSupported; }
+#endif
+
 // 64-row kernels: (unit, row block) of this workgroup. Workgroups are handed
 // to the 8 XCDs round-robin by their linear id, so the row blocks of one unit
 // (which read the same pages) take ids that are equal mod 8 and share that
@@ -405,7 +442,7 @@ struct UnitT {
     pc_t0 = t0;
     const int lane = threadIdx.x & 63;
     const int t = t0 + lane;
-    page_cache = t < bp_tiles ? a.block_table[(size_t)bp * a.p.max_pages + t] : 0;
+    page_cache = table_page(a.block_table + (size_t)bp * a.p.max_pages, t, bp_tiles, a.p.max_pages);
     // drain here (rare path) so the per-tile readlane below needs no wait
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
   }
@@ -493,7 +530,7 @@ struct UnitT {
     ti.rows = bp_qlen * a.p.num_heads;
     ti.qrow0 = bp_qrow0;
     if (ti.t - pc_t0 >= 64) load_pages(a, ti.t);
-    const int page = uniform(__builtin_amdgcn_readlane(page_cache, ti.t - pc_t0));
+    const int page = checked_page(uniform(__builtin_amdgcn_readlane(page_cache, ti.t - pc_t0)), a.p.num_pages);
     const int nvalid = min(kPage, ti.L - ti.t * kPage);
     dma.plan(a.kv, a.p.kv_scale, page, nvalid, dst, sdst, tid);
     return ti;

@@ -52,6 +52,7 @@ struct DecodeParams {
   int q_rows;                 // rows held by q (B * rows, or T * H with cu_q)
   int grid_units;             // work units of the launch (set by launch_decode)
   int max_pages;
+  int num_pages;              // pages in the pool (page-id bounds checks of MLA_DEBUG_BOUNDS builds)
   float scale_log2;           // softmax_scale * log2(e)
 };
 
@@ -117,6 +118,10 @@ hipError_t launch_prefill_q8(const uint16_t* q, const uint8_t* qkv, const int32_
                              int batch, int max_q_len, long long total_k, int num_heads, float softmax_scale,
                              float* out, float* lse, hipStream_t s, hipEvent_t ev_start = nullptr,
                              hipEvent_t ev_stop = nullptr);
+// Page-id bounds violations counted by a MLA_DEBUG_BOUNDS build's decode
+// kernels (one counter per translation unit); hipErrorNotSupported otherwise.
+hipError_t page_violations_kernels(unsigned* count, bool reset);
+hipError_t page_violations_so(unsigned* count, bool reset);
 int prefill_rows_per_block();
 hipError_t launch_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,
                           const int32_t* cu_q, const int32_t* cu_k, int batch, int max_q_len, int num_heads,

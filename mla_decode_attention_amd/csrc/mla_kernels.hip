@@ -2136,6 +2136,8 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min
   return hipGetLastError();
 }
 
+MLA_PAGE_VIOLATIONS_ACCESSOR(page_violations_kernels)
+
 hipError_t launch_combine(const float* part_out, const float* part_lse, const int32_t* offsets,
                           const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
                           float* lse, int skip_single, hipStream_t s, const int32_t* md, int units,

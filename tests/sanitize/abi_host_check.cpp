@@ -151,6 +151,8 @@ hipError_t launch_prefill_q8(const uint16_t*, const uint8_t* qkv, const int32_t*
   g_launches.push_back(l);
   return hipSuccess;
 }
+hipError_t page_violations_kernels(unsigned* c, bool) { *c = 0; return hipErrorNotSupported; }
+hipError_t page_violations_so(unsigned* c, bool) { *c = 0; return hipErrorNotSupported; }
 hipError_t scratch_address(int dev, void** out) {
   ++g_scratch_lookups;
   *out = dev == g_dev ? g_scratch : nullptr;
@@ -427,6 +429,11 @@ static void check_metadata_and_others() {
                               (float*)g_buf[5], nullptr) == MLA_ERR_INVALID_ARG);
   CHECK(mla_prefill_quant_fwd(q, qkv, n1, sl, sl, 1, 10, 10, 1, INFINITY, (float*)g_buf[4], (float*)g_buf[5],
                               nullptr) == MLA_ERR_INVALID_ARG);
+
+  // page-id bounds counters: this build has none
+  uint64_t nviol = 7;
+  CHECK(mla_debug_page_violations(1, &nviol) == MLA_ERR_UNSUPPORTED);
+  CHECK(mla_debug_page_violations(1, nullptr) == MLA_ERR_INVALID_ARG);
 }
 
 static void check_profile_hook() {

@@ -34,6 +34,15 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_bounds_checking_build_exports_the_same_symbols():
+    path = os.path.join(os.path.dirname(mla.library_path()), "libmla_decode_debug.so")
+    if not os.path.exists(path):
+        pytest.skip("libmla_decode_debug.so not built")
+    dbg = ctypes.CDLL(path)
+    for n in declared_functions():
+        assert hasattr(dbg, n), n
+
+
 def test_abi_and_status_strings(lib):
     assert lib.mla_abi_version() == 2
     assert lib.mla_status_string(0) == b"MLA_OK"
