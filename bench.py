@@ -614,7 +614,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): this build "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the library "
               "has no multi-GPU path; the per-GPU kernel is the whole computation.", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1:

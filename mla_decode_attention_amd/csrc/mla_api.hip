@@ -265,6 +265,8 @@ int decode_impl(const void* q, const int32_t* cu_q, int total_q, const void* kv_
     return fail(MLA_ERR_INVALID_ARG, "lse, block_table, cache_seqlens, kv_scale, cu_seqlens_q must be 4-byte aligned");
   if (metadata) {
     if (num_units < 1) return fail(MLA_ERR_INVALID_ARG, "num_units must be >= 1 with metadata");
+    if ((long long)batch * q_len * num_heads > INT32_MAX)
+      return fail(MLA_ERR_INVALID_ARG, "batch * q_len * num_heads exceeds the merge's 32-bit row index");
     if (!aligned(metadata, 4)) return fail(MLA_ERR_INVALID_ARG, "metadata must be 4-byte aligned");
     if (!workspace || !aligned(workspace, 16))
       return fail(MLA_ERR_INVALID_ARG, "split decode needs a 16-byte aligned workspace");
@@ -471,6 +473,8 @@ int mla_combine(const float* part_out, const float* part_lse, const int32_t* seq
     return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   if (batch < 1 || rows_per_seq < 1 || rows_per_seq > MLA_MAX_ROWS)
     return fail(MLA_ERR_INVALID_ARG, "batch >= 1 and 1 <= rows_per_seq <= %d required", MLA_MAX_ROWS);
+  if ((long long)batch * rows_per_seq > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARG, "batch * rows_per_seq exceeds the 32-bit row index");
   if (!aligned(part_out, 16) || !aligned(out, 16))
     return fail(MLA_ERR_INVALID_ARG, "part_out and out must be 16-byte aligned");
   if (!aligned(part_lse, 4) || !aligned(lse, 4) || !aligned(seq_part_offsets, 4))

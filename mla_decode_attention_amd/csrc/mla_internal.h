@@ -13,7 +13,8 @@ constexpr int kThreads = 256;     // 4 waves of 64 lanes per workgroup
 
 // Metadata layout (int32 words, device):
 //   [0] magic  [1] batch  [2] num_units  [3] units cut (U')  [4] total_partials
-//   [5] units_used  [6] sequence start cost (tiles)  [7] reserved
+//   [5] units_used  [6] sequence start cost (tiles)
+//   [7] max_pieces: the largest number of partials of one sequence
 //   [8 .. 8+B]                 prefix: first flattened tile of each sequence [B+1]
 //   [9+B .. 9+2B]              split_offset: first partial slot of each sequence [B+1]
 //   [10+2B .. 10+2B+U)         unit_first_seq: sequence holding each unit's first tile
@@ -21,7 +22,7 @@ constexpr int kThreads = 256;     // 4 waves of 64 lanes per workgroup
 //   [11+2B+2U .. 11+3B+2U)     seq_first_unit: unit holding each sequence's first tile
 constexpr int kMdMagic = 0x4D4C4132;  // 'MLA2'
 enum { MD_MAGIC = 0, MD_BATCH = 1, MD_UNITS = 2, MD_UNITS_CUT = 3, MD_TOTAL_PARTIALS = 4,
-       MD_UNITS_USED = 5, MD_SEQ_COST = 6, MD_HEADER = 8 };
+       MD_UNITS_USED = 5, MD_SEQ_COST = 6, MD_MAX_PIECES = 7, MD_HEADER = 8 };
 constexpr int kDefaultMinTiles = 8;
 // A sequence's start (query rows, epilogue, partial write, metadata) costs
 // about as much as this many 64-token tiles; the split schedule charges it.

@@ -1835,7 +1835,9 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
   constexpr int kLdsSeqs = 4096;   // batches up to this size place units by a search in LDS
   __shared__ int wave_tot[64];
   __shared__ int s_wpre[kLdsSeqs + 1], s_prefix[kLdsSeqs + 1];
+  __shared__ int s_max_pieces;
   const int tid = threadIdx.x;
+  if (tid == 0) s_max_pieces = 0;   // published by the first scan's barriers
   const int per = (B + 1023) / 1024;
   const int lo = min(tid * per, B), hi = min(lo + per, B);
   int32_t* prefix = md + MD_HEADER;
@@ -1875,6 +1877,7 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
   auto pieces = [&](int wp, int t) { return t ? owner(wp + c + t - 1) - owner(wp + c) + 1 : 0; };
   const bool lds_search = B <= kLdsSeqs;
   int2 acc2 = make_int2(0, 0);
+  int max_pieces = 0;
   {
     int tp = run.x, wp = run.y;
     for (int bb = lo; bb < hi; ++bb) {
@@ -1886,6 +1889,7 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
       }
       first_unit[bb] = t ? owner(wp + c) : 0;
       if (t) {
+        max_pieces = max(max_pieces, pieces(wp, t));
         acc2.x += pieces(wp, t);
         acc2.y += (wp > 0 && owner(wp - 1) == owner(wp + c)) ? 1 : 0;
       }
@@ -1912,8 +1916,9 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
       wp += t ? t + c : 0;
     }
   }
+  atomicMax(&s_max_pieces, max_pieces);
   int2 tot2;
-  const int2 run2 = block_exclusive_scan2(acc2, wave_tot, &tot2);   // its barriers also publish s_wpre, s_prefix
+  const int2 run2 = block_exclusive_scan2(acc2, wave_tot, &tot2);   // its barriers also publish s_wpre, s_prefix, s_max_pieces
   if (lds_search) {
     // one unit per thread: the sequence holding position cut(u) is the last
     // one whose weighted prefix is at or below it
@@ -1954,7 +1959,7 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
     md[MD_TOTAL_PARTIALS] = tot2.x;
     md[MD_UNITS_USED] = tot2.x - tot2.y;
     md[MD_SEQ_COST] = c;
-    md[7] = 0;
+    md[MD_MAX_PIECES] = s_max_pieces;
   }
 }
 
@@ -1968,6 +1973,18 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
 // memory round trips of one pass over all of them; the group states are then
 // merged through LDS. A partial with LSE -inf weighs nothing and its values
 // are not used (they may be anything, NaN included).
+// Dispatch order: one workgroup per (sequence, row), the sequence index
+// running fastest (grid x). When the decode's metadata says that
+// some sequence needs more than one pass (more than 16 partials) and the
+// batch has at most kCombineOrderMaxB sequences, those sequences take the
+// first places and the others follow, each class in index order: their rows
+// then start in the first round of workgroups instead of wherever their index
+// puts them, and a long context's merge, the longest of the grid, no longer
+// runs alone at the end. (Ranking costs every workgroup a load of all the
+// offsets and three barriers, so it is skipped when no sequence needs it.)
+// When the metadata shows every sequence in exactly one partial (largest count
+// 1, total equal to the batch), the decode has written every output itself
+// and each workgroup returns after reading the header.
 // md (nullable): the decode's metadata; the merge does nothing unless it was
 // built for this batch and num_units (as the decode kernels check). The
 // header is read before the offsets, which sit in the metadata at positions
@@ -1977,6 +1994,7 @@ constexpr int kCombineRows = 1;      // rows per workgroup
 constexpr int kCombineGroups = 4;    // partial groups per row
 constexpr int kCombineInFlight = 4;  // partials per group whose loads are issued together
 constexpr int kCombineThreads = kCombineRows * kCombineGroups * 64;
+constexpr int kCombineOrderMaxB = kCombineThreads;   // one thread per sequence ranks them
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part_out,
                                                       const float* __restrict__ part_lse,
@@ -1987,15 +2005,53 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
                                                       const int32_t* __restrict__ md, int units) {
   __shared__ float s_ms[kCombineRows][kCombineGroups][2];               // (max, sum)
   __shared__ f32x4 s_acc[kCombineRows][kCombineGroups - 1][2][64];       // groups 1.., two halves
-  const int b = blockIdx.x;
-  if (md && ((md[MD_MAGIC] != kMdMagic) | (md[MD_BATCH] != B) | (md[MD_UNITS] != units))) return;
+  __shared__ int s_order[kCombineThreads / 64 + 1];
+  constexpr int kPass = kCombineGroups * kCombineInFlight;     // partials one pass takes
+  int max_pieces = 0, total_partials = -1;
+  if (md) {
+    // the header words are read together (one round trip)
+    const int h_magic = md[MD_MAGIC], h_batch = md[MD_BATCH], h_units = md[MD_UNITS];
+    max_pieces = md[MD_MAX_PIECES];
+    total_partials = md[MD_TOTAL_PARTIALS];
+    if ((h_magic != kMdMagic) | (h_batch != B) | (h_units != units)) return;
+  }
+  // every sequence in exactly one partial: the decode wrote all the outputs
+  if (skip_single && max_pieces <= 1 && total_partials == B) return;
+  int rb = blockIdx.y;
+  int b = blockIdx.x;
+  if (B <= kCombineOrderMaxB && max_pieces > kPass) {
+    // place b of the order: rows of the heavy sequences, then the others
+    const int t = threadIdx.x, w = t >> 6;
+    const int nt = t < B ? offsets[t + 1] - offsets[t] : 0;
+    const bool heavy = nt > kPass;
+    const uint64_t hb = __builtin_amdgcn_ballot_w64(heavy);
+    if ((t & 63) == 0) s_order[w] = __builtin_popcountll(hb);
+    __syncthreads();
+    int heavy_before = 0, heavy_all = 0;
+#pragma unroll
+    for (int v = 0; v < kCombineThreads / 64; ++v) {
+      heavy_before += v < w ? s_order[v] : 0;
+      heavy_all += s_order[v];
+    }
+    const int hr = heavy_before + __builtin_popcountll(hb & ((1ull << (t & 63)) - 1));   // heavy before t
+    const int my_pos = heavy ? hr : heavy_all + (t - hr);
+    // linear id -> (place, row block): the heavy sequences' rows first, the
+    // place running fastest within each class
+    const int id = blockIdx.x + B * blockIdx.y, hitems = heavy_all * gridDim.y;
+    const int pos = id < hitems ? id % heavy_all : heavy_all + (id - hitems) % (B - heavy_all);
+    rb = id < hitems ? id / heavy_all : (id - hitems) / (B - heavy_all);
+    __syncthreads();
+    if (t < B && my_pos == pos) s_order[kCombineThreads / 64] = t;
+    __syncthreads();
+    b = s_order[kCombineThreads / 64];
+  }
   const int k0 = offsets[b];
   const int n = offsets[b + 1] - k0;
   if (skip_single && n == 1) return;
   const int half = threadIdx.x / (kCombineGroups * 64);         // row of the workgroup
   const int grp = (threadIdx.x >> 6) % kCombineGroups;
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.y * kCombineRows + half;
+  const int r = rb * kCombineRows + half;
   // partial slots hold R rows; sequence b owns the first rows_b of them
   const int rows_b = cu_q ? (cu_q[b + 1] - cu_q[b]) * num_heads : R;
   const size_t out_row0 = cu_q ? (size_t)cu_q[b] * num_heads : (size_t)b * R;
@@ -2142,6 +2198,8 @@ hipError_t launch_combine(const float* part_out, const float* part_lse, const in
                           const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
                           float* lse, int skip_single, hipStream_t s, const int32_t* md, int units,
                           hipEvent_t ev_start, hipEvent_t ev_stop) {
+  // the ordered dispatch indexes (sequence, row block) pairs in 32 bits
+  if ((long long)batch * ((rows + kCombineRows - 1) / kCombineRows) > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid(batch, (rows + kCombineRows - 1) / kCombineRows);
   if (ev_start || ev_stop)
     hipExtLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, ev_start, ev_stop, 0, part_out, part_lse,

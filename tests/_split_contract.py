@@ -31,7 +31,7 @@ def unpack_metadata(md, batch, units):
     base = HEADER + 2 * (B + 1)
     return dict(
         magic=md[0], batch=md[1], units=md[2], units_cut=md[3], total_partials=md[4],
-        units_used=md[5], seq_cost=md[6],
+        units_used=md[5], seq_cost=md[6], max_pieces=md[7],
         prefix=md[HEADER:HEADER + B + 1],
         split_offset=md[HEADER + B + 1:HEADER + 2 * B + 2],
         unit_first_seq=md[base:base + U],
@@ -97,6 +97,8 @@ def check_metadata(md, seqlens, units, min_tiles_per_unit, seq_cost):
         offs.append(offs[-1] + len(units_b))
     assert m["split_offset"] == offs, "split offsets"
     assert m["total_partials"] == offs[-1]
+    assert m["max_pieces"] == max([offs[b + 1] - offs[b] for b in range(B)] + [0]), "largest partial count"
+
 
     c = int(seq_cost)
     assert m["seq_cost"] == c
@@ -179,5 +181,6 @@ def schedule_words(seqlens, num_units, min_tiles_per_unit, seq_cost):
     """The metadata words split_schedule's result would be written as."""
     s = split_schedule(seqlens, num_units, min_tiles_per_unit, seq_cost)
     B = len(seqlens)
-    return ([MAGIC, B, int(num_units), s["units_cut"], s["total_partials"], s["units_used"], seq_cost, 0]
+    return ([MAGIC, B, int(num_units), s["units_cut"], s["total_partials"], s["units_used"], seq_cost,
+             max(s["num_splits"] + [0])]
             + s["prefix"] + s["split_offset"] + s["unit_first_seq"] + s["unit_begin"] + s["seq_first_unit"])

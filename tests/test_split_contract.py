@@ -115,7 +115,7 @@ def test_checker_accepts_another_valid_rule():
     # one sequence per unit is valid, but its balance is not within the
     # library's bound unless the cut count says so: give the largest piece's
     # cost as the bound by claiming one cut
-    words = ([0x4D4C4132, B, U, 1, offs[-1], len(live), 3, 0] + prefix + offs + unit_first_seq + unit_begin
+    words = ([0x4D4C4132, B, U, 1, offs[-1], len(live), 3, 1] + prefix + offs + unit_first_seq + unit_begin
              + seq_first_unit)
     check_metadata(words, lens, U, W, 3)
 
@@ -137,6 +137,7 @@ def _mutations(words, B, U):
     yield "first unit wrong", m(lambda w: w.__setitem__(fsu0 + 1, w[fsu0 + 1] + 1))
     yield "unit first sequence wrong", m(lambda w: w.__setitem__(base + 1, w[base + 1] + 1))
     yield "units used wrong", m(lambda w: w.__setitem__(5, w[5] - 1))
+    yield "largest partial count wrong", m(lambda w: w.__setitem__(7, w[7] - 1))
 
 
 def test_checker_rejects_broken_schedules():
