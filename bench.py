@@ -23,7 +23,7 @@ its `configs` array holds every workload:
                                committed rocprofv3 counters (null if the
                                kernel source changed since)
 `clocks` holds the graphics clock of each XCD and the memory clock read with
-amd-smi while the headline workload runs.
+the amdsmi library while the headline workload runs.
 
 --config NAME measures one workload (also varlen, fp8mma, prefill, extend).
 """
@@ -35,7 +35,6 @@ import math
 import os
 import re
 import statistics
-import subprocess
 import sys
 import time
 
@@ -153,26 +152,52 @@ def stats(ms):
             "mean": round(sum(ms) / len(ms), 5), "n": len(ms)}
 
 
-def read_clocks(busy):
-    """Graphics clock of each XCD and the memory clock (MHz) from amd-smi,
-    read while `busy()` keeps the GPU working; None if amd-smi is missing."""
+def read_clocks(submit, done, sync, steps):
+    """Graphics clock of each XCD and the memory clock (MHz), read in this
+    process with the amdsmi library (no child program) while the GPU works
+    through `steps` queued steps (`submit()` queues one, `done()` tells whether
+    the queue has drained); None if the library or the metrics are not
+    available. The firmware's readings lag a load change, so samples from the
+    first 0.1 s are dropped; per XCD the median of the rest."""
     try:
-        p = subprocess.Popen(["amd-smi", "metric", "-c"], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
-                             text=True)
-    except OSError:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception:
         return None
-    t0 = time.time()
-    while p.poll() is None and time.time() - t0 < 20:
-        busy()
-    if p.poll() is None:
-        p.kill()
+
+    def mhz(v):
+        vals = v if isinstance(v, (list, tuple)) else [v]
+        return [int(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 10000]
+    gfx, mem = [], []
+    try:
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        for _ in range(steps):
+            submit()
+        t0 = time.time()
+        while not done() and time.time() - t0 < 10:
+            time.sleep(0.02)
+            if time.time() - t0 < 0.1:
+                continue
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            g = mhz(m.get("current_gfxclks", []))
+            if g:
+                gfx.append(g)
+            mem += mhz(m.get("current_uclk", []))
+        sync()
+    except Exception:
         return None
-    out = p.stdout.read()
-    gfx = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out)]
-    mem = [int(m) for m in re.findall(r"MEM_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out)]
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
     if not gfx:
         return None
-    return {"sclk_mhz": gfx, "mclk_mhz": mem, "source": "amd-smi metric -c during graph replays"}
+    n = min(len(g) for g in gfx)
+    return {"sclk_mhz": [int(statistics.median(g[i] for g in gfx)) for i in range(n)],
+            "mclk_mhz": [int(statistics.median(mem))] if mem else [], "samples": len(gfx),
+            "source": "amdsmi gpu metrics (current_gfxclks, current_uclk), sampled every 20 ms during ~1 s "
+                      "of queued graph replays"}
 
 
 def roofline_for(alg, fp8_mma):
@@ -393,12 +418,12 @@ def bench_decode(args):
             if not args.no_clocks:
                 i_box = [0]
 
-                def busy():
-                    for _ in range(20):
-                        run.run_step(i_box[0])
-                        i_box[0] += 1
-                    torch.cuda.synchronize()
-                clocks = read_clocks(busy)
+                def submit():
+                    run.run_step(i_box[0])
+                    i_box[0] += 1
+                n_busy = max(50, int(1.0 / max(e["step_ms"]["median"] * 1e-3, 1e-5)))
+                clocks = read_clocks(submit, lambda: torch.cuda.current_stream().query(),
+                                     torch.cuda.synchronize, n_busy)
         if name != headline:
             del run
             torch.cuda.empty_cache()
@@ -600,7 +625,7 @@ def main():
                     help="minimum tiles per split unit (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-clocks", action="store_true", help="do not read the clocks with amd-smi")
+    ap.add_argument("--no-clocks", action="store_true", help="do not read the clocks (amdsmi library)")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="also run the cache append (mla_append_kv) of this many new tokens per sequence "
                          "in every step, before the decode (their rows are the last positions of each "

@@ -54,6 +54,18 @@ __device__ __forceinline__ int swz3(int key) {
 __device__ __forceinline__ int lds_byte(int key, int chunk) {
   return ((chunk >> 3) * 512 + key * 8 + ((chunk ^ swz3(key)) & 7)) * 16;
 }
+// The 64-row kernel for per-sequence query counts (decode_kernel_x) keeps the
+// tile in the same arrangement under swz3x = (k1, k0^k2, k0^k3): its operand
+// fetches (32 consecutive keys at two chunks for QK; 4 keys x 4 chunks for each
+// half-wave of the transposed V read, keys 0-3 and 4-7 in the two halves)
+// measure 29% bank-conflict cycles under swz3 and none under swz3x, while
+// the 16-row kernel's (8 keys x 2 chunks) measure the reverse.
+__device__ __forceinline__ int swz3x(int key) {
+  return (((key >> 1) & 1) << 2) | (((key ^ (key >> 2)) & 1) << 1) | ((key ^ (key >> 3)) & 1);
+}
+__device__ __forceinline__ int lds_byte_x(int key, int chunk) {
+  return ((chunk >> 3) * 512 + key * 8 + ((chunk ^ swz3x(key)) & 7)) * 16;
+}
 constexpr int kLineGroupBytes = 8192;   // one 128-byte line of all 64 keys
 
 __device__ __forceinline__ void lds_barrier() {
@@ -156,7 +168,9 @@ __device__ __forceinline__ void dma4(uint32_t voff, const uint8_t* sbase, uint32
 template <bool FP8>
 struct TileDma;
 
-// bf16 page, 256 threads: 18 loads per thread straight into the tile layout.
+// bf16 page, 256 threads: 18 loads per thread straight into the lds_byte_x
+// arrangement of decode_kernel_x, the kernel that streams pages with it (the
+// 16-row kernel takes only the page facts from its plan).
 // Load i of thread t fills line group i/2 of key 32(i%2) + t/8, in-line
 // position t%8 (the lane fetches the chunk that belongs there, so the 8 lanes
 // of an octet read one whole 128-byte line of one key row); keys at or past
@@ -175,7 +189,7 @@ struct TileDma<false> {
     for (int par = 0; par < 2; ++par) {
       const int key = 32 * par + (tid >> 3);
       const int src_key = key < nvalid ? key : nvalid - 1;
-      voff[par] = src_key * kRowBytes + 16 * ((tid & 7) ^ swz3(key));
+      voff[par] = src_key * kRowBytes + 16 * ((tid & 7) ^ swz3x(key));   // lds_byte_x arrangement
     }
     lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
   }

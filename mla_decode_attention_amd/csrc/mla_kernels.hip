@@ -684,10 +684,10 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 
   // ---- per-lane constant LDS offsets
   // QK operand, k-step c = 4m + q: key 32kh + n, chunk 36fh + 2c + h
-  // = lds_byte(key, 36fh + 2q + h) + m line groups
+  // = lds_byte_x(key, 36fh + 2q + h) + m line groups
   int k_lane[4];
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) k_lane[q4] = lds_byte(32 * kh + n, 36 * fh + 2 * q4 + h);
+  for (int q4 = 0; q4 < 4; ++q4) k_lane[q4] = lds_byte_x(32 * kh + n, 36 * fh + 2 * q4 + h);
   // V transposed fetch: 16-lane group q covers features 64w + 32fb + 16(q%2)
   // + 0..15 and keys 16ks + 4h + j/4 (+8 for the second read): chunk
   // 8w + 4fb + 2(q%2) + (j%4)/2 = line group w, chunk 4fb + 2(q%2) + (j%4)/2
@@ -700,7 +700,7 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb)
         v_lane[second][fb] = wave * kLineGroupBytes +
-                             lds_byte(4 * h + (j >> 2) + 8 * second, 4 * fb + 2 * (q & 1) + ((j & 3) >> 1)) +
+                             lds_byte_x(4 * h + (j >> 2) + 8 * second, 4 * fb + 2 * (q & 1) + ((j & 3) >> 1)) +
                              8 * (j & 1);
   }
   // exchange area: partial scores [wave][2 x 16 B][lane]; a wave reads its
