@@ -8,7 +8,7 @@ unsplit single-launch path. Inputs are seeded synthetic data already resident
 in HBM. To keep the 256 MB Infinity Cache from serving repeat reads, steps
 rotate over several copies of the page pool.
 
-By default the five decode workloads are measured and ONE JSON line is printed.
+By default the six decode workloads are measured and ONE JSON line is printed.
 Its headline (value, ms_per_step, roofline, cpu_baseline) is the largest one,
 fp8 (batch 128, 128 heads, q_len 2 causal, 8192 cached tokens, fp8 cache), and
 its `configs` array holds every workload:
@@ -46,7 +46,7 @@ METRIC = "MLA decode TFLOP/s + effective KV GB/s, % of roofline, per batch/heads
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
-DECODE_CONFIGS = ["tiny", "share16", "mtp", "ragged", "fp8"]
+DECODE_CONFIGS = ["tiny", "share16", "share16_fp8", "mtp", "ragged", "fp8"]
 HEADLINE = "fp8"
 # the tiny workload's four pages are one work unit either way: one launch,
 # no schedule, no merge
@@ -382,7 +382,8 @@ def roofline_object(e, kernel_name):
             "t_roof_us": e["t_roof_us"]}
 
 
-KERNEL_NAMES = {"tiny": "decode_kernel_pc", "share16": "decode_kernel_pc", "mtp": "decode_kernel_so<false>",
+KERNEL_NAMES = {"tiny": "decode_kernel_pc", "share16": "decode_kernel_pc", "share16_fp8": "decode_kernel_pc8",
+                "mtp": "decode_kernel_so<false>",
                 "ragged": "decode_kernel_so<false>", "fp8": "decode_kernel_so<true>", "varlen": "decode_kernel_x",
                 "fp8mma": "decode_kernel_q8"}
 
@@ -612,9 +613,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--reps", type=int, default=100, help="kernel launches timed per workload (at least 50)")
     ap.add_argument("--config", default="all",
-                    choices=["all", "tiny", "share16", "mtp", "ragged", "fp8", "varlen", "fp8mma", "prefill",
-                             "extend", "prefill_q8", "extend_q8"],
-                    help="all = the five decode workloads, headline fp8; fp8mma = the fp8 workload on "
+                    choices=["all", "tiny", "share16", "share16_fp8", "mtp", "ragged", "fp8", "varlen", "fp8mma",
+                             "prefill", "extend", "prefill_q8", "extend_q8"],
+                    help="all = the six decode workloads, headline fp8; fp8mma = the fp8 workload on "
                          "mla_decode_fwd_fp8mma (queries and P in E4M3, fp8 matrix cores; an approximation of "
                          "the default path); prefill / extend = the second workload (mla_prefill_fwd); "
                          "prefill_q8 / extend_q8 = the same on the quantised path (mla_prefill_quantize_kv + "

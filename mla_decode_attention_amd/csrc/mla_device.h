@@ -200,44 +200,9 @@ struct TileDma<false> {
   __device__ __forceinline__ void load_ct() const { load(I); }
 };
 
-// fp8 page: a plain copy of the 36 KiB page into a staging buffer (9 loads per
-// thread, each load one contiguous KiB of the page), plus the page's 64
-// per-token scales (one 4-byte load per lane of wave 0). Keys at or past
-// `nvalid` re-read the last valid key and its scale.
+// fp8 page: 64 rows of 576 E4M3 codes, plus 64 fp32 token scales elsewhere
 constexpr int kFp8RowBytes = kDqk;                        // 576
 constexpr int kFp8TileBytes = kPage * kFp8RowBytes;       // 36864
-constexpr int kFp8Loads = kFp8TileBytes / (kThreads * 16);  // 9
-static_assert(kFp8Loads * kThreads * 16 == kFp8TileBytes, "fp8 tile must split evenly");
-
-template <>
-struct TileDma<true> {
-  static constexpr int kLoads = kFp8Loads;
-  const uint8_t* page;
-  const uint8_t* scale;
-  uint32_t lds0, sc_lds, sc_off;
-  int nvalid, tid;
-  __device__ __forceinline__ void plan(const uint8_t* kv, const float* kv_scale, int page_id, int nv,
-                                       LDS_AS uint8_t* buf, LDS_AS float* sbuf, int t) {
-    page = kv + (size_t)page_id * kFp8TileBytes;
-    scale = (const uint8_t*)(kv_scale + (size_t)page_id * kPage);
-    nvalid = nv;
-    tid = t;
-    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
-    sc_lds = (uint32_t)uniform((int)(uintptr_t)sbuf);
-    const int lane = tid & 63;
-    sc_off = 4 * (lane < nvalid ? lane : nvalid - 1);
-  }
-  __device__ __forceinline__ void load(int i) const {
-    const int sidx = i * kThreads + tid;            // 16-byte slot of the page
-    uint32_t voff = sidx * 16;
-    if (nvalid < kPage) {
-      const int key = sidx / 36;
-      if (key >= nvalid) voff = (nvalid - 1) * kFp8RowBytes + (sidx - key * 36) * 16;
-    }
-    dma16(voff, page, lds0 + i * 4096);
-    if (i == 0 && tid < 64) dma4(sc_off, scale, sc_lds);
-  }
-};
 
 // Spread the loads of the next tile evenly over the M QK MFMA slots of the
 // current one (issued back to back they stall the wave on the full
@@ -267,34 +232,6 @@ __device__ __forceinline__ void dma_slot_ct(const Dma& dma, int slot, std::integ
 template <int M, class Dma>
 __device__ __forceinline__ void dma_slot_ct(const Dma& dma, int slot) {
   dma_slot_ct<M>(dma, slot, std::make_integer_sequence<int, Dma::kLoads>{});
-}
-
-// fp8 staging page -> bf16 tile (exact: every E4M3FN value is a bf16 value).
-// Each thread widens 9 slots of 16 codes into 2 chunks of 8 bf16 each.
-__device__ __forceinline__ void widen_fp8_tile(const LDS_AS uint8_t* stage, LDS_AS uint8_t* tile, int tid) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-#pragma unroll
-  for (int j = 0; j < kFp8Loads; ++j) {
-    const int sidx = j * kThreads + tid;
-    const int key = sidx / 36, c16 = sidx - key * 36;
-    const u32x4 w = *(const LDS_AS u32x4*)(stage + sidx * 16);
-    u32x4 lo, hi;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bf16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false);
-      const bf16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true);
-      const unsigned u0 = __builtin_bit_cast(unsigned, x0), u1 = __builtin_bit_cast(unsigned, x1);
-      if (e < 2) {
-        lo[2 * e] = u0;
-        lo[2 * e + 1] = u1;
-      } else {
-        hi[2 * (e - 2)] = u0;
-        hi[2 * (e - 2) + 1] = u1;
-      }
-    }
-    *(LDS_AS u32x4*)(tile + lds_byte(key, 2 * c16)) = lo;
-    *(LDS_AS u32x4*)(tile + lds_byte(key, 2 * c16 + 1)) = hi;
-  }
 }
 
 // Pairwise reductions across lanes l and l ^ 32 (l ^ 16) on the VALU

@@ -32,13 +32,16 @@
 //   NARROW16PC (R <= 16, bf16): 8 waves, 4 producers + 4 consumers; the
 //                        consumers split the keys for QK and the output
 //                        features for PV (16x16 MFMA).
-//   NARROW16   (R <= 16, fp8):  4 waves split each tile's 64 keys, partial
-//                        states merged at the end (16x16 MFMA).
-//   WIDE64X    (R > 16): 64 rows, 8 waves; QK split by row half x feature
-//                        half x key half, PV by output columns (32x32 MFMA).
-//                        bf16 cache: decode_kernel_x; fp8 cache:
-//                        decode_kernel_xf (E4M3 tile in LDS, operands widened
-//                        in registers).
+//   NARROW16PC8 (R <= 16, fp8): the same roles over E4M3 pages kept in LDS,
+//                        the operands widened in registers.
+//   WIDE64X    (R > 16, per-sequence query counts): 64 rows, 8 waves; QK
+//                        split by row half x feature half x key half, PV by
+//                        output columns (32x32 MFMA). bf16 cache:
+//                        decode_kernel_x; fp8 cache: decode_kernel_xf (E4M3
+//                        tile in LDS, operands widened in registers). With
+//                        one query count for all sequences the 64-row kernel
+//                        with score and output waves runs instead
+//                        (mla_decode_so.hip).
 //   Q8         (fp8 cache, mla_decode_fwd_fp8mma): queries and P in E4M3 on
 //                        fp8 MFMA, 64 rows, 8 waves.
 // (The prefill / extend kernel is in mla_prefill.hip.)
@@ -56,265 +59,9 @@
 
 namespace mla {
 
-// ---------------------------------------------------------------------------
-// 16-row kernel for the fp8 cache (up to 16 rows per sequence): 4 waves, wave
-// w takes keys 16w..16w+15 of every page; v_mfma_f32_16x16x32_bf16 for QK,
-// v_mfma_f32_16x16x16_bf16 for PV; the four key quarters' softmax states are
-// merged in LDS at a sequence's end. The fp8 page is copied to a staging
-// buffer and widened to bf16 in LDS. (A bf16 cache at these row counts takes
-// decode_kernel_pc below.)
-// ---------------------------------------------------------------------------
-
-constexpr int kQkDepth = 6;   // LDS operand fetches in flight ahead of the QK MFMAs
-constexpr int kPvDepth = 4;   // ... ahead of the PV MFMAs
-
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_kernel16_fp8(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
-    const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
-    const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
-    const uint8_t* __restrict__ kv_) {
-  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
-  constexpr int ROWS_WG = 16;
-  constexpr int kQChunks = kDqk / 32;        // 18 k-steps of 32 features
-  constexpr int kFeatBlocks = kDv / 16;      // 32 output blocks of 16 features
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kTileBytes];
-  __shared__ float mrg[2][4][16];
-  __shared__ __attribute__((aligned(16))) float sbuf[2][kPage];   // fp8 per-token scales
-  LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
-  LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
-  // buf0 holds the widened bf16 tile, buf1 the two fp8 staging pages
-  LDS_AS uint8_t* const stage0 = buf1;
-  LDS_AS uint8_t* const stage1 = buf1 + kFp8TileBytes;
-  LDS_AS float* const sb0 = (LDS_AS float*)(&sbuf[0][0]);
-  LDS_AS float* const sb1 = (LDS_AS float*)(&sbuf[1][0]);
-
-  const DecodeParams& p = a.p;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, li = lane & 15;
-  const int R = p.rows;
-  const int row = blockIdx.y * ROWS_WG + li;
-  const int key_blk = wave;                  // the 16-key block of this wave
-  const int u = blockIdx.x;
-
-  Unit unit;
-  if (!unit.init(a, u)) {
-    if (!a.md) write_empty(p, unit.b0, blockIdx.y * ROWS_WG, blockIdx.y * ROWS_WG + ROWS_WG, 4);
-    return;
-  }
-
-  // ---- per-lane constant LDS offsets
-  // QK operand for k-step c: key 16 key_blk + li, chunk 4c + g
-  //   = (c/2) line groups + chunk 4(c%2) + g of the line
-  int qk_lane[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) qk_lane[par] = lds_byte(16 * key_blk + li, 4 * par + g);
-  // V transposed fetch: keys 16 kblk + 4g + li/4, features 16fb + 4(li%4):
-  //   chunk 2fb + (li%4)/2 = (fb/4) line groups + chunk 2(fb%4) + (li%4)/2
-  int v_lane[4];
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4)
-    v_lane[q4] = lds_byte(16 * key_blk + 4 * g + (li >> 2), 2 * q4 + ((li & 3) >> 1)) + 8 * (li & 1);
-
-  bf16x8 qreg[kQChunks];
-  f32x4 o[kFeatBlocks];
-  float m_run = -INFINITY, l_run = 0.f;
-
-  TileDma<true> dma;
-  TileInfo next = unit.prepare(a, unit.f_begin, stage0, sb0, tid, dma);
-  dma_all(dma);
-
-  // cur: bf16 tile computed in this step; nxt: staging page the next tile's
-  // loads go to; stage / sbc / sbn: fp8 staging page of this tile and the
-  // scale buffers.
-  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt,
-                  const LDS_AS uint8_t* const stage, const LDS_AS float* const sbc,
-                  LDS_AS float* const sbn) {
-    const TileInfo ti = next;
-    const int bc = ti.b, t = ti.t, L = ti.L;
-
-    if (ti.first) {
-      // new sequence: its query rows into registers, fresh softmax state
-      const int rr = row < ti.rows ? row : max(ti.rows - 1, 0);
-      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
-#pragma unroll
-      for (int c = 0; c < kQChunks; ++c) {
-        bf16x8 v = qrow[4 * c + g];
-        qreg[c] = row < ti.rows ? v : bf16x8{};
-      }
-#pragma unroll
-      for (int fb = 0; fb < kFeatBlocks; ++fb) o[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_run = -INFINITY;
-      l_run = 0.f;
-      // Drain here, once per sequence, before the next page's loads are
-      // issued: the query rows (and the current page) are then known to be in
-      // place and the compiler needs no wait at their first use.
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    }
-    const bool final_out = ti.final_out;
-    const int slot = ti.slot;
-
-    const bool more = f + 1 < unit.f_end;
-    wait_tile();
-    widen_fp8_tile(stage, cur, tid);
-    lds_barrier();
-    if (more) next = unit.prepare(a, f + 1, nxt, sbn, tid, dma);
-
-    // ---- QK GEMM: S^T (keys x rows) for this wave's keys, K from LDS, Q^T in
-    //      registers; the k-steps alternate between two accumulators (two
-    //      independent MFMA chains), summed at the end
-    f32x4 s[2];
-    s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      auto kaddr = [&](int c) { return cur + qk_lane[c & 1] + (c >> 1) * kLineGroupBytes; };
-      bf16x8 ring[kQkDepth];
-#pragma unroll
-      for (int i = 0; i < kQkDepth; ++i) ring[i] = ld128(kaddr(i));
-#pragma unroll
-      for (int c = 0; c < kQChunks; ++c) {
-        const bf16x8 av = ring[c % kQkDepth];
-        if (c + kQkDepth < kQChunks) ring[c % kQkDepth] = ld128(kaddr(c + kQkDepth));
-        s[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[c], s[c & 1], 0, 0, 0);
-        dma_slot<kQChunks>(dma, more, c);
-        sched_fence();
-      }
-    }
-    s[0] += s[1];
-
-    // ---- online softmax (base 2)
-    const int key0 = t * kPage + key_blk * 16;
-    const int vis = L - ti.qlen + (row < ti.rows ? row : max(ti.rows - 1, 0)) / p.num_heads + 1;
-    const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
-    // per-token scales of this lane's keys (folded into scores and P)
-    const f32x4 ksc = *(const LDS_AS f32x4*)(sbc + 16 * key_blk + 4 * g);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = s[0][r] * (ksc[r] * p.scale_log2);
-      if (need_mask && (key0 + 4 * g + r) >= vis) v = -INFINITY;
-      s[0][r] = v;
-      mx = fmaxf(mx, v);
-    }
-    mx = max_xor32(max_xor16(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const bool raise = m_new > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float alpha = raise ? exp2_fast(m_run - m_new) : 1.0f;
-      if (raise) m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int fb = 0; fb < kFeatBlocks; ++fb) o[fb] *= alpha;
-    }
-    const float m_eff = (m_run == -INFINITY) ? 0.0f : m_run;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float pr = exp2_fast(s[0][r] - m_eff);
-      s[0][r] = pr * ksc[r];   // PV weight of the unscaled fp8 row
-      l_run += pr;
-    }
-
-    // ---- PV GEMM: O^T (features x rows) += V^T . P^T, V^T read transposed from LDS
-    {
-      auto vaddr = [&](int fb) { return cur + v_lane[fb & 3] + (fb >> 2) * kLineGroupBytes; };
-      bf16x4 pb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pb[r] = (__bf16)s[0][r];
-      const i16x4 pbs = __builtin_bit_cast(i16x4, pb);
-      bf16x4 ring[kPvDepth];
-#pragma unroll
-      for (int i = 0; i < kPvDepth; ++i) ring[i] = tr_read(vaddr(i));
-#pragma unroll
-      for (int fb = 0; fb < kFeatBlocks; ++fb) {
-        const bf16x4 v = ring[fb % kPvDepth];
-        if (fb + kPvDepth < kFeatBlocks) ring[fb % kPvDepth] = tr_read(vaddr(fb + kPvDepth));
-        o[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v), pbs, o[fb], 0, 0, 0);
-        sched_fence();
-      }
-    }
-
-    lds_barrier();  // every wave is done with `cur`
-
-    if (!ti.last) return;
-
-    // ---- epilogue for sequence bc
-    float l_row = sum_xor32(sum_xor16(l_run));
-    float m_row = m_run;
-
-    {
-      // merge the 4 waves' key quarters of the same 16 rows (fixed order)
-      if (g == 0) {
-        mrg[0][wave][li] = m_run;
-        mrg[1][wave][li] = l_row;
-      }
-      lds_barrier();
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg[0][w][li]);
-      float Ltot = 0.f, mine = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = mrg[0][w][li];
-        const float cw = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
-        Ltot += cw * mrg[1][w][li];
-        if (w == wave) mine = cw;
-      }
-      const float scl = Ltot > 0.f ? mine : 0.f;
-#pragma unroll
-      for (int fb = 0; fb < kFeatBlocks; ++fb) o[fb] *= scl;
-      LDS_AS f32x4* region = (LDS_AS f32x4*)cur;   // 2 x (32 x 64) f32x4 = 64 KiB
-      if (wave >= 2) {
-#pragma unroll
-        for (int fb = 0; fb < kFeatBlocks; ++fb) region[(wave - 2) * 2048 + fb * 64 + lane] = o[fb];
-      }
-      lds_barrier();
-      if (wave < 2) {
-#pragma unroll
-        for (int fb = 0; fb < kFeatBlocks; ++fb) o[fb] += region[wave * 2048 + fb * 64 + lane];
-      }
-      lds_barrier();
-      if (wave == 1) {
-#pragma unroll
-        for (int fb = 0; fb < kFeatBlocks; ++fb) region[2048 + fb * 64 + lane] = o[fb];
-      }
-      lds_barrier();
-      if (wave == 0) {
-#pragma unroll
-        for (int fb = 0; fb < kFeatBlocks; ++fb) o[fb] += region[2048 + fb * 64 + lane];
-      }
-      l_row = Ltot;
-      m_row = M;
-    }
-
-    if (wave == 0) {
-      const bool live = l_row > 0.f;
-      const float inv = live ? 1.0f / l_row : 0.f;
-      const float lse_v = live ? (m_row + log2_fast(l_row)) * kLn2 : -INFINITY;
-      if (row < ti.rows) {
-        float* dst_o;
-        float* dst_l;
-        if (final_out) {
-          dst_o = p.out + ((size_t)ti.qrow0 + row) * kDv;
-          dst_l = p.lse + (size_t)ti.qrow0 + row;
-        } else {
-          dst_o = p.ws_out + ((size_t)slot * R + row) * kDv;
-          dst_l = p.ws_lse + (size_t)slot * R + row;
-        }
-#pragma unroll
-        for (int fb = 0; fb < kFeatBlocks; ++fb) *(f32x4*)(dst_o + 16 * fb + 4 * g) = o[fb] * inv;
-        if (g == 0) *dst_l = lse_v;
-      }
-    }
-    lds_barrier();  // `cur` is widened into again by the next step
-  };
-
-  // Two copies of the step with the staging buffers fixed at compile time.
-  for (int f = unit.f_begin; f < unit.f_end; f += 2) {
-    step(f, buf0, stage1, stage0, sb0, sb1);
-    if (f + 1 < unit.f_end) step(f + 1, buf0, stage0, stage1, sb1, sb0);
-  }
-}
+// LDS operand fetches in flight ahead of the MFMAs of the 16-row kernel
+constexpr int kQkDepth = 6;   // QK
+constexpr int kPvDepth = 4;   // PV
 
 // Register-staged page stream (producer waves of NARROW16PC, 256 threads).
 // Two register stages of one page each (18 x 16-byte loads per lane) keep two
@@ -448,7 +195,7 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
     return;
   }
 
-  // consumer LDS offsets (as in decode_kernel16_fp8): QK operand of key 16cw + li,
+  // consumer LDS offsets: QK operand of key 16cw + li,
   // chunk 4c + g; transposed V operand of keys 4g + li/4 (+ 16 per key block)
   int qk_lane[2];
 #pragma unroll
@@ -585,6 +332,289 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
           r1[i % kPvDepth] = tr_read(vaddr(i + kPvDepth, 1));
         }
         o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[fb], 0, 0, 0);
+        sched_fence();
+      }
+    }
+
+    if (ti.last) {
+      const float l_row = ssum[0][li] + ssum[1][li] + ssum[2][li] + ssum[3][li];
+      const bool live = l_row > 0.f;
+      const float inv = live ? 1.0f / l_row : 0.f;
+      if (row < ti.rows) {
+        float* dst_o;
+        float* dst_l;
+        if (ti.final_out) {
+          dst_o = p.out + ((size_t)ti.qrow0 + row) * kDv;
+          dst_l = p.lse + (size_t)ti.qrow0 + row;
+        } else {
+          dst_o = p.ws_out + ((size_t)ti.slot * R + row) * kDv;
+          dst_l = p.ws_lse + (size_t)ti.slot * R + row;
+        }
+#pragma unroll
+        for (int fb = 0; fb < kFb; ++fb) *(f32x4*)(dst_o + 128 * cw + 16 * fb + 4 * g) = o[fb] * inv;
+        if (cw == 0 && g == 0) *dst_l = live ? (m_run + log2_fast(l_row)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NARROW16PC8 (fp8 cache, up to 16 rows): the roles of decode_kernel_pc over
+// E4M3 pages, which stay E4M3 in LDS (the K and V^T operands are widened to
+// bf16 in registers, exactly, as in the 64-row fp8 kernel).
+//   Waves 4-7 are producers: direct-to-LDS loads of whole pages (codes and
+//   the page's 64 token scales) into a ring of three buffers, two pages in
+//   flight while the consumers compute the third (a fourth buffer, three
+//   pages in flight, measured slower).
+//   Waves 0-3 are consumers: wave c computes S^T for keys 16c..16c+15
+//   (v_mfma_f32_16x16x32_bf16; one 16-byte LDS read of 16 codes serves two
+//   k-steps, the query registers follow that feature order), scales each
+//   score by its token's scale, exchanges the row maxima, writes
+//   P_j s_j (bf16) into LDS as the PV B operand with k-slot 8g + e = key
+//   8g + e of the k-step, and accumulates O^T for output features
+//   128c..128c+127 with V^T from ds_read_b64_tr_b8 (8 consecutive keys of one
+//   feature per lane); the row sums take the unscaled P.
+//   Three workgroup barriers per tile, as in decode_kernel_pc.
+// Tile layout: chunk c (16 codes) of key k at ((c/4) * 64 + k) * 64 +
+// ((c%4) ^ swz8p(k)) * 16 (64-byte line groups of 4 KiB), swz8p(k) = (k3, k2):
+// every 16 consecutive keys at one chunk (QK operand) and 16 consecutive keys
+// x 2 halves of one chunk (V^T operand) cover 16 distinct 16-byte bank groups.
+// The 64 scales (256 bytes) follow the codes.
+// ---------------------------------------------------------------------------
+constexpr int kPc8BufBytes = kFp8TileBytes + 1024;   // 37888: codes, scales, padding to 1 KiB
+constexpr int kPc8Bufs = 3;
+constexpr int kPc8Loads = 9;                         // code loads per producer lane and page
+__device__ __forceinline__ int swz8p(int key) { return (((key >> 3) & 1) << 1) | ((key >> 2) & 1); }
+__device__ __forceinline__ int byte8p(int key, int chunk) {
+  return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz8p(key)) << 4);
+}
+
+// Load i < 9 of producer lane t fills line group i, key t / 4, 16-byte unit
+// t % 4 (the lane fetches the chunk that belongs there); load 9, issued by
+// lanes 0-15 of wave 4 only, brings the page's 64 scales. Keys at or past
+// `nvalid` re-read the last valid key.
+struct TileDmaPc8 {
+  static constexpr int kLoads = kPc8Loads + 1;
+  const uint8_t* page;
+  const uint8_t* scales;
+  uint32_t voff, lds0;
+  __device__ __forceinline__ void plan(const uint8_t* kv, const float* kv_scale, int page_id, int nvalid,
+                                       LDS_AS uint8_t* buf, LDS_AS float* /*sbuf*/, int ptid) {
+    page = kv + (size_t)page_id * kFp8TileBytes;
+    scales = (const uint8_t*)(kv_scale + (size_t)page_id * kPage);
+    const int key = ptid >> 2, pos = ptid & 3;
+    const int src_key = min(key, nvalid - 1);
+    voff = src_key * kFp8RowBytes + 16 * (pos ^ swz8p(key));
+    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (ptid & ~63) * 16));
+  }
+  __device__ __forceinline__ void load(int i) const {
+    if (i < 9) {
+      dma16(voff + 64 * i, page, lds0 + i * 4096);
+    } else if (threadIdx.x < 256 + 16) {
+      // (wave 4 only, a wave-uniform choice; within it lanes 0-15)
+      dma16(16 * (threadIdx.x & 15), scales, lds0 + 9 * 4096);
+    }
+  }
+};
+
+// vmcnt(n) with expcnt and lgkmcnt untouched (gfx9 encoding)
+constexpr int vm_imm_n(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 3) << 14); }
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void decode_kernel_pc8(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
+    const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
+    const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
+    const uint8_t* __restrict__ kv_) {
+  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
+  constexpr int kQChunks = kDqk / 32;        // 18 k-steps of 32 features
+  constexpr int kFb = 8;                     // 16-feature output blocks per consumer
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kPc8Bufs * kPc8BufBytes];
+  __shared__ __attribute__((aligned(16))) bf16x8 p_lds[2][64];   // [k-step][lane]
+  __shared__ float smax[4][16];
+  __shared__ float ssum[4][16];
+  __shared__ int info_lds[4][8];                                  // tile facts, ring of 4
+  LDS_AS uint8_t* const bufs = (LDS_AS uint8_t*)(smem);
+  LDS_AS int* const info_ring = (LDS_AS int*)(&info_lds[0][0]);
+  auto buf = [&](int f) { return bufs + (f % kPc8Bufs) * kPc8BufBytes; };
+
+  const DecodeParams& p = a.p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const bool producer = wave >= 4;
+  const int cw = wave & 3;
+  const int g = lane >> 4, li = lane & 15;
+  const int R = p.rows;
+  const int row = li;
+  const int u = blockIdx.x;
+
+  Unit unit;
+  if (!unit.init(a, u)) {
+    if (!a.md && !producer) write_empty(p, unit.b0, 0, 16, 4);
+    return;
+  }
+  const int f0 = unit.f_begin, fe = unit.f_end;
+
+  if (producer) {
+    // ---- page stream: tiles f0 .. f0 + 2 ahead, then f + 3 after barrier B0
+    //      of tile f (the buffer of tile f - 1 is free by then)
+    const int ptid = tid - 256;
+    constexpr int AHEAD = kPc8Bufs - 1;
+    TileDmaPc8 dma;
+    auto issue = [&](int f) {
+      const TileInfo ti = unit.prepare(a, f, buf(f), nullptr, ptid, dma);
+      if (ptid == 0) put_info(info_ring + 8 * (f & 3), ti);
+#pragma unroll
+      for (int i = 0; i < TileDmaPc8::kLoads; ++i) dma.load(i);
+    };
+    // tile f has landed when at most the loads of the tiles issued after it
+    // are outstanding (wave 4 issues one more load per tile than the others)
+    auto wait_landed = [&](int f, int last_issued) {
+      const int after = last_issued - f;
+      if (wave == 4) {
+        if (after >= 2) __builtin_amdgcn_s_waitcnt(vm_imm_n(2 * (kPc8Loads + 1)));
+        else if (after == 1) __builtin_amdgcn_s_waitcnt(vm_imm_n(kPc8Loads + 1));
+        else __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      } else {
+        if (after >= 2) __builtin_amdgcn_s_waitcnt(vm_imm_n(2 * kPc8Loads));
+        else if (after == 1) __builtin_amdgcn_s_waitcnt(vm_imm_n(kPc8Loads));
+        else __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      }
+    };
+    static_assert(AHEAD <= 3 && 2 * (kPc8Loads + 1) <= 63, "wait counts");
+    for (int j = 0; j < AHEAD && f0 + j < fe; ++j) issue(f0 + j);
+    wait_landed(f0, min(f0 + AHEAD - 1, fe - 1));
+    for (int f = f0; f < fe; ++f) {
+      lds_barrier();   // B0: tile f and its facts are in LDS
+      if (f + AHEAD < fe) issue(f + AHEAD);
+      lds_barrier();   // B1
+      lds_barrier();   // B2
+      if (f + 1 < fe) wait_landed(f + 1, min(f + AHEAD, fe - 1));
+    }
+    return;
+  }
+
+  // ---- consumer operand offsets: K of key 16 cw + li at chunk g of each line
+  //      group (16 codes: features 64 r + 16 g .. + 15 of read r); V^T of
+  //      keys 8 g + li / 2 (+ 32 per k-step), feature chunk 8 cw + fb, half li % 2
+  const int k_lane = byte8p(16 * cw + li, g);
+  int v_lane[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) v_lane[q4] = byte8p(8 * g + (li >> 1), 8 * cw + q4) + 8 * (li & 1);
+
+  bf16x8 qreg[kQChunks];   // k-step j: features 64 (j / 2) + 16 g + 8 (j % 2) .. + 7 of this lane's row
+  f32x4 o[kFb];
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto fetch_q = [&](const TileInfo& nt) {
+    const int rr = row < nt.rows ? row : max(nt.rows - 1, 0);
+    const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(nt.qrow0 + rr, p.q_rows - 1) * kDqk);
+#pragma unroll
+    for (int j = 0; j < kQChunks; ++j) qreg[j] = qrow[8 * (j >> 1) + 2 * g + (j & 1)];
+  };
+  {
+    TileDma<false> plan_only;   // the first tile's facts, to fetch its query rows early
+    fetch_q(unit.prepare(a, f0, bufs, nullptr, tid & 255, plan_only));
+  }
+
+  for (int f = f0; f < fe; ++f) {
+    const LDS_AS uint8_t* const cur = buf(f);
+    const bool more = f + 1 < fe;
+
+    lds_barrier();   // B0
+    const TileInfo ti = get_info(info_ring + 8 * (f & 3));
+    const int t = ti.t, L = ti.L;
+    if (ti.first) {
+#pragma unroll
+      for (int fb = 0; fb < kFb; ++fb) o[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run = -INFINITY;
+      l_run = 0.f;
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);   // its query rows (fetched a tile ahead)
+    }
+
+    // QK: S^T[keys 16cw.., 16 rows]; read r feeds k-steps 2r and 2r + 1
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
+    {
+      constexpr int NR = kQChunks / 2, D = 4;
+      u32x4 ring[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) ring[i] = *(const LDS_AS u32x4*)(cur + k_lane + i * 4096);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const u32x4 w = ring[r % D];
+        if (r + D < NR) ring[r % D] = *(const LDS_AS u32x4*)(cur + k_lane + (r + D) * 4096);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w[0], w[1]), qreg[2 * r], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w[2], w[3]), qreg[2 * r + 1], sb, 0, 0, 0);
+        sched_fence();
+      }
+    }
+    f32x4 sv = sa + sb;
+    if (more) {
+      const TileInfo nt = get_info(info_ring + 8 * ((f + 1) & 3));
+      if (nt.first) fetch_q(nt);
+    }
+
+    const f32x4 ksc = *(const LDS_AS f32x4*)(cur + kFp8TileBytes + (16 * cw + 4 * g) * 4);
+    const int key0 = t * kPage + 16 * cw + 4 * g;
+    const int vis = L - ti.qlen + (row < ti.rows ? row : max(ti.rows - 1, 0)) / p.num_heads + 1;
+    const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = sv[r] * (ksc[r] * p.scale_log2);
+      if (need_mask && (key0 + r) >= vis) v = -INFINITY;
+      sv[r] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = max_xor32(max_xor16(mx));
+    if (g == 0) smax[cw][li] = mx;
+    lds_barrier();   // B1
+
+    const float tmax = fmaxf(fmaxf(smax[0][li], smax[1][li]), fmaxf(smax[2][li], smax[3][li]));
+    const float m_new = fmaxf(m_run, tmax);
+    const bool raise = m_new > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? exp2_fast(m_run - m_new) : 1.0f;
+      if (raise) m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int fb = 0; fb < kFb; ++fb) o[fb] *= alpha;
+    }
+    const float m_eff = (m_run == -INFINITY) ? 0.0f : m_run;
+    bf16x4 pq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pr = exp2_fast(sv[r] - m_eff);
+      l_run += pr;
+      // masked keys may carry any scale (NaN in a page's unused tail)
+      pq[r] = (__bf16)(sv[r] == -INFINITY ? 0.f : pr * ksc[r]);
+    }
+    // key 16 (cw % 2) + 4 g + r of k-step cw / 2 is k-slot 8 g' + e, g' = 2 (cw % 2) + g / 2
+    *(LDS_AS bf16x4*)((LDS_AS uint8_t*)&p_lds[cw >> 1][li + 16 * (2 * (cw & 1) + (g >> 1))] + 8 * (g & 1)) = pq;
+    if (ti.last) {
+      const float ls = sum_xor32(sum_xor16(l_run));
+      if (g == 0) ssum[cw][li] = ls;
+    }
+    lds_barrier();   // B2
+
+    // PV: O^T[features 128cw.., 16 rows] += V^T . P^T, V^T widened from the codes
+    {
+      constexpr int NPV = 2 * kFb, D = 4;
+      auto vaddr = [&](int i) {
+        const int ks = i / kFb, fb = i % kFb;
+        return cur + v_lane[fb & 3] + (fb >> 2) * 4096 + ks * 2048;
+      };
+      i32x2 ring[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) ring[i] = tr8_read(vaddr(i));
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int ks = i / kFb, fb = i % kFb;
+        if (fb == 0) pb = p_lds[ks][lane];
+        const i32x2 x = ring[i % D];
+        if (i + D < NPV) ring[i % D] = tr8_read(vaddr(i + D));
+        o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8((unsigned)x[0], (unsigned)x[1]), pb, o[fb], 0, 0, 0);
         sched_fence();
       }
     }
@@ -2169,7 +2199,7 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
   } while (0)
   const bool fp8 = p.kv_scale != nullptr;
   if (variant == VAR_NARROW16) {
-    if (fp8) MLA_LAUNCH(decode_kernel16_fp8, kThreads);
+    if (fp8) MLA_LAUNCH(decode_kernel_pc8, 2 * kThreads);
     else MLA_LAUNCH(decode_kernel_pc, 2 * kThreads);
   } else if (variant == VAR_Q8) {
     MLA_LAUNCH(decode_kernel_q8, kThreadsX);

@@ -20,7 +20,7 @@ def _step(w, d, plan, out, lse, fp8_mma=False):
                plan=plan, out=out, lse=lse, fp8_mma=fp8_mma)
 
 
-@pytest.mark.parametrize("name", ["share16", "mtp", "ragged", "fp8"])
+@pytest.mark.parametrize("name", ["share16", "share16_fp8", "mtp", "ragged", "fp8"])
 def test_graph_replay_matches_eager(name):
     w = config(name, small=True, seed=4)
     d = to_device(w)

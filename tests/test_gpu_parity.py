@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 # ----------------------------------------------------------------- small configs
 
-@pytest.mark.parametrize("name", ["tiny", "share16", "mtp", "ragged", "fp8"])
+@pytest.mark.parametrize("name", ["tiny", "share16", "share16_fp8", "mtp", "ragged", "fp8"])
 @pytest.mark.parametrize("split", [False, True])
 def test_small_config_parity(name, split):
     w = config(name, small=True, seed=1)
@@ -208,14 +208,14 @@ def test_combine_matches_oracle_merge(R):
 # ----------------------------------------------------------------- full sizes, sampled
 
 # every sequence of the smaller workloads; at least 16 of the two largest
-FULL_SIZE_SAMPLE = {"tiny": None, "share16": None, "ragged": None, "mtp": 16, "fp8": 16}
+FULL_SIZE_SAMPLE = {"tiny": None, "share16": None, "share16_fp8": None, "ragged": None, "mtp": 16, "fp8": 16}
 
 
-@pytest.mark.parametrize("name", ["tiny", "share16", "mtp", "ragged", "fp8"])
+@pytest.mark.parametrize("name", ["tiny", "share16", "share16_fp8", "mtp", "ragged", "fp8"])
 def test_full_size(name):
     """Whole-batch run in the launch configuration the benchmark times (default
-    split plan), compared with the oracle on every sequence of tiny, share16
-    and ragged, and on 16 sequences (the first, the last and 14 drawn) of mtp
+    split plan), compared with the oracle on every sequence of tiny, share16,
+    share16_fp8 and ragged, and on 16 sequences (the first, the last and 14 drawn) of mtp
     and fp8."""
     w = config(name, seed=0)
     out, lse, _ = run_gpu(w, split=True)

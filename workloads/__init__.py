@@ -212,6 +212,9 @@ CONFIGS = {
     "tiny": dict(batch=1, num_heads=16, q_len=1, seqlens=[256], kv_dtype="bf16", table="identity"),
     "share16": dict(batch=64, num_heads=16, q_len=1, seqlens=_uniform_lengths(1024, 4096, 64),
                     kv_dtype="bf16", table="shuffled"),
+    # the same batch over an fp8 cache (the 16-row fp8 kernel)
+    "share16_fp8": dict(batch=64, num_heads=16, q_len=1, seqlens=_uniform_lengths(1024, 4096, 64),
+                        kv_dtype="fp8_e4m3", table="shuffled"),
     "mtp": dict(batch=128, num_heads=128, q_len=2, seqlens=[4096] * 128, kv_dtype="bf16", table="shuffled"),
     "ragged": dict(batch=32, num_heads=128, q_len=1, seqlens=_ragged_lengths(31, 512, 16384, 65536),
                    kv_dtype="bf16", table="shuffled"),
@@ -225,6 +228,8 @@ CONFIGS = {
 CONFIG_TEXT = {
     "tiny": "batch 1, H=16, q_len=1, seqlen 256, bf16, identity block table",
     "share16": "batch 64, H=16, q_len=1, seqlens U[1024,4096], bf16, permuted block table",
+    "share16_fp8": "batch 64, H=16, q_len=1, seqlens U[1024,4096], fp8 e4m3 cache + per-token fp32 scale, "
+                   "permuted block table",
     "mtp": "batch 128, H=128, q_len=2 causal, seqlen 4096, bf16, shuffled block table",
     "ragged": "batch 32, H=128, q_len=1, 31 log-uniform seqlens in [512,16384] + one 65536, bf16",
     "fp8": "batch 128, H=128, q_len=2 causal, seqlen 8192, fp8 e4m3 cache + per-token fp32 scale",
@@ -236,6 +241,8 @@ SMALL = {
     "tiny": dict(CONFIGS["tiny"]),
     "share16": dict(batch=6, num_heads=16, q_len=1, seqlens=_uniform_lengths(1024, 4096, 6),
                     kv_dtype="bf16", table="shuffled"),
+    "share16_fp8": dict(batch=6, num_heads=16, q_len=1, seqlens=_uniform_lengths(1024, 4096, 6),
+                        kv_dtype="fp8_e4m3", table="shuffled"),
     "mtp": dict(batch=3, num_heads=128, q_len=2, seqlens=[4096, 1000, 130], kv_dtype="bf16",
                 table="shuffled"),
     "ragged": dict(batch=5, num_heads=128, q_len=1, seqlens=_ragged_lengths(4, 512, 4000, 16384),
