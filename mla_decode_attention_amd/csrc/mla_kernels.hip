@@ -1946,7 +1946,11 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
       wp += t ? t + c : 0;
     }
   }
-  atomicMax(&s_max_pieces, max_pieces);
+  // the largest count: a wave maximum first (one LDS atomic per wave, not one
+  // per thread on a single word)
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) max_pieces = max(max_pieces, __shfl_xor(max_pieces, d));
+  if ((tid & 63) == 0) atomicMax(&s_max_pieces, max_pieces);
   int2 tot2;
   const int2 run2 = block_exclusive_scan2(acc2, wave_tot, &tot2);   // its barriers also publish s_wpre, s_prefix, s_max_pieces
   if (lds_search) {
