@@ -53,6 +53,7 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 #include <math.h>
+#include <algorithm>
 #include <utility>
 
 #include "mla_device.h"
@@ -1998,37 +1999,43 @@ __global__ __launch_bounds__(1024) void metadata_kernel(const int32_t* seqlens, 
 }
 
 // ---------------------------------------------------------------------------
-// LSE merge of partials: one workgroup per (sequence, row), 4 groups of 64
-// threads per row, 8 features per thread (d..d+3 and 256+d..256+d+3, so each
-// load of a wave covers 1 KiB contiguous). Group g takes the partials
-// k = g, g + 4, ... in one online pass (running max, rescaled sum and output;
-// the loads of four partials issued together), so a sequence cut into many
-// partials (a long context over many units) costs about a quarter of the
-// memory round trips of one pass over all of them; the group states are then
-// merged through LDS. A partial with LSE -inf weighs nothing and its values
-// are not used (they may be anything, NaN included).
-// Dispatch order: one workgroup per (sequence, row), the sequence index
-// running fastest (grid x). When the decode's metadata says that
-// some sequence needs more than one pass (more than 16 partials) and the
-// batch has at most kCombineOrderMaxB sequences, those sequences take the
-// first places and the others follow, each class in index order: their rows
-// then start in the first round of workgroups instead of wherever their index
-// puts them, and a long context's merge, the longest of the grid, no longer
-// runs alone at the end. (Ranking costs every workgroup a load of all the
-// offsets and three barriers, so it is skipped when no sequence needs it.)
-// When the metadata shows every sequence in exactly one partial (largest count
-// 1, total equal to the batch), the decode has written every output itself
-// and each workgroup returns after reading the header.
+// LSE merge of partials. A partial with LSE -inf weighs nothing and its values
+// are not used (they may be anything, NaN included). Each thread holds 8
+// features of a row (d..d+3 and 256+d..256+d+3, so each load of a wave covers
+// 1 KiB contiguous) and merges partials in an online pass (running max,
+// rescaled sum and output; the loads of four partials issued together).
+// Two shapes of workgroup (4 waves):
+//   light: four rows of one sequence, one wave per row, every partial of the
+//          row in that wave (sequences of at most 16 partials, one or a few
+//          passes);
+//   heavy: one row, the four waves each taking every fourth partial, merged
+//          through LDS (sequences of more than 16 partials: a long context
+//          over many units; a quarter of the memory round trips).
+// Heavy workgroups exist only when the decode's metadata says some sequence
+// has more than 16 partials and the batch has at most kCombineOrderMaxB
+// sequences: every workgroup then ranks the sequences (heavy first, each
+// class in index order) and the heavy sequences' rows take the first ids, so
+// they start in the first round instead of wherever their index puts them.
+// Otherwise every workgroup is light. The grid has room for the light
+// workgroups of the whole batch plus the extra ones of as many heavy
+// sequences as the unit count allows (each has at least 16 partials beyond
+// its first, and there are fewer than `units` of those in all); workgroups
+// past the need return at once. When the metadata shows every sequence in
+// exactly one partial (largest count 1, total equal to the batch), the decode
+// has written every output itself and each workgroup returns after reading
+// the header.
 // md (nullable): the decode's metadata; the merge does nothing unless it was
 // built for this batch and num_units (as the decode kernels check). The
 // header is read before the offsets, which sit in the metadata at positions
 // this call's batch sets (metadata built for a smaller batch is shorter).
 // ---------------------------------------------------------------------------
-constexpr int kCombineRows = 1;      // rows per workgroup
-constexpr int kCombineGroups = 4;    // partial groups per row
-constexpr int kCombineInFlight = 4;  // partials per group whose loads are issued together
-constexpr int kCombineThreads = kCombineRows * kCombineGroups * 64;
-constexpr int kCombineOrderMaxB = kCombineThreads;   // one thread per sequence ranks them
+constexpr int kCombineGroups = 4;    // waves per workgroup: partial groups of a heavy row, rows of a light one
+constexpr int kCombineInFlight = 4;  // partials per wave whose loads are issued together
+constexpr int kCombineThreads = kCombineGroups * 64;
+constexpr int kCombinePass = kCombineGroups * kCombineInFlight;   // partials a heavy row takes per pass
+constexpr int kCombineOrderMaxB = kCombineThreads;                // one thread per sequence ranks them
+
+__device__ __forceinline__ int combine_light_blocks(int R) { return (R + kCombineGroups - 1) / kCombineGroups; }
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part_out,
                                                       const float* __restrict__ part_lse,
@@ -2037,10 +2044,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
                                                       int B, int R, float* __restrict__ out,
                                                       float* __restrict__ lse, int skip_single,
                                                       const int32_t* __restrict__ md, int units) {
-  __shared__ float s_ms[kCombineRows][kCombineGroups][2];               // (max, sum)
-  __shared__ f32x4 s_acc[kCombineRows][kCombineGroups - 1][2][64];       // groups 1.., two halves
-  __shared__ int s_order[kCombineThreads / 64 + 1];
-  constexpr int kPass = kCombineGroups * kCombineInFlight;     // partials one pass takes
+  __shared__ float s_ms[kCombineGroups][2];               // (max, sum)
+  __shared__ f32x4 s_acc[kCombineGroups - 1][2][64];       // groups 1.., two halves
+  __shared__ int s_count[kCombineThreads / 64];
+  __shared__ int s_seq[kCombineOrderMaxB];                 // place -> sequence
   int max_pieces = 0, total_partials = -1;
   if (md) {
     // the header words are read together (one round trip)
@@ -2049,62 +2056,69 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
     total_partials = md[MD_TOTAL_PARTIALS];
     if ((h_magic != kMdMagic) | (h_batch != B) | (h_units != units)) return;
   }
-  // every sequence in exactly one partial: the decode wrote all the outputs
   if (skip_single && max_pieces <= 1 && total_partials == B) return;
-  int rb = blockIdx.y;
-  int b = blockIdx.x;
-  if (B <= kCombineOrderMaxB && max_pieces > kPass) {
-    // place b of the order: rows of the heavy sequences, then the others
-    const int t = threadIdx.x, w = t >> 6;
+  const int RL = combine_light_blocks(R);
+  const int id = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  bool heavy_wg = false;
+  int b, r0;
+  if (B <= kCombineOrderMaxB && max_pieces > kCombinePass) {
+    // the order: heavy sequences first, each class in index order
+    const int t = threadIdx.x;
     const int nt = t < B ? offsets[t + 1] - offsets[t] : 0;
-    const bool heavy = nt > kPass;
+    const bool heavy = nt > kCombinePass;
     const uint64_t hb = __builtin_amdgcn_ballot_w64(heavy);
-    if ((t & 63) == 0) s_order[w] = __builtin_popcountll(hb);
+    if (lane == 0) s_count[wave] = __builtin_popcountll(hb);
     __syncthreads();
     int heavy_before = 0, heavy_all = 0;
 #pragma unroll
     for (int v = 0; v < kCombineThreads / 64; ++v) {
-      heavy_before += v < w ? s_order[v] : 0;
-      heavy_all += s_order[v];
+      heavy_before += v < wave ? s_count[v] : 0;
+      heavy_all += s_count[v];
     }
-    const int hr = heavy_before + __builtin_popcountll(hb & ((1ull << (t & 63)) - 1));   // heavy before t
-    const int my_pos = heavy ? hr : heavy_all + (t - hr);
-    // linear id -> (place, row block): the heavy sequences' rows first, the
-    // place running fastest within each class
-    const int id = blockIdx.x + B * blockIdx.y, hitems = heavy_all * gridDim.y;
-    const int pos = id < hitems ? id % heavy_all : heavy_all + (id - hitems) % (B - heavy_all);
-    rb = id < hitems ? id / heavy_all : (id - hitems) / (B - heavy_all);
+    const int hr = heavy_before + __builtin_popcountll(hb & ((1ull << lane) - 1));
+    if (t < B) s_seq[heavy ? hr : heavy_all + (t - hr)] = t;
     __syncthreads();
-    if (t < B && my_pos == pos) s_order[kCombineThreads / 64] = t;
-    __syncthreads();
-    b = s_order[kCombineThreads / 64];
+    // ids: one per row of the heavy sequences, then one per four rows of the
+    // others, the place running fastest within each class
+    const int hitems = heavy_all * R, light = B - heavy_all;
+    if (id < hitems) {
+      heavy_wg = true;
+      b = s_seq[id % heavy_all];
+      r0 = id / heavy_all;
+    } else {
+      const int j = id - hitems;
+      if (j >= light * RL) return;
+      b = s_seq[heavy_all + j % light];
+      r0 = kCombineGroups * (j / light);
+    }
+  } else {
+    if (id >= B * RL) return;
+    b = id % B;
+    r0 = kCombineGroups * (id / B);
   }
   const int k0 = offsets[b];
   const int n = offsets[b + 1] - k0;
   if (skip_single && n == 1) return;
-  const int half = threadIdx.x / (kCombineGroups * 64);         // row of the workgroup
-  const int grp = (threadIdx.x >> 6) % kCombineGroups;
-  const int lane = threadIdx.x & 63;
-  const int r = rb * kCombineRows + half;
   // partial slots hold R rows; sequence b owns the first rows_b of them
   const int rows_b = cu_q ? (cu_q[b + 1] - cu_q[b]) * num_heads : R;
   const size_t out_row0 = cu_q ? (size_t)cu_q[b] * num_heads : (size_t)b * R;
-  const bool row_ok = r < rows_b;
-  const int d = lane * 4;                                        // features d.. and 256 + d..
-  const float* pl = part_lse + (size_t)k0 * R + r;
-  const float* po = part_out + ((size_t)k0 * R + r) * kDv + d;
+  const int d = lane * 4;
   const size_t lstride = R, ostride = (size_t)R * kDv;
-
   constexpr int kU = kCombineInFlight;
+
+  // online pass of this wave over partials k0 + first, + step, ... of row r
   float M = -INFINITY, S = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  if (row_ok) {
-    for (int k = grp; k < n; k += kCombineGroups * kU) {
+  auto pass = [&](int r, int first, int step) {
+    const float* pl = part_lse + (size_t)k0 * R + r;
+    const float* po = part_out + ((size_t)k0 * R + r) * kDv + d;
+    for (int k = first; k < n; k += step * kU) {
       float v[kU];
       f32x4 o0[kU], o1[kU];
 #pragma unroll
       for (int j = 0; j < kU; ++j) {
-        const int kk = k + j * kCombineGroups;
+        const int kk = k + j * step;
         const bool in = kk < n;
         v[j] = in ? pl[kk * lstride] : -INFINITY;
         o0[j] = in ? *(const f32x4*)(po + kk * ostride) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -2127,42 +2141,58 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
         }
       }
     }
+  };
+  auto store = [&](int r, float Mt, float St, f32x4 a0, f32x4 a1) {
+    const bool live = Mt != -INFINITY;
+    const float inv = live ? 1.f / St : 0.f;
+    float* dst = out + (out_row0 + r) * kDv + d;
+    *(f32x4*)dst = a0 * inv;
+    *(f32x4*)(dst + 256) = a1 * inv;
+    if (lane == 0) lse[out_row0 + r] = live ? Mt + logf(St) : -INFINITY;
+  };
+
+  if (!heavy_wg) {
+    const int r = r0 + wave;
+    if (r >= rows_b) return;
+    pass(r, 0, 1);
+    store(r, M, S, acc0, acc1);
+    return;
   }
+
+  // heavy: one row, wave g takes partials g, g + 4, ...; states merged through LDS
+  const int r = r0;
+  const bool row_ok = r < rows_b;
+  if (row_ok) pass(r, wave, kCombineGroups);
   if (lane == 0) {
-    s_ms[half][grp][0] = M;
-    s_ms[half][grp][1] = S;
+    s_ms[wave][0] = M;
+    s_ms[wave][1] = S;
   }
-  if (grp > 0) {
-    s_acc[half][grp - 1][0][lane] = acc0;
-    s_acc[half][grp - 1][1][lane] = acc1;
+  if (wave > 0) {
+    s_acc[wave - 1][0][lane] = acc0;
+    s_acc[wave - 1][1][lane] = acc1;
   }
   __syncthreads();
-  if (grp != 0 || !row_ok) return;
+  if (wave != 0 || !row_ok) return;
   float Mt = M;
 #pragma unroll
-  for (int g = 1; g < kCombineGroups; ++g) Mt = fmaxf(Mt, s_ms[half][g][0]);
-  const bool live = Mt != -INFINITY;
+  for (int g = 1; g < kCombineGroups; ++g) Mt = fmaxf(Mt, s_ms[g][0]);
   float St = 0.f;
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  if (live) {
+  if (Mt != -INFINITY) {
     const float c0 = M == -INFINITY ? 0.f : expf(M - Mt);
     St = S * c0;
     a0 = acc0 * c0;
     a1 = acc1 * c0;
 #pragma unroll
     for (int g = 1; g < kCombineGroups; ++g) {
-      const float mg = s_ms[half][g][0];
+      const float mg = s_ms[g][0];
       const float cg = mg == -INFINITY ? 0.f : expf(mg - Mt);
-      St += s_ms[half][g][1] * cg;
-      a0 += cg * s_acc[half][g - 1][0][lane];
-      a1 += cg * s_acc[half][g - 1][1][lane];
+      St += s_ms[g][1] * cg;
+      a0 += cg * s_acc[g - 1][0][lane];
+      a1 += cg * s_acc[g - 1][1][lane];
     }
   }
-  const float inv = live ? 1.f / St : 0.f;
-  float* dst = out + (out_row0 + r) * kDv + d;
-  *(f32x4*)dst = a0 * inv;
-  *(f32x4*)(dst + 256) = a1 * inv;
-  if (lane == 0) lse[out_row0 + r] = live ? Mt + logf(St) : -INFINITY;
+  store(r, Mt, St, a0, a1);
 }
 
 // ---------------------------------------------------------------------------
@@ -2232,9 +2262,14 @@ hipError_t launch_combine(const float* part_out, const float* part_lse, const in
                           const int32_t* cu_q, int num_heads, int batch, int rows, float* out,
                           float* lse, int skip_single, hipStream_t s, const int32_t* md, int units,
                           hipEvent_t ev_start, hipEvent_t ev_stop) {
-  // the ordered dispatch indexes (sequence, row block) pairs in 32 bits
-  if ((long long)batch * ((rows + kCombineRows - 1) / kCombineRows) > INT32_MAX) return hipErrorInvalidValue;
-  dim3 grid(batch, (rows + kCombineRows - 1) / kCombineRows);
+  // light workgroups for the whole batch, plus the extra rows of as many heavy
+  // sequences as there can be: each has more than kCombinePass partials, and
+  // the extra partials of all sequences number fewer than `units`
+  const long long light = (long long)batch * ((rows + kCombineGroups - 1) / kCombineGroups);
+  const long long heavy_max = md ? std::min<long long>(batch, std::max(units - 1, 0) / kCombinePass) : 0;
+  const long long wgs = light + heavy_max * (rows - (rows + kCombineGroups - 1) / kCombineGroups);
+  if (wgs < 1 || wgs > INT32_MAX) return hipErrorInvalidValue;   // ids are 32-bit
+  dim3 grid((unsigned)wgs);
   if (ev_start || ev_stop)
     hipExtLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, ev_start, ev_stop, 0, part_out, part_lse,
                           offsets, cu_q, num_heads, batch, rows, out, lse, skip_single, md, units);
