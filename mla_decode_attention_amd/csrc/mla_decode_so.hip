@@ -696,12 +696,435 @@ void decode_kernel_so(DecodeParams p_, const int32_t* __restrict__ md_, const in
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// fp8 cache on fp8 MFMA with score and output waves (uniform q_len): the
+// approximation of the fp8 matrix-core path -- query rows in E4M3 with a
+// power-of-two scale per row (the smallest 2^k with max|q| <= 448 * 2^k),
+// P'_j = P_j s_j in E4M3 with a power-of-two scale per (row, 32-key half of
+// the page) whose block maximum lands in [128, 256), both contractions on
+// E4M3 operands and fp32 accumulation (PaddleNLP issue #10157, quantization
+// section, SageAttention2) -- on the wave split above, one page per step:
+//   score wave (rh, kh)  S^T[32 keys of half kh, 32 rows of half rh] on
+//                        v_mfma_scale_f32_32x32x64_f8f6f4, nine k-steps of 64
+//                        features (one row per lane pair: a row's reductions
+//                        take one cross-lane step); the softmax of those
+//                        scores, P' into the P8 buffer and its E8M0 byte.
+//   output wave ow       O^T[128 features, 64 rows] += V^T . P'^T on
+//                        v_mfma_scale_f32_32x32x64_f8f6f4: one MFMA per 32
+//                        features and row half takes the page's 64 keys, the
+//                        B-operand block scales being the two key halves'
+//                        E8M0 bytes; V^T comes transposed from the tile
+//                        (ds_read_b64_tr_b8), no widening anywhere.
+// The references are whole numbers (a raise rounds the new maximum up), so
+// every rescale factor is a power of two: where a key half's reference is
+// below the output wave's, its factor goes into that half's E8M0 block scale,
+// exactly, and P itself is never touched. Otherwise the exchange, the lazy
+// raise and the epilogue are those of the kernel above.
+// fp8 tile in LDS: chunk c (16 codes) of key k at lds8q_byte(k, c); the 64
+// per-token scales after the codes, then padding, 10 loads x 256 lanes x 16 B.
+// ---------------------------------------------------------------------------
+constexpr int kBufBytes8 = 10 * 256 * 16;   // 40960
+constexpr int kBufs8 = 3;
+constexpr int kLoads8 = 10;
+constexpr int kNk8 = kDqk / 64;              // 9 k-steps of 64 features in the QK GEMM
+constexpr int kPStride8 = 80;                // bytes per row of the P8 buffer: 64 keys + pad
+constexpr int kP8Bytes = kRowsSo * kPStride8;
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void decode_kernel_so8(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
+                       const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
+                       const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
+                       const uint8_t* __restrict__ kv_) {
+  constexpr int NB = kBufs8;
+  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
+  // buffers | P8 [parity][row][key] | E8M0 [parity][row][key half] | M | L
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * kBufBytes8 + 2 * kP8Bytes + 2 * kRowsSo * 2 +
+                                                         2 * kMBytes];
+  LDS_AS uint8_t* const bufs = (LDS_AS uint8_t*)smem;
+  LDS_AS uint8_t* const p8 = bufs + NB * kBufBytes8;
+  LDS_AS uint8_t* const psc = p8 + 2 * kP8Bytes;
+  LDS_AS float* const mpub = (LDS_AS float*)(psc + 2 * kRowsSo * 2);
+  LDS_AS float* const lpub = mpub + kMBytes / 4;
+
+  const DecodeParams& p = a.p;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = uniform(tid >> 6);
+  const int R = p.rows;
+  const WgCoord wc = wg_coord((R + kRowsSo - 1) / kRowsSo);
+  if (wc.unit >= p.grid_units) return;
+  const int row0 = wc.rb * kRowsSo;
+  const int u = wc.unit;
+
+  Walk<false> walk;
+  if (!walk.init(a, u)) {
+    if (!a.md) write_empty(p, u, row0, row0 + kRowsSo, kThreadsSo / 64);
+    return;
+  }
+  const int n_steps = walk.f_end - walk.f_begin;   // one page per step
+  auto buf = [&](int k) { return bufs + (k % NB) * kBufBytes8; };
+
+  if (wave >= 4) {
+    // ======================================================== output waves
+    const int ow = wave - 4;                 // features 128 ow .. 128 ow + 127
+    const int tt = tid - 256;                // 0..255: lane of the page loads
+    const int n = lane & 31, h = lane >> 5;
+
+    // ---- page loads: load i of lane tt fills LDS slot 256 i + tt = line
+    // group i, key tt / 4, position tt % 4; the tenth brings the page's 64
+    // per-token scales (wave 4; the others re-read them into the padding),
+    // those past the valid keys repeating the last valid one
+    Walk<true> wload;
+    wload.init(a, u);
+    int plan_page = 0, plan_nvalid = 1;
+    uint32_t voff = 0;
+    const uint8_t* src = nullptr;
+    auto plan_step = [&](int /*j*/) {
+      wload.next(a, plan_page, plan_nvalid);
+      const int key = tt >> 2, pos = tt & 3;
+      const int src_key = min(key, plan_nvalid - 1);
+      src = a.kv + (size_t)plan_page * kFp8TileBytes;
+      voff = src_key * kFp8RowBytes + 16 * (pos ^ swz2q(key));
+    };
+    auto load_all = [&](int j) {
+      LDS_AS uint8_t* const b = buf(j);
+#pragma unroll
+      for (int i = 0; i < kLoads8 - 1; ++i)
+        dma16(voff + 64 * i, src, (uint32_t)uniform((int)(uintptr_t)(b + (4 * i + ow) * 1024)));
+      const uint8_t* sc = (const uint8_t*)(p.kv_scale + (size_t)plan_page * kPage);
+      dma4(4 * min(lane, plan_nvalid - 1), sc, (uint32_t)uniform((int)(uintptr_t)(b + (4 * (kLoads8 - 1) + ow) * 1024)));
+    };
+
+    // prologue: step 0 landed
+    plan_step(0);
+    load_all(0);
+    __builtin_amdgcn_s_waitcnt(vm_imm(0));
+    lds_barrier();
+
+    // ---- V^T operand offsets (32x32x64 A operand): 16-lane group gi covers
+    // features 32 fb + 16 (gi % 2) + 0..15 of this wave's 128 and key half
+    // gi / 2 of each 32-key block; as a source, lane i reads key
+    // 16 (gi / 2) + 8 r1 + i / 2 at byte 8 (i % 2) of chunk 8 ow + 2 fb + gi % 2.
+    // Read r of a feature block: r1 = r % 2, plus 32 keys (2048 bytes) for r / 2.
+    int v_lane[4][2];
+    {
+      const int gi = lane >> 4, i = lane & 15;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int r1 = 0; r1 < 2; ++r1)
+          v_lane[fb][r1] = lds8q_byte(16 * (gi >> 1) + 8 * r1 + (i >> 1), 8 * ow + 2 * fb + (gi & 1)) + 8 * (i & 1);
+    }
+
+    f32x16 o[4][2];   // [feature block][row half]
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) o[fb][0] = o[fb][1] = f32x16{};
+    float M[2] = {-INFINITY, -INFINITY};
+    float pend_inv[2] = {0.f, 0.f}, pend_lse[2] = {0.f, 0.f};
+    TileInfo pend_ti{};
+
+    auto flush = [&]() {
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        const int row = row0 + 32 * rh + n;
+        if (row < pend_ti.rows) {
+          float* dst_o;
+          float* dst_l;
+          if (pend_ti.final_out) {
+            dst_o = p.out + ((size_t)pend_ti.qrow0 + row) * kDv;
+            dst_l = p.lse + (size_t)pend_ti.qrow0 + row;
+          } else {
+            dst_o = p.ws_out + ((size_t)pend_ti.slot * R + row) * kDv;
+            dst_l = p.ws_lse + (size_t)pend_ti.slot * R + row;
+          }
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const f32x4 v = {o[fb][rh][4 * jj], o[fb][rh][4 * jj + 1], o[fb][rh][4 * jj + 2],
+                               o[fb][rh][4 * jj + 3]};
+              *(f32x4*)(dst_o + 128 * ow + 32 * fb + 8 * jj + 4 * h) = v * pend_inv[rh];
+            }
+          if (ow == 0 && h == 0) *dst_l = pend_lse[rh];
+        }
+      }
+      M[0] = M[1] = -INFINITY;
+    };
+
+    // iteration 0: the score waves take step 0, the output waves load step 1
+    if (n_steps > 1) {
+      plan_step(1);
+      load_all(1);
+    }
+    bool pend = false;   // a finished sequence's results are still to be stored
+    TileInfo ti{};
+    for (int k = 1; k <= n_steps + 1; ++k) {
+      // the end of iteration k - 1, at the top of this one (so that no code
+      // motion puts the PV MFMAs of iteration k - 1 behind the wait): step k
+      // has landed; then a finished sequence's results go out, and have this
+      // iteration to complete
+      __builtin_amdgcn_s_waitcnt(vm_imm(0));
+      if (pend) {
+        flush();
+        pend = false;
+      }
+      lds_barrier();
+      if (k > n_steps) break;
+      const int t = k - 1;   // the step computed here
+      const int par = t & 1;
+      const LDS_AS uint8_t* cur = buf(t);
+      // step k + 1's loads go out first: they have this iteration to land
+      if (k + 1 < n_steps) {
+        plan_step(k + 1);
+        load_all(k + 1);
+      }
+      // the references of the two key halves for this lane's rows, P'^T and
+      // its block scales, and every V^T operand of the step
+      float r[2][2];   // [key half][row half]
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) r[kh][rh] = mpub[(par * 2 + kh) * 64 + 32 * rh + n];
+      i32x8 pf[2];
+      int psb[2];
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        const LDS_AS uint8_t* prow = p8 + par * kP8Bytes + (32 * rh + n) * kPStride8 + 16 * h;
+        pf[rh] = cat8(ld128u(prow), ld128u(prow + 32));
+        psb[rh] = psc[par * 2 * kRowsSo + (32 * rh + n) * 2 + h];
+      }
+      i32x2 vr[4][4];   // [feature block][read]
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int rd = 0; rd < 4; ++rd) vr[fb][rd] = tr8_read(cur + v_lane[fb][rd & 1] + (rd >> 1) * 2048);
+
+      ti = walk.next(a);
+
+      const bool odd = (r[0][0] != M[0]) | (r[1][0] != M[0]) | (r[0][1] != M[1]) | (r[1][1] != M[1]) |
+                       (M[0] == -INFINITY) | (M[1] == -INFINITY);
+      if (__builtin_amdgcn_ballot_w64(odd) != 0) {
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) {
+          const float mn = fmaxf(M[rh], fmaxf(r[0][rh], r[1][rh]));
+          // whole-number references: the factors are exact powers of two
+          const float alpha = M[rh] == -INFINITY ? 0.f : ldexpf(1.f, (int)(M[rh] - mn));
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb) o[fb][rh] *= alpha;
+          // this lane supplies the block scale of key half h: lowered by the
+          // distance of that half's reference from the new one (a half still
+          // at -inf has P' = 0)
+          const float rk = h ? r[1][rh] : r[0][rh];
+          if (rk != -INFINITY && mn != -INFINITY) psb[rh] = max(psb[rh] + (int)(rk - mn), 0);
+          M[rh] = mn;
+        }
+      }
+
+      // ---- PV GEMM: 4 feature blocks x 2 row halves, 64 keys each
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        const i32x8 vf = {vr[fb][0][0], vr[fb][0][1], vr[fb][1][0], vr[fb][1][1],
+                          vr[fb][2][0], vr[fb][2][1], vr[fb][3][0], vr[fb][3][1]};
+        o[fb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf[0], o[fb][0], 0, 0, 0, 127, 0, psb[0]);
+        o[fb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf[1], o[fb][1], 0, 0, 0, 127, 0, psb[1]);
+      }
+
+      // row sums of the two key halves in this lane's reference (read every
+      // step, used at a sequence's end)
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        float l = 0.f;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const float lk = lpub[(par * 2 + kh) * 64 + 32 * rh + n];
+          l += r[kh][rh] != -INFINITY ? lk * ldexpf(1.f, (int)(r[kh][rh] - M[rh])) : 0.f;
+        }
+        const bool live = l > 0.f;
+        pend_inv[rh] = live ? 1.0f / l : 0.f;
+        pend_lse[rh] = live ? (M[rh] + log2_fast(l)) * kLn2 : -INFINITY;
+      }
+      if (ti.last) {
+        pend_ti = ti;
+        pend = true;
+      }
+    }
+    return;
+  }
+
+  // ========================================================== score waves
+  const int rh = wave & 1, kh = wave >> 1;
+  const int n = lane & 31, h = lane >> 5;
+  // K operand (32x32x64 A operand): lane (n, h) holds key 32 kh + n, features
+  // 16 h .. 16 h + 15 (bytes 0-15) and 32 + 16 h .. (bytes 16-31) of the
+  // k-step = chunks 4 cc + h and 4 cc + 2 + h (one line group per k-step)
+  int k_lane[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) k_lane[e] = lds8q_byte(32 * kh + n, 2 * e + h);
+  i32x8 q8[kNk8];              // E4M3 codes of row 32 rh + n, same feature order
+  float qsc = 0.f;             // 2^kq * softmax scale * log2(e)
+  float m_run = -INFINITY;     // reference (base 2) of the row over this key half
+  float l_run = 0.f;           // partial row sum (this lane's keys)
+  int row_tok = 0;
+
+  // the query row of a sequence to E4M3 with a power-of-two scale 2^kq, the
+  // smallest with max|row| <= 448 * 2^kq (not below 2^-126): the maximum from
+  // one pass over the row (the lane's half, then the partner lane's), then a
+  // second pass (cache hits) to the codes of the exact products q * 2^-kq
+  auto quant_q = [&](const TileInfo& tq) {
+    const int rr = min(row0 + 32 * rh + n, max(tq.rows - 1, 0));
+    const u32x4* qrow = (const u32x4*)(a.qptr + (size_t)min(tq.qrow0 + rr, p.q_rows - 1) * kDqk);
+    // part 0-3: features 64 cc + 16 h + 0..7, + 8..15, 64 cc + 32 + 16 h + 0..7, + 8..15
+    auto qword = [&](int cc, int part) { return qrow[8 * cc + 4 * (part >> 1) + 2 * h + (part & 1)]; };
+    float amax = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < kNk8; ++cc)
+#pragma unroll
+      for (int part = 0; part < 4; ++part) {
+        const u32x4 w = qword(cc, part);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, w[e] << 16)),
+                                   fabsf(__builtin_bit_cast(float, w[e] & 0xFFFF0000u))));
+      }
+    amax = max_xor32(amax);
+    // amax = 1.f * 2^E: 448 * 2^(E - 8) = 1.75 * 2^E covers it unless f > .75
+    const unsigned ab = __builtin_bit_cast(unsigned, amax);
+    int kq = amax > 0.f ? (int)(ab >> 23) - 127 - 8 + ((ab & 0x7FFFFFu) > 0x600000u ? 1 : 0) : 0;
+    kq = max(kq, -126);
+    const float down = __builtin_bit_cast(float, (unsigned)(127 - kq) << 23);
+    qsc = __builtin_bit_cast(float, (unsigned)(127 + kq) << 23) * p.scale_log2;
+    auto qv = [&](unsigned bits) { return __builtin_bit_cast(float, bits) * down; };
+#pragma unroll
+    for (int cc = 0; cc < kNk8; ++cc) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) {
+        const u32x4 x = qword(cc, part);
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2)
+          q8[cc][2 * part + e2] = pack_fp8x4(qv(x[2 * e2] << 16), qv(x[2 * e2] & 0xFFFF0000u),
+                                             qv(x[2 * e2 + 1] << 16), qv(x[2 * e2 + 1] & 0xFFFF0000u));
+      }
+      sched_fence();   // keeps the second pass's loads from piling up in registers
+    }
+  };
+
+  TileInfo ti = walk.next(a);   // page of step 0
+  quant_q(ti);
+  lds_barrier();   // the prologue's loads of step 0 have landed
+  const int row = 32 * rh + n;
+  for (int k = 0; k <= n_steps; ++k) {
+    if (k < n_steps) {
+      const int par = k & 1;
+      const LDS_AS uint8_t* cur = buf(k);
+      if (ti.first) {
+        // another sequence of this unit: its query row (a reload in the
+        // middle of the step, once the MFMAs have read the registers, spills)
+        if (k > 0) quant_q(ti);
+        m_run = -INFINITY;
+        l_run = 0.f;
+        row_tok = min(row0 + row, max(ti.rows - 1, 0)) / p.num_heads;
+      }
+      // the partner's reference of the previous step, read ahead of its use
+      const float pm = ti.first ? -INFINITY : mpub[((par ^ 1) * 2 + (kh ^ 1)) * 64 + row];
+      // ---- QK GEMM: S^T[32 keys of half kh, 32 rows of half rh], 9 k-steps
+      f32x16 s = f32x16{};
+      {
+        constexpr int NR = 2 * kNk8;   // read i: k-step i / 2, half i % 2
+        constexpr int D = SO_KD < NR ? SO_KD : NR;
+        auto kread = [&](int i) { return ld128u(cur + k_lane[i & 1] + (i >> 1) * 4096); };
+        u32x4 kr[D];
+#pragma unroll
+        for (int i = 0; i < D; ++i) kr[i] = kread(i);
+#pragma unroll
+        for (int cc = 0; cc < kNk8; ++cc) {
+          const i32x8 kf = cat8(kr[(2 * cc) % D], kr[(2 * cc + 1) % D]);
+          if (2 * cc + D < NR) kr[(2 * cc) % D] = kread(2 * cc + D);
+          if (2 * cc + 1 + D < NR) kr[(2 * cc + 1) % D] = kread(2 * cc + 1 + D);
+          s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, q8[cc], s, 0, 0, 0, 127, 0, 127);
+          sched_fence();
+        }
+      }
+      // ---- scores (lane (n, h): keys 32 kh + 8 jj + 4 h + e of row 32 rh + n);
+      //      the per-token scales past a page's valid keys repeat the last
+      //      valid one, so every scale is finite
+      f32x4 ksc[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        ksc[jj] = *(const LDS_AS f32x4*)(cur + kFp8TileBytes + (32 * kh + 8 * jj + 4 * h) * 4);
+      float sv[16];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[4 * jj + e] = s[4 * jj + e] * (qsc * ksc[jj][e]);
+
+      // the record of the next page
+      TileInfo nti = ti;
+      if (k + 1 < n_steps) nti = walk.next(a);
+
+      const int step_key0 = ti.t * kPage;
+      if (__builtin_expect((step_key0 + kPage) > (ti.L - ti.qlen + 1), 0)) {
+        const int vis = ti.L - ti.qlen + row_tok + 1;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (step_key0 + 32 * kh + 8 * jj + 4 * h + e >= vis) sv[4 * jj + e] = -INFINITY;
+      }
+      // ---- softmax, P' to E4M3
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+      mx = max_xor32(mx);
+      // adopt the partner's reference of the previous step; a raise goes to
+      // the new maximum rounded up to a whole number
+      const float base = fmaxf(m_run, pm);
+      const float m_new = (mx > base + kRescaleThreshold) ? ceilf(mx) : base;
+      if (m_new != m_run) {
+        l_run = m_run == -INFINITY ? 0.f : l_run * ldexpf(1.f, (int)(m_run - m_new));
+        m_run = m_new;
+      }
+      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+      float pp[16];
+      float pmax = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pr = exp2_fast(sv[4 * jj + e] - m_ref);
+          l_run += pr;
+          pp[4 * jj + e] = pr * ksc[jj][e];
+          pmax = fmaxf(pmax, pp[4 * jj + e]);
+        }
+      pmax = max_xor32(pmax);
+      // block scale 2^e with pmax / 2^e in [128, 256)
+      int ex = pmax > 0.f ? (int)((__builtin_bit_cast(unsigned, pmax) >> 23) & 255u) - 126 - 8 : 0;
+      ex = min(max(ex, -126), 126);
+      const float inv = __builtin_bit_cast(float, (unsigned)(127 - ex) << 23);
+      LDS_AS uint8_t* const prow = p8 + par * kP8Bytes + row * kPStride8 + 32 * kh + 4 * h;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *(LDS_AS int*)(prow + 8 * jj) =
+            pack_fp8x4(pp[4 * jj] * inv, pp[4 * jj + 1] * inv, pp[4 * jj + 2] * inv, pp[4 * jj + 3] * inv);
+      if (h == 0) {
+        psc[par * 2 * kRowsSo + row * 2 + kh] = (uint8_t)(127 + ex);
+        mpub[(par * 2 + kh) * 64 + row] = m_run;
+      }
+      if (ti.last) {
+        const float lt = sum_xor32(l_run);
+        if (h == 0) lpub[(par * 2 + kh) * 64 + row] = lt;
+      }
+      ti = nti;
+    }
+    lds_barrier();
+  }
+}
+
 }  // namespace so
 
 MLA_PAGE_VIOLATIONS_ACCESSOR(page_violations_so)
 
 hipError_t launch_decode_so(const DecodeParams& p, int grid_units, hipStream_t s, hipEvent_t ev_start,
-                            hipEvent_t ev_stop) {
+                            hipEvent_t ev_stop, bool fp8_mma) {
   const int rb = (p.rows + so::kRowsSo - 1) / so::kRowsSo;
   dim3 grid(((grid_units + 7) / 8) * 8 * rb);
   KernelArgs a;
@@ -715,7 +1138,7 @@ hipError_t launch_decode_so(const DecodeParams& p, int grid_units, hipStream_t s
   a.qptr = p.q;
   a.kv = p.kv;
   const bool fp8 = p.kv_scale != nullptr;
-  auto kern = fp8 ? so::decode_kernel_so<true> : so::decode_kernel_so<false>;
+  auto kern = fp8_mma ? so::decode_kernel_so8 : fp8 ? so::decode_kernel_so<true> : so::decode_kernel_so<false>;
   if (ev_start || ev_stop)
     hipExtLaunchKernelGGL(kern, grid, dim3(so::kThreadsSo), 0, s, ev_start, ev_stop, 0, a.p, a.md, a.prefix,
                           a.split_off, a.seqlens, a.block_table, a.qptr, a.kv);

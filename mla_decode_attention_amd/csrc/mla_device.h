@@ -519,6 +519,27 @@ __device__ __forceinline__ int lds8_byte(int key, int chunk) {
   return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz2(key)) << 4);
 }
 
+// The fp8 matrix-core kernels' tile: the E4M3 layout with swizzle
+// (k2, k2^k3) (high to low bit), under which both of their operand reads -- 16
+// consecutive keys x 4 chunk pairs (K, 16-byte reads) and 8 key pairs x 2
+// chunks (V^T, transposed 8-byte reads) -- measure free of LDS bank conflicts
+// on gfx950, where the shared fp8 layout's (k2, k3) conflicts on the K reads.
+__device__ __forceinline__ int swz2q(int key) { return (((key >> 2) & 1) << 1) | (((key >> 2) ^ (key >> 3)) & 1); }
+__device__ __forceinline__ int lds8q_byte(int key, int chunk) {
+  return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz2q(key)) << 4);
+}
+
+// 32 bytes of fp8 operand from two 16-byte halves; four floats -> four E4M3
+// codes (RNE; the caller keeps them within +-448)
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+__device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+__device__ __forceinline__ u32x4 ld128u(const LDS_AS uint8_t* p) { return *(const LDS_AS u32x4*)p; }
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+}
 __device__ __forceinline__ i32x2 tr8_read(const LDS_AS uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)p);
 }

@@ -70,8 +70,9 @@ int variant_rows(int variant);
 hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s,
                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // 64-row kernel with score and output waves (mla_decode_so.hip), uniform q_len.
+// fp8_mma: the fp8 cache on fp8 MFMA (queries and P in E4M3).
 hipError_t launch_decode_so(const DecodeParams& p, int grid_units, hipStream_t s, hipEvent_t ev_start = nullptr,
-                            hipEvent_t ev_stop = nullptr);
+                            hipEvent_t ev_stop = nullptr, bool fp8_mma = false);
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int units, int min_tiles, int seq_cost,
                            int32_t* md, hipStream_t s, hipEvent_t ev_start = nullptr,
                            hipEvent_t ev_stop = nullptr);

@@ -43,7 +43,8 @@
 //                        with score and output waves runs instead
 //                        (mla_decode_so.hip).
 //   Q8         (fp8 cache, mla_decode_fwd_fp8mma): queries and P in E4M3 on
-//                        fp8 MFMA, 64 rows, 8 waves.
+//                        fp8 MFMA, 64 rows, score and output waves
+//                        (decode_kernel_so8 in mla_decode_so.hip).
 // (The prefill / extend kernel is in mla_prefill.hip.)
 //
 // Split-KV: work units of equal tile count over the flattened
@@ -1019,89 +1020,8 @@ void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int
   }
 }
 
-// ---------------------------------------------------------------------------
-// Q8 (fp8 cache on fp8 MFMA): both contractions run on E4M3 operands. P goes
-// to FP8 and meets an FP8 V with one dequantisation of the product, the
-// scheme PaddleNLP issue #10157 gives for SageAttention2 (quantization
-// section); here the query rows are quantised to E4M3 as well.
-// It trades accuracy (about 5% of max|O| on random data, see the tests) for
-// half the operand bytes and twice the MFMA rate of the bf16 path.
-//   Query rows: per-row scale sq = max|q| / 448, q8 = E4M3(q / sq) (RNE, the
-//   rule of the cache's per-token codes), held in registers for the sequence. Keys and values stay in the cache's E4M3
-//   codes; the per-token scale s_j multiplies the score and the P weight.
-//   QK: wave w has row quarter rq = w%4 (16 rows) and key half kh = w/4 (32
-//   keys); S^T[16 keys, 16 rows] blocks on v_mfma_scale_f32_16x16x128_f8f6f4
-//   (unit scales), five k-steps of 128 features (the last one is the 64 rope
-//   features, zero-padded). No partial sums cross waves.
-//   Softmax: base-2 online softmax as in the bf16 kernels (lazy rescale,
-//   optimistic P, raise flag). P'_j = P_j * s_j is quantised per (row,
-//   32-key block) with a power-of-two scale 2^e chosen so the block max lands
-//   in [128, 256); the E8M0 byte 127 + e is the B-operand block scale of the
-//   PV MFMA, which multiplies it back exactly.
-//   PV: wave w accumulates O^T[64 features 64w.., 64 rows] on
-//   v_mfma_scale_f32_32x32x64_f8f6f4: V^T comes from the fp8 tile through
-//   ds_read_b64_tr_b8 (16-lane groups: lane i receives byte i%8 of the chunks
-//   read by lanes 2j + i/8, j = 0..7, i.e. 8 keys of one feature), P^T from
-//   the P8 buffer. In a 32x32x64 operand, bytes 0-15 of lane (n, h) belong to
-//   k-block 0 and bytes 16-31 to k-block 1, and lane n + 32kb supplies the
-//   scale of block kb: lane (n, h) holds keys 16h..16h+15 (block 0) and
-//   32+16h.. (block 1), so block kb is exactly the 32 keys of key half kb.
-//   fp8 tile layout in LDS: chunk c (16 bytes, features 16c..16c+15) of key k
-//   at ((c/4) * 64 + k) * 64 + ((c%4) ^ swz2q(k)) * 16, swz2q(k) = (k2,
-//   k2^k3) (high to low bit), chosen by measuring the LDS bank-conflict
-//   counter on both operand reads of this kernel (the LDS's bank selection
-//   hashes address bits, so a plain row/bank analysis does not predict it).
-// ---------------------------------------------------------------------------
-constexpr int kQ8PStride = 80;     // bytes per row of the P8 buffer: 64 keys + pad (conflict-free rows)
-constexpr int kQ8TileBytes = kFp8TileBytes + kPage * 4;   // codes + per-token scales
-
-typedef __attribute__((ext_vector_type(8))) int i32x8;
-
-// The fp8 matrix-core kernel's tile: the E4M3 layout with swizzle
-// (k2, k2^k3) (high to low bit), under which both of its operand reads -- 16
-// consecutive keys x 4 chunk pairs (K, 16-byte reads) and 8 key pairs x 2
-// chunks (V^T, transposed 8-byte reads) -- measure free of LDS bank conflicts
-// on gfx950, where the shared fp8 layout's (k2, k3) conflicts on the K reads.
-__device__ __forceinline__ int swz2q(int key) { return (((key >> 2) & 1) << 1) | (((key >> 2) ^ (key >> 3)) & 1); }
-__device__ __forceinline__ int lds8q_byte(int key, int chunk) {
-  return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz2q(key)) << 4);
-}
-
-// One fp8 page into the Q8 tile layout, 512 threads. Load i of thread t fills
-// LDS slot 512i + t = (line group, key, position) = (2i + t/256, (t/4)%64, t%4),
-// so the key and position of a thread are the same for every load and the
-// load offset is a multiple of 128 bytes; keys past nvalid re-read the last
-// valid key. The last load is made by waves 0-3 only. Wave 0 also loads the
-// page's 64 per-token scales after the codes.
-struct TileDmaQ8 {
-  static constexpr int kLoads = kFp8LoadsX;
-  const uint8_t* page;
-  const uint8_t* scale;
-  uint32_t voff, lds0, sc_lds, sc_off;
-  int tid;
-  __device__ __forceinline__ void plan(const uint8_t* kv, const float* kv_scale, int page_id, int nvalid,
-                                       LDS_AS uint8_t* buf, LDS_AS float* /*sbuf*/, int t) {
-    page = kv + (size_t)page_id * kFp8TileBytes;
-    scale = (const uint8_t*)(kv_scale + (size_t)page_id * kPage);
-    tid = t;
-    const int key = (t >> 2) & 63, pos = t & 3;
-    const int src_key = key < nvalid ? key : nvalid - 1;
-    voff = src_key * kFp8RowBytes + 64 * (t >> 8) + 16 * (pos ^ swz2q(key));
-    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (t & ~63) * 16));
-    sc_lds = (uint32_t)uniform((int)(uintptr_t)(buf + kFp8TileBytes));
-    const int lane = t & 63;
-    sc_off = 4 * (lane < nvalid ? lane : nvalid - 1);
-  }
-  __device__ __forceinline__ void load(int i) const {
-    if (i * kThreadsX + (tid & ~63) >= kFp8SlotsX) return;   // wave-uniform
-    // (readfirstlane: should the plan pass through a phi the compiler cannot
-    // prove uniform, M0's source stays scalar)
-    dma16(voff, page + 128 * i, (uint32_t)uniform((int)(lds0 + i * kThreadsX * 16)));
-    if (i == 0 && tid < 64) dma4(sc_off, scale, (uint32_t)uniform((int)sc_lds));
-  }
-  template <int I>
-  __device__ __forceinline__ void load_ct() const { load(I); }
-};
+// An fp8 page in LDS with its 64 per-token scales after the codes.
+constexpr int kQ8TileBytes = kFp8TileBytes + kPage * 4;
 
 // The same page layout from 256 threads (waves 0-3 of the 64-row fp8 kernel):
 // load j of thread t fills LDS slot 256j + t, i.e. line group j, key
@@ -1136,337 +1056,10 @@ struct TileDmaQ8Half {
 };
 static_assert(TileDmaQ8Half::kLoads * 256 * 16 == kFp8TileBytes, "fp8 tile must split evenly");
 
-__device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
-  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-__device__ __forceinline__ u32x4 ld128u(const LDS_AS uint8_t* p) { return *(const LDS_AS u32x4*)p; }
-// four floats -> four E4M3 codes (RNE, saturating to +-448 by the caller's range)
-__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
-}
-
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void decode_kernel_q8(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
-    const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
-    const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
-    const uint8_t* __restrict__ kv_) {
-  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
-  constexpr int ROWS_WG = 64;
-  constexpr int NK = 5;                      // k-steps of 128 features (the last: rope + zeros)
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kQ8TileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kQ8TileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t p8[ROWS_WG * kQ8PStride];
-  __shared__ __attribute__((aligned(16))) float smax[2 * ROWS_WG];   // [key half][row]
-  __shared__ __attribute__((aligned(16))) float ssum[2 * ROWS_WG];   // [key half][row]
-  __shared__ uint8_t pscale[ROWS_WG * 2];                            // E8M0 [row][key half]
-  __shared__ int raise_flag;
-  LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
-  LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
-  LDS_AS uint8_t* const pb8 = (LDS_AS uint8_t*)(p8);
-  LDS_AS float* const smx = (LDS_AS float*)(smax);
-  LDS_AS float* const ssm = (LDS_AS float*)(ssum);
-  LDS_AS uint8_t* const psc = (LDS_AS uint8_t*)(pscale);
-  LDS_AS int* const flag = (LDS_AS int*)(&raise_flag);
-
-  const DecodeParams& p = a.p;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = uniform(tid >> 6);
-  const int rq = wave & 3, kh = wave >> 2;
-  const int n16 = lane & 15, g = lane >> 4;      // QK / softmax lane roles
-  const int n = lane & 31, h = lane >> 5;        // PV lane roles
-  const int R = p.rows;
-  const WgCoord wc = wg_coord((R + ROWS_WG - 1) / ROWS_WG);
-  if (wc.unit >= p.grid_units) return;
-  const int row0 = wc.rb * ROWS_WG;
-  const int rs = 16 * rq + n16;                   // softmax row within the workgroup
-  const int row_qk = row0 + rs;
-  const int u = wc.unit;
-
-  UnitT<false> unit;
-  if (!unit.init(a, u)) {
-    if (!a.md) write_empty(p, unit.b0, row0, row0 + ROWS_WG, kThreadsX / 64);
-    return;
-  }
-  if (tid == 0) *flag = -1;
-
-  // ---- per-lane constant LDS offsets
-  // QK operand of key block kb, half e of the 32 bytes: key 32kh + 16kb + n16,
-  // chunk 2g + e (+ 8 chunks = 8192 bytes per k-step)
-  int k_lane[2][2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) k_lane[kb][e] = lds8q_byte(32 * kh + 16 * kb + n16, 2 * g + e);
-  // V^T transposed reads: 16-lane group gi covers features 64w + 32fb + 16(gi%2)
-  // + 0..15 and key half h = gi/2; as a source, lane i reads key
-  // kbase + i/2 (kbase = 32(r/2) + 16h + 8(r%2) for read r) at byte 8(i%2) of
-  // chunk 4w + 2fb + gi%2. Offsets for r%2 = 0/1; r/2 adds 32 keys = 2048 bytes.
-  int v_lane[2][2];   // [fb][r % 2]
-  {
-    const int gi = lane >> 4, i = lane & 15;
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-      for (int r1 = 0; r1 < 2; ++r1)
-        v_lane[fb][r1] = lds8q_byte(16 * (gi >> 1) + 8 * r1 + (i >> 1), 4 * wave + 2 * fb + (gi & 1)) + 8 * (i & 1);
-  }
-
-  i32x8 q8[NK];
-  float qscale = 0.f;                        // sq * softmax_scale * log2(e) of row_qk
-  f32x16 o[2][2];                            // [feature block][row half]
-#pragma unroll
-  for (int fb = 0; fb < 2; ++fb) {
-    o[fb][0] = f32x16{};
-    o[fb][1] = f32x16{};
-  }
-  float m_pv[2] = {-INFINITY, -INFINITY};    // running max of rows row0 + n, row0 + 32 + n
-  float m_sm = -INFINITY;                    // running max of row_qk (same values, softmax lanes)
-  float l_run = 0.f;                         // partial row sum of row_qk (this key half, lane group)
-  bool restart = true;
-  int row_tok = 0;
-
-  TileDmaQ8 dma;
-  TileInfo next = unit.prepare(a, unit.f_begin, buf0, nullptr, tid, dma);
-  if (row0 < next.rows) dma_all(dma);
-
-  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
-    const TileInfo ti = next;
-    const int t = ti.t, L = ti.L;
-    const bool skip = row0 >= ti.rows;
-    const LDS_AS float* const sbc = (const LDS_AS float*)(cur + kFp8TileBytes);
-
-    if (ti.first && !skip) {
-      // query row -> E4M3 with a per-row scale; lane (n16, g) holds features
-      // 128c + 32g + 0..31 of k-step c (k-step 4: rope, lanes g >= 2 zero)
-      const int rr = row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0);
-      const u32x4* qrow = (const u32x4*)(a.qptr + (size_t)min(ti.qrow0 + rr, p.q_rows - 1) * kDqk);
-      const bool live = row_qk < ti.rows;
-      // two passes over the row (the second load hits the cache): the max,
-      // then the codes, so the row is never held in registers as floats
-      auto qword = [&](int c, int part) {
-        return (live && (c < NK - 1 || g < 2)) ? qrow[16 * c + 4 * g + part] : u32x4{0u, 0u, 0u, 0u};
-      };
-      float amax = 0.f;
-#pragma unroll
-      for (int c = 0; c < NK; ++c)
-#pragma unroll
-        for (int part = 0; part < 4; ++part) {
-          const u32x4 w = qword(c, part);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, w[e] << 16)),
-                                     fabsf(__builtin_bit_cast(float, w[e] & 0xFFFF0000u))));
-        }
-      amax = max_xor16(amax);
-      amax = max_xor32(amax);
-      // the cache's per-token rule: sq = max|q| / 448, code = E4M3(clamp(q / sq))
-      // with an IEEE division (the quotient may exceed 448 by a rounding)
-      const float sq = amax > 0.f ? amax / 448.0f : 1.0f;
-      auto qv = [&](unsigned bits) { return fminf(fmaxf(__builtin_bit_cast(float, bits) / sq, -448.0f), 448.0f); };
-#pragma unroll
-      for (int c = 0; c < NK; ++c)
-#pragma unroll
-        for (int part = 0; part < 4; ++part) {
-          const u32x4 w = qword(c, part);
-#pragma unroll
-          for (int e2 = 0; e2 < 2; ++e2)
-            q8[c][2 * part + e2] = pack_fp8x4(qv(w[2 * e2] << 16), qv(w[2 * e2] & 0xFFFF0000u),
-                                              qv(w[2 * e2 + 1] << 16), qv(w[2 * e2 + 1] & 0xFFFF0000u));
-        }
-      qscale = sq * p.scale_log2;
-      m_pv[0] = m_pv[1] = m_sm = -INFINITY;
-      restart = true;
-      row_tok = rr / p.num_heads;
-    }
-    const bool final_out = ti.final_out;
-    const int slot = ti.slot;
-
-    const bool more = f + 1 < unit.f_end;
-    if (more) next = unit.prepare(a, f + 1, nxt, nullptr, tid, dma);
-    wait_tile();
-    const bool load_next = more && row0 < next.rows;
-    if (skip) {
-      if (load_next) dma_all(dma);
-      return;
-    }
-
-    // ---- QK: S^T[16 keys of block kb, 16 rows of quarter rq], k-steps c
-    f32x4 acc[2] = {f32x4{}, f32x4{}};
-    auto qk = [&](auto with_loads) {
-#pragma unroll
-      for (int i = 0; i < 2 * NK; ++i) {
-        const int c = i >> 1, kb = i & 1;
-        i32x8 kf;
-        if (c < NK - 1 || g < 2)
-          kf = cat8(ld128u(cur + k_lane[kb][0] + c * 8192), ld128u(cur + k_lane[kb][1] + c * 8192));
-        else
-          kf = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        acc[kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, q8[c], acc[kb], 0, 0, 0, 127, 0, 127);
-        if constexpr (decltype(with_loads)::value) dma_slot_ct<2 * NK>(dma, i);
-      }
-    };
-    if (load_next) qk(std::true_type{});
-    else qk(std::false_type{});
-
-    // ---- softmax on 8 scores per lane: row rs, keys 32kh + 16kb + 4g + j
-    float sv[8], ks[8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const f32x4 s4 = *(const LDS_AS f32x4*)(sbc + 32 * kh + 16 * kb + 4 * g);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ks[4 * kb + j] = s4[j];
-        sv[4 * kb + j] = acc[kb][j] * (qscale * s4[j]);
-      }
-    }
-    const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
-    if (__builtin_expect(need_mask, 0)) {
-      const int vis = L - ti.qlen + row_tok + 1;
-      const int key0 = t * kPage + 32 * kh + 4 * g;
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (key0 + 16 * (r >> 2) + (r & 3) >= vis) sv[r] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sv[r]);
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    if (g == 0) smx[kh * 64 + rs] = mx;
-    if (!restart && __builtin_amdgcn_ballot_w64(mx > m_sm + kRescaleThreshold) && lane == 0) *flag = f;
-
-    float l_tile = 0.f;
-    auto make_p = [&](float m_ref) {
-      float pp[8];
-      float pm = 0.f;
-      l_tile = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float pr = exp2_fast(sv[r] - m_ref);
-        l_tile += pr;
-        pp[r] = pr * ks[r];
-        pm = fmaxf(pm, pp[r]);
-      }
-      pm = max_xor16(pm);
-      pm = max_xor32(pm);
-      // block scale 2^e with pm / 2^e in [128, 256)
-      int e = pm > 0.f ? (int)((__builtin_bit_cast(unsigned, pm) >> 23) & 255u) - 126 - 8 : 0;
-      e = min(max(e, -126), 126);
-      const float inv = __builtin_bit_cast(float, (unsigned)(127 - e) << 23);
-      LDS_AS uint8_t* const prow = pb8 + rs * kQ8PStride + 32 * kh + 4 * g;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        *(LDS_AS int*)(prow + 16 * kb) =
-            pack_fp8x4(pp[4 * kb] * inv, pp[4 * kb + 1] * inv, pp[4 * kb + 2] * inv, pp[4 * kb + 3] * inv);
-      if (g == 0) psc[rs * 2 + kh] = (uint8_t)(127 + e);
-    };
-    if (!restart) make_p((m_sm == -INFINITY) ? 0.0f : m_sm);
-    lds_barrier();
-
-    if (restart || uniform(*flag) == f) {
-      // some row's max moved (or a sequence starts): new running maxima for
-      // the PV rows (n, 32 + n) and the softmax row, from the half maxima
-      float alpha[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float tmax = fmaxf(smx[32 * rb + n], smx[64 + 32 * rb + n]);
-        const float m_new = fmaxf(m_pv[rb], tmax);
-        const bool raise = m_new > m_pv[rb] + kRescaleThreshold;
-        alpha[rb] = restart ? 0.0f : raise ? exp2_fast(m_pv[rb] - m_new) : 1.0f;
-        if (raise) m_pv[rb] = m_new;
-      }
-      {
-        const float tmax = fmaxf(smx[rs], smx[64 + rs]);
-        const float m_new = fmaxf(m_sm, tmax);
-        const bool raise = m_new > m_sm + kRescaleThreshold;
-        const float al = restart ? 0.0f : raise ? exp2_fast(m_sm - m_new) : 1.0f;
-        if (raise) m_sm = m_new;
-        l_run *= al;
-      }
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb) {
-        o[fb][0] *= alpha[0];
-        o[fb][1] *= alpha[1];
-      }
-      make_p((m_sm == -INFINITY) ? 0.0f : m_sm);
-      lds_barrier();
-    }
-    restart = false;
-    l_run += l_tile;
-
-    // ---- PV: O^T[64 features of this wave, 64 rows] += V^T . P'^T (block-scaled)
-    {
-      i32x8 pf[2];
-      int psb[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const LDS_AS uint8_t* prow = pb8 + (32 * rb + n) * kQ8PStride + 16 * h;
-        pf[rb] = cat8(ld128u(prow), ld128u(prow + 32));
-        psb[rb] = psc[(32 * rb + n) * 2 + h];
-      }
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb) {
-        i32x8 vf;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const i32x2 x = tr8_read(cur + v_lane[fb][r & 1] + (r >> 1) * 2048);
-          vf[2 * r] = x[0];
-          vf[2 * r + 1] = x[1];
-        }
-        o[fb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf[0], o[fb][0], 0, 0, 0, 127, 0, psb[0]);
-        o[fb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf[1], o[fb][1], 0, 0, 0, 127, 0, psb[1]);
-      }
-    }
-
-    if (!ti.last) return;
-
-    // ---- epilogue for this sequence
-    float lh = sum_xor16(l_run);
-    lh = sum_xor32(lh);
-    if (g == 0) ssm[kh * 64 + rs] = lh;
-    lds_barrier();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int row = row0 + 32 * rb + n;
-      const float l_row = ssm[32 * rb + n] + ssm[64 + 32 * rb + n];
-      const bool live = l_row > 0.f;
-      const float inv = live ? 1.0f / l_row : 0.f;
-      if (row < ti.rows) {
-        float* dst_o;
-        float* dst_l;
-        if (final_out) {
-          dst_o = p.out + ((size_t)ti.qrow0 + row) * kDv;
-          dst_l = p.lse + (size_t)ti.qrow0 + row;
-        } else {
-          dst_o = p.ws_out + ((size_t)slot * R + row) * kDv;
-          dst_l = p.ws_lse + (size_t)slot * R + row;
-        }
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            f32x4 v = {o[fb][rb][4 * jj], o[fb][rb][4 * jj + 1], o[fb][rb][4 * jj + 2], o[fb][rb][4 * jj + 3]};
-            *(f32x4*)(dst_o + 64 * wave + 32 * fb + 8 * jj + 4 * h) = v * inv;
-          }
-        }
-        if (wave == 0 && h == 0)
-          *dst_l = live ? (m_pv[rb] + log2_fast(l_row)) * kLn2 : -INFINITY;
-      }
-    }
-  };
-
-  for (int f = unit.f_begin; f < unit.f_end; f += 2) {
-    step(f, buf0, buf1);
-    if (f + 1 < unit.f_end) step(f + 1, buf1, buf0);
-  }
-}
-
 
 // ---------------------------------------------------------------------------
 // WIDE64X on an fp8 cache without widening the page in LDS: the E4M3 tile
-// stays in LDS (the Q8 layout), and each MFMA operand is widened exactly to
+// stays in LDS (the shared fp8 layout), and each MFMA operand is widened exactly to
 // bf16 in registers right after its LDS read (v_cvt_scalef32_pk_bf16_fp8,
 // scale 1). K: one 16-byte read feeds two k-steps. V^T: ds_read_b64_tr_b8
 // gives a lane 8 consecutive keys of one feature, so the PV k-slot 8h + e is
@@ -2205,6 +1798,8 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
                          hipEvent_t ev_start, hipEvent_t ev_stop) {
   // uniform q_len over 16 rows: the kernel with score and output waves
   if (variant == VAR_WIDE64X && !p.cu_q) return launch_decode_so(p, grid_units, s, ev_start, ev_stop);
+  // the fp8 cache on fp8 MFMA (uniform q_len only)
+  if (variant == VAR_Q8) return p.cu_q ? hipErrorInvalidValue : launch_decode_so(p, grid_units, s, ev_start, ev_stop, true);
   const int rb = (p.rows + variant_rows(variant) - 1) / variant_rows(variant);
   // 64-row kernels: 1-D grid, units padded to a multiple of 8 (see wg_coord)
   const bool wide = variant == VAR_WIDE64X || variant == VAR_Q8;
@@ -2235,8 +1830,6 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
   if (variant == VAR_NARROW16) {
     if (fp8) MLA_LAUNCH(decode_kernel_pc8, 2 * kThreads);
     else MLA_LAUNCH(decode_kernel_pc, 2 * kThreads);
-  } else if (variant == VAR_Q8) {
-    MLA_LAUNCH(decode_kernel_q8, kThreadsX);
   } else {
     if (fp8) MLA_LAUNCH(decode_kernel_xf, kThreadsX);
     else MLA_LAUNCH(decode_kernel_x, kThreadsX);

@@ -25,7 +25,7 @@ from .mla_oracle import (  # noqa: F401
     bf16_bits_to_f64, e4m3fn_value, E4M3FN_TABLE, decode_e4m3fn,
     sequence_rows, visible_counts, attend, attend_partials, lse_merge,
     mla_decode, mla_decode_sequence, mla_decode_varlen,
-    E4M3FN_MAX, encode_e4m3fn, quantize_token_e4m3, append_kv, quantize_query_rows_e4m3,
+    E4M3FN_MAX, encode_e4m3fn, quantize_token_e4m3, append_kv, quantize_query_rows_e4m3, query_row_exponent,
     D_NOPE, D_ROPE, D_QK_PREFILL, D_V_PREFILL, mla_prefill,
 )
 from . import prefill_quant  # noqa: F401,E402

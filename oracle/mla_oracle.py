@@ -293,20 +293,39 @@ def append_kv(latent_bits, block_table, seqlens, cache, kv_scale=None, kv_dtype=
     return cache, kv_scale
 
 
+def query_row_exponent(amax) -> int:
+    """The exponent k of a query row's power-of-two scale: the smallest
+    integer with max|row| <= 448 * 2^k, never below -126 (rows whose maximum
+    lies under 448 * 2^-127 keep k = -126)."""
+    amax = float(amax)
+    if amax <= 0.0:
+        return 0
+    m, e = np.frexp(amax)                 # amax = m * 2^e, m in [0.5, 1)
+    k = int(e) - 1 - 8                    # 2^(e-1) <= amax < 2^e; 448 = 1.75 * 2^8
+    while amax > E4M3FN_MAX * 2.0 ** k:
+        k += 1
+    while k > -126 and amax <= E4M3FN_MAX * 2.0 ** (k - 1):
+        k -= 1
+    return max(k, -126)
+
+
 def quantize_query_rows_e4m3(q_bits) -> np.ndarray:
     """E4M3 image of the query rows for a decode that runs the contractions on
     FP8 operands (PaddleNLP issue #10157, quantization section: SageAttention2
-    quantises the attention operands dynamically and dequantises the products
-    once). Each row of 576 values is quantised like a cache token:
-    quantize_token_e4m3 (scale = max|row| / 448 in fp32, nearest-even codes);
-    returns scale * value(code) as float64, shape of q_bits (bf16 bits)."""
-    q = bf16_bits_to_f64(q_bits).astype(np.float32)
-    flat = q.reshape(-1, q.shape[-1])
+    quantises the attention operands dynamically, one scale per block of
+    values, and dequantises the products once; the form of the scale is left
+    open there). Each row of 576 values gets a power-of-two scale 2^k, k from
+    query_row_exponent (the E8M0 form of the fp8 matrix cores' block scales),
+    and nearest-even E4M3FN codes of x * 2^-k (exact products, |x| 2^-k <= 448);
+    returns 2^k * value(code) as float64, shape of q_bits (bf16 bits)."""
+    x = bf16_bits_to_f64(q_bits)
+    flat = x.reshape(-1, x.shape[-1])
     out = np.empty(flat.shape, dtype=np.float64)
     for r in range(flat.shape[0]):
-        codes, sc = quantize_token_e4m3(flat[r])
-        out[r] = decode_e4m3fn(codes) * np.float64(sc)
-    return out.reshape(q.shape)
+        k = query_row_exponent(np.max(np.abs(flat[r])))
+        codes = encode_e4m3fn(flat[r] * 2.0 ** -k)
+        out[r] = decode_e4m3fn(codes) * 2.0 ** k
+    return out.reshape(x.shape)
 
 
 # --------------------------------------------------------------------------

@@ -478,35 +478,56 @@ def test_varlen_uniform_q_len_equals_batched_call():
 # ------------------------------------------- E4M3 image of the query rows
 
 def test_query_quantisation_worked_example():
-    """Row max 1.0 -> scale 1/448 (fp32); 0.3 * 448 = 134.4 lies between the
-    E4M3 codes 128 and 144 (spacing 16 in [128, 256)), so it maps to 128/448;
-    -1.0 maps to -448 * scale exactly; 0 stays 0."""
+    """Row max 1.0: the smallest 2^k with 1.0 <= 448 * 2^k is 2^-8 (448 * 2^-9
+    = 0.875 is too small); bf16(0.3) = 0.30078125 scales to 77.0, between the
+    E4M3 codes 72 and 80 (spacing 8 in [64, 128)), so it maps to 80 * 2^-8;
+    -1.0 maps to -256 * 2^-8 exactly; 0 stays 0. A row max of 1.875 (mantissa
+    above 1.75) needs 2^-7: 1.875 * 2^7 = 240 is a code, 1.875 * 2^8 = 480
+    exceeds 448; bf16(0.1) * 2^7 = 12.8125 rounds to 13."""
     row = np.zeros(576, dtype=np.float32)
     row[0], row[1], row[2] = 1.0, 0.3, -1.0
     got = oracle.quantize_query_rows_e4m3(_bits(row)[None])[0]
-    sc = np.float64(np.float32(np.float32(1.0) / np.float32(448.0)))
-    assert got[0] == 448 * sc and got[2] == -448 * sc
-    assert got[1] == 128 * sc
+    assert got[0] == 1.0 and got[2] == -1.0
+    assert got[1] == 80 / 256
     assert np.all(got[3:] == 0)
+    assert oracle.query_row_exponent(1.0) == -8
+    row2 = np.zeros(576, dtype=np.float32)
+    row2[5], row2[6] = 1.875, 0.1
+    got2 = oracle.quantize_query_rows_e4m3(_bits(row2)[None])[0]
+    assert oracle.query_row_exponent(1.875) == -7
+    assert got2[5] == 1.875 and got2[6] == 13 / 128
+    # 448 * 2^k itself keeps k; anything above moves to k + 1
+    assert oracle.query_row_exponent(448.0) == 0 and oracle.query_row_exponent(448.0 * (1 + 2 ** -7)) == 1
+    # the floor: tiny rows keep k = -126
+    assert oracle.query_row_exponent(1e-40) == -126
 
 
-def test_query_quantisation_bound_and_powers_of_two():
+def test_query_quantisation_against_torch_float8():
+    """Random rows (with a spread of magnitudes) against torch's own
+    float8_e4m3fn rounding (round to nearest even) of x * 2^-k, k from the
+    exact condition 448 * 2^(k-1) < max|x| <= 448 * 2^k (above the -126 floor)."""
+    import math
+    import torch
     rng = np.random.default_rng(5)
-    q = _bits(rng.standard_normal((3, 4, 576)).astype(np.float32))
-    x = oracle.bf16_bits_to_f64(q)
-    got = oracle.quantize_query_rows_e4m3(q)
+    q = rng.standard_normal((3, 4, 576)) * np.exp(rng.uniform(-20, 20, (3, 4, 1)))
+    qb = _bits(q.astype(np.float32))
+    x = oracle.bf16_bits_to_f64(qb)
+    got = oracle.quantize_query_rows_e4m3(qb)
     assert got.shape == x.shape
-    amax = np.abs(x).max(axis=-1, keepdims=True)
-    # normal-range values keep a relative error <= 2^-4 (3 mantissa bits, nearest);
-    # values below the smallest normal (2^-6 after scaling) an absolute one <= 2^-10 * scale
-    scale = amax / 448
-    err = np.abs(got - x)
-    assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale) * (1 + 1e-6))
-    # the row maximum is reproduced (up to the fp32 scale)
-    assert np.allclose(np.abs(got).max(axis=-1), amax[..., 0], rtol=1e-6)
-    # a row of powers of two with max 2^k: scale 2^k / 448 is not a power of
-    # two, but 2^j / scale for j <= k is representable when the quotient is;
-    # zero rows stay zero
+    for idx in np.ndindex(x.shape[:-1]):
+        row = x[idx]
+        amax = float(np.max(np.abs(row)))
+        k = math.ceil(math.log2(amax / 448.0))
+        k += 1 if amax > 448.0 * 2.0 ** k else 0
+        k -= 1 if amax <= 448.0 * 2.0 ** (k - 1) else 0
+        assert 448.0 * 2.0 ** (k - 1) < amax <= 448.0 * 2.0 ** k
+        ref = torch.from_numpy(row * 2.0 ** -k).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64)
+        assert np.array_equal(got[idx], ref.numpy() * 2.0 ** k), idx
+        # nearest: relative error <= 2^-4 for normal codes, absolute <= 2^-10 * 2^k below
+        err = np.abs(got[idx] - row)
+        assert np.all(err <= np.maximum(np.abs(row) * 2.0 ** -4, 2.0 ** -10 * 2.0 ** k))
+        # the largest code lands in [224, 448]
+        assert 224.0 <= np.max(np.abs(got[idx])) * 2.0 ** -k <= 448.0
     z = np.zeros((1, 576), dtype=np.float32)
     assert np.all(oracle.quantize_query_rows_e4m3(_bits(z)) == 0)
 
