@@ -302,10 +302,11 @@ void decode_kernel_so(DecodeParams p_, const int32_t* __restrict__ md_, const in
         if (i < 9) {
           dma16(voff + 64 * i, src, dst);
         } else {
-          // the page's 64 scales (lanes 0-15 of wave 4); the rest re-read
-          // them into the padding
+          // the page's 64 per-token scales (wave 4; the others re-read them
+          // into the padding), those past the valid keys repeating the last
+          // valid one, so that every scale in LDS is finite
           const uint8_t* sc = (const uint8_t*)(p.kv_scale + (size_t)plan_page * kPage);
-          dma16(16 * (lane & 15), sc, dst);
+          dma4(4 * min(lane, plan_nvalid - 1), sc, dst);
         }
       }
     };
@@ -674,8 +675,7 @@ void decode_kernel_so(DecodeParams p_, const int32_t* __restrict__ md_, const in
             const float pr = exp2_fast(sv[kb][rb][i] - m_ref);
             l_run[rb] += pr;
             if constexpr (FP8) {
-              // masked keys may carry any scale (NaN in a page's unused tail)
-              pq[i] = (__bf16)(sv[kb][rb][i] == -INFINITY ? 0.f : pr * ksc[kb][i]);
+              pq[i] = (__bf16)(pr * ksc[kb][i]);
             } else {
               pq[i] = (__bf16)pr;
             }
