@@ -385,7 +385,7 @@ def roofline_object(e, kernel_name):
 KERNEL_NAMES = {"tiny": "decode_kernel_pc", "share16": "decode_kernel_pc", "share16_fp8": "decode_kernel_pc8",
                 "mtp": "decode_kernel_so<false>",
                 "ragged": "decode_kernel_so<false>", "fp8": "decode_kernel_so<true>", "varlen": "decode_kernel_x",
-                "fp8mma": "decode_kernel_q8"}
+                "fp8mma": "decode_kernel_so8"}
 
 
 def bench_decode(args):
