@@ -384,7 +384,7 @@ def roofline_object(e, kernel_name):
 
 KERNEL_NAMES = {"tiny": "decode_kernel_pc", "share16": "decode_kernel_pc", "share16_fp8": "decode_kernel_pc8",
                 "mtp": "decode_kernel_so<false>",
-                "ragged": "decode_kernel_so<false>", "fp8": "decode_kernel_so<true>", "varlen": "decode_kernel_x",
+                "ragged": "decode_kernel_so<false>", "fp8": "decode_kernel_so<true>", "varlen": "decode_kernel_so<false>",
                 "fp8mma": "decode_kernel_so8"}
 
 

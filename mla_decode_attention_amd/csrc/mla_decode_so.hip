@@ -48,7 +48,9 @@
 // the PV GEMM, P_j into the row sum). The per-token scales past a page's valid
 // keys repeat the last valid one, so every scale in LDS is finite.
 //
-// Used for uniform q_len (no per-sequence query counts); q_len * heads > 16.
+// Used for q_len * heads > 16 rows, with one query count for all sequences or
+// per-sequence counts (a workgroup passes over sequences with no row in its
+// 64-row block).
 #include "mla_device.h"
 
 namespace mla {
@@ -126,17 +128,21 @@ __device__ __forceinline__ void wait_steps_in_flight(int steps) {
 #define CONST_AS __attribute__((address_space(4)))
 __device__ __forceinline__ int sld(const int32_t* p, size_t i) { return ((const CONST_AS int32_t*)p)[i]; }
 
-// Page walk of one work unit (uniform q_len): the flattened tiles
-// [f_begin, f_end) of the unit, one page record at a time, every fact in
-// scalar registers (read with scalar loads on a sequence change). PAGES: also
-// the page ids, from a vector register of 64 cached ids (lane i = tile
-// pc_t0 + i). Each role of wave walks the unit at its own pace: the page loads
-// ahead, the score waves at their step, the output waves one step behind.
+// Page walk of one work unit: the flattened tiles [f_begin, f_end) of the
+// unit, one page record at a time, every fact in scalar registers (read with
+// scalar loads on a sequence change). With per-sequence query counts
+// (cu_seqlens_q) a sequence with no row at the workgroup's first row row0 is
+// passed over: its pages are neither loaded nor computed. PAGES: also the page
+// ids, from a vector register of 64 cached ids (lane i = tile pc_t0 + i). Each
+// role of wave walks the unit at its own pace: the page loads ahead, the score
+// waves at their step, the output waves one step behind.
 template <bool PAGES>
 struct Walk {
-  int u, f, f_begin, f_end;
+  int u, f, f_begin, f_end, n_pages;   // n_pages: the unit's pages this workgroup computes
   int b, bfirst, blast, L;   // sequence of page f, its first flattened tile, the next sequence's, its length
   int final_out, slot;
+  int qlen, rows, qrow0;     // query tokens of sequence b, its rows, its first q / out row
+  int row0;
   int pc_t0, page_cache;     // lane i of page_cache: the page of tile pc_t0 + i of sequence b
 
   // page ids of tiles t0 .. t0 + 63 of sequence b into page_cache (a vector
@@ -150,10 +156,15 @@ struct Walk {
     page_cache = table_page(p.block_table + (size_t)b * p.max_pages, t, tiles, p.max_pages);
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
   }
+  __device__ __forceinline__ int seq_rows(const DecodeParams& p, int bb) const {
+    return p.cu_q ? (sld(p.cu_q, bb + 1) - sld(p.cu_q, bb)) * p.num_heads : p.rows;
+  }
 
-  // false if the unit has no tiles (or the metadata was not built for this call)
-  __device__ __forceinline__ bool init(const KernelArgs& a, int unit) {
+  // false if the unit has no pages for this workgroup (or the metadata was
+  // not built for this call)
+  __device__ __forceinline__ bool init(const KernelArgs& a, int unit, int r0) {
     u = unit;
+    row0 = r0;
     const DecodeParams& p = a.p;
     if (a.md) {
       const int B = p.batch;
@@ -171,12 +182,37 @@ struct Walk {
       if (f_end <= 0) return false;
       enter(a, u);
     }
-    return true;
+    n_pages = f_end - f_begin;
+    if (p.cu_q) {
+      // the pages of the unit's sequences that have rows at row0
+      n_pages = 0;
+      int ff = f, bb = b, bl = blast;
+      while (true) {
+        const int e = min(bl, f_end);
+        if (seq_rows(p, bb) > row0) n_pages += e - ff;
+        if (e >= f_end) break;
+        ff = e;
+        ++bb;
+        while (sld(a.prefix, bb + 1) <= ff) ++bb;   // sequences without tiles in between
+        bl = sld(a.prefix, bb + 1);
+      }
+      pass_over(a);
+    }
+    return n_pages > 0;
   }
   __device__ __forceinline__ void enter(const KernelArgs& a, int bb) {
     const DecodeParams& p = a.p;
     b = bb;
     L = max(sld(p.seqlens, b), 0);
+    if (p.cu_q) {
+      const int c0 = sld(p.cu_q, b);
+      qlen = sld(p.cu_q, b + 1) - c0;
+      qrow0 = c0 * p.num_heads;
+    } else {
+      qlen = p.q_len;
+      qrow0 = b * p.rows;
+    }
+    rows = qlen * p.num_heads;
     if (a.md) {
       bfirst = sld(a.prefix, b);
       blast = sld(a.prefix, b + 1);
@@ -189,7 +225,16 @@ struct Walk {
       final_out = 1;
       slot = 0;
     }
-    load_pages(a, f - bfirst);
+    if (rows > row0) load_pages(a, f - bfirst);
+  }
+  // past the pages of sequences with no row at row0 (per-sequence q_len)
+  __device__ __forceinline__ void pass_over(const KernelArgs& a) {
+    while (rows <= row0 && blast < f_end) {
+      f = blast;
+      int bb = b + 1;
+      while (sld(a.prefix, bb + 1) <= f) ++bb;
+      enter(a, bb);
+    }
   }
   // the record of page f (and with PAGES its page id and valid tokens); then
   // the next page
@@ -203,6 +248,7 @@ struct Walk {
       int bb = b + 1;
       while (sld(a.prefix, bb + 1) <= f) ++bb;   // sequences without tiles in between
       enter(a, bb);
+      if (p.cu_q) pass_over(a);
     }
     TileInfo ti;
     ti.b = b;
@@ -212,9 +258,9 @@ struct Walk {
     ti.last = f + 1 == f_end || f + 1 == blast;
     ti.final_out = final_out != 0;
     ti.slot = slot;
-    ti.qlen = p.q_len;
-    ti.rows = p.rows;
-    ti.qrow0 = b * p.rows;
+    ti.qlen = qlen;
+    ti.rows = rows;
+    ti.qrow0 = qrow0;
     page = 0;
     if (PAGES) {
       if (ti.t - pc_t0 >= 64) load_pages(a, ti.t);
@@ -255,11 +301,11 @@ void decode_kernel_so(DecodeParams p_, const int32_t* __restrict__ md_, const in
   const int u = wc.unit;
 
   Walk<false> walk;   // this wave's own step (score waves) or the step behind (output waves)
-  if (!walk.init(a, u)) {
+  if (!walk.init(a, u, row0)) {
     if (!a.md) write_empty(p, u, row0, row0 + kRowsSo, kThreadsSo / 64);
     return;
   }
-  const int n_steps = SPP * (walk.f_end - walk.f_begin);
+  const int n_steps = SPP * walk.n_pages;
   auto buf = [&](int k) { return bufs + (k % NB) * C::kBufBytes; };
 
   if (wave >= 4) {
@@ -272,7 +318,7 @@ void decode_kernel_so(DecodeParams p_, const int32_t* __restrict__ md_, const in
     // buf(j); load i of lane tt fills LDS slot 256 i + tt (one KiB per wave
     // and load).
     Walk<true> wload;   // the page loads' walk, ahead of every other
-    wload.init(a, u);
+    wload.init(a, u, row0);
     int plan_page = 0, plan_nvalid = 1, plan_hh = 0;
     uint32_t voff = 0;
     const uint8_t* src = nullptr;
@@ -824,11 +870,11 @@ void decode_kernel_so8(DecodeParams p_, const int32_t* __restrict__ md_, const i
   const int u = wc.unit;
 
   Walk<false> walk;
-  if (!walk.init(a, u)) {
+  if (!walk.init(a, u, row0)) {
     if (!a.md) write_empty(p, u, row0, row0 + kRowsSo, kThreadsSo / 64);
     return;
   }
-  const int n_steps = walk.f_end - walk.f_begin;   // one page per step
+  const int n_steps = walk.n_pages;   // one page per step
   auto buf = [&](int k) { return bufs + (k % NB) * kBufBytes8; };
 
   if (wave >= 4) {
@@ -842,7 +888,7 @@ void decode_kernel_so8(DecodeParams p_, const int32_t* __restrict__ md_, const i
     // per-token scales (wave 4; the others re-read them into the padding),
     // those past the valid keys repeating the last valid one
     Walk<true> wload;
-    wload.init(a, u);
+    wload.init(a, u, row0);
     int plan_page = 0, plan_nvalid = 1;
     uint32_t voff = 0;
     const uint8_t* src = nullptr;

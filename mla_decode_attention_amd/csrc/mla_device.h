@@ -54,18 +54,6 @@ __device__ __forceinline__ int swz3(int key) {
 __device__ __forceinline__ int lds_byte(int key, int chunk) {
   return ((chunk >> 3) * 512 + key * 8 + ((chunk ^ swz3(key)) & 7)) * 16;
 }
-// The 64-row kernel for per-sequence query counts (decode_kernel_x) keeps the
-// tile in the same arrangement under swz3x = (k1, k0^k2, k0^k3): its operand
-// fetches (32 consecutive keys at two chunks for QK; 4 keys x 4 chunks for each
-// half-wave of the transposed V read, keys 0-3 and 4-7 in the two halves)
-// measure 29% bank-conflict cycles under swz3 and none under swz3x, while
-// the 16-row kernel's (8 keys x 2 chunks) measure the reverse.
-__device__ __forceinline__ int swz3x(int key) {
-  return (((key >> 1) & 1) << 2) | (((key ^ (key >> 2)) & 1) << 1) | ((key ^ (key >> 3)) & 1);
-}
-__device__ __forceinline__ int lds_byte_x(int key, int chunk) {
-  return ((chunk >> 3) * 512 + key * 8 + ((chunk ^ swz3x(key)) & 7)) * 16;
-}
 constexpr int kLineGroupBytes = 8192;   // one 128-byte line of all 64 keys
 
 __device__ __forceinline__ void lds_barrier() {
@@ -165,74 +153,16 @@ __device__ __forceinline__ void dma4(uint32_t voff, const uint8_t* sbase, uint32
       : "memory");
 }
 
-template <bool FP8>
-struct TileDma;
-
-// bf16 page, 256 threads: 18 loads per thread straight into the lds_byte_x
-// arrangement of decode_kernel_x, the kernel that streams pages with it (the
-// 16-row kernel takes only the page facts from its plan).
-// Load i of thread t fills line group i/2 of key 32(i%2) + t/8, in-line
-// position t%8 (the lane fetches the chunk that belongs there, so the 8 lanes
-// of an octet read one whole 128-byte line of one key row); keys at or past
-// `nvalid` re-read the last valid key. The 64-row kernel issues these from
-// its waves 0-3; the 16-row bf16 kernel uses only the plan.
-template <>
-struct TileDma<false> {
-  static constexpr int kLoads = kLoadsPerThread;
-  const uint8_t* page;
-  uint32_t voff[2], lds0;
-  __device__ __forceinline__ void plan(const uint8_t* kv, const float* /*kv_scale*/, int page_id,
-                                       int nvalid, LDS_AS uint8_t* buf, LDS_AS float* /*sbuf*/,
-                                       int tid) {
-    page = kv + (size_t)page_id * kTileBytes;
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int key = 32 * par + (tid >> 3);
-      const int src_key = key < nvalid ? key : nvalid - 1;
-      voff[par] = src_key * kRowBytes + 16 * ((tid & 7) ^ swz3x(key));   // lds_byte_x arrangement
-    }
-    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (tid & ~63) * 16));
-  }
-  __device__ __forceinline__ void load(int i) const {
-    dma16(voff[i & 1] + 128 * (i >> 1), page, lds0 + i * 4096);
-  }
-  template <int I>
-  __device__ __forceinline__ void load_ct() const { load(I); }
+// The plan argument of the tile stream for callers that take only a tile's
+// record (the 16-row kernels stream their pages themselves).
+struct TileFacts {
+  __device__ __forceinline__ void plan(const uint8_t*, const float*, int, int, LDS_AS uint8_t*, LDS_AS float*,
+                                       int) {}
 };
 
 // fp8 page: 64 rows of 576 E4M3 codes, plus 64 fp32 token scales elsewhere
 constexpr int kFp8RowBytes = kDqk;                        // 576
 constexpr int kFp8TileBytes = kPage * kFp8RowBytes;       // 36864
-
-// Spread the loads of the next tile evenly over the M QK MFMA slots of the
-// current one (issued back to back they stall the wave on the full
-// vector-memory queue): load k goes right after slot ((k + 1) * M) / N - 1.
-// Slots are compile-time constants in the unrolled loops, so this folds away.
-template <int M, class Dma>
-__device__ __forceinline__ void dma_slot(const Dma& dma, bool more, int slot) {
-  constexpr int N = Dma::kLoads;
-#pragma unroll
-  for (int k = 0; k < N; ++k)
-    if (((k + 1) * M) / N - 1 == slot && more) dma.load(k);
-}
-
-template <class Dma>
-__device__ __forceinline__ void dma_all(const Dma& dma) {
-#pragma unroll
-  for (int k = 0; k < Dma::kLoads; ++k) dma.load(k);
-}
-
-// Same spreading for loaders whose load index is a template argument (so it
-// can become an immediate offset); the caller decides `more` once, outside
-// its MFMA loop.
-template <int M, class Dma, int... K>
-__device__ __forceinline__ void dma_slot_ct(const Dma& dma, int slot, std::integer_sequence<int, K...>) {
-  ((((K + 1) * M) / Dma::kLoads - 1 == slot ? dma.template load_ct<K>() : void()), ...);
-}
-template <int M, class Dma>
-__device__ __forceinline__ void dma_slot_ct(const Dma& dma, int slot) {
-  dma_slot_ct<M>(dma, slot, std::make_integer_sequence<int, Dma::kLoads>{});
-}
 
 // Pairwise reductions across lanes l and l ^ 32 (l ^ 16) on the VALU
 // (v_permlane32_swap / v_permlane16_swap), with no LDS round trip. Both lanes

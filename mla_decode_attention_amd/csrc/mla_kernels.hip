@@ -34,14 +34,10 @@
 //                        features for PV (16x16 MFMA).
 //   NARROW16PC8 (R <= 16, fp8): the same roles over E4M3 pages kept in LDS,
 //                        the operands widened in registers.
-//   WIDE64X    (R > 16, per-sequence query counts): 64 rows, 8 waves; QK
-//                        split by row half x feature half x key half, PV by
-//                        output columns (32x32 MFMA). bf16 cache:
-//                        decode_kernel_x; fp8 cache: decode_kernel_xf (E4M3
-//                        tile in LDS, operands widened in registers). With
-//                        one query count for all sequences the 64-row kernel
-//                        with score and output waves runs instead
-//                        (mla_decode_so.hip).
+//   WIDE64X    (R > 16): 64 rows, 8 waves, score waves (QK, softmax) and
+//                        output waves (PV, page loads); bf16 and fp8 cache,
+//                        one query count for all sequences or per-sequence
+//                        counts (decode_kernel_so in mla_decode_so.hip).
 //   Q8         (fp8 cache, mla_decode_fwd_fp8mma): queries and P in E4M3 on
 //                        fp8 MFMA, 64 rows, score and output waves
 //                        (decode_kernel_so8 in mla_decode_so.hip).
@@ -226,7 +222,7 @@ void decode_kernel_pc(DecodeParams p_, const int32_t* __restrict__ md_, const in
     for (int c = 0; c < kQChunks; ++c) qreg[c] = qrow[4 * c + g];
   };
   {
-    TileDma<false> plan_only;   // the first tile's facts, to fetch its query rows early
+    TileFacts plan_only;   // the first tile's facts, to fetch its query rows early
     fetch_q(unit.prepare(a, unit.f_begin, buf0, nullptr, tid & 255, plan_only));
   }
 
@@ -515,7 +511,7 @@ void decode_kernel_pc8(DecodeParams p_, const int32_t* __restrict__ md_, const i
     for (int j = 0; j < kQChunks; ++j) qreg[j] = qrow[8 * (j >> 1) + 2 * g + (j & 1)];
   };
   {
-    TileDma<false> plan_only;   // the first tile's facts, to fetch its query rows early
+    TileFacts plan_only;   // the first tile's facts, to fetch its query rows early
     fetch_q(unit.prepare(a, f0, bufs, nullptr, tid & 255, plan_only));
   }
 
@@ -640,761 +636,6 @@ void decode_kernel_pc8(DecodeParams p_, const int32_t* __restrict__ md_, const i
         if (cw == 0 && g == 0) *dst_l = live ? (m_run + log2_fast(l_row)) * kLn2 : -INFINITY;
       }
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// WIDE64X: 64 rows per workgroup on v_mfma_f32_32x32x16_bf16, 8 waves (two
-// per SIMD, so one wave's LDS fetches and softmax run under the other's MFMAs).
-//   Wave w has row half rh = w%2, feature half fh = (w/2)%2 and key half
-//   kh = w/4. QK: wave w computes the partial S^T[32 keys of half kh, 32 rows
-//   of half rh] over features 288fh..288fh+287 (18 k-steps of 16 features),
-//   holding Q of its 32 rows for those features (72 registers). Every K byte of
-//   the tile is read from LDS by two waves (the two row halves).
-//   The two feature halves are added through LDS: wave w keeps the 16 keys
-//   16kq..16kq+15 of the tile, kq = 2kh + fh, and takes the partner's partial
-//   scores for them (partner w ^ 2).
-//   PV is split by output columns: wave w accumulates O^T[64 features, 64 rows]
-//   for features 64w..64w+63 (O: 64 registers per lane).
-//   C layout of a 32x32 block: lane l holds element [8j + 4h + i][l%32] for
-//   register r = 4j + i, h = l/32.
-//   In PV k-step ks (keys 16ks..16ks+15) the k-slot 8h + e is key
-//   16ks + 4h + e (e < 4) or 16ks + 8 + 4h + (e - 4): exactly the kept S
-//   registers of the owning wave's lane. So each lane stores its P values for
-//   a k-step as one 16-byte word, and the PV waves read it back as their MFMA
-//   B operand from the same lane position (P exchange through LDS with no
-//   transposition).
-//   The row max of a tile needs all four key quarters: the owning waves publish
-//   their quarter maxima, and every wave derives the same running max for all
-//   64 rows (it needs the rescale factor of every row for its O columns).
-//   LDS: two bf16 tiles (bf16 cache) or one bf16 tile plus the next page's
-//   codes and scales (fp8 cache); a 16 KiB exchange area that holds the
-//   partial scores, then the P operand, then (epilogue) the row sums; the row
-//   maxima live in the rope columns of the current tile, dead once QK is done.
-// ---------------------------------------------------------------------------
-constexpr int kThreadsX = 512;
-constexpr int kQkDepthX = 4;
-constexpr int kPvDepthX = 4;
-constexpr int kXchgBytes = 16384;
-constexpr int kFp8SlotsX = kFp8TileBytes / 16;                                 // 2304
-constexpr int kFp8LoadsX = (kFp8SlotsX + kThreadsX - 1) / kThreadsX;           // 5
-
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void decode_kernel_x(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
-    const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
-    const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
-    const uint8_t* __restrict__ kv_) {
-  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
-  constexpr int ROWS_WG = 64;
-  constexpr int NQ = kDqk / 32;              // 18 QK MFMAs per wave and tile (k-steps of one feature half)
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t xchg[kXchgBytes];
-  LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
-  LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
-  LDS_AS uint8_t* const xb = (LDS_AS uint8_t*)(xchg);
-
-  const DecodeParams& p = a.p;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = uniform(tid >> 6);
-  const int n = lane & 31, h = lane >> 5;
-  const int rh = wave & 1, fh = (wave >> 1) & 1, kh = wave >> 2;
-  const int kq = 2 * kh + fh;                // key quarter this wave owns after the exchange
-  const int R = p.rows;
-  const WgCoord wc = wg_coord((R + ROWS_WG - 1) / ROWS_WG);
-  if (wc.unit >= p.grid_units) return;
-  const int row0 = wc.rb * ROWS_WG;
-  const int row_qk = row0 + 32 * rh + n;
-  const int u = wc.unit;
-
-  Unit unit;
-  if (!unit.init(a, u)) {
-    if (!a.md) write_empty(p, unit.b0, row0, row0 + ROWS_WG, kThreadsX / 64);
-    return;
-  }
-
-  // ---- per-lane constant LDS offsets
-  // QK operand, k-step c = 4m + q: key 32kh + n, chunk 36fh + 2c + h
-  // = lds_byte_x(key, 36fh + 2q + h) + m line groups
-  int k_lane[4];
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) k_lane[q4] = lds_byte_x(32 * kh + n, 36 * fh + 2 * q4 + h);
-  // V transposed fetch: 16-lane group q covers features 64w + 32fb + 16(q%2)
-  // + 0..15 and keys 16ks + 4h + j/4 (+8 for the second read): chunk
-  // 8w + 4fb + 2(q%2) + (j%4)/2 = line group w, chunk 4fb + 2(q%2) + (j%4)/2
-  // of the line; +2048 per k-step of 16 keys.
-  int v_lane[2][2];   // [second][fb]
-  {
-    const int q = lane >> 4, j = lane & 15;
-#pragma unroll
-    for (int second = 0; second < 2; ++second)
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
-        v_lane[second][fb] = wave * kLineGroupBytes +
-                             lds_byte_x(4 * h + (j >> 2) + 8 * second, 4 * fb + 2 * (q & 1) + ((j & 3) >> 1)) +
-                             8 * (j & 1);
-  }
-  // exchange area: partial scores [wave][2 x 16 B][lane]; a wave reads its
-  // partner's (w ^ 2) block
-  LDS_AS uint8_t* const x_give = xb + (wave * 2 * 64 + lane) * 16;
-  const LDS_AS uint8_t* const x_take = xb + ((wave ^ 2) * 2 * 64 + lane) * 16;
-
-  bf16x8 qreg[NQ];
-  f32x16 o[2][2];                            // [feature block][row half]
-#pragma unroll
-  for (int fb = 0; fb < 2; ++fb) {
-    o[fb][0] = f32x16{};
-    o[fb][1] = f32x16{};
-  }
-  float m_run[2] = {-INFINITY, -INFINITY};   // running max of rows row0 + n, row0 + 32 + n
-  float l_run = 0.f;                         // partial row sum of row_qk (this key quarter, lane half)
-  bool restart = true;                       // next rescale zeroes O and l (a sequence starts)
-  int row_tok = 0;                           // query token of row_qk in the current sequence
-
-  // Waves 0-3 (one per SIMD) issue the page's direct-to-LDS loads, 18 each,
-  // one after every QK MFMA (the 256-thread plan of TileDma<false>); waves
-  // 4-7 issue none, so while a loading wave waits on the vector-memory queue
-  // its SIMD partner keeps issuing MFMAs.
-  TileDma<false> dma;
-  TileInfo next = unit.prepare(a, unit.f_begin, buf0, nullptr, tid, dma);
-  // a row block past a sequence's rows (per-sequence q_len) skips its tiles:
-  // no loads, no compute
-  if (row0 < next.rows && wave < 4) dma_all(dma);
-
-  // cur: tile computed in this step; nxt: where the next tile's loads go
-  // query rows of this wave's row into registers (no wait: the first use
-  // waits); issued at a sequence's first tile, or right after the QK of the
-  // previous sequence's last tile when both are in the unit (q_ready). A row
-  // past the sequence's rows takes its last row: the values go into qreg
-  // untouched (a select on them would wait for the loads at once), and such
-  // rows are never stored.
-  bool q_ready = false;
-  auto load_q = [&](const TileInfo& tq) {
-    const int rr = row_qk < tq.rows ? row_qk : max(tq.rows - 1, 0);
-    const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(tq.qrow0 + rr, p.q_rows - 1) * kDqk);
-#pragma unroll
-    for (int c = 0; c < NQ; ++c) qreg[c] = qrow[36 * fh + 2 * c + h];
-  };
-
-  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
-    const TileInfo ti = next;
-    const int t = ti.t, L = ti.L;
-    const bool skip = row0 >= ti.rows;
-
-    if (ti.first && !skip) {
-      const int rr = row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0);
-      if (!q_ready) load_q(ti);
-      q_ready = false;
-      // O and l restart through the rescale below (alpha = 0), so the
-      // accumulators are never reset outside the one rescale path
-      m_run[0] = m_run[1] = -INFINITY;
-      restart = true;
-      row_tok = rr / p.num_heads;
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    }
-    const bool final_out = ti.final_out;
-    const int slot = ti.slot;
-
-    // the next tile's facts and load plan (addresses only) are set up while
-    // this tile's loads may still be landing
-    const bool more = f + 1 < unit.f_end;
-    if (more) next = unit.prepare(a, f + 1, nxt, nullptr, tid, dma);
-    // the same wait as wait_tile's, as a builtin the compiler tracks: it then
-    // knows that query rows prefetched after the previous tile's QK have
-    // landed and puts no waits of its own into this tile's QK loop (where
-    // they would also wait for the next tile's direct-to-LDS loads)
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    wait_tile();
-    const bool load_next = more && row0 < next.rows;
-    if (skip) {
-      if (load_next && wave < 4) dma_all(dma);
-      return;
-    }
-
-    // ---- QK GEMM: partial S^T[32 keys of half kh, 32 rows of half rh] over feature half fh
-    f32x16 sacc = f32x16{};
-    // one copy of the loop with the next tile's loads and one without, so
-    // the load slots need no per-slot branch
-    auto qk = [&](auto with_loads) {
-      auto kaddr = [&](int c) { return cur + k_lane[c & 3] + (c >> 2) * kLineGroupBytes; };
-      bf16x8 ring[kQkDepthX];
-#pragma unroll
-      for (int i = 0; i < kQkDepthX; ++i) ring[i] = ld128(kaddr(i));
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const bf16x8 av = ring[i % kQkDepthX];
-        if (i + kQkDepthX < NQ) ring[i % kQkDepthX] = ld128(kaddr(i + kQkDepthX));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[i], sacc, 0, 0, 0);
-        if constexpr (decltype(with_loads)::value) dma_slot_ct<NQ>(dma, i);
-        sched_fence();
-      }
-    };
-    if (load_next && wave < 4) qk(std::true_type{});
-    else qk(std::false_type{});
-    // the next tile starts a sequence of this unit: its query rows now (qreg is free)
-    if (ti.last && more && row0 < next.rows) {
-      load_q(next);
-      q_ready = true;
-    }
-
-    // ---- add the two feature halves: keep registers 8fh..8fh+7 (keys
-    //      16kq + 0..15), give registers 8(1-fh).. to the partner. fh is
-    //      wave-uniform: a scalar branch with constant register indices
-    //      (a select on fh would become a per-element indexed extract).
-    float sv[8];
-    if (fh) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = sacc[8 + e];
-      *(LDS_AS f32x4*)(x_give) = f32x4{sacc[0], sacc[1], sacc[2], sacc[3]};
-      *(LDS_AS f32x4*)(x_give + 1024) = f32x4{sacc[4], sacc[5], sacc[6], sacc[7]};
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = sacc[e];
-      *(LDS_AS f32x4*)(x_give) = f32x4{sacc[8], sacc[9], sacc[10], sacc[11]};
-      *(LDS_AS f32x4*)(x_give + 1024) = f32x4{sacc[12], sacc[13], sacc[14], sacc[15]};
-    }
-    lds_barrier();
-#pragma unroll
-    for (int part = 0; part < 2; ++part) {
-      const f32x4 v = *(const LDS_AS f32x4*)(x_take + part * 1024);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sv[4 * part + e] += v[e];
-    }
-
-    // ---- softmax. P is computed against the running max before the tile
-    //      maxima of the other waves are known: with the lazy rescale the
-    //      running max moves only when some row's tile max exceeds it by more
-    //      than the threshold (so P <= 2^threshold otherwise). The quarter
-    //      maxima are published with P; after the barrier every wave checks
-    //      all 64 rows (the same decision in every wave) and, on the rare tiles
-    //      that raise a row's max (always on a sequence's first tile), rescales
-    //      O and l and rewrites P behind one more barrier.
-    LDS_AS float* const smax = (LDS_AS float*)(cur + 8 * kLineGroupBytes);   // [key quarter][row]
-    const int key0 = t * kPage + 16 * kq + 4 * h;
-    // keys at or past vis are masked (causal rule / cache tail); only the
-    // tiles that reach past L - qlen + 1 can hold such keys
-    const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) sv[r] *= p.scale_log2;
-    if (__builtin_expect(need_mask, 0)) {
-      const int vis = L - ti.qlen + row_tok + 1;
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if ((key0 + 8 * (r >> 2) + (r & 3)) >= vis) sv[r] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sv[r]);
-    mx = max_xor32(mx);
-    if (h == 0) smax[kq * 64 + 32 * rh + n] = mx;
-    // A wave that sees a row max past the threshold stamps the tile index
-    // into the flag word (left over values of other tiles never match f; a
-    // stray match would only take the exact slow path below).
-    LDS_AS int* const raise_flag = (LDS_AS int*)(smax + 256);
-    if (!restart && __builtin_amdgcn_ballot_w64(mx > m_run[rh] + kRescaleThreshold) && lane == 0)
-      *raise_flag = f;
-    // P operand [k-step][row half][lane] in the exchange area (the partial
-    // scores there were consumed before the barrier above)
-    LDS_AS bf16x8* const p_out = (LDS_AS bf16x8*)(xb + ((kq * 2 + rh) * 64 + lane) * 16);
-    float l_tile = 0.f;
-    auto make_p = [&](float m_ref) {
-      bf16x8 pb;
-      l_tile = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pr = exp2_fast(sv[e] - m_ref);
-        l_tile += pr;
-        pb[e] = (__bf16)pr;
-      }
-      *p_out = pb;
-    };
-    // (a row whose keys were all masked so far keeps m = -inf: reference 0, P = 0)
-    if (!restart) make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
-    lds_barrier();
-
-    // the first V^T fragments of the PV GEMM, read before the raise check
-    // (a raise rewrites P, never V)
-    auto vaddr = [&](int i, int second) {
-      const int ks = i >> 1, fb = i & 1;
-      return cur + v_lane[second][fb] + ks * 2048;
-    };
-    constexpr int NPV = 8;   // (k-step, feature block) pairs; each feeds 2 row halves
-    bf16x4 r0[kPvDepthX], r1[kPvDepthX];
-#pragma unroll
-    for (int i = 0; i < kPvDepthX; ++i) {
-      r0[i] = tr_read(vaddr(i, 0));
-      r1[i] = tr_read(vaddr(i, 1));
-    }
-
-    if (restart || uniform(*raise_flag) == f) {
-      // some row's max moved (or a sequence starts): every wave derives the
-      // new running max of all 64 rows from the quarter maxima
-      float alpha[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float tmax = fmaxf(fmaxf(smax[32 * rb + n], smax[64 + 32 * rb + n]),
-                                 fmaxf(smax[128 + 32 * rb + n], smax[192 + 32 * rb + n]));
-        const float m_new = fmaxf(m_run[rb], tmax);
-        const bool raise = m_new > m_run[rb] + kRescaleThreshold;
-        alpha[rb] = restart ? 0.0f : raise ? exp2_fast(m_run[rb] - m_new) : 1.0f;
-        if (raise) m_run[rb] = m_new;
-      }
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb) {
-        o[fb][0] *= alpha[0];
-        o[fb][1] *= alpha[1];
-      }
-      l_run *= alpha[rh];
-      make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
-      lds_barrier();
-    }
-    restart = false;
-    l_run += l_tile;
-
-    // ---- PV GEMM: O^T[64 features of this wave, 64 rows] += V^T . P^T
-    {
-      bf16x8 pbr[2];
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        const int ks = i >> 1, fb = i & 1;
-        if (fb == 0) {
-          pbr[0] = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 0) * 64 + lane) * 16);
-          pbr[1] = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 1) * 64 + lane) * 16);
-        }
-        const bf16x8 av = __builtin_shufflevector(r0[i % kPvDepthX], r1[i % kPvDepthX], 0, 1, 2, 3, 4, 5, 6, 7);
-        if (i + kPvDepthX < NPV) {
-          r0[i % kPvDepthX] = tr_read(vaddr(i + kPvDepthX, 0));
-          r1[i % kPvDepthX] = tr_read(vaddr(i + kPvDepthX, 1));
-        }
-        o[fb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbr[0], o[fb][0], 0, 0, 0);
-        o[fb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbr[1], o[fb][1], 0, 0, 0);
-        sched_fence();
-      }
-    }
-
-    // The next step's first barrier orders this PV's LDS reads before any
-    // write into `cur` or the exchange area; only the epilogue needs one here.
-    if (!ti.last) return;
-    lds_barrier();   // every wave is done reading P from the exchange area
-
-    // ---- epilogue for this sequence: full row sums, then O / l and LSE
-    LDS_AS float* const ssum = (LDS_AS float*)xb;   // [key quarter][row]
-    const float lh = sum_xor32(l_run);
-    if (h == 0) ssum[kq * 64 + 32 * rh + n] = lh;
-    lds_barrier();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int row = row0 + 32 * rb + n;
-      const float l_row = (ssum[32 * rb + n] + ssum[64 + 32 * rb + n]) +
-                          (ssum[128 + 32 * rb + n] + ssum[192 + 32 * rb + n]);
-      const bool live = l_row > 0.f;
-      const float inv = live ? 1.0f / l_row : 0.f;
-      if (row < ti.rows) {
-        float* dst_o;
-        float* dst_l;
-        if (final_out) {
-          dst_o = p.out + ((size_t)ti.qrow0 + row) * kDv;
-          dst_l = p.lse + (size_t)ti.qrow0 + row;
-        } else {
-          dst_o = p.ws_out + ((size_t)slot * R + row) * kDv;
-          dst_l = p.ws_lse + (size_t)slot * R + row;
-        }
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            f32x4 v = {o[fb][rb][4 * jj], o[fb][rb][4 * jj + 1], o[fb][rb][4 * jj + 2], o[fb][rb][4 * jj + 3]};
-            *(f32x4*)(dst_o + 64 * wave + 32 * fb + 8 * jj + 4 * h) = v * inv;
-          }
-        }
-        if (wave == 0 && h == 0)
-          *dst_l = live ? (m_run[rb] + log2_fast(l_row)) * kLn2 : -INFINITY;
-      }
-    }
-  };
-
-  for (int f = unit.f_begin; f < unit.f_end; f += 2) {
-    step(f, buf0, buf1);
-    if (f + 1 < unit.f_end) step(f + 1, buf1, buf0);
-  }
-}
-
-// An fp8 page in LDS with its 64 per-token scales after the codes.
-constexpr int kQ8TileBytes = kFp8TileBytes + kPage * 4;
-
-// The same page layout from 256 threads (waves 0-3 of the 64-row fp8 kernel):
-// load j of thread t fills LDS slot 256j + t, i.e. line group j, key
-// (t/4)%64, position t%4, so the thread's key and position are fixed and load
-// j reads bytes 64j.. of that key's row. Wave 0 also loads the 64 per-token
-// scales with its first load.
-struct TileDmaQ8Half {
-  static constexpr int kLoads = kFp8TileBytes / (256 * 16);   // 9
-  const uint8_t* page;
-  const uint8_t* scale;
-  uint32_t voff, lds0, sc_lds, sc_off;
-  int tid;
-  __device__ __forceinline__ void plan(const uint8_t* kv, const float* kv_scale, int page_id, int nvalid,
-                                       LDS_AS uint8_t* buf, LDS_AS float* /*sbuf*/, int t) {
-    page = kv + (size_t)page_id * kFp8TileBytes;
-    scale = (const uint8_t*)(kv_scale + (size_t)page_id * kPage);
-    tid = t;
-    const int key = (t >> 2) & 63, pos = t & 3;
-    const int src_key = key < nvalid ? key : nvalid - 1;
-    voff = src_key * kFp8RowBytes + 16 * (pos ^ swz2(key));
-    lds0 = (uint32_t)uniform((int)(uintptr_t)(buf + (t & ~63) * 16));
-    sc_lds = (uint32_t)uniform((int)(uintptr_t)(buf + kFp8TileBytes));
-    const int lane = t & 63;
-    sc_off = 4 * (lane < nvalid ? lane : nvalid - 1);
-  }
-  __device__ __forceinline__ void load(int j) const {
-    dma16(voff, page + 64 * j, (uint32_t)uniform((int)(lds0 + j * 4096)));
-    if (j == 0 && tid < 64) dma4(sc_off, scale, (uint32_t)uniform((int)sc_lds));
-  }
-  template <int I>
-  __device__ __forceinline__ void load_ct() const { load(I); }
-};
-static_assert(TileDmaQ8Half::kLoads * 256 * 16 == kFp8TileBytes, "fp8 tile must split evenly");
-
-
-// ---------------------------------------------------------------------------
-// WIDE64X on an fp8 cache without widening the page in LDS: the E4M3 tile
-// stays in LDS (the shared fp8 layout), and each MFMA operand is widened exactly to
-// bf16 in registers right after its LDS read (v_cvt_scalef32_pk_bf16_fp8,
-// scale 1). K: one 16-byte read feeds two k-steps. V^T: ds_read_b64_tr_b8
-// gives a lane 8 consecutive keys of one feature, so the PV k-slot 8h + e is
-// key 16ks + 8h + e and P is stored in that order. Otherwise as the bf16
-// wide kernel above (same split, exchange, softmax and epilogue).
-// ---------------------------------------------------------------------------
-
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void decode_kernel_xf(DecodeParams p_, const int32_t* __restrict__ md_, const int32_t* __restrict__ prefix_,
-    const int32_t* __restrict__ split_off_, const int32_t* __restrict__ seqlens_,
-    const int32_t* __restrict__ block_table_, const uint16_t* __restrict__ qptr_,
-    const uint8_t* __restrict__ kv_) {
-  const KernelArgs a{p_, md_, prefix_, split_off_, seqlens_, block_table_, qptr_, kv_};
-  constexpr int ROWS_WG = 64;
-  constexpr int NQ = kDqk / 32;              // 18 QK MFMAs per wave and tile (k-steps of one feature half)
-
-  constexpr bool FP8 = true;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kQ8TileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kQ8TileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t xchg[kXchgBytes];
-  LDS_AS uint8_t* const buf0 = (LDS_AS uint8_t*)(smem0);
-  LDS_AS uint8_t* const buf1 = (LDS_AS uint8_t*)(smem1);
-  LDS_AS uint8_t* const xb = (LDS_AS uint8_t*)(xchg);
-
-  const DecodeParams& p = a.p;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = uniform(tid >> 6);
-  const int n = lane & 31, h = lane >> 5;
-  const int rh = wave & 1, fh = (wave >> 1) & 1, kh = wave >> 2;
-  const int kq = 2 * kh + fh;                // key quarter this wave owns after the exchange
-  const int R = p.rows;
-  const WgCoord wc = wg_coord((R + ROWS_WG - 1) / ROWS_WG);
-  if (wc.unit >= p.grid_units) return;
-  const int row0 = wc.rb * ROWS_WG;
-  const int row_qk = row0 + 32 * rh + n;
-  const int u = wc.unit;
-
-  UnitT<false> unit;
-  if (!unit.init(a, u)) {
-    if (!a.md) write_empty(p, unit.b0, row0, row0 + ROWS_WG, kThreadsX / 64);
-    return;
-  }
-
-  // ---- per-lane constant LDS offsets (E4M3 tile, 64-byte line groups)
-  // QK: one 16-byte read per two k-steps. Lane (n, h) reads chunk
-  // 18fh + h + 2j of key 32kh + n (j = 0..8): bytes 0-7 feed k-step 2j, bytes
-  // 8-15 k-step 2j+1 (the query registers use the same feature order).
-  // Chunks 2 apart are one line group (4096 bytes) apart with the same swizzle.
-  int k_lane[2];
-#pragma unroll
-  for (int jp = 0; jp < 2; ++jp) k_lane[jp] = lds8_byte(32 * kh + n, 18 * fh + h + 2 * jp);
-  // V^T: ds_read_b64_tr_b8 in 16-lane groups gi: lane i of the group, as a
-  // source, reads 8 bytes (half i%2 of chunk 4w + 2fb + gi%2) of key
-  // 16ks + 8h + i/2, and receives 8 keys 16ks + 8h + 0..7 of feature
-  // 64w + 32fb + 16(gi%2) + i; +1024 bytes per k-step of 16 keys.
-  int v_lane[2];   // [fb]
-  {
-    const int gi = lane >> 4, i = lane & 15;
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-      v_lane[fb] = lds8_byte(8 * h + (i >> 1), 4 * wave + 2 * fb + (gi & 1)) + 8 * (i & 1);
-  }
-  // exchange area: partial scores [wave][2 x 16 B][lane]; a wave reads its
-  // partner's (w ^ 2) block
-  LDS_AS uint8_t* const x_give = xb + (wave * 2 * 64 + lane) * 16;
-  const LDS_AS uint8_t* const x_take = xb + ((wave ^ 2) * 2 * 64 + lane) * 16;
-
-  bf16x8 qreg[NQ];
-  f32x16 o[2][2];                            // [feature block][row half]
-#pragma unroll
-  for (int fb = 0; fb < 2; ++fb) {
-    o[fb][0] = f32x16{};
-    o[fb][1] = f32x16{};
-  }
-  float m_run[2] = {-INFINITY, -INFINITY};   // running max of rows row0 + n, row0 + 32 + n
-  float l_run = 0.f;                         // partial row sum of row_qk (this key quarter, lane half)
-  bool restart = true;                       // next rescale zeroes O and l (a sequence starts)
-  int row_tok = 0;                           // query token of row_qk in the current sequence
-
-  // waves 0-3 issue the page's loads (9 each), waves 4-7 none, as in the
-  // bf16 kernel
-  TileDmaQ8Half dma;
-  TileInfo next = unit.prepare(a, unit.f_begin, buf0, nullptr, tid, dma);
-  // a row block past a sequence's rows (per-sequence q_len) skips its tiles:
-  // no loads, no compute
-  if (row0 < next.rows && wave < 4) dma_all(dma);
-
-  // cur: E4M3 tile (codes, then the 64 scales) of this step; nxt: where the
-  // next tile's loads go
-  // query rows of this wave's row into registers (no wait: the first use
-  // waits); issued at a sequence's first tile, or right after the QK of the
-  // previous sequence's last tile when both are in the unit (q_ready)
-  bool q_ready = false;
-  auto load_q = [&](const TileInfo& tq) {
-    const int rr = row_qk < tq.rows ? row_qk : max(tq.rows - 1, 0);
-    const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(tq.qrow0 + rr, p.q_rows - 1) * kDqk);
-#pragma unroll
-    for (int c = 0; c < NQ; ++c) {
-      bf16x8 v = qrow[36 * fh + 4 * (c >> 1) + 2 * h + (c & 1)];
-      qreg[c] = row_qk < tq.rows ? v : bf16x8{};
-    }
-  };
-
-  auto step = [&](const int f, LDS_AS uint8_t* const cur, LDS_AS uint8_t* const nxt) {
-    const LDS_AS float* const sbc = (const LDS_AS float*)(cur + kFp8TileBytes);
-    const TileInfo ti = next;
-    const int t = ti.t, L = ti.L;
-    const bool skip = row0 >= ti.rows;
-
-    if (ti.first && !skip) {
-      const int rr = row_qk < ti.rows ? row_qk : max(ti.rows - 1, 0);
-      if (!q_ready) load_q(ti);
-      q_ready = false;
-      // O and l restart through the rescale below (alpha = 0), so the
-      // accumulators are never reset outside the one rescale path
-      m_run[0] = m_run[1] = -INFINITY;
-      restart = true;
-      row_tok = rr / p.num_heads;
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    }
-    const bool final_out = ti.final_out;
-    const int slot = ti.slot;
-
-    // the next tile's facts and load plan (addresses only) are set up while
-    // this tile's loads may still be landing
-    const bool more = f + 1 < unit.f_end;
-    if (more) next = unit.prepare(a, f + 1, nxt, nullptr, tid, dma);
-    wait_tile();
-    const bool load_next = more && row0 < next.rows;
-    if (skip) {
-      if (load_next && wave < 4) dma_all(dma);
-      return;
-    }
-
-    // ---- QK GEMM: partial S^T[32 keys of half kh, 32 rows of half rh] over feature half fh
-    f32x16 sacc = f32x16{};
-    // one copy of the loop with the next tile's loads and one without, so
-    // the load slots need no per-slot branch
-    auto qk = [&](auto with_loads) {
-      constexpr int NJ = NQ / 2, D = 3;
-      auto kaddr = [&](int j) { return cur + k_lane[j & 1] + (j >> 1) * 4096; };
-      u32x4 ring[D];
-#pragma unroll
-      for (int j = 0; j < D; ++j) ring[j] = *(const LDS_AS u32x4*)kaddr(j);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const u32x4 w = ring[j % D];
-        if (j + D < NJ) ring[j % D] = *(const LDS_AS u32x4*)kaddr(j + D);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const bf16x8 av = widen8(w[2 * e], w[2 * e + 1]);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[2 * j + e], sacc, 0, 0, 0);
-        }
-        if constexpr (decltype(with_loads)::value) dma_slot_ct<NJ>(dma, j);
-        sched_fence();
-      }
-    };
-    if (load_next && wave < 4) qk(std::true_type{});
-    else qk(std::false_type{});
-    // the next tile starts a sequence of this unit: its query rows now (qreg is free)
-    if (ti.last && more && row0 < next.rows) {
-      load_q(next);
-      q_ready = true;
-    }
-
-    // ---- add the two feature halves: keep registers 8fh..8fh+7 (keys
-    //      16kq + 0..15), give registers 8(1-fh).. to the partner. fh is
-    //      wave-uniform: a scalar branch with constant register indices
-    //      (a select on fh would become a per-element indexed extract).
-    float sv[8];
-    if (fh) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = sacc[8 + e];
-      *(LDS_AS f32x4*)(x_give) = f32x4{sacc[0], sacc[1], sacc[2], sacc[3]};
-      *(LDS_AS f32x4*)(x_give + 1024) = f32x4{sacc[4], sacc[5], sacc[6], sacc[7]};
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = sacc[e];
-      *(LDS_AS f32x4*)(x_give) = f32x4{sacc[8], sacc[9], sacc[10], sacc[11]};
-      *(LDS_AS f32x4*)(x_give + 1024) = f32x4{sacc[12], sacc[13], sacc[14], sacc[15]};
-    }
-    lds_barrier();
-#pragma unroll
-    for (int part = 0; part < 2; ++part) {
-      const f32x4 v = *(const LDS_AS f32x4*)(x_take + part * 1024);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sv[4 * part + e] += v[e];
-    }
-
-    // ---- softmax. P is computed against the running max before the tile
-    //      maxima of the other waves are known: with the lazy rescale the
-    //      running max moves only when some row's tile max exceeds it by more
-    //      than the threshold (so P <= 2^threshold otherwise). The quarter
-    //      maxima are published with P; after the barrier every wave checks
-    //      all 64 rows (the same decision in every wave) and, on the rare tiles
-    //      that raise a row's max (always on a sequence's first tile), rescales
-    //      O and l and rewrites P behind one more barrier.
-    LDS_AS float* const smax = (LDS_AS float*)(cur + 8 * 4096);   // rope line group: [key quarter][row]
-    const int key0 = t * kPage + 16 * kq + 4 * h;
-    // keys at or past vis are masked (causal rule / cache tail); only the
-    // tiles that reach past L - qlen + 1 can hold such keys
-    const bool need_mask = (t * kPage + kPage) > (L - ti.qlen + 1);
-    f32x4 ksc[2];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-      ksc[jj] = FP8 ? *(const LDS_AS f32x4*)(sbc + 16 * kq + 8 * jj + 4 * h) : f32x4{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-    for (int r = 0; r < 8; ++r) sv[r] *= FP8 ? ksc[r >> 2][r & 3] * p.scale_log2 : p.scale_log2;
-    if (__builtin_expect(need_mask, 0)) {
-      const int vis = L - ti.qlen + row_tok + 1;
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if ((key0 + 8 * (r >> 2) + (r & 3)) >= vis) sv[r] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sv[r]);
-    mx = max_xor32(mx);
-    if (h == 0) smax[kq * 64 + 32 * rh + n] = mx;
-    // A wave that sees a row max past the threshold stamps the tile index
-    // into the flag word (left over values of other tiles never match f; a
-    // stray match would only take the exact slow path below).
-    LDS_AS int* const raise_flag = (LDS_AS int*)(smax + 256);
-    if (!restart && __builtin_amdgcn_ballot_w64(mx > m_run[rh] + kRescaleThreshold) && lane == 0)
-      *raise_flag = f;
-    // P operand [k-step][row half][lane (n, h)] in the exchange area (the
-    // partial scores there were consumed before the barrier above): reader
-    // lane (n, h) holds keys 16ks + 8h + 0..7, so this lane's keys 4h + 0..3
-    // go to reader half 0 and keys 8 + 4h + 0..3 to reader half 1, at byte 8h
-    LDS_AS uint8_t* const p_out = xb + ((kq * 2 + rh) * 64 + n) * 16 + 8 * h;
-    float l_tile = 0.f;
-    auto make_p = [&](float m_ref) {
-      bf16x4 pa, pc;
-      l_tile = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pr = exp2_fast(sv[e] - m_ref);
-        l_tile += pr;
-        const __bf16 v = (__bf16)(pr * ksc[e >> 2][e & 3]);
-        if (e < 4) pa[e] = v;
-        else pc[e - 4] = v;
-      }
-      *(LDS_AS bf16x4*)p_out = pa;
-      *(LDS_AS bf16x4*)(p_out + 32 * 16) = pc;
-    };
-    // (a row whose keys were all masked so far keeps m = -inf: reference 0, P = 0)
-    if (!restart) make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
-    lds_barrier();
-
-    if (restart || uniform(*raise_flag) == f) {
-      // some row's max moved (or a sequence starts): every wave derives the
-      // new running max of all 64 rows from the quarter maxima
-      float alpha[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float tmax = fmaxf(fmaxf(smax[32 * rb + n], smax[64 + 32 * rb + n]),
-                                 fmaxf(smax[128 + 32 * rb + n], smax[192 + 32 * rb + n]));
-        const float m_new = fmaxf(m_run[rb], tmax);
-        const bool raise = m_new > m_run[rb] + kRescaleThreshold;
-        alpha[rb] = restart ? 0.0f : raise ? exp2_fast(m_run[rb] - m_new) : 1.0f;
-        if (raise) m_run[rb] = m_new;
-      }
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb) {
-        o[fb][0] *= alpha[0];
-        o[fb][1] *= alpha[1];
-      }
-      l_run *= alpha[rh];
-      make_p((m_run[rh] == -INFINITY) ? 0.0f : m_run[rh]);
-      lds_barrier();
-    }
-    restart = false;
-    l_run += l_tile;
-
-    // ---- PV GEMM: O^T[64 features of this wave, 64 rows] += V^T . P^T, V^T
-    //      through the transposed byte read and widened in registers
-    {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 pb0 = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 0) * 64 + lane) * 16);
-        const bf16x8 pb1 = *(const LDS_AS bf16x8*)(xb + ((ks * 2 + 1) * 64 + lane) * 16);
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb) {
-          const i32x2 x = tr8_read(cur + v_lane[fb] + ks * 1024);
-          const bf16x8 av = widen8((unsigned)x[0], (unsigned)x[1]);
-          o[fb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb0, o[fb][0], 0, 0, 0);
-          o[fb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb1, o[fb][1], 0, 0, 0);
-        }
-      }
-    }
-
-    // The next step's first barrier orders this PV's LDS reads before any
-    // write into `cur` or the exchange area; only the epilogue needs one here.
-    if (!ti.last) return;
-    lds_barrier();   // every wave is done reading P from the exchange area
-
-    // ---- epilogue for this sequence: full row sums, then O / l and LSE
-    LDS_AS float* const ssum = (LDS_AS float*)xb;   // [key quarter][row]
-    const float lh = sum_xor32(l_run);
-    if (h == 0) ssum[kq * 64 + 32 * rh + n] = lh;
-    lds_barrier();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int row = row0 + 32 * rb + n;
-      const float l_row = (ssum[32 * rb + n] + ssum[64 + 32 * rb + n]) +
-                          (ssum[128 + 32 * rb + n] + ssum[192 + 32 * rb + n]);
-      const bool live = l_row > 0.f;
-      const float inv = live ? 1.0f / l_row : 0.f;
-      if (row < ti.rows) {
-        float* dst_o;
-        float* dst_l;
-        if (final_out) {
-          dst_o = p.out + ((size_t)ti.qrow0 + row) * kDv;
-          dst_l = p.lse + (size_t)ti.qrow0 + row;
-        } else {
-          dst_o = p.ws_out + ((size_t)slot * R + row) * kDv;
-          dst_l = p.ws_lse + (size_t)slot * R + row;
-        }
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            f32x4 v = {o[fb][rb][4 * jj], o[fb][rb][4 * jj + 1], o[fb][rb][4 * jj + 2], o[fb][rb][4 * jj + 3]};
-            *(f32x4*)(dst_o + 64 * wave + 32 * fb + 8 * jj + 4 * h) = v * inv;
-          }
-        }
-        if (wave == 0 && h == 0)
-          *dst_l = live ? (m_run[rb] + log2_fast(l_row)) * kLn2 : -INFINITY;
-      }
-    }
-  };
-
-  for (int f = unit.f_begin; f < unit.f_end; f += 2) {
-    step(f, buf0, buf1);
-    if (f + 1 < unit.f_end) step(f + 1, buf1, buf0);
   }
 }
 
@@ -1796,14 +1037,13 @@ int variant_rows(int variant) { return variant == VAR_NARROW16 ? 16 : 64; }   //
 
 hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hipStream_t s,
                          hipEvent_t ev_start, hipEvent_t ev_stop) {
-  // uniform q_len over 16 rows: the kernel with score and output waves
-  if (variant == VAR_WIDE64X && !p.cu_q) return launch_decode_so(p, grid_units, s, ev_start, ev_stop);
+  // over 16 rows: the 64-row kernels with score and output waves
+  if (variant == VAR_WIDE64X) return launch_decode_so(p, grid_units, s, ev_start, ev_stop);
   // the fp8 cache on fp8 MFMA (uniform q_len only)
   if (variant == VAR_Q8) return p.cu_q ? hipErrorInvalidValue : launch_decode_so(p, grid_units, s, ev_start, ev_stop, true);
+  // up to 16 rows: the producer/consumer kernels
   const int rb = (p.rows + variant_rows(variant) - 1) / variant_rows(variant);
-  // 64-row kernels: 1-D grid, units padded to a multiple of 8 (see wg_coord)
-  const bool wide = variant == VAR_WIDE64X || variant == VAR_Q8;
-  dim3 grid = wide ? dim3(((grid_units + 7) / 8) * 8 * rb) : dim3(grid_units, rb);
+  dim3 grid(grid_units, rb);
   KernelArgs a;
   a.p = p;
   a.p.grid_units = grid_units;
@@ -1827,13 +1067,8 @@ hipError_t launch_decode(const DecodeParams& p, int variant, int grid_units, hip
                          a.block_table, a.qptr, a.kv);                                                   \
   } while (0)
   const bool fp8 = p.kv_scale != nullptr;
-  if (variant == VAR_NARROW16) {
-    if (fp8) MLA_LAUNCH(decode_kernel_pc8, 2 * kThreads);
-    else MLA_LAUNCH(decode_kernel_pc, 2 * kThreads);
-  } else {
-    if (fp8) MLA_LAUNCH(decode_kernel_xf, kThreadsX);
-    else MLA_LAUNCH(decode_kernel_x, kThreadsX);
-  }
+  if (fp8) MLA_LAUNCH(decode_kernel_pc8, 2 * kThreads);
+  else MLA_LAUNCH(decode_kernel_pc, 2 * kThreads);
 #undef MLA_LAUNCH
   return hipGetLastError();
 }
