@@ -12,9 +12,11 @@
 //                     all 576 features, the 32 query rows of the wave in
 //                     registers (bf16 cache: 16 keys on
 //                     v_mfma_f32_16x16x32_bf16; fp8 cache: 32 keys on
-//                     v_mfma_f32_32x32x16_bf16, one row per lane pair), then
-//                     the softmax of those scores, and the probabilities P
-//                     (bf16) into LDS in the B-operand layout of the PV GEMM.
+//                     v_mfma_scale_f32_32x32x64_f8f6f4 straight from the
+//                     E4M3 codes, the query row split exactly into two E4M3
+//                     parts, one row per lane pair), then the softmax of
+//                     those scores, and the probabilities P (bf16) into LDS
+//                     in the B-operand layout of the PV GEMM.
 //   output waves 4-7  O^T[128 features, 64 rows] += V^T . P^T
 //                     (v_mfma_f32_32x32x16_bf16, V^T read transposed from the
 //                     same LDS tile), and the page loads.
@@ -41,11 +43,10 @@
 // l_0 2^(m_0 - M) + l_1 2^(m_1 - M), so O / l and LSE = M + log2 l are exact
 // for any interleaving of raises.
 //
-// fp8 cache: the E4M3 codes stay in LDS; the K operand is widened to bf16 in
-// registers after a 16-byte read that serves two k-steps (the query registers
-// follow the same feature order), V^T comes from the transposed byte read, the
-// token's scale multiplies its score and its probability (P_j s_j goes into
-// the PV GEMM, P_j into the row sum). The per-token scales past a page's valid
+// fp8 cache: the E4M3 codes stay in LDS and are the A operand of the QK MFMAs
+// as they are; V^T comes from the transposed byte read and is widened to bf16
+// in registers for the PV MFMAs; the token's scale multiplies its score and
+// its probability (P_j s_j goes into the PV GEMM, P_j into the row sum). The per-token scales past a page's valid
 // keys repeat the last valid one, so every scale in LDS is finite.
 //
 // Used for q_len * heads > 16 rows, with one query count for all sequences or
@@ -557,73 +558,125 @@ void decode_kernel_so(DecodeParams p_, const int32_t* __restrict__ md_, const in
   // ========================================================== score waves
   if constexpr (FP8) {
     // fp8 cache: S^T[32 keys of half kh, 32 rows of half rh] on
-    // v_mfma_f32_32x32x16_bf16, one row per lane pair (lane (n, h): row
-    // 32 rh + n, keys 32 kh + 8 jj + 4 h + e), so a row's reductions take one
-    // cross-lane step. Feature order inside the contraction: k-step 2m + s
-    // takes, from lane half h, features 16 (2m + h) + 8 s .. + 7, so that one
-    // 16-byte read of chunk 2m + h feeds both k-steps of m, widened to bf16 in
-    // registers (the query registers follow the same order).
+    // v_mfma_scale_f32_32x32x64_f8f6f4 straight from the cache's E4M3 codes,
+    // one row per lane pair (lane (n, h): row 32 rh + n, keys
+    // 32 kh + 8 jj + 4 h + e), so a row's reductions take one cross-lane step.
+    // The query row enters as two E4M3 parts, q = hi 2^k + lo 2^(k-4), k the
+    // smallest with max|q| <= 448 2^k: a bf16 value has 8 significant bits,
+    // hi takes the leading 4 (nearest even) and the remainder, a multiple of
+    // 2^(e-7) of at most 2^(e-4) in size, is exact in lo (for every element
+    // at or above 2^-6 of 448 2^k; below that, lo rounds). The powers of two
+    // are the B-operand block scales of two MFMAs per k-step, so QK runs on the
+    // fp8 matrix core with no conversion of the page (lane (n, h) holds
+    // features 64 cc + 16 h .. + 15 and 64 cc + 32 + 16 h .. + 15 of k-step
+    // cc: chunks 4 cc + h and 4 cc + 2 + h).
     const int rh = wave & 1, kh = wave >> 1;
     const int n = lane & 31, h = lane >> 5;
     const int row = 32 * rh + n;
     int k_lane[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) k_lane[e] = C::byte(32 * kh + n, 2 * e + h);
-    constexpr int NQ = kDqk / 16;   // 36 k-steps
-    bf16x8 q[NQ];
+    constexpr int NK = kDqk / 64;   // 9 k-steps of 64 features
+    i32x8 qhi[NK], qlo[NK];
+    int sc_hi = 127, sc_lo = 127;   // their E8M0 scale bytes: 2^k, 2^(k-4)
     float m_run = -INFINITY, l_run = 0.f;
     int row_tok = 0;
-    auto load_q = [&](const TileInfo& tq) {
+    // the query row of a sequence: its maximum from one pass over the row
+    // (the lane's half, then the partner lane's), then a second pass (cache
+    // hits), one k-step at a time, to the two parts
+    auto quant_q = [&](const TileInfo& tq) {
       const int rr = min(row0 + row, max(tq.rows - 1, 0));
-      const bf16x8* qrow = (const bf16x8*)(a.qptr + (size_t)min(tq.qrow0 + rr, p.q_rows - 1) * kDqk);
+      const u32x4* qrow = (const u32x4*)(a.qptr + (size_t)min(tq.qrow0 + rr, p.q_rows - 1) * kDqk);
+      // part 0-3: features 64 cc + 16 h + 0..7, + 8..15, 64 cc + 32 + 16 h + 0..7, + 8..15
+      auto qword = [&](int cc, int part) { return qrow[8 * cc + 4 * (part >> 1) + 2 * h + (part & 1)]; };
+      float amax = 0.f;
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) q[j] = qrow[4 * (j >> 1) + 2 * h + (j & 1)];
+      for (int cc = 0; cc < NK; ++cc)
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {
+          const u32x4 w = qword(cc, part);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, w[e] << 16)),
+                                     fabsf(__builtin_bit_cast(float, w[e] & 0xFFFF0000u))));
+        }
+      amax = max_xor32(amax);
+      // amax = 1.f * 2^E: 448 * 2^(E - 8) = 1.75 * 2^E covers it unless f > .75
+      const unsigned ab = __builtin_bit_cast(unsigned, amax);
+      int kq = amax > 0.f ? (int)(ab >> 23) - 127 - 8 + ((ab & 0x7FFFFFu) > 0x600000u ? 1 : 0) : 0;
+      kq = min(max(kq, -122), 126);
+      const float down_hi = __builtin_bit_cast(float, (unsigned)(127 - kq) << 23);       // 2^-k
+      const float down_lo = __builtin_bit_cast(float, (unsigned)(127 - kq + 4) << 23);   // 2^(4-k)
+      const float up_hi = __builtin_bit_cast(float, (unsigned)(127 + kq) << 23);         // 2^k
+      sc_hi = 127 + kq;
+      sc_lo = 127 + kq - 4;
+      sched_fence();
+#pragma unroll
+      for (int cc = 0; cc < NK; ++cc) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {
+          const u32x4 x = qword(cc, part);
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            float v[4];
+            v[0] = __builtin_bit_cast(float, x[2 * e2] << 16);
+            v[1] = __builtin_bit_cast(float, x[2 * e2] & 0xFFFF0000u);
+            v[2] = __builtin_bit_cast(float, x[2 * e2 + 1] << 16);
+            v[3] = __builtin_bit_cast(float, x[2 * e2 + 1] & 0xFFFF0000u);
+            const int hi4 = pack_fp8x4(v[0] * down_hi, v[1] * down_hi, v[2] * down_hi, v[3] * down_hi);
+            typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+            const f32x2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi4, false);
+            const f32x2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi4, true);
+            // the remainders are exact: both terms are multiples of 2^(e-7)
+            qhi[cc][2 * part + e2] = hi4;
+            qlo[cc][2 * part + e2] =
+                pack_fp8x4((v[0] - d01[0] * up_hi) * down_lo, (v[1] - d01[1] * up_hi) * down_lo,
+                           (v[2] - d23[0] * up_hi) * down_lo, (v[3] - d23[1] * up_hi) * down_lo);
+          }
+        }
+        sched_fence();   // keeps the second pass's loads from piling up in registers
+      }
     };
 
     TileInfo ti = walk.next(a);   // page of step 0
-    load_q(ti);
+    quant_q(ti);
     lds_barrier();   // the prologue's loads of step 0 have landed
     for (int k = 0; k <= n_steps; ++k) {
       if (k < n_steps) {
         const int par = k & 1;
         const LDS_AS uint8_t* cur = buf(k);
         if (ti.first) {
-          // its query row was loaded before the loop or after the previous
-          // step's QK
+          // another sequence of this unit: its query row
+          if (k > 0) quant_q(ti);
           m_run = -INFINITY;
           l_run = 0.f;
           row_tok = min(row0 + row, max(ti.rows - 1, 0)) / p.num_heads;
-          __builtin_amdgcn_s_waitcnt(kVmcntZero);
         }
         // the partner's reference of the previous step, read ahead of its use
         const float pm = ti.first ? -INFINITY : mpub[((par ^ 1) * 2 + (kh ^ 1)) * 64 + row];
-        // ---- QK GEMM: read m is chunk 2m + h of the lane's key (k-steps 2m, 2m + 1)
+        // ---- QK GEMM: two fp8 MFMAs per k-step, read i is half i % 2 of
+        //      k-step i / 2
         f32x16 sacc = f32x16{};
         {
-          constexpr int NR = NQ / 2;
-          constexpr int D = SO_KD < NR ? SO_KD : NR;
-          auto kaddr = [&](int m) { return cur + k_lane[m & 1] + (m >> 1) * C::kLineGroup; };
+          constexpr int NR = 2 * NK;
+          constexpr int D = 6;   // three k-steps (six 64-cycle MFMAs) ahead
+          auto kread = [&](int i) { return ld128u(cur + k_lane[i & 1] + (i >> 1) * C::kLineGroup); };
           u32x4 kr[D];
 #pragma unroll
-          for (int i = 0; i < D; ++i) kr[i] = *(const LDS_AS u32x4*)kaddr(i);
+          for (int i = 0; i < D; ++i) kr[i] = kread(i);
 #pragma unroll
-          for (int m = 0; m < NR; ++m) {
-            const u32x4 w = kr[m % D];
-            if (m + D < NR) kr[m % D] = *(const LDS_AS u32x4*)kaddr(m + D);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8(w[2 * e], w[2 * e + 1]), q[2 * m + e], sacc, 0,
-                                                              0, 0);
+          for (int cc = 0; cc < NK; ++cc) {
+            const i32x8 kf = cat8(kr[(2 * cc) % D], kr[(2 * cc + 1) % D]);
+            if (2 * cc + D < NR) kr[(2 * cc) % D] = kread(2 * cc + D);
+            if (2 * cc + 1 + D < NR) kr[(2 * cc + 1) % D] = kread(2 * cc + 1 + D);
+            sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qhi[cc], sacc, 0, 0, 0, 127, 0, sc_hi);
+            sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qlo[cc], sacc, 0, 0, 0, 127, 0, sc_lo);
             sched_fence();
           }
         }
-        // the next step starts another sequence of this unit: its query row
-        // now (the registers are free once the MFMAs above have read them)
+        // the record of the next page
         TileInfo nti = ti;
-        if (k + 1 < n_steps) {
-          nti = walk.next(a);   // the next page
-          if (ti.last) load_q(nti);
-        }
+        if (k + 1 < n_steps) nti = walk.next(a);
         // ---- softmax of this wave's keys; the per-token scales past a
         //      page's valid keys repeat the last valid one, so all are finite
         const int step_key0 = ti.t * kPage;
