@@ -430,7 +430,7 @@ static void check_metadata_and_others() {
   CHECK(mla_prefill_quant_fwd(q, qkv, n1, sl, sl, 1, 10, 10, 1, INFINITY, (float*)g_buf[4], (float*)g_buf[5],
                               nullptr) == MLA_ERR_INVALID_ARG);
 
-  // page-id bounds counters: this build has none
+  // page-id bounds counters: a library built without the page-id checks has none
   uint64_t nviol = 7;
   CHECK(mla_debug_page_violations(1, &nviol) == MLA_ERR_UNSUPPORTED);
   CHECK(mla_debug_page_violations(1, nullptr) == MLA_ERR_INVALID_ARG);
