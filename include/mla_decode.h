@@ -179,8 +179,9 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const float* kv_scale, i
  * section, SageAttention2) quantises P to FP8 and multiplies it with FP8 V,
  * dequantising the product once; this entry point does that and also
  * quantises the query rows:
- *   q8 = E4M3(q / sq) per row with sq = max|q_row| / 448 (round to nearest
- *   even); scores from the E4M3 codes of q8 and the cache, times sq, the
+ *   q8 = E4M3(q / sq) per row (round to nearest even) with sq = 2^k, k the
+ *   smallest integer with max|q_row| <= 448 * 2^k (not below -126), so that
+ *   q / sq is exact; scores from the E4M3 codes of q8 and the cache, times sq, the
  *   key's per-token scale and softmax_scale; P'_j = P_j * s_j (s_j the
  *   per-token scale) quantised to E4M3 per (row, 32-key block) with a
  *   power-of-two scale, undone exactly by the MFMA's block scale.
