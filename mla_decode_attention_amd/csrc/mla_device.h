@@ -129,12 +129,6 @@ __device__ __forceinline__ WgCoord wg_coord(int row_blocks) {
   const int l = blockIdx.x, xcd = l & 7, k = l >> 3;
   return WgCoord{(k / row_blocks) * 8 + xcd, k % row_blocks};
 }
-// x, hidden from the optimiser: values derived from it are recomputed where
-// they are used instead of being hoisted out of the tile loop into registers.
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
 
 // The 18 direct-to-LDS loads of one page. Load i of thread t fills slot
 // i*256 + t: line group i/2, key 32(i%2) + t/8, in-line position t%8; the
@@ -439,21 +433,17 @@ __device__ __forceinline__ void wait_tile() {
 }
 
 // ---------------------------------------------------------------------------
-// E4M3 tile layout (fp8 cache): 64-byte line groups of all keys of the tile;
+// E4M3 tile layouts (fp8 cache): 64-byte line groups of all keys of the tile;
 // chunk c (16 codes = features 16c..16c+15) of key k sits in line group c/4
-// at position (c % 4) ^ swz2(k).
+// at position (c % 4) ^ swz(k), a two-bit swizzle of the key.
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(2))) int i32x2;
-__device__ __forceinline__ int swz2(int key) { return ((key >> 3) & 1) | (((key >> 2) & 1) << 1); }
-__device__ __forceinline__ int lds8_byte(int key, int chunk) {
-  return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz2(key)) << 4);
-}
 
 // The fp8 matrix-core kernels' tile: the E4M3 layout with swizzle
 // (k2, k2^k3) (high to low bit), under which both of their operand reads -- 16
 // consecutive keys x 4 chunk pairs (K, 16-byte reads) and 8 key pairs x 2
 // chunks (V^T, transposed 8-byte reads) -- measure free of LDS bank conflicts
-// on gfx950, where the shared fp8 layout's (k2, k3) conflicts on the K reads.
+// on gfx950, where the swizzle (k2, k3) conflicts on the K reads.
 __device__ __forceinline__ int swz2q(int key) { return (((key >> 2) & 1) << 1) | (((key >> 2) ^ (key >> 3)) & 1); }
 __device__ __forceinline__ int lds8q_byte(int key, int chunk) {
   return ((chunk >> 2) * 64 + key) * 64 + (((chunk & 3) ^ swz2q(key)) << 4);
