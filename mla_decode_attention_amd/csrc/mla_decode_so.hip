@@ -63,7 +63,7 @@ namespace so {
 #define SO_KD 8
 #endif
 #ifndef SO_VD
-#define SO_VD 8
+#define SO_VD 4
 #endif
 constexpr int kThreadsSo = 512;
 constexpr int kRowsSo = 64;
